@@ -1,0 +1,148 @@
+"""Thin ctypes binding of libgraft.so (include/graft.h).  Argument marshalling
+only: every function forwards to the C entry point of the same name and raises
+on a nonzero status.  Pointers are plain integers (device addresses, e.g.
+``tensor.data_ptr()``) or None; ``stream`` is a raw hipStream_t handle.
+
+There is no fallback: if the HIP library has not been built this module fails
+loudly at load time.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgraft.so")
+
+GRAFT_OK = 0
+GRAFT_EINVAL = -1
+GRAFT_EUNSUPPORTED = -2
+GRAFT_EDEVICE = -3
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+MODE_TREE = 0
+MODE_TAIL = 1
+LAYOUT = {"compact": 0, "in_place": 1, "chain": 2}
+MAX_ROWS = 64
+MAX_K = 8
+
+EXPORTS = (
+    "graft_prune_select", "graft_template_master", "graft_retrieve_expand",
+    "graft_build_tree_mask", "graft_verify_accept", "graft_update_topk",
+    "graft_workspace_bytes", "graft_status_string",
+)
+
+
+class GraftError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = _LIB.graft_status_string(status).decode() if _LIB is not None else str(status)
+        super().__init__("%s failed: %d (%s)" % (fn, status, msg))
+
+
+class PruneCfg(C.Structure):
+    _fields_ = [("ckpt_layer", C.c_int32 * 3), ("log_thr", C.c_float * 3),
+                ("keep", C.c_int32 * 3), ("tail_thr", C.c_float)]
+
+
+class Template(C.Structure):
+    _fields_ = [("size", C.c_int32), ("parent", C.c_void_p), ("rank", C.c_void_p),
+                ("depth", C.c_void_p)]
+
+
+_LIB = None
+
+
+def load():
+    """Load libgraft.so (raises if it was not built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libgraft.so not found at %s: build it with "
+                          "`python -m hybrid_draft_tree_amd.build` (there is no CPU fallback)" % LIB_PATH)
+    L = C.CDLL(LIB_PATH)
+    P, I, I64, S = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+    L.graft_prune_select.argtypes = [I, I, I, P, P, P, C.POINTER(PruneCfg), P, P, P, P, P]
+    L.graft_template_master.argtypes = [I, I, I, P, P, P]
+    L.graft_retrieve_expand.argtypes = [I, I, I, I, I, P, P, P, P, I, C.POINTER(Template),
+                                        C.POINTER(PruneCfg), P, P, P, I, P]
+    L.graft_build_tree_mask.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P]
+    L.graft_verify_accept.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
+    L.graft_update_topk.argtypes = [I64, I, I, I, P, P, P, P, P, P, P, P, S, P]
+    L.graft_workspace_bytes.argtypes = [I64, I, I, I]
+    L.graft_workspace_bytes.restype = S
+    L.graft_status_string.argtypes = [I]
+    L.graft_status_string.restype = C.c_char_p
+    for name in EXPORTS:
+        if name not in ("graft_workspace_bytes", "graft_status_string"):
+            getattr(L, name).restype = C.c_int
+    _LIB = L
+    return L
+
+
+def _chk(fn, rc):
+    if rc < 0:
+        raise GraftError(fn, rc)
+    return rc
+
+
+def prune_cfg(ckpt_layers, log_thr, keep, tail_thr) -> PruneCfg:
+    c = PruneCfg()
+    for i in range(3):
+        c.ckpt_layer[i] = int(ckpt_layers[i])
+        c.log_thr[i] = float(log_thr[i])
+        c.keep[i] = int(keep[i])
+    c.tail_thr = float(tail_thr)
+    return c
+
+
+def graft_prune_select(B, Nd, mode, d_parent, d_layer, d_score, cfg, stage, n_keep, keep, cum_out, stream):
+    return _chk("graft_prune_select", load().graft_prune_select(
+        B, Nd, mode, d_parent, d_layer, d_score, C.byref(cfg), stage, n_keep, keep, cum_out, stream))
+
+
+def graft_template_master(width, depth, cap):
+    """Returns (parent, rank, depth) host lists of the master template order."""
+    par = (C.c_int32 * max(cap, 1))()
+    rk = (C.c_int32 * max(cap, 1))()
+    dp = (C.c_int32 * max(cap, 1))()
+    n = _chk("graft_template_master", load().graft_template_master(width, depth, cap, par, rk, dp))
+    return list(par[:n]), list(rk[:n]), list(dp[:n])
+
+
+def graft_retrieve_expand(B, V, k, mode, slots, table, root_tok, n_keep, d_tok, Nd, tpl, cfg,
+                          ret_tok, ret_parent, n_ret, r_out, stream):
+    return _chk("graft_retrieve_expand", load().graft_retrieve_expand(
+        B, V, k, mode, slots, table, root_tok, n_keep, d_tok, Nd,
+        C.byref(tpl) if tpl is not None else None, C.byref(cfg) if cfg is not None else None,
+        ret_tok, ret_parent, n_ret, r_out, stream))
+
+
+def graft_build_tree_mask(B, Nd, T1, layout, root_tok, base_pos, d_tok, d_parent, keep, n_keep,
+                          ret_tok, ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, stream):
+    return _chk("graft_build_tree_mask", load().graft_build_tree_mask(
+        B, Nd, T1, layout, root_tok, base_pos, d_tok, d_parent, keep, n_keep, ret_tok, ret_parent,
+        n_ret, r_out, tok, parent, depth, pos_id, anc, stream))
+
+
+def graft_verify_accept(B, T1, V, k, dtype, logits, tok, parent, depth, topk, topk_prob,
+                        accept_len, accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream):
+    return _chk("graft_verify_accept", load().graft_verify_accept(
+        B, T1, V, k, dtype, logits, tok, parent, depth, topk, topk_prob, accept_len, accept_idx,
+        dmax, bonus, base_pos_io, ws, ws_bytes, stream))
+
+
+def graft_update_topk(n_rows, V, k, dtype, logits, topk_in, prob_in, row_tok, table, table_prob,
+                      topk_out, ws, ws_bytes, stream):
+    return _chk("graft_update_topk", load().graft_update_topk(
+        n_rows, V, k, dtype, logits, topk_in, prob_in, row_tok, table, table_prob, topk_out,
+        ws, ws_bytes, stream))
+
+
+def graft_workspace_bytes(n_rows, V, k, dtype):
+    return int(load().graft_workspace_bytes(n_rows, V, k, dtype))
+
+
+def graft_status_string(status):
+    return load().graft_status_string(status).decode()

@@ -1,0 +1,210 @@
+// C ABI of the Graft per-step path (declared in include/graft.h): host-side
+// argument validation, workspace planning and kernel launches.  No call
+// allocates, frees or keeps state; every launch is asynchronous on the
+// caller's stream.
+#include <algorithm>
+#include <vector>
+
+#include "graft.h"
+#include "launchers.hpp"
+
+using namespace graft;
+
+namespace {
+
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? GRAFT_OK : GRAFT_EDEVICE;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// workspace: [top-k partials | softmax stats | top-k rows | top-k probs]
+struct WsLayout {
+    TopkPlan plan;
+    size_t off_stats = 0, off_topk = 0, off_prob = 0, total = 0;
+};
+
+WsLayout ws_layout(int64_t n_rows, int V, int k, int dtype) {
+    WsLayout L;
+    L.plan = plan_topk(n_rows, V, dtype);
+    L.off_stats = align256(L.plan.partial_bytes);
+    L.off_topk = L.off_stats + align256(L.plan.stats_bytes);
+    L.off_prob = L.off_topk + align256((size_t)n_rows * k * sizeof(int32_t));
+    L.total = L.off_prob + align256((size_t)n_rows * k * sizeof(float));
+    return L;
+}
+
+bool dtype_ok(int dtype) { return dtype == GRAFT_DTYPE_F32 || dtype == GRAFT_DTYPE_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char *graft_status_string(int status) {
+    switch (status) {
+        case GRAFT_OK: return "ok";
+        case GRAFT_EINVAL: return "invalid argument (null or misaligned pointer, bad size or shape)";
+        case GRAFT_EUNSUPPORTED: return "unsupported dtype, mode or layout";
+        case GRAFT_EDEVICE: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+size_t graft_workspace_bytes(int64_t n_rows, int V, int k, int dtype) {
+    if (n_rows < 0 || V <= 0 || k < 1 || k > GRAFT_MAX_K || k > V || !dtype_ok(dtype)) return 0;
+    return ws_layout(n_rows, V, k, dtype).total;
+}
+
+int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const int32_t *d_layer,
+                       const float *d_score, const graft_prune_cfg *cfg, int32_t *stage,
+                       int32_t *n_keep, uint8_t *keep, float *cum_out, hipStream_t stream) {
+    if (mode != GRAFT_MODE_TREE && mode != GRAFT_MODE_TAIL) return GRAFT_EUNSUPPORTED;
+    if (B < 0 || Nd < 1 || Nd > GRAFT_MAX_ROWS || !cfg) return GRAFT_EINVAL;
+    if (B == 0) return GRAFT_OK;
+    if (!d_score || !stage || !n_keep || !keep) return GRAFT_EINVAL;
+    if (mode == GRAFT_MODE_TREE) {
+        if (!d_parent || !d_layer) return GRAFT_EINVAL;
+        for (int s = 0; s < 3; ++s)
+            if (cfg->keep[s] < 0 || cfg->keep[s] > Nd) return GRAFT_EINVAL;
+    }
+    launch_prune(B, Nd, mode, d_parent, d_layer, d_score, *cfg, stage, n_keep, keep, cum_out, stream);
+    return launch_status();
+}
+
+int graft_template_master(int width, int depth, int cap, int32_t *parent, int32_t *rank,
+                          int32_t *tdepth) {
+    if (width < 1 || depth < 1 || cap < 0 || !parent || !rank || !tdepth) return GRAFT_EINVAL;
+    // Enumerate (rank j, depth d) chain nodes and order them: root children, the
+    // rank-0 chain, then the rest by (j + d, j).
+    struct Node {
+        int j, d, cls, key;
+    };
+    std::vector<Node> nodes;
+    for (int j = 0; j < width; ++j)
+        for (int d = 1; d <= depth; ++d) {
+            int cls = d == 1 ? 0 : (j == 0 ? 1 : 2);
+            nodes.push_back({j, d, cls, cls == 0 ? j : (cls == 1 ? d : (j + d) * 1024 + j)});
+        }
+    std::stable_sort(nodes.begin(), nodes.end(), [](const Node &a, const Node &b) {
+        return a.cls != b.cls ? a.cls < b.cls : a.key < b.key;
+    });
+    const int n = std::min<int>(cap, (int)nodes.size());
+    std::vector<int> where((size_t)width * (depth + 1), -1);
+    for (int t = 0; t < n; ++t) where[(size_t)nodes[t].j * (depth + 1) + nodes[t].d] = t;
+    for (int t = 0; t < n; ++t) {
+        const Node &x = nodes[t];
+        parent[t] = x.d == 1 ? -1 : where[(size_t)x.j * (depth + 1) + x.d - 1];
+        rank[t] = x.d == 1 ? x.j : 0;
+        tdepth[t] = x.d;
+    }
+    return n;
+}
+
+int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_t *table,
+                          const int32_t *root_tok, const int32_t *n_keep, const int32_t *d_tok,
+                          int Nd, const graft_template *tpl, const graft_prune_cfg *cfg,
+                          int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret, int r_out,
+                          hipStream_t stream) {
+    if (mode != GRAFT_MODE_TREE && mode != GRAFT_MODE_TAIL) return GRAFT_EUNSUPPORTED;
+    if (B < 0 || V < 1 || k < 1 || k > GRAFT_MAX_K || slots < 0 || r_out < 1 ||
+        r_out > GRAFT_MAX_ROWS)
+        return GRAFT_EINVAL;
+    if (B == 0) return GRAFT_OK;
+    if (!table || !root_tok || !n_keep || !ret_tok || !ret_parent || !n_ret) return GRAFT_EINVAL;
+    int tsize = 0;
+    const int32_t *tp = nullptr, *tr = nullptr, *td = nullptr;
+    if (mode == GRAFT_MODE_TREE) {
+        if (!tpl || !cfg || tpl->size < 0 || tpl->size > GRAFT_MAX_ROWS) return GRAFT_EINVAL;
+        if (tpl->size > 0 && (!tpl->parent || !tpl->rank || !tpl->depth)) return GRAFT_EINVAL;
+        if (r_out < tpl->size) return GRAFT_EINVAL;
+        for (int s = 0; s < 3; ++s)
+            if (slots - cfg->keep[s] > tpl->size || slots - cfg->keep[s] < 0) return GRAFT_EINVAL;
+        tsize = tpl->size;
+        tp = tpl->parent;
+        tr = tpl->rank;
+        td = tpl->depth;
+    } else {
+        if (!d_tok || Nd < 1 || Nd > GRAFT_MAX_ROWS || slots > r_out) return GRAFT_EINVAL;
+    }
+    launch_retrieve(B, V, k, mode, slots, table, root_tok, n_keep, d_tok, Nd, tsize, tp, tr, td,
+                    ret_tok, ret_parent, n_ret, r_out, stream);
+    return launch_status();
+}
+
+int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root_tok,
+                          const int32_t *base_pos, const int32_t *d_tok, const int32_t *d_parent,
+                          const uint8_t *keep, const int32_t *n_keep, const int32_t *ret_tok,
+                          const int32_t *ret_parent, const int32_t *n_ret, int r_out, int32_t *tok,
+                          int32_t *parent, int32_t *depth, int32_t *pos_id, uint64_t *anc,
+                          hipStream_t stream) {
+    if (layout != GRAFT_LAYOUT_COMPACT && layout != GRAFT_LAYOUT_IN_PLACE &&
+        layout != GRAFT_LAYOUT_CHAIN)
+        return GRAFT_EUNSUPPORTED;
+    if (B < 0 || Nd < 1 || Nd > GRAFT_MAX_ROWS || T1 < 2 || T1 > GRAFT_MAX_ROWS || r_out < 1 ||
+        r_out > GRAFT_MAX_ROWS)
+        return GRAFT_EINVAL;
+    if (layout == GRAFT_LAYOUT_IN_PLACE && T1 != Nd + 1) return GRAFT_EINVAL;
+    if (B == 0) return GRAFT_OK;
+    if (!root_tok || !base_pos || !d_tok || !keep || !n_keep || !ret_tok || !ret_parent || !n_ret ||
+        !tok || !parent || !depth || !pos_id || !anc)
+        return GRAFT_EINVAL;
+    if (layout != GRAFT_LAYOUT_CHAIN && !d_parent) return GRAFT_EINVAL;
+    if (!aligned(anc, 8)) return GRAFT_EINVAL;
+    launch_flatten(B, Nd, T1, layout, root_tok, base_pos, d_tok, d_parent, keep, n_keep, ret_tok,
+                   ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, stream);
+    return launch_status();
+}
+
+int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logits,
+                        const int32_t *tok, const int32_t *parent, const int32_t *depth,
+                        int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
+                        int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
+    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || k < 1 || k > GRAFT_MAX_K || k > V ||
+        dmax < 0)
+        return GRAFT_EINVAL;
+    if (B == 0) return GRAFT_OK;
+    if (!logits || !tok || !parent || !depth || !topk || !accept_len || !bonus ||
+        (dmax > 0 && !accept_idx) || !ws)
+        return GRAFT_EINVAL;
+    if (!aligned(logits, 16) || !aligned(ws, 256)) return GRAFT_EINVAL;
+    const int64_t n_rows = (int64_t)B * T1;
+    const WsLayout L = ws_layout(n_rows, V, k, dtype);
+    if (ws_bytes < L.total) return GRAFT_EINVAL;
+    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, ws, stream);
+    launch_accept(B, T1, k, topk, tok, parent, depth, accept_len, accept_idx, dmax, bonus,
+                  base_pos_io, stream);
+    return launch_status();
+}
+
+int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logits,
+                      const int32_t *topk_in, const float *prob_in, const int32_t *row_tok,
+                      int32_t *table, float *table_prob, int32_t *topk_out, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
+    if (n_rows < 0 || V < 1 || k < 1 || k > GRAFT_MAX_K || k > V) return GRAFT_EINVAL;
+    if (n_rows == 0) return GRAFT_OK;
+    if (!row_tok || !table || (!logits && !topk_in)) return GRAFT_EINVAL;
+    const int32_t *tk = topk_in;
+    const float *pr = prob_in;
+    if (logits) {
+        if (!ws || !aligned(logits, 16) || !aligned(ws, 256)) return GRAFT_EINVAL;
+        const WsLayout L = ws_layout(n_rows, V, k, dtype);
+        if (ws_bytes < L.total) return GRAFT_EINVAL;
+        int32_t *tk_ws = topk_out ? topk_out : (int32_t *)((char *)ws + L.off_topk);
+        float *pr_ws = table_prob ? (float *)((char *)ws + L.off_prob) : nullptr;
+        launch_topk(L.plan, dtype, logits, k, tk_ws, pr_ws, ws, stream);
+        tk = tk_ws;
+        pr = pr_ws;
+    } else if (table_prob && !prob_in) {
+        return GRAFT_EINVAL;
+    }
+    launch_update(n_rows, V, k, tk, table_prob ? pr : nullptr, row_tok, table, table_prob, stream);
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+"""Device-resident Graft pipeline over the C ABI.
+
+PyTorch provides device memory and the stream; every step of the method runs
+in libgraft.so.  One ``GraftPipeline`` holds, for a batch of B requests:
+
+* the continuation matrix ``table`` int32 [V, k] (every row starts as 0..k-1),
+* the roots (last committed token per request) and their positions,
+* per-step buffers for the draft tree, the hybrid tree and the verification
+  outputs, and one workspace for the row-wise top-k.
+
+A decode step is ``build(draft)`` (prune -> retrieve -> flatten), the target
+forward that scores the flattened rows (outside this library), then
+``verify_update(logits)`` (top-k -> accept -> matrix update).  ``bonus`` is
+written straight into the root buffer and ``base_pos`` is advanced on the
+device, so consecutive steps need no host round trip.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+class GraftPipeline:
+    def __init__(self, *, V, B, k=8, slots=60, mode="tree", layout="compact", dtype="bf16",
+                 n_draft=60, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), keep=(8, 24, 40),
+                 tail_thr=0.5, tpl_width=8, tpl_depth=8, want_prob=False, device="cuda"):
+        L.load()
+        self.V, self.B, self.k = int(V), int(B), int(k)
+        self.mode = L.MODE_TREE if mode == "tree" else L.MODE_TAIL
+        self.layout = L.LAYOUT[layout]
+        self.dtype = L.DTYPE_BF16 if dtype == "bf16" else L.DTYPE_F32
+        self.slots = int(slots)
+        self.Nd = int(n_draft)
+        self.T1 = self.slots + 1
+        self.dmax = self.T1 - 1
+        self.want_prob = bool(want_prob)
+        self.device = torch.device(device)
+        dev = self.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        log_thr = [float(np.float32(math.log(t))) for t in tau]
+        self.cfg = L.prune_cfg(ckpt_layers, log_thr, keep, tail_thr)
+
+        self.table = torch.arange(self.k, **i32).repeat(self.V, 1).contiguous()
+        self.table_prob = torch.zeros(self.V, self.k, dtype=torch.float32, device=dev) if want_prob else None
+        self.roots = torch.zeros(self.B, **i32)
+        self.base_pos = torch.zeros(self.B, **i32)
+
+        B, Nd, T1 = self.B, self.Nd, self.T1
+        self.d_parent = torch.full((B, Nd), -1, **i32)
+        self.d_layer = torch.zeros(B, Nd, **i32)
+        self.d_score = torch.zeros(B, Nd, dtype=torch.float32, device=dev)
+        self.d_tok = torch.zeros(B, Nd, **i32)
+        self.stage = torch.zeros(B, **i32)
+        self.n_keep = torch.zeros(B, **i32)
+        self.keep = torch.zeros(B, Nd, dtype=torch.uint8, device=dev)
+        self.cum = torch.zeros(B, Nd, dtype=torch.float32, device=dev)
+
+        if self.mode == L.MODE_TREE:
+            par, rk, dp = L.graft_template_master(tpl_width, tpl_depth, self.slots - min(keep))
+            self.tpl_parent = torch.tensor(par, **i32)
+            self.tpl_rank = torch.tensor(rk, **i32)
+            self.tpl_depth = torch.tensor(dp, **i32)
+            self.tpl = L.Template(len(par), self.tpl_parent.data_ptr(), self.tpl_rank.data_ptr(),
+                                  self.tpl_depth.data_ptr())
+            self.r_out = max(len(par), 1)
+        else:
+            self.tpl = None
+            self.r_out = self.slots
+        self.ret_tok = torch.zeros(B, self.r_out, **i32)
+        self.ret_parent = torch.zeros(B, self.r_out, **i32)
+        self.n_ret = torch.zeros(B, **i32)
+
+        self.tok = torch.zeros(B, T1, **i32)
+        self.parent = torch.zeros(B, T1, **i32)
+        self.depth = torch.zeros(B, T1, **i32)
+        self.pos_id = torch.zeros(B, T1, **i32)
+        self.anc = torch.zeros(B, T1, dtype=torch.int64, device=dev)
+
+        self.topk = torch.zeros(B, T1, self.k, **i32)
+        self.topk_prob = torch.zeros(B, T1, self.k, dtype=torch.float32, device=dev) if want_prob else None
+        self.accept_len = torch.zeros(B, **i32)
+        self.accept_idx = torch.zeros(B, max(self.dmax, 1), **i32)
+        self.ws_bytes = L.graft_workspace_bytes(B * T1, self.V, self.k, self.dtype)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self._ingest_ws = None
+
+    @classmethod
+    def from_config(cls, cfg, want_prob=False, device="cuda"):
+        return cls(V=cfg.V, B=cfg.B, k=cfg.k,
+                   slots=cfg.tail_block if cfg.mode == "tail" else cfg.slots,
+                   mode=cfg.mode, layout=cfg.layout, dtype=cfg.dtype, n_draft=cfg.n_draft,
+                   ckpt_layers=cfg.ckpt_layers, tau=cfg.tau, keep=cfg.keep, tail_thr=cfg.tail_thr,
+                   tpl_width=cfg.tpl_width, tpl_depth=cfg.tpl_depth, want_prob=want_prob, device=device)
+
+    # ------------------------------------------------------------------ state
+    def stream(self):
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def set_roots(self, roots, base_pos):
+        self.roots.copy_(torch.as_tensor(np.asarray(roots, np.int32)))
+        self.base_pos.copy_(torch.as_tensor(np.asarray(base_pos, np.int32)))
+
+    # ------------------------------------------------------------------ gear 1 + 2 + flatten
+    def load_draft(self, draft):
+        """Copy one step's draft inputs into the device buffers."""
+        if self.mode == L.MODE_TREE:
+            self.d_parent.copy_(torch.as_tensor(np.asarray(draft["parent"], np.int32)))
+            self.d_layer.copy_(torch.as_tensor(np.asarray(draft["layer"], np.int32)))
+            self.d_score.copy_(torch.as_tensor(np.asarray(draft["logp"], np.float32)))
+        else:
+            self.d_score.copy_(torch.as_tensor(np.asarray(draft["conf"], np.float32)))
+        self.d_tok.copy_(torch.as_tensor(np.asarray(draft["tok"], np.int32)))
+
+    def build_device(self):
+        """prune -> retrieve -> flatten on the draft already in the device buffers."""
+        s = self.stream()
+        B, Nd, T1 = self.B, self.Nd, self.T1
+        L.graft_prune_select(B, Nd, self.mode, self.d_parent.data_ptr(), self.d_layer.data_ptr(),
+                             self.d_score.data_ptr(), self.cfg, self.stage.data_ptr(),
+                             self.n_keep.data_ptr(), self.keep.data_ptr(),
+                             self.cum.data_ptr() if self.mode == L.MODE_TREE else None, s)
+        L.graft_retrieve_expand(B, self.V, self.k, self.mode, self.slots, self.table.data_ptr(),
+                                self.roots.data_ptr(), self.n_keep.data_ptr(), self.d_tok.data_ptr(),
+                                Nd, self.tpl, self.cfg if self.mode == L.MODE_TREE else None,
+                                self.ret_tok.data_ptr(), self.ret_parent.data_ptr(),
+                                self.n_ret.data_ptr(), self.r_out, s)
+        L.graft_build_tree_mask(B, Nd, T1, self.layout, self.roots.data_ptr(), self.base_pos.data_ptr(),
+                                self.d_tok.data_ptr(), self.d_parent.data_ptr(), self.keep.data_ptr(),
+                                self.n_keep.data_ptr(), self.ret_tok.data_ptr(),
+                                self.ret_parent.data_ptr(), self.n_ret.data_ptr(), self.r_out,
+                                self.tok.data_ptr(), self.parent.data_ptr(), self.depth.data_ptr(),
+                                self.pos_id.data_ptr(), self.anc.data_ptr(), s)
+
+    def build(self, draft):
+        self.load_draft(draft)
+        self.build_device()
+        out = {"stage": self.stage, "n_keep": self.n_keep, "keep": self.keep, "ret_tok": self.ret_tok,
+               "ret_parent": self.ret_parent, "n_ret": self.n_ret, "tok": self.tok, "parent": self.parent,
+               "depth": self.depth, "pos_id": self.pos_id, "anc": self.anc}
+        if self.mode == L.MODE_TREE:
+            out["cum"] = self.cum
+        return out
+
+    # ------------------------------------------------------------------ verify + update
+    def verify_update_device(self, logits):
+        """top-k -> accept -> matrix update for logits [B*T1, V] on the device."""
+        s = self.stream()
+        B, T1 = self.B, self.T1
+        L.graft_verify_accept(B, T1, self.V, self.k, self.dtype, logits.data_ptr(), self.tok.data_ptr(),
+                              self.parent.data_ptr(), self.depth.data_ptr(), self.topk.data_ptr(),
+                              self.topk_prob.data_ptr() if self.want_prob else None,
+                              self.accept_len.data_ptr(), self.accept_idx.data_ptr(), self.dmax,
+                              self.roots.data_ptr(), self.base_pos.data_ptr(), self.ws.data_ptr(),
+                              self.ws_bytes, s)
+        L.graft_update_topk(B * T1, self.V, self.k, self.dtype, None, self.topk.data_ptr(),
+                            self.topk_prob.data_ptr() if self.want_prob else None, self.tok.data_ptr(),
+                            self.table.data_ptr(), self.table_prob.data_ptr() if self.want_prob else None,
+                            None, None, 0, s)
+
+    def verify_update(self, logits):
+        self._check_logits(logits, self.B * self.T1)
+        self.verify_update_device(logits)
+        out = {"accept_len": self.accept_len, "accept_idx": self.accept_idx, "bonus": self.roots.clone(),
+               "topk": self.topk, "base_pos": self.base_pos}
+        if self.want_prob:
+            out["topk_prob"] = self.topk_prob
+        return out
+
+    # ------------------------------------------------------------------ prompt ingest
+    def ingest_chunk(self, row_tok, logits):
+        """table[row_tok[p]] <- top-k(logits[p]) for the rows in order; returns the
+        chunk's top-k rows (device)."""
+        n = int(logits.shape[0])
+        self._check_logits(logits, n)
+        rt = torch.as_tensor(np.asarray(row_tok, np.int32)).to(self.device)
+        need = L.graft_workspace_bytes(n, self.V, self.k, self.dtype)
+        if self._ingest_ws is None or self._ingest_ws.numel() < need:
+            self._ingest_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        out = torch.empty(n, self.k, dtype=torch.int32, device=self.device)
+        L.graft_update_topk(n, self.V, self.k, self.dtype, logits.data_ptr(), None, None, rt.data_ptr(),
+                            self.table.data_ptr(), self.table_prob.data_ptr() if self.want_prob else None,
+                            out.data_ptr(), self._ingest_ws.data_ptr(), self._ingest_ws.numel(),
+                            self.stream())
+        return out
+
+    def _check_logits(self, logits, n_rows):
+        want = torch.bfloat16 if self.dtype == L.DTYPE_BF16 else torch.float32
+        if logits.dtype != want or not logits.is_contiguous() or logits.device != self.device:
+            raise ValueError("logits must be a contiguous %s tensor on %s" % (want, self.device))
+        if logits.numel() != n_rows * self.V:
+            raise ValueError("logits must hold %d rows of %d" % (n_rows, self.V))

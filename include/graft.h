@@ -1,0 +1,198 @@
+/*
+ * graft.h -- C ABI of the Graft per-step hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Graft ("精简草稿，增强检索：投机解码的混合树构建", arXiv 2605.20104) prunes a
+ * speculative draft tree at confidence checkpoints, fills the freed
+ * verification slots with tokens retrieved from a GPU-resident continuation
+ * matrix (V rows x k successor ids), verifies the hybrid tree greedily against
+ * the target and then writes the target's top-k at every verified position
+ * back into the matrix.  Section numbers below refer to the Chinese news
+ * write-up of the paper: section 二 ("three gears") describes every step,
+ * section 四 the batched static-slot serving variant and long context,
+ * section 七 the DFlash TAIL variant.
+ *
+ * Conventions (all entry points):
+ *  - Array arguments are DEVICE pointers owned by the caller unless marked
+ *    "host".  The library never allocates, frees or retains them.  Scratch
+ *    comes from a caller workspace sized by graft_workspace_bytes().
+ *  - Work is enqueued asynchronously on `stream`; nothing is synchronised.
+ *    Calls on different streams touching disjoint buffers are independent.
+ *  - Return value: GRAFT_OK, or a negative status.  Arguments are validated
+ *    on the host before anything is enqueued; on an error nothing is
+ *    enqueued.  GRAFT_EDEVICE reports a launch failure (hipGetLastError).
+ *  - Device-side data preconditions (token ids in [0, V), parents before
+ *    children, log-probs finite) are the caller's; no NaN is handled.
+ *  - Row-major layouts throughout; "[B, T1]" means B*T1 contiguous elements.
+ *  - The continuation matrix is int32 [V, k]; only graft_update_topk writes it.
+ */
+#ifndef GRAFT_H
+#define GRAFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GRAFT_OK 0
+#define GRAFT_EINVAL (-1)       /* null/misaligned pointer, bad size or shape */
+#define GRAFT_EUNSUPPORTED (-2) /* unknown dtype, mode or layout */
+#define GRAFT_EDEVICE (-3)      /* the HIP runtime reported a launch error */
+
+#define GRAFT_DTYPE_F32 0
+#define GRAFT_DTYPE_BF16 1
+
+#define GRAFT_MODE_TREE 0 /* autoregressive draft tree (section 二) */
+#define GRAFT_MODE_TAIL 1 /* 16-token DFlash block, tail replaced (section 七) */
+
+#define GRAFT_LAYOUT_COMPACT 0  /* root, kept draft nodes ascending, retrieval in template order */
+#define GRAFT_LAYOUT_IN_PLACE 1 /* static slots: draft slot i -> row i+1, vacated rows take retrieval */
+#define GRAFT_LAYOUT_CHAIN 2    /* TAIL: root, kept block prefix, retrieval chain */
+
+#define GRAFT_MAX_ROWS 64 /* rows per request (root + candidate slots); one wavefront */
+#define GRAFT_MAX_K 8     /* successors per matrix row */
+
+/* Prune configuration (host POD).  Section 二, gear 1: checkpoints at draft
+ * depths 0, 1 and 5 compare the best cumulative path confidence with a
+ * calibrated threshold; a prune there keeps 8, 24 or 40 draft nodes of the
+ * 60-slot budget.  log_thr[s] = (float)ln(tau_s).  tail_thr: the TAIL
+ * confidence cut (0.5 in section 七). */
+typedef struct graft_prune_cfg {
+    int32_t ckpt_layer[3]; /* draft layers of the checkpoints; layer 0 = the root's children */
+    float log_thr[3];      /* fire when best cumulative log-confidence < log_thr[s] */
+    int32_t keep[3];       /* draft nodes kept when checkpoint s fires */
+    float tail_thr;        /* TAIL: keep the longest prefix with confidence >= tail_thr */
+} graft_prune_cfg;
+
+/* Retrieval template (host struct holding DEVICE arrays of `size` entries), in
+ * the master order of graft_template_master(); a budget of R retrieval slots
+ * uses entries 0..R-1.  parent[t] < t is a template index, -1 for the root. */
+typedef struct graft_template {
+    int32_t size;
+    const int32_t *parent; /* device [size] */
+    const int32_t *rank;   /* device [size]: successor rank in the parent's matrix row, < k */
+    const int32_t *depth;  /* device [size]: 1 for children of the root */
+} graft_template;
+
+/* graft_prune_select -- section 二, gear 1 (TREE); section 七 (TAIL).
+ * TREE: per request b, cum[i] = cum[parent[i]] + score[i] in fp32 (score =
+ *   draft log-probability, root = 0).  Checkpoint s fires when layer
+ *   ckpt_layer[s] is non-empty, layers <= ckpt_layer[s] hold at least keep[s]
+ *   nodes, and the maximum cum over that layer is < log_thr[s]; the first s
+ *   that fires is the stage (3 = none).  Kept: the keep[s] nodes of layers
+ *   <= ckpt_layer[s] with the largest cum (ties -> lower index); stage 3 keeps
+ *   all Nd nodes.
+ * TAIL: score = block confidence; n_keep = the longest prefix with
+ *   score >= tail_thr; stage = 0 when the block is cut, else 3.
+ *   d_parent/d_layer are ignored and may be NULL.
+ * d_parent, d_layer: int32 [B, Nd], parent[i] in [-1, i).  d_score: fp32 [B, Nd].
+ * cfg: host.  Outputs: stage int32 [B], n_keep int32 [B], keep uint8 [B, Nd]
+ * (1 = kept), cum_out fp32 [B, Nd] (nullable; TREE only).
+ * Requires 1 <= Nd <= 64, B >= 0 (B == 0 enqueues nothing). */
+int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const int32_t *d_layer,
+                       const float *d_score, const graft_prune_cfg *cfg, int32_t *stage,
+                       int32_t *n_keep, uint8_t *keep, float *cum_out, hipStream_t stream);
+
+/* graft_template_master -- host only; section 二's stage-adaptive asymmetric
+ * template and section 五's depth/width optimum (8, 8).  Writes the master
+ * order into HOST arrays of capacity `cap`: the `width` children of the root
+ * (rank j), then the rank-0 chain under rank 0 down to `depth`, then the other
+ * chain nodes (rank j >= 1 continued by rank-0 successors to depth d >= 2) by
+ * increasing j + d, ties by increasing j.  Budget R takes the first R entries,
+ * so higher-ranked successors get longer chains.  Returns the node count
+ * (min(cap, width*depth)) or GRAFT_EINVAL. */
+int graft_template_master(int width, int depth, int cap, int32_t *parent, int32_t *rank,
+                          int32_t *tdepth);
+
+/* graft_retrieve_expand -- section 二, gear 2: one matrix row lookup per node,
+ * GPU only.
+ * TREE: R_b = slots - n_keep[b] retrieval nodes (0 <= R_b <= tpl->size); node
+ *   t reads ret_tok[t] = table[src][rank[t]] with src = root_tok[b] for root
+ *   children, else ret_tok[parent[t]].  cfg (host) is used to check
+ *   slots - keep[s] <= tpl->size for every stage.  d_tok may be NULL.
+ * TAIL: R_b = slots - n_keep[b]; a chain x <- table[x][0] of R_b steps from
+ *   the last kept block token d_tok[b, n_keep-1] (root_tok[b] when n_keep is
+ *   0); ret_parent[t] = t-1.  tpl and cfg may be NULL.
+ * table int32 [V, k] (1 <= k <= 8); root_tok, n_keep int32 [B]; d_tok int32
+ * [B, Nd].  Outputs: ret_tok, ret_parent int32 [B, r_out] (-1 beyond R_b),
+ * n_ret int32 [B].  Requires r_out <= 64 and r_out >= the largest R_b. */
+int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_t *table,
+                          const int32_t *root_tok, const int32_t *n_keep, const int32_t *d_tok,
+                          int Nd, const graft_template *tpl, const graft_prune_cfg *cfg,
+                          int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret, int r_out,
+                          hipStream_t stream);
+
+/* graft_build_tree_mask -- section 二, gear 3: flatten the hybrid tree into
+ * one sequence, rebuild tree position ids and the attention mask.  Row 0 is
+ * the root.  Layouts: GRAFT_LAYOUT_COMPACT, GRAFT_LAYOUT_IN_PLACE (section
+ * 四: fixed slots per request, low-confidence draft slots replaced in place;
+ * needs T1 == Nd + 1), GRAFT_LAYOUT_CHAIN (TAIL).  Every layout is
+ * topological (parent row < child row).
+ * Inputs: root_tok, base_pos int32 [B]; d_tok, d_parent int32 [B, Nd];
+ * keep uint8 [B, Nd]; n_keep int32 [B]; ret_tok, ret_parent int32 [B, r_out];
+ * n_ret int32 [B].  n_keep + n_ret must equal T1 - 1 per request.
+ * Outputs [B, T1]: tok, parent (-1 at the root), depth, pos_id = base_pos +
+ * depth (int32), anc (uint64: bit g set iff row g is an ancestor of the row or
+ * the row itself).  Requires 2 <= T1 <= 64, Nd <= 64, r_out <= 64. */
+int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root_tok,
+                          const int32_t *base_pos, const int32_t *d_tok, const int32_t *d_parent,
+                          const uint8_t *keep, const int32_t *n_keep, const int32_t *ret_tok,
+                          const int32_t *ret_parent, const int32_t *n_ret, int r_out, int32_t *tok,
+                          int32_t *parent, int32_t *depth, int32_t *pos_id, uint64_t *anc,
+                          hipStream_t stream);
+
+/* graft_verify_accept -- section 二, gear 3: strict greedy verification.
+ * Row-wise top-k of logits [B, T1, V] (value descending, ties -> lower id,
+ * -0 == +0; top-k of the softmax equals top-k of the logits), g = column 0.
+ * A row is accepted iff every row on its path from the root (root excluded)
+ * carries the token g of its parent row; the deepest accepted row wins, ties
+ * -> lowest row.  Outputs: topk int32 [B, T1, k]; topk_prob fp32 [B, T1, k]
+ * (nullable: softmax probability of each top-k id); accept_len int32 [B]
+ * (candidate tokens accepted, root excluded); accept_idx int32 [B, dmax]
+ * (rows of the accepted path from depth 1, -1 padded); bonus int32 [B] (g at
+ * the accepted row: the next root; `bonus` may alias the root buffer of the
+ * next step); base_pos_io int32 [B] (nullable; += accept_len + 1).
+ * tok, parent, depth: int32 [B, T1] from graft_build_tree_mask.  logits must
+ * be 16-byte aligned.  ws: device workspace of at least
+ * graft_workspace_bytes(B*T1, V, k, dtype) bytes.
+ * Requires 1 <= T1 <= 64, 1 <= k <= 8, k <= V, dmax >= 0. */
+int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logits,
+                        const int32_t *tok, const int32_t *parent, const int32_t *depth,
+                        int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
+                        int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* graft_update_topk -- section 二 gear 3 and section 六: online update of the
+ * continuation matrix.  For every verified row P (accepted or rejected), in
+ * increasing P, table[row_tok[P]] <- the row's top-k (the whole row is
+ * overwritten); on a collision the highest P wins.  Either logits [n_rows, V]
+ * (prompt ingest, section 四: the top-k is computed here) or topk_in int32
+ * [n_rows, k] (the top-k graft_verify_accept already produced, so the logits
+ * are read once per step) must be given; logits wins if both are.
+ * table_prob fp32 [V, k] (nullable) receives the probabilities: from the
+ * logits, or from prob_in fp32 [n_rows, k] (required then with topk_in).
+ * row_tok int32 [n_rows].  topk_out int32 [n_rows, k] (nullable) receives the
+ * top-k computed from `logits` (e.g. the last prompt row's greedy token is the
+ * first decode root); ignored with topk_in.  ws as for graft_verify_accept
+ * with n_rows rows.  Requires n_rows >= 0, 1 <= k <= 8. */
+int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logits,
+                      const int32_t *topk_in, const float *prob_in, const int32_t *row_tok,
+                      int32_t *table, float *table_prob, int32_t *topk_out, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by graft_verify_accept / graft_update_topk for
+ * n_rows rows of V logits (0 on invalid sizes).  The workspace needs no
+ * initialisation and holds nothing between calls. */
+size_t graft_workspace_bytes(int64_t n_rows, int V, int k, int dtype);
+
+/* Static description of a status code. */
+const char *graft_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRAFT_H */

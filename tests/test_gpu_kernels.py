@@ -1,0 +1,429 @@
+"""GPU parity of each C-ABI entry point against the CPU oracle, element by
+element, on seeded inputs plus adversarial ones (ties, signed zeros, all-equal
+rows, negative-only rows, ragged and tiny vocabularies, every prune stage,
+maximal update collisions).  Integers and indices must match bit for bit;
+probabilities within 1e-5 relative of the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from hybrid_draft_tree_amd import _lib as L  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from synth import generators as G  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _s():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _t(a, dtype=None):
+    return torch.as_tensor(np.ascontiguousarray(a)).to(DEV) if dtype is None else \
+        torch.as_tensor(np.ascontiguousarray(a)).to(DEV, dtype)
+
+
+def gpu_topk(rows, k, dtype, want_prob=False):
+    """Top-k through graft_update_topk (logits given, topk_out set)."""
+    n, V = rows.shape
+    if dtype == "bf16":
+        lg = _t(rows.view(np.int16)).view(torch.bfloat16)
+        dt = L.DTYPE_BF16
+    else:
+        lg = _t(rows.view(np.float32))
+        dt = L.DTYPE_F32
+    out = torch.full((n, k), -7, dtype=torch.int32, device=DEV)
+    table = torch.zeros(max(V, 1), k, dtype=torch.int32, device=DEV)
+    tprob = torch.zeros(max(V, 1), k, dtype=torch.float32, device=DEV) if want_prob else None
+    row_tok = torch.arange(n, dtype=torch.int32, device=DEV) % V
+    wsb = L.graft_workspace_bytes(n, V, k, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    L.graft_update_topk(n, V, k, dt, lg.data_ptr(), None, None, row_tok.data_ptr(), table.data_ptr(),
+                        tprob.data_ptr() if want_prob else None, out.data_ptr(), ws.data_ptr(), wsb, _s())
+    torch.cuda.synchronize()
+    res = out.cpu().numpy()
+    if want_prob:
+        # the last writer of table row x is the highest row with row_tok == x
+        return res, tprob.cpu().numpy(), table.cpu().numpy()
+    return res
+
+
+def _bf16(z):
+    return G.f32_to_bf16_bits(np.asarray(z, np.float32)).reshape(np.shape(z))
+
+
+def _rows_suite(rng, n, V):
+    z = rng.standard_normal((n, V)).astype(np.float32)
+    suite = {"normal": _bf16(z)}
+    suite["quantised_ties"] = _bf16(np.round(z * 2) / 2)
+    eq = np.full((n, V), 0x3F80, np.uint16)
+    suite["all_equal"] = eq
+    neg = _bf16(-np.abs(z) - 0.25)
+    suite["negative_only"] = neg
+    sz = _bf16(np.round(z))
+    zeros = sz == 0
+    sz[zeros & (rng.random((n, V)) < 0.5)] = 0x8000
+    suite["signed_zeros"] = sz
+    asc = _bf16(np.tile(np.linspace(-3, 3, V, dtype=np.float32), (n, 1)))
+    suite["ascending"] = asc
+    suite["descending"] = asc[:, ::-1].copy()
+    bump = _bf16(np.clip(z, -4, 4))
+    cols = rng.integers(0, V, size=n)
+    bump[np.arange(n), cols] = _bf16(np.full(n, 6.0))
+    suite["bump"] = bump
+    return suite
+
+
+@pytest.mark.parametrize("V", [151936, 32000, 1001, 4097, 9, 8, 15])
+def test_topk_bf16_parity(V):
+    rng = np.random.default_rng(V)
+    n = 24 if V > 10000 else 40
+    for name, rows in _rows_suite(rng, n, V).items():
+        got = gpu_topk(rows, 8, "bf16")
+        want = O.topk(rows, 8, "bf16")
+        assert (got == want).all(), (name, V, np.nonzero((got != want).any(1))[0][:5])
+
+
+@pytest.mark.parametrize("V,k", [(32000, 8), (1003, 8), (5, 5), (64, 3), (128256, 1)])
+def test_topk_f32_parity(V, k):
+    rng = np.random.default_rng(V + k)
+    z = rng.standard_normal((20, V)).astype(np.float32)
+    z[1] = np.round(z[1])
+    z[2] = 0.0
+    z[3, ::3] = -0.0
+    z[4] = -np.abs(z[4]) - 1
+    z[5] = np.float32(1e-40) * np.sign(z[5])        # subnormals
+    z[6, :] = -np.inf
+    z[6, V // 2] = -3.0
+    got = gpu_topk(z, k, "f32")
+    want = O.topk(z, k, "f32")
+    assert (got == want).all(), np.nonzero((got != want).any(1))[0]
+
+
+def test_topk_prob_parity():
+    rng = np.random.default_rng(3)
+    V = 151936
+    z = (rng.standard_normal((12, V)) * 2.0).astype(np.float32)
+    z[0] = 0.0
+    rows = _bf16(z)
+    tk, tprob, table = gpu_topk(rows, 8, "bf16", want_prob=True)
+    want_tk, want_p = O.topk(rows, 8, "bf16", want_prob=True)
+    assert (tk == want_tk).all()
+    # rows wrote table rows 0..11 (row_tok = row index)
+    np.testing.assert_allclose(tprob[:12], want_p, rtol=1e-5, atol=0)
+
+
+def test_topk_many_rows_and_ragged_split():
+    # many rows, V chosen so the last range of a row is ragged
+    rng = np.random.default_rng(4)
+    V = 50_003
+    rows = _bf16(rng.standard_normal((300, V)).astype(np.float32))
+    got = gpu_topk(rows, 8, "bf16")
+    assert (got == O.topk(rows, 8, "bf16")).all()
+
+
+# ----------------------------------------------------------------------------- prune / retrieve / flatten
+
+TOPO = G.static_tree()
+
+
+def _random_logp(rng, B):
+    par, lay, _ = TOPO
+    out = []
+    for b in range(B):
+        mode = b % 5
+        lp = np.log(rng.dirichlet(np.ones(8), size=60).max(1)).astype(np.float32)
+        if mode == 0:
+            lp[lay == 0] -= 1.5
+        elif mode == 1:
+            lp[lay == 1] -= 1.2
+        elif mode == 2:
+            lp[lay == 5] -= 3.0
+        elif mode == 3:
+            lp[:] = 0.0
+        out.append(lp)
+    return np.array(out, np.float32)
+
+
+def gpu_prune(parent, layer, score, mode, cfg_t):
+    B, Nd = score.shape
+    cfg = L.prune_cfg(cfg_t["ckpt"], [float(np.float32(math.log(t))) for t in cfg_t["tau"]],
+                      cfg_t["keep"], cfg_t["tail_thr"])
+    dp, dl, ds = _t(parent, torch.int32), _t(layer, torch.int32), _t(score, torch.float32)
+    st = torch.zeros(B, dtype=torch.int32, device=DEV)
+    nk = torch.zeros(B, dtype=torch.int32, device=DEV)
+    kp = torch.zeros(B, Nd, dtype=torch.uint8, device=DEV)
+    cum = torch.zeros(B, Nd, dtype=torch.float32, device=DEV)
+    L.graft_prune_select(B, Nd, mode, dp.data_ptr(), dl.data_ptr(), ds.data_ptr(), cfg, st.data_ptr(),
+                         nk.data_ptr(), kp.data_ptr(), cum.data_ptr() if mode == L.MODE_TREE else None, _s())
+    torch.cuda.synchronize()
+    return st.cpu().numpy(), nk.cpu().numpy(), kp.cpu().numpy(), cum.cpu().numpy()
+
+
+CFG = {"ckpt": (0, 1, 5), "tau": (0.3, 0.2, 0.1), "keep": (8, 24, 40), "tail_thr": 0.5}
+
+
+def test_prune_tree_parity():
+    rng = np.random.default_rng(10)
+    B = 67
+    par, lay, _ = TOPO
+    lp = _random_logp(rng, B)
+    # exact ties at the keep boundary and thresholds hit exactly
+    lp[5, :] = np.float32(math.log(0.7))
+    lp[5, lay == 5] = np.float32(math.log(0.05))
+    lp[6, lay == 0] = np.float32(math.log(0.3))
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    st, nk, kp, cum = gpu_prune(P, Ly, lp, L.MODE_TREE, CFG)
+    o = O.prune_tree(P, Ly, lp, want_cum=True)
+    np.testing.assert_array_equal(st, o["stage"])
+    np.testing.assert_array_equal(nk, o["n_keep"])
+    np.testing.assert_array_equal(kp, o["keep"])
+    np.testing.assert_array_equal(cum.view(np.uint32), o["cum"].view(np.uint32))
+    assert set(st.tolist()) == {0, 1, 2, 3}
+
+
+def test_prune_small_trees_and_unreached_checkpoints():
+    rng = np.random.default_rng(11)
+    par = np.array([-1, -1, 0, 0, 1, 2, 2, 3], np.int32)
+    lay = np.array([0, 0, 1, 1, 1, 2, 2, 2], np.int32)
+    B = 30
+    lp = np.log(rng.uniform(0.01, 1.0, size=(B, 8))).astype(np.float32)
+    cfg = dict(CFG, keep=(2, 5, 6))
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    st, nk, kp, cum = gpu_prune(P, Ly, lp, L.MODE_TREE, cfg)
+    o = O.prune_tree(P, Ly, lp, cfg["ckpt"], cfg["tau"], cfg["keep"], want_cum=True)
+    np.testing.assert_array_equal(st, o["stage"])
+    np.testing.assert_array_equal(kp, o["keep"])
+    np.testing.assert_array_equal(nk, o["n_keep"])
+
+
+def test_prune_tail_parity():
+    rng = np.random.default_rng(12)
+    B = 40
+    conf = np.sort(rng.beta(4, 2, size=(B, 16)), axis=1)[:, ::-1].astype(np.float32)
+    conf[0] = 0.9
+    conf[1] = 0.1
+    conf[2] = 0.5
+    conf[3, :] = np.float32(0.5) - np.float32(1e-7)
+    conf[4] = rng.random(16).astype(np.float32)       # not monotone: prefix rule still applies
+    st, nk, kp, _ = gpu_prune(np.zeros((B, 16), np.int32), np.zeros((B, 16), np.int32), conf, L.MODE_TAIL, CFG)
+    o = O.prune_tail(conf, 0.5)
+    np.testing.assert_array_equal(st, o["stage"])
+    np.testing.assert_array_equal(nk, o["n_keep"])
+    np.testing.assert_array_equal(kp, o["keep"])
+
+
+def _tpl_dev(R):
+    par, rk, dp = L.graft_template_master(8, 8, R)
+    tp, tr, td = (_t(np.array(x, np.int32)) for x in (par, rk, dp))
+    return L.Template(len(par), tp.data_ptr(), tr.data_ptr(), td.data_ptr()), (tp, tr, td), len(par)
+
+
+def gpu_retrieve_tree(table, roots, n_keep, slots=60, R=52, V=None):
+    B = len(roots)
+    V = table.shape[0] if V is None else V
+    tpl, keepalive, r_out = _tpl_dev(R)
+    cfg = L.prune_cfg(CFG["ckpt"], [-1.0] * 3, CFG["keep"], 0.5)
+    tb, rt, nk = _t(table, torch.int32), _t(roots, torch.int32), _t(n_keep, torch.int32)
+    ret_tok = torch.zeros(B, r_out, dtype=torch.int32, device=DEV)
+    ret_par = torch.zeros(B, r_out, dtype=torch.int32, device=DEV)
+    n_ret = torch.zeros(B, dtype=torch.int32, device=DEV)
+    L.graft_retrieve_expand(B, V, table.shape[1], L.MODE_TREE, slots, tb.data_ptr(), rt.data_ptr(),
+                            nk.data_ptr(), None, 60, tpl, cfg, ret_tok.data_ptr(), ret_par.data_ptr(),
+                            n_ret.data_ptr(), r_out, _s())
+    torch.cuda.synchronize()
+    return ret_tok.cpu().numpy(), ret_par.cpu().numpy(), n_ret.cpu().numpy()
+
+
+def test_retrieve_tree_parity():
+    rng = np.random.default_rng(13)
+    V = 151936
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    B = 37
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    n_keep = rng.choice([8, 24, 40, 60], size=B).astype(np.int32)
+    rt, rp, nr = gpu_retrieve_tree(table, roots, n_keep)
+    o = O.retrieve_tree(table, roots, n_keep, 60, O.template(8, 8, 52))
+    np.testing.assert_array_equal(nr, o["n_ret"])
+    np.testing.assert_array_equal(rt, o["ret_tok"])
+    np.testing.assert_array_equal(rp, o["ret_parent"])
+
+
+def test_retrieve_tail_parity():
+    rng = np.random.default_rng(14)
+    V = 151936
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    B = 33
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    d_tok = rng.integers(0, V, size=(B, 16)).astype(np.int32)
+    n_keep = rng.integers(0, 17, size=B).astype(np.int32)
+    n_keep[:3] = [0, 16, 1]
+    tb, r, nk, dt = (_t(x, torch.int32) for x in (table, roots, n_keep, d_tok))
+    ret_tok = torch.zeros(B, 16, dtype=torch.int32, device=DEV)
+    ret_par = torch.zeros(B, 16, dtype=torch.int32, device=DEV)
+    n_ret = torch.zeros(B, dtype=torch.int32, device=DEV)
+    L.graft_retrieve_expand(B, V, 8, L.MODE_TAIL, 16, tb.data_ptr(), r.data_ptr(), nk.data_ptr(), dt.data_ptr(),
+                            16, None, None, ret_tok.data_ptr(), ret_par.data_ptr(), n_ret.data_ptr(), 16, _s())
+    torch.cuda.synchronize()
+    o = O.retrieve_tail(table, roots, d_tok, n_keep)
+    np.testing.assert_array_equal(n_ret.cpu().numpy(), o["n_ret"])
+    np.testing.assert_array_equal(ret_tok.cpu().numpy(), o["ret_tok"])
+    np.testing.assert_array_equal(ret_par.cpu().numpy(), o["ret_parent"])
+
+
+def gpu_flatten(layout, T1, roots, base, d_tok, d_parent, keep, n_keep, ret):
+    B, Nd = d_tok.shape
+    r_out = ret["ret_tok"].shape[1]
+    args = [_t(x, torch.int32) for x in (roots, base, d_tok, d_parent)]
+    kp = _t(keep, torch.uint8)
+    nk = _t(n_keep, torch.int32)
+    rt, rp, nr = (_t(ret[k], torch.int32) for k in ("ret_tok", "ret_parent", "n_ret"))
+    outs = [torch.zeros(B, T1, dtype=torch.int32, device=DEV) for _ in range(4)]
+    anc = torch.zeros(B, T1, dtype=torch.int64, device=DEV)
+    L.graft_build_tree_mask(B, Nd, T1, L.LAYOUT[layout], args[0].data_ptr(), args[1].data_ptr(),
+                            args[2].data_ptr(), args[3].data_ptr(), kp.data_ptr(), nk.data_ptr(),
+                            rt.data_ptr(), rp.data_ptr(), nr.data_ptr(), r_out,
+                            *[o.data_ptr() for o in outs], anc.data_ptr(), _s())
+    torch.cuda.synchronize()
+    res = [o.cpu().numpy() for o in outs]
+    return {"tok": res[0], "parent": res[1], "depth": res[2], "pos_id": res[3],
+            "anc": anc.cpu().numpy().view(np.uint64)}
+
+
+@pytest.mark.parametrize("layout", ["compact", "in_place"])
+def test_flatten_tree_parity(layout):
+    rng = np.random.default_rng(15)
+    B = 45
+    V = 5000
+    par, lay, _ = TOPO
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    lp = _random_logp(rng, B)
+    pr = O.prune_tree(P, Ly, lp)
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, O.template(8, 8, 52))
+    d_tok = rng.integers(0, V, size=(B, 60)).astype(np.int32)
+    base = rng.integers(0, 100000, size=B).astype(np.int32)
+    got = gpu_flatten(layout, 61, roots, base, d_tok, P, pr["keep"], pr["n_keep"], ret)
+    want = O.flatten(layout, 61, roots, base, d_tok, P, pr["keep"], pr["n_keep"], ret)
+    for key in ("tok", "parent", "depth", "pos_id", "anc"):
+        np.testing.assert_array_equal(got[key], want[key], err_msg=key)
+
+
+def test_flatten_chain_parity():
+    rng = np.random.default_rng(16)
+    B = 30
+    V = 1000
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    d_tok = rng.integers(0, V, size=(B, 16)).astype(np.int32)
+    conf = rng.random((B, 16)).astype(np.float32)
+    conf[0] = 0.9
+    conf[1] = 0.1
+    pr = O.prune_tail(conf, 0.5)
+    ret = O.retrieve_tail(table, roots, d_tok, pr["n_keep"])
+    base = rng.integers(0, 1000, size=B).astype(np.int32)
+    dpar = np.tile(np.arange(-1, 15, dtype=np.int32), (B, 1))
+    got = gpu_flatten("chain", 17, roots, base, d_tok, dpar, pr["keep"], pr["n_keep"], ret)
+    want = O.flatten("chain", 17, roots, base, d_tok, dpar, pr["keep"], pr["n_keep"], ret)
+    for key in ("tok", "parent", "depth", "pos_id", "anc"):
+        np.testing.assert_array_equal(got[key], want[key], err_msg=key)
+
+
+# ----------------------------------------------------------------------------- verify / update
+
+def gpu_verify(rows, tok, parent, depth, k=8, dtype="bf16", want_prob=False, base=None):
+    B, T1 = tok.shape
+    V = rows.shape[-1]
+    lg = _t(rows.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else _t(rows.view(np.float32))
+    dt = L.DTYPE_BF16 if dtype == "bf16" else L.DTYPE_F32
+    tk = torch.zeros(B, T1, k, dtype=torch.int32, device=DEV)
+    pr = torch.zeros(B, T1, k, dtype=torch.float32, device=DEV) if want_prob else None
+    al = torch.zeros(B, dtype=torch.int32, device=DEV)
+    ai = torch.zeros(B, T1 - 1, dtype=torch.int32, device=DEV)
+    bo = torch.zeros(B, dtype=torch.int32, device=DEV)
+    bp = _t(base if base is not None else np.zeros(B, np.int32), torch.int32)
+    t_, p_, d_ = (_t(x, torch.int32) for x in (tok, parent, depth))
+    wsb = L.graft_workspace_bytes(B * T1, V, k, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    L.graft_verify_accept(B, T1, V, k, dt, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
+                          tk.data_ptr(), pr.data_ptr() if want_prob else None, al.data_ptr(), ai.data_ptr(),
+                          T1 - 1, bo.data_ptr(), bp.data_ptr(), ws.data_ptr(), wsb, _s())
+    torch.cuda.synchronize()
+    out = {"topk": tk.cpu().numpy(), "accept_len": al.cpu().numpy(), "accept_idx": ai.cpu().numpy(),
+           "bonus": bo.cpu().numpy(), "base_pos": bp.cpu().numpy()}
+    if want_prob:
+        out["topk_prob"] = pr.cpu().numpy()
+    return out
+
+
+def _random_flat_trees(rng, B, T1, V):
+    tok = rng.integers(0, V, size=(B, T1)).astype(np.int32)
+    par = np.zeros((B, T1), np.int32)
+    for b in range(B):
+        par[b, 0] = -1
+        for f in range(1, T1):
+            par[b, f] = rng.integers(max(0, f - 6), f)
+    dep = np.zeros((B, T1), np.int32)
+    for b in range(B):
+        for f in range(1, T1):
+            dep[b, f] = dep[b, par[b, f]] + 1
+    return tok, par, dep
+
+
+@pytest.mark.parametrize("T1,V", [(61, 5), (61, 3), (17, 4), (64, 2), (1, 7), (2, 3)])
+def test_verify_accept_parity(T1, V):
+    rng = np.random.default_rng(T1 * 100 + V)
+    B = 29
+    tok, par, dep = _random_flat_trees(rng, B, T1, V)
+    rows = _bf16(rng.standard_normal((B, T1, V)).astype(np.float32))
+    base = rng.integers(0, 1000, size=B).astype(np.int32)
+    got = gpu_verify(rows, tok, par, dep, k=min(8, V), base=base)
+    want_tk = O.topk(rows.reshape(B * T1, V), min(8, V), "bf16").reshape(B, T1, -1)
+    np.testing.assert_array_equal(got["topk"], want_tk)
+    acc = O.accept(tok, par, want_tk[:, :, 0], max(T1 - 1, 0) if T1 > 1 else 0)
+    np.testing.assert_array_equal(got["accept_len"], acc["accept_len"])
+    np.testing.assert_array_equal(got["bonus"], acc["bonus"])
+    if T1 > 1:
+        np.testing.assert_array_equal(got["accept_idx"], acc["accept_idx"])
+    np.testing.assert_array_equal(got["base_pos"], base + acc["accept_len"] + 1)
+    assert got["accept_len"].max() > 0
+
+
+def test_verify_with_probabilities():
+    rng = np.random.default_rng(20)
+    B, T1, V = 4, 61, 128256
+    tok, par, dep = _random_flat_trees(rng, B, T1, 50)
+    rows = _bf16((rng.standard_normal((B, T1, V)) * 1.5).astype(np.float32))
+    got = gpu_verify(rows, tok, par, dep, want_prob=True)
+    tk, p = O.topk(rows.reshape(-1, V), 8, "bf16", want_prob=True)
+    np.testing.assert_array_equal(got["topk"].reshape(-1, 8), tk)
+    np.testing.assert_allclose(got["topk_prob"].reshape(-1, 8), p, rtol=1e-5, atol=0)
+
+
+def gpu_update(table, row_tok, topk_rows):
+    V, k = table.shape
+    tb = _t(table, torch.int32)
+    rt = _t(row_tok, torch.int32)
+    tk = _t(topk_rows, torch.int32)
+    L.graft_update_topk(len(row_tok), V, k, L.DTYPE_BF16, None, tk.data_ptr(), None, rt.data_ptr(),
+                        tb.data_ptr(), None, None, None, 0, _s())
+    torch.cuda.synchronize()
+    return tb.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,ntok", [(976, 151936), (976, 1), (976, 7), (2048, 300), (9000, 50), (17, 17), (1, 5)])
+def test_update_parity_collisions(n, ntok):
+    rng = np.random.default_rng(n + ntok)
+    V, k = max(ntok, 64), 8
+    table = rng.integers(0, V, size=(V, k)).astype(np.int32)
+    row_tok = rng.integers(0, ntok, size=n).astype(np.int32)
+    tk = rng.integers(0, V, size=(n, k)).astype(np.int32)
+    got = gpu_update(table.copy(), row_tok, tk)
+    want = table.copy()
+    O.update(want, row_tok, tk)
+    np.testing.assert_array_equal(got, want)

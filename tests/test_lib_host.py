@@ -1,0 +1,90 @@
+"""Host-side checks of libgraft.so that need no GPU: the library loads, exports
+every entry point include/graft.h declares, validates arguments before
+launching anything, and its host-built retrieval template equals the oracle's
+independently written one."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from hybrid_draft_tree_amd import _lib as L
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "graft.h")).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char \*)\s*\**\s*(graft_\w+)\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    names = _declared()
+    assert set(names) == set(L.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_product_package_has_no_oracle_dependency():
+    pkg = os.path.join(ROOT, "hybrid_draft_tree_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
+
+
+def test_status_strings():
+    assert L.graft_status_string(0) == "ok"
+    assert "invalid" in L.graft_status_string(-1)
+    assert "unsupported" in L.graft_status_string(-2)
+
+
+def test_workspace_bytes():
+    assert L.graft_workspace_bytes(976, 151936, 8, L.DTYPE_BF16) > 976 * 8 * 8
+    assert L.graft_workspace_bytes(10, 100, 9, L.DTYPE_BF16) == 0      # k > 8
+    assert L.graft_workspace_bytes(10, 4, 8, L.DTYPE_BF16) == 0        # k > V
+    assert L.graft_workspace_bytes(10, 100, 8, 7) == 0                 # bad dtype
+    assert L.graft_workspace_bytes(0, 100, 8, L.DTYPE_F32) >= 0
+
+
+@pytest.mark.parametrize("W,D,R", [(8, 8, 52), (8, 8, 64), (8, 8, 20), (4, 6, 24), (1, 3, 3), (5, 1, 5)])
+def test_template_matches_oracle(W, D, R):
+    par, rk, dp = L.graft_template_master(W, D, R)
+    o = O.template(W, D, R)
+    assert par == o["parent"].tolist()
+    assert rk == o["rank"].tolist()
+    assert dp == o["depth"].tolist()
+
+
+def test_host_validation_rejects_without_launch():
+    cfg = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 40), 0.5)
+    lib = L.load()
+    P = 0x1000  # never dereferenced: every call below fails validation first
+    # unsupported mode / layout / dtype
+    assert lib.graft_prune_select(1, 60, 7, P, P, P, ctypes.byref(cfg), P, P, P, None, None) == L.GRAFT_EUNSUPPORTED
+    assert lib.graft_build_tree_mask(1, 60, 61, 9, *([P] * 9), 52, *([P] * 5), None) == L.GRAFT_EUNSUPPORTED
+    assert lib.graft_verify_accept(1, 61, 100, 8, 5, *([P] * 8), 60, P, None, P, 1 << 20, None) == L.GRAFT_EUNSUPPORTED
+    # bad sizes
+    assert lib.graft_prune_select(1, 65, 0, P, P, P, ctypes.byref(cfg), P, P, P, None, None) == L.GRAFT_EINVAL
+    assert lib.graft_prune_select(1, 0, 0, P, P, P, ctypes.byref(cfg), P, P, P, None, None) == L.GRAFT_EINVAL
+    bad = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 70), 0.5)
+    assert lib.graft_prune_select(1, 60, 0, P, P, P, ctypes.byref(bad), P, P, P, None, None) == L.GRAFT_EINVAL
+    assert lib.graft_build_tree_mask(1, 60, 65, 0, *([P] * 9), 52, *([P] * 5), None) == L.GRAFT_EINVAL
+    assert lib.graft_build_tree_mask(1, 60, 60, 1, *([P] * 9), 52, *([P] * 5), None) == L.GRAFT_EINVAL  # in-place needs T1 = Nd + 1
+    assert lib.graft_verify_accept(1, 61, 100, 9, 1, *([P] * 8), 60, P, None, P, 1 << 20, None) == L.GRAFT_EINVAL
+    assert lib.graft_verify_accept(1, 61, 100, 8, 1, P + 2, *([P] * 7), 60, P, None, P, 1 << 20, None) == L.GRAFT_EINVAL  # misaligned logits
+    assert lib.graft_verify_accept(1, 61, 100, 8, 1, *([P] * 8), 60, P, None, P, 16, None) == L.GRAFT_EINVAL  # workspace too small
+    # null pointers
+    assert lib.graft_prune_select(1, 60, 0, None, P, P, ctypes.byref(cfg), P, P, P, None, None) == L.GRAFT_EINVAL
+    assert lib.graft_update_topk(10, 100, 8, 1, None, None, None, P, P, None, None, P, 1 << 20, None) == L.GRAFT_EINVAL
+    # template budget check: slots - keep must fit the template
+    tpl = L.Template(20, P, P, P)
+    assert lib.graft_retrieve_expand(1, 100, 8, 0, 60, P, P, P, None, 60, ctypes.byref(tpl),
+                                     ctypes.byref(cfg), P, P, P, 52, None) == L.GRAFT_EINVAL
+    # empty batches enqueue nothing and succeed
+    assert lib.graft_prune_select(0, 60, 0, None, None, None, ctypes.byref(cfg), None, None, None, None, None) == 0
+    assert lib.graft_update_topk(0, 100, 8, 1, None, None, None, None, None, None, None, None, 0, None) == 0
