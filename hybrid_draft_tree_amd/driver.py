@@ -39,6 +39,8 @@ class GraftPipeline:
         self.dmax = self.T1 - 1
         self.want_prob = bool(want_prob)
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         dev = self.device
         i32 = dict(dtype=torch.int32, device=dev)
         log_thr = [float(np.float32(math.log(t))) for t in tau]

@@ -391,7 +391,8 @@ def test_verify_accept_parity(T1, V):
     if T1 > 1:
         np.testing.assert_array_equal(got["accept_idx"], acc["accept_idx"])
     np.testing.assert_array_equal(got["base_pos"], base + acc["accept_len"] + 1)
-    assert got["accept_len"].max() > 0
+    if T1 > 1:
+        assert got["accept_len"].max() > 0
 
 
 def test_verify_with_probabilities():
