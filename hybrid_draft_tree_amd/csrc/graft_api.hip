@@ -21,17 +21,16 @@ inline int launch_status() {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// workspace: [top-k partials | softmax stats | top-k rows | top-k probs]
+// workspace: [top-k partials | softmax stats | counters | top-k rows | top-k probs]
 struct WsLayout {
     TopkPlan plan;
-    size_t off_stats = 0, off_topk = 0, off_prob = 0, total = 0;
+    size_t off_topk = 0, off_prob = 0, total = 0;
 };
 
 WsLayout ws_layout(int64_t n_rows, int V, int k, int dtype) {
     WsLayout L;
     L.plan = plan_topk(n_rows, V, dtype);
-    L.off_stats = align256(L.plan.partial_bytes);
-    L.off_topk = L.off_stats + align256(L.plan.stats_bytes);
+    L.off_topk = align256(L.plan.ws_bytes);
     L.off_prob = L.off_topk + align256((size_t)n_rows * k * sizeof(int32_t));
     L.total = L.off_prob + align256((size_t)n_rows * k * sizeof(float));
     return L;
@@ -175,9 +174,17 @@ int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logi
     const int64_t n_rows = (int64_t)B * T1;
     const WsLayout L = ws_layout(n_rows, V, k, dtype);
     if (ws_bytes < L.total) return GRAFT_EINVAL;
-    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, ws, stream);
-    launch_accept(B, T1, k, topk, tok, parent, depth, accept_len, accept_idx, dmax, bonus,
-                  base_pos_io, stream);
+    VerifyArgs v;
+    v.T1 = T1;
+    v.tok = tok;
+    v.parent = parent;
+    v.depth = depth;
+    v.accept_len = accept_len;
+    v.accept_idx = accept_idx;
+    v.dmax = dmax;
+    v.bonus = bonus;
+    v.base_pos_io = base_pos_io;
+    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, ws, &v, stream);
     return launch_status();
 }
 
@@ -197,7 +204,7 @@ int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logit
         if (ws_bytes < L.total) return GRAFT_EINVAL;
         int32_t *tk_ws = topk_out ? topk_out : (int32_t *)((char *)ws + L.off_topk);
         float *pr_ws = table_prob ? (float *)((char *)ws + L.off_prob) : nullptr;
-        launch_topk(L.plan, dtype, logits, k, tk_ws, pr_ws, ws, stream);
+        launch_topk(L.plan, dtype, logits, k, tk_ws, pr_ws, ws, nullptr, stream);
         tk = tk_ws;
         pr = pr_ws;
     } else if (table_prob && !prob_in) {

@@ -27,7 +27,7 @@ void launch_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
                     int32_t *parent, int32_t *depth, int32_t *pos_id, uint64_t *anc,
                     hipStream_t s);
 
-// ---- row-wise top-k (topk_kernels.hip) ----------------------------------------------
+// ---- row-wise top-k + fused acceptance walk (topk_kernels.hip) ----------------------
 struct TopkPlan {
     int64_t n_rows = 0;
     int V = 0;
@@ -35,21 +35,46 @@ struct TopkPlan {
     int chunk = 0;      // elements per range (multiple of 8)
     size_t partial_bytes = 0;
     size_t stats_bytes = 0;
+    size_t off_stats = 0;     // workspace offsets
+    size_t off_counters = 0;
+    size_t ws_bytes = 0;      // bytes of workspace the kernel uses (zeroed counters inside)
 };
 
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype);
 
-// Phase A: per-range top-8 candidates (and softmax statistics when want_prob).
-// Phase B: merge per row into topk [n_rows, k] (+ probabilities).
+struct TopkArgs {
+    const void *logits;
+    int64_t n_rows;
+    int V, S, chunk;
+    uint64_t *partials;
+    float2 *stats;
+    uint32_t *row_cnt;
+    int k;
+    int32_t *topk;
+    float *prob;
+};
+
+struct VerifyArgs {
+    int T1 = 0;
+    const int32_t *tok = nullptr;
+    const int32_t *parent = nullptr;
+    const int32_t *depth = nullptr;
+    int32_t *accept_len = nullptr;
+    int32_t *accept_idx = nullptr;
+    int dmax = 0;
+    int32_t *bonus = nullptr;
+    int32_t *base_pos_io = nullptr;
+    uint32_t *req_cnt = nullptr;
+};
+
+// Row-wise top-k of logits [n_rows, V] into topk [n_rows, k] (+ probabilities);
+// with `verify` the acceptance walk of every request (n_rows = B * verify->T1)
+// runs in the same launch.  The workspace counters must be zero on entry and
+// are zero again on exit.
 void launch_topk(const TopkPlan &plan, int dtype, const void *logits, int k, int32_t *topk,
-                 float *prob, void *ws, hipStream_t s);
+                 float *prob, void *ws, const VerifyArgs *verify, hipStream_t s);
 
-// ---- verify / update (verify_kernels.hip) -------------------------------------------
-void launch_accept(int B, int T1, int k, const int32_t *topk, const int32_t *tok,
-                   const int32_t *parent, const int32_t *depth, int32_t *accept_len,
-                   int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io,
-                   hipStream_t s);
-
+// ---- matrix update (verify_kernels.hip) ---------------------------------------------
 void launch_update(int64_t n_rows, int V, int k, const int32_t *topk, const float *prob,
                    const int32_t *row_tok, int32_t *table, float *table_prob, hipStream_t s);
 

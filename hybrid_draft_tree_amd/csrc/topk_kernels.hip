@@ -5,15 +5,17 @@
 // Order: value descending, ties -> lower id, -0 == +0.  The kernel is an HBM
 // stream: no MFMA (nothing is a contraction).
 //
-// Phase A: each wavefront owns a contiguous range of one row and streams it
+// Each wavefront owns a contiguous range of one row and streams it
 //   with 16-byte loads (8 bf16 or 4 fp32 per lane, U loads in flight).  A
 //   wave-uniform threshold -- the key of the wave's current 8th-best value --
 //   filters groups with a few packed integer ops; the rare groups that pass
 //   are compacted into LDS with a ballot, and merged into the wave's exact
 //   top-8 (8 rounds of wave-wide max) when 64 are pending.  The range's top-8
 //   goes to the workspace as 64-bit (value, id) ranks.
-// Phase B: one wavefront per row merges the ranges' candidates into the final
-//   top-k (and combines online-softmax statistics for probabilities).
+// Epilogue: the last range of a row to finish merges the ranges' candidates
+//   into the final top-k (and combines online-softmax statistics); with the
+//   acceptance walk fused, the last row of a request to be merged runs the
+//   walk for that request.  One launch per call.
 #include "device_utils.hpp"
 #include "launchers.hpp"
 
@@ -153,10 +155,85 @@ struct SoftStats {
     }
 };
 
-template <typename TR, bool PROB, bool NT>
-__global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_phase_a(
-    const void *__restrict__ logits, int64_t n_rows, int V, int S, int chunk,
-    uint64_t *__restrict__ partials, float2 *__restrict__ stats) {
+// Merge the ranges' candidates of one row into its final top-k (+ softmax
+// probabilities), one wavefront.
+constexpr int kMaxPerLaneB = 4;  // S * 8 <= 256 candidates per row
+
+__device__ __forceinline__ void merge_row(const TopkArgs &a, int64_t row) {
+    const int lane = lane_id();
+    const int n = a.S * kTop;
+    uint64_t c[kMaxPerLaneB];
+#pragma unroll
+    for (int i = 0; i < kMaxPerLaneB; ++i) {
+        const int j = i * kWave + lane;
+        c[i] = j < n ? a.partials[row * n + j] : 0ull;
+    }
+    uint64_t top = 0;
+    merge_top8<uint64_t, kMaxPerLaneB>(c, top);
+    if (lane < a.k) a.topk[row * a.k + lane] = top ? (int32_t)rank64_id(top) : -1;
+    if (a.prob) {
+        const float2 sv = lane < a.S ? a.stats[row * a.S + lane] : make_float2(-INFINITY, 0.0f);
+        const float M = wave_max_f32(sv.x);
+        const float s = (sv.x == -INFINITY) ? 0.0f : sv.y * __expf(sv.x - M);
+        const float Ssum = wave_sum_f32(s);
+        if (lane < a.k) {
+            const float x = key_to_f32(rank64_key(top));
+            a.prob[row * a.k + lane] = top ? __expf(x - M) / Ssum : 0.0f;
+        }
+    }
+}
+
+// Strict greedy acceptance walk of request b (section 二, gear 3), one wavefront;
+// lane f is flattened row f.  A row is accepted iff every row on its path from
+// the root carries the greedy token of its parent row; the deepest accepted row
+// wins, ties -> lowest row.
+__device__ __forceinline__ void accept_walk(const VerifyArgs &v, int k, const int32_t *topk, int b) {
+    const int lane = lane_id();
+    const int T1 = v.T1;
+    const bool row = lane < T1;
+    const size_t o = (size_t)b * T1 + lane;
+    const int g = row ? topk[o * k] : -1;
+    const int t = row ? v.tok[o] : -1;
+    const int p = (row && lane > 0) ? v.parent[o] : -1;
+    const int d = row ? v.depth[o] : 0;
+    const int gp = __shfl(g, p >= 0 ? p : lane);
+    bool ok = row && (lane == 0 || (p >= 0 && t == gp));
+    // AND of the edge checks along the path and the ancestor-or-self mask, by
+    // pointer doubling over parent links
+    int a = p;
+    uint64_t A = row ? ((1ull << lane) | (a >= 0 ? (1ull << a) : 0ull)) : 0ull;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+        const int src = a >= 0 ? a : lane;
+        const int oka = __shfl((int)ok, src);
+        const uint64_t Aa = shfl_u64(A, src);
+        const int aa = __shfl(a, src);
+        if (a >= 0) {
+            ok = ok && oka;
+            A |= Aa;
+            a = aa;
+        }
+    }
+    const int key = ok ? (d << 8) | (255 - lane) : -1;
+    const int best = wave_max_i32(key);
+    const int fstar = 255 - (best & 255);
+    const int len = best >> 8;
+    const uint64_t path = shfl_u64(A, fstar);
+    const int gstar = __shfl(g, fstar);
+    // the path's rows have depths 1..len: row at depth d goes to slot d-1
+    if (row && lane > 0 && ((path >> lane) & 1ull) && d >= 1 && d <= v.dmax)
+        v.accept_idx[(size_t)b * v.dmax + d - 1] = lane;
+    for (int j = lane; j < v.dmax; j += kWave)
+        if (j >= len) v.accept_idx[(size_t)b * v.dmax + j] = -1;
+    if (lane == 0) {
+        v.accept_len[b] = len;
+        v.bonus[b] = gstar;
+        if (v.base_pos_io) v.base_pos_io[b] += len + 1;
+    }
+}
+
+template <typename TR, bool PROB, bool ACCEPT, bool NT>
+__global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a, VerifyArgs v) {
     using Rank = typename TR::Rank;
     constexpr int EPG = TR::kPerGroup;
     constexpr int ESZ = 16 / EPG;
@@ -166,12 +243,13 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_phase_a(
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6;
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlockA + wv;
-    if (w >= n_rows * S) return;
+    const int S = a.S;
+    if (w >= a.n_rows * S) return;
     const int64_t row = w / S;
     const int split = (int)(w - row * S);
-    const int c0 = split * chunk;
-    const int c1 = min(V, c0 + chunk);
-    const char *rowp = (const char *)logits + (size_t)row * (size_t)V * ESZ;
+    const int c0 = split * a.chunk;
+    const int c1 = min(a.V, c0 + a.chunk);
+    const char *rowp = (const char *)a.logits + (size_t)row * (size_t)a.V * ESZ;
 
     // head (until 16-byte alignment), body (16-byte groups), tail
     const uintptr_t a_addr = (uintptr_t)(rowp + (size_t)c0 * ESZ);
@@ -189,7 +267,6 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_phase_a(
 
     {  // head and tail elements: at most EPG-1 each
         Rank c[1] = {0};
-        uint32_t raw = 0;
         bool have = false;
         int off = 0;
         if (lane < head) {
@@ -200,7 +277,7 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_phase_a(
             have = true;
         }
         if (have) {
-            raw = TR::load_scalar(rowp, c0 + off);
+            const uint32_t raw = TR::load_scalar(rowp, c0 + off);
             c[0] = TR::make(raw, off);
             if constexpr (PROB) st.add(TR::value(raw));
         }
@@ -282,59 +359,56 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_phase_a(
         process();
     }
 
-    if (lane < kTop) partials[w * kTop + lane] = top ? TR::to_row_rank(top, c0) : 0ull;
+    // Publish this range's candidates.  The last range of a row to finish
+    // (device-scope counter) merges the row; with ACCEPT, the last row of a
+    // request to be merged runs that request's acceptance walk.  Counters are
+    // reset by the wave that consumed them, so the workspace is left zeroed.
+    if (lane < kTop) a.partials[w * kTop + lane] = top ? TR::to_row_rank(top, c0) : 0ull;
     if constexpr (PROB) {
         const float M = wave_max_f32(st.m);
         const float s = (st.m == -INFINITY) ? 0.0f : st.s * __expf(st.m - M);
         const float Ssum = wave_sum_f32(s);
-        if (lane == 0) stats[w] = make_float2(M, Ssum);
+        if (lane == 0) a.stats[w] = make_float2(M, Ssum);
     }
-}
-
-// Phase B: one wavefront per row.
-constexpr int kRowsPerBlockB = 4;
-constexpr int kMaxPerLaneB = 4;  // S * 8 <= 256 candidates per row
-
-__global__ __launch_bounds__(kWave *kRowsPerBlockB) void k_topk_phase_b(
-    const uint64_t *__restrict__ partials, const float2 *__restrict__ stats, int64_t n_rows, int S,
-    int k, int32_t *__restrict__ topk, float *__restrict__ prob) {
-    const int lane = lane_id();
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlockB + (threadIdx.x >> 6);
-    if (row >= n_rows) return;
-    const int n = S * kTop;
-    uint64_t c[kMaxPerLaneB];
-#pragma unroll
-    for (int i = 0; i < kMaxPerLaneB; ++i) {
-        const int j = i * kWave + lane;
-        c[i] = j < n ? partials[row * n + j] : 0ull;
-    }
-    uint64_t top = 0;
-    merge_top8<uint64_t, kMaxPerLaneB>(c, top);
-    if (lane < k) topk[row * k + lane] = top ? (int32_t)rank64_id(top) : -1;
-    if (prob) {
-        const float2 sv = lane < S ? stats[row * S + lane] : make_float2(-INFINITY, 0.0f);
-        const float M = wave_max_f32(sv.x);
-        const float s = (sv.x == -INFINITY) ? 0.0f : sv.y * __expf(sv.x - M);
-        const float Ssum = wave_sum_f32(s);
-        if (lane < k) {
-            const float x = key_to_f32(rank64_key(top));
-            prob[row * k + lane] = top ? __expf(x - M) / Ssum : 0.0f;
-        }
+    __threadfence();
+    uint32_t prev = 0;
+    if (lane == 0) prev = atomicAdd(&a.row_cnt[row], 1u);
+    prev = __shfl(prev, 0);
+    if (prev != (uint32_t)(S - 1)) return;
+    __threadfence();
+    merge_row(a, row);
+    if (lane == 0) a.row_cnt[row] = 0u;
+    if constexpr (ACCEPT) {
+        const int b = (int)(row / v.T1);
+        __threadfence();
+        uint32_t prev_r = 0;
+        if (lane == 0) prev_r = atomicAdd(&v.req_cnt[b], 1u);
+        prev_r = __shfl(prev_r, 0);
+        if (prev_r != (uint32_t)(v.T1 - 1)) return;
+        __threadfence();
+        accept_walk(v, a.k, a.topk, b);
+        if (lane == 0) v.req_cnt[b] = 0u;
     }
 }
 
 template <typename TR>
-void launch_phase_a(bool want_prob, const TopkPlan &p, const void *logits, uint64_t *partials,
-                    float2 *stats, hipStream_t s) {
-    const int64_t waves = p.n_rows * p.splits;
+void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
+    const int64_t waves = a.n_rows * a.S;
     const dim3 grid((unsigned)((waves + kWavesPerBlockA - 1) / kWavesPerBlockA));
     const dim3 block(kWave * kWavesPerBlockA);
-    if (want_prob)
-        hipLaunchKernelGGL((k_topk_phase_a<TR, true, true>), grid, block, 0, s, logits, p.n_rows, p.V,
-                           p.splits, p.chunk, partials, stats);
-    else
-        hipLaunchKernelGGL((k_topk_phase_a<TR, false, true>), grid, block, 0, s, logits, p.n_rows,
-                           p.V, p.splits, p.chunk, partials, stats);
+    const VerifyArgs vv = v ? *v : VerifyArgs{};
+    const bool prob = a.prob != nullptr;
+    if (v) {
+        if (prob)
+            hipLaunchKernelGGL((k_topk_rows<TR, true, true, true>), grid, block, 0, s, a, vv);
+        else
+            hipLaunchKernelGGL((k_topk_rows<TR, false, true, true>), grid, block, 0, s, a, vv);
+    } else {
+        if (prob)
+            hipLaunchKernelGGL((k_topk_rows<TR, true, false, true>), grid, block, 0, s, a, vv);
+        else
+            hipLaunchKernelGGL((k_topk_rows<TR, false, false, true>), grid, block, 0, s, a, vv);
+    }
 }
 
 }  // namespace
@@ -361,21 +435,37 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     p.chunk = chunk;
     p.partial_bytes = (size_t)n_rows * S * kTop * sizeof(uint64_t);
     p.stats_bytes = (size_t)n_rows * S * sizeof(float2);
+    // workspace: [partials | stats | row counters, request counters]
+    p.off_stats = (p.partial_bytes + 255) / 256 * 256;
+    p.off_counters = p.off_stats + (p.stats_bytes + 255) / 256 * 256;
+    p.ws_bytes = p.off_counters + ((size_t)n_rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
     return p;
 }
 
 void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_t *topk,
-                 float *prob, void *ws, hipStream_t s) {
+                 float *prob, void *ws, const VerifyArgs *verify, hipStream_t s) {
     if (p.n_rows <= 0) return;
-    uint64_t *partials = (uint64_t *)ws;
-    float2 *stats = (float2 *)((char *)ws + ((p.partial_bytes + 255) / 256) * 256);
+    TopkArgs a;
+    a.logits = logits;
+    a.n_rows = p.n_rows;
+    a.V = p.V;
+    a.S = p.splits;
+    a.chunk = p.chunk;
+    a.partials = (uint64_t *)ws;
+    a.stats = (float2 *)((char *)ws + p.off_stats);
+    a.row_cnt = (uint32_t *)((char *)ws + p.off_counters);
+    a.k = k;
+    a.topk = topk;
+    a.prob = prob;
+    VerifyArgs v;
+    if (verify) {
+        v = *verify;
+        v.req_cnt = a.row_cnt + p.n_rows;
+    }
     if (dtype == GRAFT_DTYPE_BF16)
-        launch_phase_a<Bf16Traits>(prob != nullptr, p, logits, partials, stats, s);
+        launch_rows<Bf16Traits>(a, verify ? &v : nullptr, s);
     else
-        launch_phase_a<F32Traits>(prob != nullptr, p, logits, partials, stats, s);
-    const dim3 gridb((unsigned)((p.n_rows + kRowsPerBlockB - 1) / kRowsPerBlockB));
-    hipLaunchKernelGGL(k_topk_phase_b, gridb, dim3(kWave * kRowsPerBlockB), 0, s, partials, stats,
-                       p.n_rows, p.splits, k, topk, prob);
+        launch_rows<F32Traits>(a, verify ? &v : nullptr, s);
 }
 
 }  // namespace graft

@@ -1,73 +1,12 @@
-// Verification-side kernels of the Graft step (section 二, gear 3 of the news
-// write-up of arXiv 2605.20104): the strict greedy acceptance walk over the
-// flattened hybrid tree, and the online update of the continuation matrix with
-// the target's top-k at every verified position.
+// Online update of the continuation matrix (section 二, gear 3 of the news
+// write-up of arXiv 2605.20104): the target's top-k at every verified position,
+// accepted or rejected, overwrites the row of that position's input token.  The
+// acceptance walk lives in the top-k kernel's epilogue (topk_kernels.hip).
 #include "device_utils.hpp"
 #include "launchers.hpp"
 
 namespace graft {
 namespace {
-
-constexpr int kReqPerBlock = 4;
-
-// One wavefront per request; lane f is flattened row f.
-__global__ __launch_bounds__(kWave *kReqPerBlock) void k_accept(
-    int B, int T1, int k, const int32_t *__restrict__ topk, const int32_t *__restrict__ tok,
-    const int32_t *__restrict__ parent, const int32_t *__restrict__ depth,
-    int32_t *__restrict__ accept_len, int32_t *__restrict__ accept_idx, int dmax,
-    int32_t *__restrict__ bonus, int32_t *__restrict__ base_pos_io) {
-    __shared__ int s_path[kReqPerBlock][kWave];
-    const int lane = lane_id();
-    const int w = threadIdx.x >> 6;
-    const int b = blockIdx.x * kReqPerBlock + w;
-    const bool live = b < B;
-    const bool row = live && lane < T1;
-    const size_t o = (size_t)b * T1 + lane;
-    const int g = row ? topk[o * k] : -1;
-    const int t = row ? tok[o] : -1;
-    const int p = (row && lane > 0) ? parent[o] : -1;
-    const int d = row ? depth[o] : 0;
-    int *sp = s_path[w];
-    sp[lane] = -1;
-
-    // edge check: the row's token equals the greedy token at its parent row
-    const int gp = __shfl(g, p >= 0 ? p : lane);
-    bool ok = row && (lane == 0 || (p >= 0 && t == gp));
-    // accepted iff every edge on the path to the root is correct, and the
-    // ancestor-or-self mask of the row: both by pointer doubling
-    int a = p;
-    uint64_t A = row ? ((1ull << lane) | (a >= 0 ? (1ull << a) : 0ull)) : 0ull;
-#pragma unroll
-    for (int r = 0; r < 6; ++r) {
-        const int src = a >= 0 ? a : lane;
-        const int oka = __shfl((int)ok, src);
-        const uint64_t Aa = shfl_u64(A, src);
-        const int aa = __shfl(a, src);
-        if (a >= 0) {
-            ok = ok && oka;
-            A |= Aa;
-            a = aa;
-        }
-    }
-    // deepest accepted row, ties -> lowest row
-    const int key = ok ? (d << 8) | (255 - lane) : -1;
-    const int best = wave_max_i32(key);
-    const int fstar = 255 - (best & 255);
-    const int len = best >> 8;
-    const uint64_t path = shfl_u64(A, fstar);
-    const int gstar = __shfl(g, fstar);
-    __syncthreads();
-    if (live && lane > 0 && ((path >> lane) & 1ull) && d >= 1 && d <= kWave) sp[d - 1] = lane;
-    __syncthreads();
-    if (!live) return;
-    for (int j = lane; j < dmax; j += kWave)
-        accept_idx[(size_t)b * dmax + j] = (j < len && j < kWave) ? sp[j] : -1;
-    if (lane == 0) {
-        accept_len[b] = len;
-        bonus[b] = gstar;
-        if (base_pos_io) base_pos_io[b] += len + 1;
-    }
-}
 
 // Matrix update: one workgroup; rows in blocks of kHashRows, each resolved with
 // an LDS hash table keyed by token that keeps the highest row index (atomic
@@ -135,16 +74,6 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(int64_t n_rows, int V, i
 }
 
 }  // namespace
-
-void launch_accept(int B, int T1, int k, const int32_t *topk, const int32_t *tok,
-                   const int32_t *parent, const int32_t *depth, int32_t *accept_len,
-                   int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io,
-                   hipStream_t s) {
-    if (B <= 0) return;
-    hipLaunchKernelGGL(k_accept, dim3((B + kReqPerBlock - 1) / kReqPerBlock),
-                       dim3(kWave * kReqPerBlock), 0, s, B, T1, k, topk, tok, parent, depth,
-                       accept_len, accept_idx, dmax, bonus, base_pos_io);
-}
 
 void launch_update(int64_t n_rows, int V, int k, const int32_t *topk, const float *prob,
                    const int32_t *row_tok, int32_t *table, float *table_prob, hipStream_t s) {

@@ -87,7 +87,7 @@ class GraftPipeline:
         self.accept_len = torch.zeros(B, **i32)
         self.accept_idx = torch.zeros(B, max(self.dmax, 1), **i32)
         self.ws_bytes = L.graft_workspace_bytes(B * T1, self.V, self.k, self.dtype)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
         self._ingest_ws = None
 
     @classmethod
@@ -181,7 +181,7 @@ class GraftPipeline:
         rt = torch.as_tensor(np.asarray(row_tok, np.int32)).to(self.device)
         need = L.graft_workspace_bytes(n, self.V, self.k, self.dtype)
         if self._ingest_ws is None or self._ingest_ws.numel() < need:
-            self._ingest_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self._ingest_ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
         out = torch.empty(n, self.k, dtype=torch.int32, device=self.device)
         L.graft_update_topk(n, self.V, self.k, self.dtype, logits.data_ptr(), None, None, rt.data_ptr(),
                             self.table.data_ptr(), self.table_prob.data_ptr() if self.want_prob else None,

@@ -14,7 +14,10 @@
  * Conventions (all entry points):
  *  - Array arguments are DEVICE pointers owned by the caller unless marked
  *    "host".  The library never allocates, frees or retains them.  Scratch
- *    comes from a caller workspace sized by graft_workspace_bytes().
+ *    comes from a caller workspace sized by graft_workspace_bytes(): it must
+ *    be zero-filled once after allocation; every call leaves it zero-filled
+ *    again (its completion counters are reset by the kernel that used them).
+ *    Calls that share one workspace must be ordered (same stream).
  *  - Work is enqueued asynchronously on `stream`; nothing is synchronised.
  *    Calls on different streams touching disjoint buffers are independent.
  *  - Return value: GRAFT_OK, or a negative status.  Arguments are validated
@@ -156,8 +159,9 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
  * the accepted row: the next root; `bonus` may alias the root buffer of the
  * next step); base_pos_io int32 [B] (nullable; += accept_len + 1).
  * tok, parent, depth: int32 [B, T1] from graft_build_tree_mask.  logits must
- * be 16-byte aligned.  ws: device workspace of at least
- * graft_workspace_bytes(B*T1, V, k, dtype) bytes.
+ * be 16-byte aligned.  ws: zero-filled device workspace (256-byte aligned) of
+ * at least graft_workspace_bytes(B*T1, V, k, dtype) bytes.  One kernel launch:
+ * the acceptance walk runs in the top-k kernel's epilogue.
  * Requires 1 <= T1 <= 64, 1 <= k <= 8, k <= V, dmax >= 0. */
 int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logits,
                         const int32_t *tok, const int32_t *parent, const int32_t *depth,
@@ -184,8 +188,8 @@ int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logit
                       size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes needed by graft_verify_accept / graft_update_topk for
- * n_rows rows of V logits (0 on invalid sizes).  The workspace needs no
- * initialisation and holds nothing between calls. */
+ * n_rows rows of V logits (0 on invalid sizes).  Zero-fill it once after
+ * allocating it; calls leave it zero-filled. */
 size_t graft_workspace_bytes(int64_t n_rows, int V, int k, int dtype);
 
 /* Static description of a status code. */

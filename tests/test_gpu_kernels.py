@@ -41,7 +41,7 @@ def gpu_topk(rows, k, dtype, want_prob=False):
     tprob = torch.zeros(max(V, 1), k, dtype=torch.float32, device=DEV) if want_prob else None
     row_tok = torch.arange(n, dtype=torch.int32, device=DEV) % V
     wsb = L.graft_workspace_bytes(n, V, k, dt)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     L.graft_update_topk(n, V, k, dt, lg.data_ptr(), None, None, row_tok.data_ptr(), table.data_ptr(),
                         tprob.data_ptr() if want_prob else None, out.data_ptr(), ws.data_ptr(), wsb, _s())
     torch.cuda.synchronize()
@@ -349,7 +349,7 @@ def gpu_verify(rows, tok, parent, depth, k=8, dtype="bf16", want_prob=False, bas
     bp = _t(base if base is not None else np.zeros(B, np.int32), torch.int32)
     t_, p_, d_ = (_t(x, torch.int32) for x in (tok, parent, depth))
     wsb = L.graft_workspace_bytes(B * T1, V, k, dt)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     L.graft_verify_accept(B, T1, V, k, dt, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
                           tk.data_ptr(), pr.data_ptr() if want_prob else None, al.data_ptr(), ai.data_ptr(),
                           T1 - 1, bo.data_ptr(), bp.data_ptr(), ws.data_ptr(), wsb, _s())
