@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Graft per-step hot path benchmark on one MI355X.
+
+Workload: the batched static-slot step -- B=16 requests, V=151936, 60 candidate
+slots + the root (61 verified rows per request), k=8, bf16 target logits
+[16, 61, V] (296.6 MB per step), in-place layout.  One step = prune-select ->
+retrieval expansion -> flatten/mask -> row-wise top-k + acceptance walk ->
+matrix update, all through the C ABI; the target forward is outside the path,
+so each step reads one buffer of a rotating pool of pre-generated logits
+(pool >= 4 x 296.6 MB, larger than the 256 MB Infinity Cache).
+
+The pool is filled from a real seeded trajectory (warm-up first, table warmed
+up); during timing the matrix and roots keep evolving, so accepted lengths
+differ from the pool's own trajectory but every byte is still read.
+
+Timed region: `--steps` steps as HIP-graph replays (one graph = one pass over
+the pool), bracketed by synchronisation and HIP events on the replay stream.
+The dominant kernel (graft_verify_update's single launch: row-wise top-k,
+acceptance walk and matrix update) is then timed on its own with HIP events
+around each launch, on the stream it is launched on.  The CPU oracle is timed on host copies of the same inputs.
+
+    python bench.py [--steps K] [--warmup W] [--pool P] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Graft steps/sec at batch 16, V=151936, 60 slots; achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "topk_rows_b16_v151936_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "hybrid_draft_tree_amd", "csrc", "topk_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--pool", type=int, default=4)
+    ap.add_argument("--kernel-iters", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class _Adapter:
+    """Drives the HIP pipeline through synth.runner (input generation only)."""
+
+    def __init__(self, pipe, torch):
+        from synth.device import DeviceRows
+        self.p = pipe
+        self.torch = torch
+        self.DeviceRows = DeviceRows
+        self.rows = None
+
+    def set_roots(self, roots, base_pos):
+        self.p.set_roots(roots, base_pos)
+
+    def get_roots(self):
+        return self.p.roots.cpu().numpy()
+
+    def build(self, draft):
+        return {k: v.cpu().numpy() for k, v in self.p.build(draft).items()}
+
+    def materialize(self, pool, desc):
+        if self.rows is None:
+            self.rows = self.DeviceRows(pool, self.p.device)
+        return self.rows.materialize(desc)
+
+    def verify_update(self, rows):
+        return {k: v.cpu().numpy() for k, v in self.p.verify_update(rows).items()}
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(bytes_alg):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, "kernel changed since counters were taken"
+    return d.get("hbm_bytes_per_launch"), d.get("note", "")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build measures the single-GPU Graft "
+              "step (no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from hybrid_draft_tree_amd import _lib as L
+    from hybrid_draft_tree_amd.driver import GraftPipeline
+    from synth import CONFIGS
+    from synth import generators as G
+    from synth import runner as R
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS[3]
+    B, T1, V, k = cfg.B, cfg.rows_per_request, cfg.V, cfg.k
+    n_rows = B * T1
+    P = max(1, args.pool)
+    bytes_logits = n_rows * V * 2
+
+    t0 = time.time()
+    pipe = GraftPipeline.from_config(cfg, device=dev)
+    ad = _Adapter(pipe, torch)
+    wl = R.Workload(cfg)
+    R.start(ad, wl)
+    for s in range(cfg.warmup_steps):
+        R.step(ad, wl, s, G.WARMUP_STREAM_OFFSET)
+    # pool: P steps of a real trajectory; keep each step's draft (on device) and logits
+    pool_logits, pool_drafts, acc_pool = [], [], []
+    for p in range(P):
+        roots = ad.get_roots()
+        draft = wl.draft(p, roots)
+        flat = ad.build(draft)
+        desc = wl.logit_desc(p, flat)
+        buf = torch.empty(n_rows, V, dtype=torch.bfloat16, device=dev)
+        if ad.rows is None:
+            ad.rows = ad.DeviceRows(wl.pool, dev)
+        ad.rows.materialize(desc, out=buf)
+        res = ad.verify_update(buf)
+        wl.commit(roots, flat, res)
+        acc_pool.append(int(res["accept_len"].sum()))
+        bufs = pipe.draft_buffers()
+        bufs["parent"].copy_(torch.as_tensor(draft["parent"]))
+        bufs["layer"].copy_(torch.as_tensor(draft["layer"]))
+        bufs["score"].copy_(torch.as_tensor(draft["logp"]))
+        bufs["tok"].copy_(torch.as_tensor(draft["tok"]))
+        pool_logits.append(buf)
+        pool_drafts.append(bufs)
+    torch.cuda.synchronize()
+    log("setup %.1fs: pool of %d steps (%.1f MB each), accepted per step in pool: %s"
+        % (time.time() - t0, P, bytes_logits / 1e6, acc_pool))
+
+    def one_pass():
+        for p in range(P):
+            pipe.build_device(pool_drafts[p])
+            pipe.verify_update_device(pool_logits[p])
+
+    # ---------------- timed region: whole steps ----------------
+    n_rep = max(1, math.ceil(args.steps / P))
+    K = n_rep * P
+    W = max(0, math.ceil(args.warmup / P)) * P
+    if args.no_graph:
+        run = one_pass
+    else:
+        one_pass()  # warm the launch path before capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_pass()
+        run = g.replay
+    for _ in range(W // P):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(n_rep):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / K
+    steps_per_s = 1000.0 / ms_step
+    step_bytes = bytes_logits + n_rows * k * 4
+    log("timed %d steps: %.3f ms event time, %.3f s wall, %.2f us/step" % (K, ms_total, wall, ms_step * 1e3))
+
+    # ---------------- dominant kernel alone ----------------
+    # graft_verify_update: one launch of k_topk_rows (row-wise top-k + acceptance
+    # walk + matrix update), the kernel that carries the step's logits traffic.
+    def verify_call(i):
+        L.graft_verify_update(B, T1, V, k, pipe.dtype, pool_logits[i % P].data_ptr(), pipe.tok.data_ptr(),
+                              pipe.parent.data_ptr(), pipe.depth.data_ptr(), pipe.table.data_ptr(), None,
+                              pipe.topk.data_ptr(), None, pipe.accept_len.data_ptr(), pipe.accept_idx.data_ptr(),
+                              pipe.dmax, pipe.roots.data_ptr(), None, pipe.ws.data_ptr(), pipe.ws_bytes,
+                              stream.cuda_stream)
+
+    iters = max(P, args.kernel_iters)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(min(iters, 8)):
+        verify_call(i)
+    torch.cuda.synchronize()
+    for i in range(iters):
+        a, b = evs[i]
+        a.record(stream)
+        verify_call(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    durs = sorted(a.elapsed_time(b) for a, b in evs)
+    k_ms = sum(durs) / len(durs)
+    k_med = durs[len(durs) // 2]
+    alg_bytes = bytes_logits + n_rows * k * 4
+    achieved = alg_bytes / (k_ms * 1e-3) / 1e9
+    traffic, tnote = load_traffic(alg_bytes)
+    log("dominant kernel: mean %.2f us, median %.2f us, %.0f GB/s algorithmic" % (k_ms * 1e3, k_med * 1e3, achieved))
+
+    copy_gbps = None
+    if args.copy_calib:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            y.copy_(x)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        log("plain 1 GiB copy: %.0f GB/s (read + write)" % copy_gbps)
+
+    # ---------------- CPU oracle on a bounded sample ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        from oracle.driver import OracleGraft
+        host_logits = [b.view(torch.int16).cpu().numpy().view(np.uint16) for b in pool_logits]
+        host_drafts = [{"parent": d["parent"].cpu().numpy(), "layer": d["layer"].cpu().numpy(),
+                        "logp": d["score"].cpu().numpy(), "tok": d["tok"].cpu().numpy()} for d in pool_drafts]
+        og = OracleGraft(cfg)
+        og.table = pipe.table.cpu().numpy()
+        og.set_roots(pipe.roots.cpu().numpy(), pipe.base_pos.cpu().numpy())
+        n_cpu = 0
+        c_start = time.perf_counter()
+        while True:
+            p = n_cpu % P
+            og.build(host_drafts[p])
+            og.verify_update(host_logits[p])
+            n_cpu += 1
+            el = time.perf_counter() - c_start
+            if el >= args.cpu_seconds or n_cpu >= 1000:
+                break
+        cpu = {"value": round(n_cpu / el, 3), "unit": "steps/s", "cores": O.num_threads(), "kind": "oracle",
+               "sample": "%d full oracle steps (B=16, V=151936, 61 rows/request) on host copies of the "
+                         "same pool inputs, %.1f s" % (n_cpu, el)}
+        log("cpu oracle: %d steps in %.1f s with %d threads" % (n_cpu, el, O.num_threads()))
+
+    out = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "graft_step_static_slots_b16_v151936", "batch": B, "vocab": V, "slots": cfg.slots,
+                   "rows_per_request": T1, "k": k, "layout": cfg.layout, "logits_bytes_per_step": bytes_logits,
+                   "pool_steps": P, "hip_graph": not args.no_graph},
+        "step_hbm_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"kernel": "k_topk_rows (graft_verify_update: row-wise top-k + acceptance walk + matrix update)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "kernel_us_mean": round(k_ms * 1e3, 3), "kernel_us_median": round(k_med * 1e3, 3),
+                     "alg_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    if copy_gbps is not None:
+        out["copy_1GiB_GBps"] = round(copy_gbps, 1)
+    if traffic is None:
+        out["roofline"]["traffic_note"] = tnote
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

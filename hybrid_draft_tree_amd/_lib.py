@@ -29,6 +29,7 @@ MAX_K = 8
 EXPORTS = (
     "graft_prune_select", "graft_template_master", "graft_retrieve_expand",
     "graft_build_tree_mask", "graft_verify_accept", "graft_update_topk",
+    "graft_build_hybrid_tree", "graft_verify_update",
     "graft_workspace_bytes", "graft_status_string",
 )
 
@@ -70,6 +71,9 @@ def load():
     L.graft_build_tree_mask.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P]
     L.graft_verify_accept.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
     L.graft_update_topk.argtypes = [I64, I, I, I, P, P, P, P, P, P, P, P, S, P]
+    L.graft_build_hybrid_tree.argtypes = [I, I, I, I, I, I, C.POINTER(PruneCfg), C.POINTER(Template), I, I,
+                                          P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P]
+    L.graft_verify_update.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
     L.graft_workspace_bytes.argtypes = [I64, I, I, I]
     L.graft_workspace_bytes.restype = S
     L.graft_status_string.argtypes = [I]
@@ -138,6 +142,22 @@ def graft_update_topk(n_rows, V, k, dtype, logits, topk_in, prob_in, row_tok, ta
     return _chk("graft_update_topk", load().graft_update_topk(
         n_rows, V, k, dtype, logits, topk_in, prob_in, row_tok, table, table_prob, topk_out,
         ws, ws_bytes, stream))
+
+
+def graft_build_hybrid_tree(B, Nd, T1, mode, layout, slots, cfg, tpl, V, k, table, root_tok, base_pos,
+                            d_parent, d_layer, d_score, d_tok, stage, n_keep, keep, cum_out, ret_tok,
+                            ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, stream):
+    return _chk("graft_build_hybrid_tree", load().graft_build_hybrid_tree(
+        B, Nd, T1, mode, layout, slots, C.byref(cfg), C.byref(tpl) if tpl is not None else None, V, k,
+        table, root_tok, base_pos, d_parent, d_layer, d_score, d_tok, stage, n_keep, keep, cum_out,
+        ret_tok, ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, stream))
+
+
+def graft_verify_update(B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob,
+                        accept_len, accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream):
+    return _chk("graft_verify_update", load().graft_verify_update(
+        B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob, accept_len,
+        accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream))
 
 
 def graft_workspace_bytes(n_rows, V, k, dtype):

@@ -69,7 +69,9 @@ int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const i
         for (int s = 0; s < 3; ++s)
             if (cfg->keep[s] < 0 || cfg->keep[s] > Nd) return GRAFT_EINVAL;
     }
-    launch_prune(B, Nd, mode, d_parent, d_layer, d_score, *cfg, stage, n_keep, keep, cum_out, stream);
+    PruneKernelArgs a{B, Nd, mode, d_parent, d_layer, d_score, *cfg, stage, n_keep, keep,
+                      mode == GRAFT_MODE_TREE ? cum_out : nullptr};
+    launch_prune(a, stream);
     return launch_status();
 }
 
@@ -128,8 +130,9 @@ int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_
     } else {
         if (!d_tok || Nd < 1 || Nd > GRAFT_MAX_ROWS || slots > r_out) return GRAFT_EINVAL;
     }
-    launch_retrieve(B, V, k, mode, slots, table, root_tok, n_keep, d_tok, Nd, tsize, tp, tr, td,
-                    ret_tok, ret_parent, n_ret, r_out, stream);
+    RetrieveKernelArgs a{B, V, k, mode, slots, table, root_tok, n_keep, d_tok, Nd, tsize, tp, tr, td,
+                         ret_tok, ret_parent, n_ret, r_out};
+    launch_retrieve(a, stream);
     return launch_status();
 }
 
@@ -152,8 +155,113 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
         return GRAFT_EINVAL;
     if (layout != GRAFT_LAYOUT_CHAIN && !d_parent) return GRAFT_EINVAL;
     if (!aligned(anc, 8)) return GRAFT_EINVAL;
-    launch_flatten(B, Nd, T1, layout, root_tok, base_pos, d_tok, d_parent, keep, n_keep, ret_tok,
-                   ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, stream);
+    FlattenKernelArgs a{B, Nd, T1, layout, root_tok, base_pos, d_tok, d_parent, keep, n_keep, ret_tok,
+                        ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc};
+    launch_flatten(a, stream);
+    return launch_status();
+}
+
+int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slots,
+                            const graft_prune_cfg *cfg, const graft_template *tpl, int V, int k,
+                            const int32_t *table, const int32_t *root_tok, const int32_t *base_pos,
+                            const int32_t *d_parent, const int32_t *d_layer, const float *d_score,
+                            const int32_t *d_tok, int32_t *stage, int32_t *n_keep, uint8_t *keep,
+                            float *cum_out, int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret,
+                            int r_out, int32_t *tok, int32_t *parent, int32_t *depth, int32_t *pos_id,
+                            uint64_t *anc, hipStream_t stream) {
+    if (mode != GRAFT_MODE_TREE && mode != GRAFT_MODE_TAIL) return GRAFT_EUNSUPPORTED;
+    if (layout != GRAFT_LAYOUT_COMPACT && layout != GRAFT_LAYOUT_IN_PLACE && layout != GRAFT_LAYOUT_CHAIN)
+        return GRAFT_EUNSUPPORTED;
+    if ((mode == GRAFT_MODE_TAIL) != (layout == GRAFT_LAYOUT_CHAIN)) return GRAFT_EUNSUPPORTED;
+    if (B < 0 || Nd < 1 || Nd > GRAFT_MAX_ROWS || T1 < 2 || T1 > GRAFT_MAX_ROWS || r_out < 1 ||
+        r_out > GRAFT_MAX_ROWS || V < 1 || k < 1 || k > GRAFT_MAX_K || slots < 0 || !cfg)
+        return GRAFT_EINVAL;
+    if (T1 != slots + 1) return GRAFT_EINVAL;
+    if (layout == GRAFT_LAYOUT_IN_PLACE && T1 != Nd + 1) return GRAFT_EINVAL;
+    if (B == 0) return GRAFT_OK;
+    if (!table || !root_tok || !base_pos || !d_score || !d_tok || !stage || !n_keep || !keep ||
+        !ret_tok || !ret_parent || !n_ret || !tok || !parent || !depth || !pos_id || !anc)
+        return GRAFT_EINVAL;
+    if (!aligned(anc, 8)) return GRAFT_EINVAL;
+    BuildKernelArgs a{};
+    if (mode == GRAFT_MODE_TREE) {
+        if (!d_parent || !d_layer || !tpl || tpl->size < 0 || tpl->size > GRAFT_MAX_ROWS) return GRAFT_EINVAL;
+        if (tpl->size > 0 && (!tpl->parent || !tpl->rank || !tpl->depth)) return GRAFT_EINVAL;
+        if (r_out < tpl->size) return GRAFT_EINVAL;
+        for (int s = 0; s < 3; ++s)
+            if (cfg->keep[s] < 0 || cfg->keep[s] > Nd || slots - cfg->keep[s] > tpl->size ||
+                slots - cfg->keep[s] < 0)
+                return GRAFT_EINVAL;
+        a.tpl_size = tpl->size;
+        a.tpl_parent = tpl->parent;
+        a.tpl_rank = tpl->rank;
+        a.tpl_depth = tpl->depth;
+    } else {
+        if (slots > r_out || slots > Nd) return GRAFT_EINVAL;
+    }
+    a.B = B;
+    a.Nd = Nd;
+    a.T1 = T1;
+    a.mode = mode;
+    a.layout = layout;
+    a.slots = slots;
+    a.V = V;
+    a.k = k;
+    a.cfg = *cfg;
+    a.table = table;
+    a.root_tok = root_tok;
+    a.base_pos = base_pos;
+    a.d_parent = d_parent;
+    a.d_layer = d_layer;
+    a.d_score = d_score;
+    a.d_tok = d_tok;
+    a.stage = stage;
+    a.n_keep = n_keep;
+    a.keep = keep;
+    a.cum_out = mode == GRAFT_MODE_TREE ? cum_out : nullptr;
+    a.ret_tok = ret_tok;
+    a.ret_parent = ret_parent;
+    a.n_ret = n_ret;
+    a.r_out = r_out;
+    a.tok = tok;
+    a.parent = parent;
+    a.depth = depth;
+    a.pos_id = pos_id;
+    a.anc = anc;
+    launch_build(a, stream);
+    return launch_status();
+}
+
+int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logits, const int32_t *tok,
+                        const int32_t *parent, const int32_t *depth, int32_t *table, float *table_prob,
+                        int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
+                        int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
+    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || k < 1 || k > GRAFT_MAX_K || k > V ||
+        dmax < 0)
+        return GRAFT_EINVAL;
+    if (B == 0) return GRAFT_OK;
+    if (!logits || !tok || !parent || !depth || !table || !topk || !accept_len || !bonus ||
+        (dmax > 0 && !accept_idx) || !ws || (table_prob && !topk_prob))
+        return GRAFT_EINVAL;
+    if (!aligned(logits, 16) || !aligned(ws, 256)) return GRAFT_EINVAL;
+    const int64_t n_rows = (int64_t)B * T1;
+    const WsLayout L = ws_layout(n_rows, V, k, dtype);
+    if (ws_bytes < L.total) return GRAFT_EINVAL;
+    VerifyArgs v;
+    v.T1 = T1;
+    v.tok = tok;
+    v.parent = parent;
+    v.depth = depth;
+    v.accept_len = accept_len;
+    v.accept_idx = accept_idx;
+    v.dmax = dmax;
+    v.bonus = bonus;
+    v.base_pos_io = base_pos_io;
+    v.table = table;
+    v.table_prob = table_prob;
+    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, ws, &v, stream);
     return launch_status();
 }
 

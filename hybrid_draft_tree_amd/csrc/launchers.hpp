@@ -1,5 +1,6 @@
-// Internal launch functions shared by the C-ABI layer (graft_api.hip) and the
-// kernel translation units.  Arguments are validated by the caller.
+// Internal launch interface shared by the C-ABI layer (graft_api.hip) and the
+// kernel translation units.  Arguments are validated by the caller; every
+// struct is passed to its kernel by value.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,24 +11,60 @@
 namespace graft {
 
 // ---- tree build (tree_kernels.hip) --------------------------------------------------
-void launch_prune(int B, int Nd, int mode, const int32_t *parent, const int32_t *layer,
-                  const float *score, const graft_prune_cfg &cfg, int32_t *stage, int32_t *n_keep,
-                  uint8_t *keep, float *cum_out, hipStream_t s);
+struct PruneKernelArgs {
+    int B, Nd, mode;
+    const int32_t *parent, *layer;
+    const float *score;
+    graft_prune_cfg cfg;
+    int32_t *stage, *n_keep;
+    uint8_t *keep;
+    float *cum_out;
+};
 
-void launch_retrieve(int B, int V, int k, int mode, int slots, const int32_t *table,
-                     const int32_t *root_tok, const int32_t *n_keep, const int32_t *d_tok, int Nd,
-                     int tpl_size, const int32_t *tpl_parent, const int32_t *tpl_rank,
-                     const int32_t *tpl_depth, int32_t *ret_tok, int32_t *ret_parent,
-                     int32_t *n_ret, int r_out, hipStream_t s);
+struct RetrieveKernelArgs {
+    int B, V, k, mode, slots;
+    const int32_t *table, *root_tok, *n_keep, *d_tok;
+    int Nd;
+    int tpl_size;
+    const int32_t *tpl_parent, *tpl_rank, *tpl_depth;
+    int32_t *ret_tok, *ret_parent, *n_ret;
+    int r_out;
+};
 
-void launch_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
-                    const int32_t *base_pos, const int32_t *d_tok, const int32_t *d_parent,
-                    const uint8_t *keep, const int32_t *n_keep, const int32_t *ret_tok,
-                    const int32_t *ret_parent, const int32_t *n_ret, int r_out, int32_t *tok,
-                    int32_t *parent, int32_t *depth, int32_t *pos_id, uint64_t *anc,
-                    hipStream_t s);
+struct FlattenKernelArgs {
+    int B, Nd, T1, layout;
+    const int32_t *root_tok, *base_pos, *d_tok, *d_parent;
+    const uint8_t *keep;
+    const int32_t *n_keep, *ret_tok, *ret_parent, *n_ret;
+    int r_out;
+    int32_t *tok, *parent, *depth, *pos_id;
+    uint64_t *anc;
+};
 
-// ---- row-wise top-k + fused acceptance walk (topk_kernels.hip) ----------------------
+struct BuildKernelArgs {
+    int B, Nd, T1, mode, layout, slots, V, k;
+    graft_prune_cfg cfg;
+    int tpl_size;
+    const int32_t *tpl_parent, *tpl_rank, *tpl_depth;
+    const int32_t *table, *root_tok, *base_pos;
+    const int32_t *d_parent, *d_layer;
+    const float *d_score;
+    const int32_t *d_tok;
+    int32_t *stage, *n_keep;
+    uint8_t *keep;
+    float *cum_out;
+    int32_t *ret_tok, *ret_parent, *n_ret;
+    int r_out;
+    int32_t *tok, *parent, *depth, *pos_id;
+    uint64_t *anc;
+};
+
+void launch_prune(const PruneKernelArgs &a, hipStream_t s);
+void launch_retrieve(const RetrieveKernelArgs &a, hipStream_t s);
+void launch_flatten(const FlattenKernelArgs &a, hipStream_t s);
+void launch_build(const BuildKernelArgs &a, hipStream_t s);
+
+// ---- row-wise top-k + fused acceptance walk / matrix update (topk_kernels.hip) ------
 struct TopkPlan {
     int64_t n_rows = 0;
     int V = 0;
@@ -36,8 +73,9 @@ struct TopkPlan {
     size_t partial_bytes = 0;
     size_t stats_bytes = 0;
     size_t off_stats = 0;     // workspace offsets
-    size_t off_counters = 0;
-    size_t ws_bytes = 0;      // bytes of workspace the kernel uses (zeroed counters inside)
+    size_t off_counters = 0;  // row counters [n_rows], request counters [n_rows]
+    size_t off_occ = 0;       // last occurrence per token [V], registration counter, hand-offs [n_rows]
+    size_t ws_bytes = 0;      // workspace bytes the kernel uses (all counters zero between calls)
 };
 
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype);
@@ -47,7 +85,7 @@ struct TopkArgs {
     int64_t n_rows;
     int V, S, chunk;
     uint64_t *partials;
-    float2 *stats;
+    uint64_t *stats;   // (max, sum) fp32 pairs
     uint32_t *row_cnt;
     int k;
     int32_t *topk;
@@ -65,12 +103,19 @@ struct VerifyArgs {
     int32_t *bonus = nullptr;
     int32_t *base_pos_io = nullptr;
     uint32_t *req_cnt = nullptr;
+    // fused matrix update (table != nullptr)
+    int32_t *table = nullptr;
+    float *table_prob = nullptr;
+    int32_t *last_occ = nullptr;   // [V] row+1 of the last row holding each token
+    uint32_t *reg_cnt = nullptr;   // rows registered
+    uint32_t *handoff = nullptr;   // [B] accept-done / registration-done hand-off
+    int B = 0;
 };
 
 // Row-wise top-k of logits [n_rows, V] into topk [n_rows, k] (+ probabilities);
 // with `verify` the acceptance walk of every request (n_rows = B * verify->T1)
-// runs in the same launch.  The workspace counters must be zero on entry and
-// are zero again on exit.
+// runs in the same launch, and with verify->table the matrix update too.  The
+// workspace counters must be zero on entry and are zero again on exit.
 void launch_topk(const TopkPlan &plan, int dtype, const void *logits, int k, int32_t *topk,
                  float *prob, void *ws, const VerifyArgs *verify, hipStream_t s);
 

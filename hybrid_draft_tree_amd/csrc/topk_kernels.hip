@@ -23,8 +23,9 @@ namespace graft {
 namespace {
 
 constexpr int kWavesPerBlockA = 4;
-constexpr int kLoadsInFlight = 4;  // U: 16-byte loads per lane per batch
-constexpr int kCap = kWave * (kLoadsInFlight + 1);
+constexpr int kLoadsInFlight = 2;  // U: 16-byte loads per lane per batch
+template <int U>
+constexpr int kCapOf = kWave * (U + 1);  // pending groups per wave
 constexpr int kTop = 8;
 
 typedef short short2v __attribute__((ext_vector_type(2)));
@@ -67,6 +68,14 @@ struct Bf16Traits {
         const int off = (int)(0xffffu - (r & 0xffffu));
         return rank64(rank_key(r) * 65536, (uint32_t)(col0 + off));
     }
+    // Largest raw bit pattern of the group read as int16 (equals the largest key
+    // whenever that is positive).
+    __device__ static int raw_max(const uint4 &d) {
+        const short2v m = __builtin_elementwise_max(
+            __builtin_elementwise_max(as_s2(d.x), as_s2(d.y)), __builtin_elementwise_max(as_s2(d.z), as_s2(d.w)));
+        return max((int)m.x, (int)m.y);
+    }
+    static constexpr int kRawMin = -32768;
     // Superset filter: does any element of the group have key >= thr?
     __device__ static bool group_pass(const uint4 &d, int thr) {
         if (thr >= 1) {
@@ -101,6 +110,10 @@ struct F32Traits {
     __device__ static uint64_t to_row_rank(Rank r, int col0) {
         return rank64(rank64_key(r), (uint32_t)col0 + rank64_id(r));
     }
+    __device__ static int raw_max(const uint4 &d) {
+        return max(max((int)d.x, (int)d.y), max((int)d.z, (int)d.w));
+    }
+    static constexpr int kRawMin = INT_MIN;
     __device__ static bool group_pass(const uint4 &d, int thr) {
         if (thr >= 1) {
             const int m = max(max((int)d.x, (int)d.y), max((int)d.z, (int)d.w));
@@ -143,6 +156,43 @@ __device__ __forceinline__ Rank merge_top8(Rank (&c)[N], Rank &top) {
     return kth;
 }
 
+// Same result as merge_top8, cheaper when few candidates are live: if they fit
+// one per lane next to the current top-8, compact them through the wave's LDS
+// scratch (64 entries) and extract the 8 largest with one value per lane.
+template <typename Rank, int N>
+__device__ __forceinline__ Rank merge_top8_compact(Rank (&c)[N], Rank &top, Rank *scratch) {
+    const int lane = lane_id();
+    uint64_t bal[N];
+    int total = 0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        bal[e] = ballot(c[e] != 0);
+        total += __popcll(bal[e]);
+    }
+    if (total + kTop > kWave) return merge_top8<Rank, N>(c, top);
+    int base = 0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        if (c[e] != 0) scratch[base + lanes_below(bal[e])] = c[e];
+        base += __popcll(bal[e]);
+    }
+    if (lane < kTop) scratch[total + lane] = top;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    Rank v = lane < total + kTop ? scratch[lane] : (Rank)0;
+    __builtin_amdgcn_wave_barrier();
+    Rank newtop = 0, kth = 0;
+#pragma unroll
+    for (int j = 0; j < kTop; ++j) {
+        const Rank M = wave_max_rank<Rank>(v);
+        if (lane == j) newtop = M;
+        kth = M;
+        if (v == M) v = 0;
+    }
+    top = newtop;
+    return kth;
+}
+
 struct SoftStats {
     float m = -INFINITY;
     float s = 0.0f;
@@ -166,19 +216,24 @@ __device__ __forceinline__ void merge_row(const TopkArgs &a, int64_t row) {
 #pragma unroll
     for (int i = 0; i < kMaxPerLaneB; ++i) {
         const int j = i * kWave + lane;
-        c[i] = j < n ? a.partials[row * n + j] : 0ull;
+        c[i] = j < n ? ld_agent(&a.partials[row * n + j]) : 0ull;
     }
     uint64_t top = 0;
     merge_top8<uint64_t, kMaxPerLaneB>(c, top);
-    if (lane < a.k) a.topk[row * a.k + lane] = top ? (int32_t)rank64_id(top) : -1;
+    if (lane < a.k) st_agent(&a.topk[row * a.k + lane], top ? (int32_t)rank64_id(top) : -1);
     if (a.prob) {
-        const float2 sv = lane < a.S ? a.stats[row * a.S + lane] : make_float2(-INFINITY, 0.0f);
+        float2 sv = make_float2(-INFINITY, 0.0f);
+        if (lane < a.S) {
+            const uint64_t u = ld_agent(&a.stats[row * a.S + lane]);
+            sv = make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+        }
         const float M = wave_max_f32(sv.x);
         const float s = (sv.x == -INFINITY) ? 0.0f : sv.y * __expf(sv.x - M);
         const float Ssum = wave_sum_f32(s);
         if (lane < a.k) {
             const float x = key_to_f32(rank64_key(top));
-            a.prob[row * a.k + lane] = top ? __expf(x - M) / Ssum : 0.0f;
+            const float pj = top ? __expf(x - M) / Ssum : 0.0f;
+            st_agent((int32_t *)&a.prob[row * a.k + lane], __float_as_int(pj));
         }
     }
 }
@@ -187,12 +242,12 @@ __device__ __forceinline__ void merge_row(const TopkArgs &a, int64_t row) {
 // lane f is flattened row f.  A row is accepted iff every row on its path from
 // the root carries the greedy token of its parent row; the deepest accepted row
 // wins, ties -> lowest row.
-__device__ __forceinline__ void accept_walk(const VerifyArgs &v, int k, const int32_t *topk, int b) {
+__device__ __forceinline__ void accept_walk(const VerifyArgs &v, int k, int32_t *topk, int b) {
     const int lane = lane_id();
     const int T1 = v.T1;
     const bool row = lane < T1;
     const size_t o = (size_t)b * T1 + lane;
-    const int g = row ? topk[o * k] : -1;
+    const int g = row ? ld_agent(&topk[o * k]) : -1;
     const int t = row ? v.tok[o] : -1;
     const int p = (row && lane > 0) ? v.parent[o] : -1;
     const int d = row ? v.depth[o] : 0;
@@ -232,21 +287,85 @@ __device__ __forceinline__ void accept_walk(const VerifyArgs &v, int k, const in
     }
 }
 
-template <typename TR, bool PROB, bool ACCEPT, bool NT>
+// Matrix update for the rows of request b (one wavefront, lane f = row b*T1+f):
+// a row writes its top-k into the matrix row of its token iff it is the last
+// row of the whole batch holding that token (highest row wins), then clears
+// that token's registration.  Called once every row is registered and the
+// request's rows are merged.
+__device__ __forceinline__ void update_request(const VerifyArgs &v, int V, int k, int32_t *topk,
+                                               const float *prob, int b) {
+    const int lane = lane_id();
+    if (lane >= v.T1) return;
+    const int64_t P = (int64_t)b * v.T1 + lane;
+    const int t = v.tok[P];
+    if (t < 0 || t >= V) return;
+    if (ld_agent(&v.last_occ[t]) != (int32_t)(P + 1)) return;
+    for (int j = 0; j < k; ++j) v.table[(size_t)t * k + j] = ld_agent(&topk[P * k + j]);
+    if (v.table_prob)
+        for (int j = 0; j < k; ++j)
+            v.table_prob[(size_t)t * k + j] = __int_as_float(ld_agent((const int32_t *)&prob[P * k + j]));
+    st_agent(&v.last_occ[t], 0);
+}
+
+// Hand-off between "request b accepted" and "every row registered": the second
+// of the two arrivals runs request b's update.  Returns true for the second.
+__device__ __forceinline__ bool handoff_second(const VerifyArgs &v, int b) {
+    uint32_t prev = 0;
+    if (lane_id() == 0) prev = count_in(&v.handoff[b]);
+    prev = (uint32_t)readlane_i32((int)prev, 0);
+    return prev == 1u;
+}
+
+template <typename TR, bool PROB, bool ACCEPT, bool NT, int U = kLoadsInFlight>
 __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a, VerifyArgs v) {
     using Rank = typename TR::Rank;
     constexpr int EPG = TR::kPerGroup;
     constexpr int ESZ = 16 / EPG;
-    __shared__ uint4 s_data[kWavesPerBlockA][kCap];
-    __shared__ uint16_t s_gidx[kWavesPerBlockA][kCap];
+    __shared__ uint4 s_data[kWavesPerBlockA][kCapOf<U>];
+    __shared__ uint16_t s_gidx[kWavesPerBlockA][kCapOf<U>];
+    __shared__ Rank s_merge[kWavesPerBlockA][kWave];
 
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6;
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlockA + wv;
     const int S = a.S;
+    Rank *scratch = s_merge[wv];
     if (w >= a.n_rows * S) return;
     const int64_t row = w / S;
     const int split = (int)(w - row * S);
+    if constexpr (ACCEPT) {
+        if (v.table && split == 0) {
+            // Register this row as a holder of its token (highest row wins the
+            // matrix row); the last row to register completes every request's
+            // hand-off.
+            if (lane == 0) {
+                const int t = v.tok[row];
+                if (t >= 0 && t < a.V)
+                    __hip_atomic_fetch_max(&v.last_occ[t], (int32_t)(row + 1), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
+            publish();
+            uint32_t prev = 0;
+            if (lane == 0) prev = count_in(v.reg_cnt);
+            prev = (uint32_t)readlane_i32((int)prev, 0);
+            if (prev == (uint32_t)(a.n_rows - 1)) {
+                after_count();
+                for (int b0 = 0; b0 < v.B; b0 += kWave) {
+                    const int b = b0 + lane;
+                    uint32_t old = 0;
+                    if (b < v.B) old = count_in(&v.handoff[b]);
+                    uint64_t second = ballot(b < v.B && old == 1u);
+                    while (second) {
+                        const int j = __ffsll((unsigned long long)second) - 1;
+                        second &= second - 1;
+                        update_request(v, a.V, a.k, a.topk, a.prob, b0 + j);
+                        if (lane == 0) st_agent(&v.handoff[b0 + j], 0u);
+                    }
+                }
+                if (lane == 0) st_agent(v.reg_cnt, 0u);
+            }
+        }
+    }
     const int c0 = split * a.chunk;
     const int c1 = min(a.V, c0 + a.chunk);
     const char *rowp = (const char *)a.logits + (size_t)row * (size_t)a.V * ESZ;
@@ -310,24 +429,26 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
 #pragma unroll
                 for (int e = 0; e < EPG; ++e) c[e] = 0;
             }
-            if (ballot(any)) kth = merge_top8<Rank, EPG>(c, top);
+            if (ballot(any)) kth = merge_top8_compact<Rank, EPG>(c, top, scratch);
         }
         count = 0;
         thr = kth ? TR::rank_key(kth) : INT_MIN;
     };
 
-    for (int g0 = 0; g0 < ng; g0 += kWave * kLoadsInFlight) {
-        uint4 d[kLoadsInFlight];
+    // Software-pipelined stream: the next batch's loads are in flight while the
+    // current batch is filtered.  Loads are never predicated (indices past the
+    // range are clamped to its last group and the data ignored), so the
+    // compiler's wait counts only the older batch.
+    auto issue = [&](uint4 (&d)[U], int g0) {
 #pragma unroll
-        for (int u = 0; u < kLoadsInFlight; ++u) {
-            const int gi = g0 + u * kWave + lane;
-            if (gi < ng)
-                d[u] = load16<NT>(vp + gi);
-            else
-                d[u] = make_uint4(0u, 0u, 0u, 0u);
+        for (int u = 0; u < U; ++u) {
+            const int gi = min(g0 + u * kWave + lane, ng - 1);
+            d[u] = load16<NT>(vp + gi);
         }
+    };
+    auto filter = [&](const uint4 (&d)[U], int g0) {
 #pragma unroll
-        for (int u = 0; u < kLoadsInFlight; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int gi = g0 + u * kWave + lane;
             const bool inb = gi < ng;
             if constexpr (PROB) {
@@ -347,11 +468,41 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
                 count += __popcll(bal);
             }
         }
-        if (count > kCap - kWave * kLoadsInFlight) {
+        if (count > kCapOf<U> - kWave * U) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             process();
         }
+    };
+
+    if (ng > 0) {
+        uint4 cur[U], nxt[U];
+        issue(cur, 0);
+        {
+            // Seed the threshold: the 8th largest lane maximum of the first batch is a
+            // lower bound of the range's 8th best key when it is positive (8 distinct
+            // elements reach it), so the first batch is filtered like the rest.
+            int m = TR::kRawMin;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (u * kWave + lane < ng) m = max(m, TR::raw_max(cur[u]));
+            int m8 = TR::kRawMin;
+#pragma unroll
+            for (int j = 0; j < kTop; ++j) {
+                m8 = wave_max_i32(m);
+                const uint64_t own = ballot(m == m8);
+                if (lane == __ffsll((unsigned long long)own) - 1) m = TR::kRawMin;
+            }
+            if (m8 >= 1 && m8 > thr) thr = m8;
+        }
+        int g0 = 0;
+        for (; g0 + kWave * U < ng; g0 += kWave * U) {
+            issue(nxt, g0 + kWave * U);
+            filter(cur, g0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+        filter(cur, g0);
     }
     if (count) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -363,31 +514,40 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
     // (device-scope counter) merges the row; with ACCEPT, the last row of a
     // request to be merged runs that request's acceptance walk.  Counters are
     // reset by the wave that consumed them, so the workspace is left zeroed.
-    if (lane < kTop) a.partials[w * kTop + lane] = top ? TR::to_row_rank(top, c0) : 0ull;
+    if (lane < kTop) st_agent(&a.partials[w * kTop + lane], top ? TR::to_row_rank(top, c0) : 0ull);
     if constexpr (PROB) {
         const float M = wave_max_f32(st.m);
         const float s = (st.m == -INFINITY) ? 0.0f : st.s * __expf(st.m - M);
         const float Ssum = wave_sum_f32(s);
-        if (lane == 0) a.stats[w] = make_float2(M, Ssum);
+        if (lane == 0)
+            st_agent(&a.stats[w], ((uint64_t)__float_as_uint(Ssum) << 32) | __float_as_uint(M));
     }
-    __threadfence();
+    publish();
     uint32_t prev = 0;
-    if (lane == 0) prev = atomicAdd(&a.row_cnt[row], 1u);
-    prev = __shfl(prev, 0);
+    if (lane == 0) prev = count_in(&a.row_cnt[row]);
+    prev = (uint32_t)readlane_i32((int)prev, 0);
     if (prev != (uint32_t)(S - 1)) return;
-    __threadfence();
+    after_count();
     merge_row(a, row);
-    if (lane == 0) a.row_cnt[row] = 0u;
+    if (lane == 0) st_agent(&a.row_cnt[row], 0u);
     if constexpr (ACCEPT) {
         const int b = (int)(row / v.T1);
-        __threadfence();
+        publish();
         uint32_t prev_r = 0;
-        if (lane == 0) prev_r = atomicAdd(&v.req_cnt[b], 1u);
-        prev_r = __shfl(prev_r, 0);
+        if (lane == 0) prev_r = count_in(&v.req_cnt[b]);
+        prev_r = (uint32_t)readlane_i32((int)prev_r, 0);
         if (prev_r != (uint32_t)(v.T1 - 1)) return;
-        __threadfence();
+        after_count();
         accept_walk(v, a.k, a.topk, b);
-        if (lane == 0) v.req_cnt[b] = 0u;
+        if (lane == 0) st_agent(&v.req_cnt[b], 0u);
+        if (v.table) {
+            publish();
+            if (handoff_second(v, b)) {
+                after_count();
+                update_request(v, a.V, a.k, a.topk, a.prob, b);
+                if (lane == 0) st_agent(&v.handoff[b], 0u);
+            }
+        }
     }
 }
 
@@ -435,10 +595,12 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     p.chunk = chunk;
     p.partial_bytes = (size_t)n_rows * S * kTop * sizeof(uint64_t);
     p.stats_bytes = (size_t)n_rows * S * sizeof(float2);
-    // workspace: [partials | stats | row counters, request counters]
+    // workspace: [partials | stats | row counters, request counters |
+    //             last occurrence per token [V], registration counter, hand-offs]
     p.off_stats = (p.partial_bytes + 255) / 256 * 256;
     p.off_counters = p.off_stats + (p.stats_bytes + 255) / 256 * 256;
-    p.ws_bytes = p.off_counters + ((size_t)n_rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+    p.off_occ = p.off_counters + ((size_t)n_rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+    p.ws_bytes = p.off_occ + ((size_t)(V + 1 + n_rows) * sizeof(uint32_t) + 255) / 256 * 256;
     return p;
 }
 
@@ -452,7 +614,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     a.S = p.splits;
     a.chunk = p.chunk;
     a.partials = (uint64_t *)ws;
-    a.stats = (float2 *)((char *)ws + p.off_stats);
+    a.stats = (uint64_t *)((char *)ws + p.off_stats);
     a.row_cnt = (uint32_t *)((char *)ws + p.off_counters);
     a.k = k;
     a.topk = topk;
@@ -461,6 +623,10 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     if (verify) {
         v = *verify;
         v.req_cnt = a.row_cnt + p.n_rows;
+        v.last_occ = (int32_t *)((char *)ws + p.off_occ);
+        v.reg_cnt = (uint32_t *)(v.last_occ + p.V);
+        v.handoff = v.reg_cnt + 1;
+        v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
     }
     if (dtype == GRAFT_DTYPE_BF16)
         launch_rows<Bf16Traits>(a, verify ? &v : nullptr, s);

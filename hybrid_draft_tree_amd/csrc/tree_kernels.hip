@@ -3,28 +3,37 @@
 // as described in section 二 of the news write-up of arXiv 2605.20104, with
 // the TAIL variant of section 七 and the static-slot layout of section 四.
 //
-// Each request is one wavefront: lanes are draft nodes, template nodes or
-// flattened rows (all <= 64).  Cross-lane traffic uses shuffles and ballots;
-// no LDS except the row-placement scatter of the flatten.
+// Each step of a request runs in one wavefront (lanes are draft nodes, template
+// nodes or flattened rows, all <= 64) as a device function.  The standalone
+// kernels behind graft_prune_select / graft_retrieve_expand /
+// graft_build_tree_mask run one function each; k_build_tree runs all three in
+// one launch with one workgroup per request, the retrieval chain (dependent
+// gathers, latency-bound) in one wavefront while the other prunes.
 #include "device_utils.hpp"
 #include "launchers.hpp"
 
 namespace graft {
 namespace {
 
-constexpr int kReqPerBlock = 4;  // requests (wavefronts) per workgroup
+constexpr int kReqPerBlock = 4;  // requests (wavefronts) per workgroup, standalone kernels
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Depth below the root of every node, by pointer doubling over parent links
-// (parent < 0 = child of the root, depth 1).  Lanes >= n report 0.
+// (parent < 0 = child of the root, depth 1).  Invalid lanes report 0.
 __device__ __forceinline__ int node_depth(int par, bool valid) {
-    int lane = lane_id();
+    const int lane = lane_id();
     int a = valid ? par : -1;
     int d = valid ? 1 : 0;
 #pragma unroll
     for (int r = 0; r < 6; ++r) {
-        int src = a >= 0 ? a : lane;
-        int da = __shfl(d, src);
-        int aa = __shfl(a, src);
+        const int src = a >= 0 ? a : lane;
+        const int da = __shfl(d, src);
+        const int aa = __shfl(a, src);
         if (a >= 0) {
             d += da;
             a = aa;
@@ -33,32 +42,27 @@ __device__ __forceinline__ int node_depth(int par, bool valid) {
     return d;
 }
 
-// ---------------------------------------------------------------------------------------
-// Gear 1: prune-select.
-__global__ __launch_bounds__(kWave *kReqPerBlock) void k_prune_tree(
-    int B, int Nd, const int32_t *__restrict__ parent, const int32_t *__restrict__ layer,
-    const float *__restrict__ score, graft_prune_cfg cfg, int32_t *__restrict__ stage_out,
-    int32_t *__restrict__ n_keep_out, uint8_t *__restrict__ keep_out, float *__restrict__ cum_out) {
-    const int lane = lane_id();
-    const int b = blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
-    if (b >= B) return;
-    const bool valid = lane < Nd;
-    const size_t o = (size_t)b * Nd + lane;
-    const int par = valid ? parent[o] : -1;
-    const int lay = valid ? layer[o] : 0x7fffffff;
-    const float lp = valid ? score[o] : 0.0f;
+struct PruneOut {
+    int stage;   // uniform
+    int N;       // uniform: kept draft nodes
+    bool kept;   // this lane's node
+    float cum;   // this lane's cumulative log-confidence
+};
 
-    // cum[i] = cum[parent] + logp[i]: one fp32 add per node, level by level so the
-    // parent's value is final when read (same association as the definition).
+// Gear 1 (TREE): cum[i] = cum[parent] + logp[i] in fp32, level by level so the
+// parent's value is final when read (the association of the definition);
+// checkpoints in drafting order, the first that fires is the stage; keep the
+// N nodes of layers <= c_s with the largest cum (ties -> lower index).
+__device__ __forceinline__ PruneOut prune_tree_wave(bool valid, int par, int lay, float lp, int Nd,
+                                                   const graft_prune_cfg &cfg) {
+    const int lane = lane_id();
     const int dep = node_depth(par, valid);
     const int maxd = wave_max_i32(dep);
     float cum = 0.0f;
     for (int d = 1; d <= maxd; ++d) {
-        float pc = __shfl(cum, par >= 0 ? par : lane);
+        const float pc = __shfl(cum, par >= 0 ? par : lane);
         if (valid && dep == d) cum = (par >= 0 ? pc : 0.0f) + lp;
     }
-
-    // Checkpoints in drafting order; the first that fires is the stage.
     int st = 3;
     for (int s = 0; s < 3; ++s) {
         const int c = cfg.ckpt_layer[s];
@@ -74,63 +78,31 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_prune_tree(
     const int climit = st < 3 ? cfg.ckpt_layer[st] : 0x7fffffff;
     const bool elig = valid && lay <= climit;
     const uint64_t emask = ballot(elig);
-
-    // rank among eligible nodes by (cum desc, index asc)
     int rank = 0;
     for (int j = 0; j < Nd; ++j) {
-        const float cj = __shfl(cum, j);
+        const float cj = readlane_f32(cum, j);
         const bool ej = (emask >> j) & 1ull;
         rank += (ej && (cj > cum || (cj == cum && j < lane))) ? 1 : 0;
     }
-    const bool kept = elig && rank < N;
-    if (valid) {
-        keep_out[o] = kept ? 1 : 0;
-        if (cum_out) cum_out[o] = cum;
-    }
-    if (lane == 0) {
-        stage_out[b] = st;
-        n_keep_out[b] = N;
-    }
+    return {st, N, elig && rank < N, cum};
 }
 
-// TAIL (section 七): longest prefix of the block with confidence >= tail_thr.
-__global__ __launch_bounds__(kWave *kReqPerBlock) void k_prune_tail(
-    int B, int Nd, const float *__restrict__ conf, float thr, int32_t *__restrict__ stage_out,
-    int32_t *__restrict__ n_keep_out, uint8_t *__restrict__ keep_out) {
+// TAIL (section 七): the longest prefix of the block with confidence >= thr.
+__device__ __forceinline__ PruneOut prune_tail_wave(bool valid, float conf, int Nd, float thr) {
     const int lane = lane_id();
-    const int b = blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
-    if (b >= B) return;
-    const bool valid = lane < Nd;
-    const float c = valid ? conf[(size_t)b * Nd + lane] : 1.0f;
-    const uint64_t low = ballot(valid && !(c >= thr));
+    const uint64_t low = ballot(valid && !(conf >= thr));
     const int p = low ? (__ffsll((unsigned long long)low) - 1) : Nd;
-    if (valid) keep_out[(size_t)b * Nd + lane] = lane < p ? 1 : 0;
-    if (lane == 0) {
-        n_keep_out[b] = p;
-        stage_out[b] = p < Nd ? 0 : 3;
-    }
+    return {p < Nd ? 0 : 3, p, lane < p, 0.0f};
 }
 
-// ---------------------------------------------------------------------------------------
-// Gear 2: retrieval from the continuation matrix.  Template node t (a lane) reads
-// one entry of the row of its parent's token; depth levels are dependent gathers.
-__global__ __launch_bounds__(kWave *kReqPerBlock) void k_retrieve_tree(
-    int B, int V, int k, int slots, const int32_t *__restrict__ table,
-    const int32_t *__restrict__ root_tok, const int32_t *__restrict__ n_keep, int tpl_size,
-    const int32_t *__restrict__ tpl_parent, const int32_t *__restrict__ tpl_rank,
-    const int32_t *__restrict__ tpl_depth, int32_t *__restrict__ ret_tok,
-    int32_t *__restrict__ ret_parent, int32_t *__restrict__ n_ret, int r_out) {
+// Gear 2 (TREE): template node t (lane t < R) reads one entry of the matrix row
+// of its parent's token (the root's for root children); depth levels are
+// dependent gathers.  Returns the node's token (-1 for lanes >= R).
+__device__ __forceinline__ int retrieve_tree_wave(int R, int tp, int tr, int td, int root,
+                                                  const int32_t *__restrict__ table, int V, int k) {
     const int lane = lane_id();
-    const int b = blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
-    if (b >= B) return;
-    int R = slots - n_keep[b];
-    R = R < 0 ? 0 : (R > tpl_size ? tpl_size : R);
     const bool act = lane < R;
-    const int tp = act ? tpl_parent[lane] : -1;
-    const int tr = act ? tpl_rank[lane] : 0;
-    const int td = act ? tpl_depth[lane] : 0;
-    const int root = root_tok[b];
-    const int maxd = wave_max_i32(td);
+    const int maxd = wave_max_i32(act ? td : 0);
     int val = -1;
     for (int d = 1; d <= maxd; ++d) {
         const int pv = __shfl(val, tp >= 0 ? tp : lane);
@@ -138,137 +110,104 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_retrieve_tree(
         if (act && td == d)
             val = (src >= 0 && src < V && tr >= 0 && tr < k) ? table[(size_t)src * k + tr] : -1;
     }
-    if (lane < r_out) {
-        ret_tok[(size_t)b * r_out + lane] = act ? val : -1;
-        ret_parent[(size_t)b * r_out + lane] = act ? tp : -1;
-    }
-    if (lane == 0) n_ret[b] = R;
+    return act ? val : -1;
 }
 
-// TAIL: chain of rank-0 successors from the last kept block token.
-__global__ __launch_bounds__(kWave *kReqPerBlock) void k_retrieve_tail(
-    int B, int V, int k, int slots, const int32_t *__restrict__ table,
-    const int32_t *__restrict__ root_tok, const int32_t *__restrict__ n_keep,
-    const int32_t *__restrict__ d_tok, int Nd, int32_t *__restrict__ ret_tok,
-    int32_t *__restrict__ ret_parent, int32_t *__restrict__ n_ret, int r_out) {
+// TAIL: chain of rank-0 successors x <- M[x][0], R steps from x0; lane t gets
+// the t-th chain token.
+__device__ __forceinline__ int retrieve_tail_wave(int R, int x0, const int32_t *__restrict__ table,
+                                                  int V, int k) {
     const int lane = lane_id();
-    const int b = blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
-    if (b >= B) return;
-    const int p = min(max(n_keep[b], 0), Nd);
-    int R = slots - p;
-    R = R < 0 ? 0 : (R > r_out ? r_out : R);
-    int x = (p <= 0) ? root_tok[b] : d_tok[(size_t)b * Nd + (p - 1)];
-    // one lane walks the chain; the others fill padding
-    int mine = -1;
+    int x = x0, mine = -1;
     for (int t = 0; t < R; ++t) {
         int nx = -1;
         if (lane == 0) nx = (x >= 0 && x < V) ? table[(size_t)x * k] : -1;
-        x = __shfl(nx, 0);
+        x = readlane_i32(nx, 0);
         if (lane == t) mine = x;
     }
-    if (lane < r_out) {
-        ret_tok[(size_t)b * r_out + lane] = lane < R ? mine : -1;
-        ret_parent[(size_t)b * r_out + lane] = lane < R ? lane - 1 : -1;
-    }
-    if (lane == 0) n_ret[b] = R;
+    return mine;
 }
 
-// ---------------------------------------------------------------------------------------
-// Gear 3a: flatten + tree position ids + ancestor mask.  Source lanes (draft node
-// i, retrieval node t) scatter their row into LDS; then lane f owns row f.
-__global__ __launch_bounds__(kWave *kReqPerBlock) void k_flatten(
-    int B, int Nd, int T1, int layout, const int32_t *__restrict__ root_tok,
-    const int32_t *__restrict__ base_pos, const int32_t *__restrict__ d_tok,
-    const int32_t *__restrict__ d_parent, const uint8_t *__restrict__ keep,
-    const int32_t *__restrict__ n_keep, const int32_t *__restrict__ ret_tok,
-    const int32_t *__restrict__ ret_parent, const int32_t *__restrict__ n_ret, int r_out,
-    int32_t *__restrict__ tok_out, int32_t *__restrict__ par_out, int32_t *__restrict__ dep_out,
-    int32_t *__restrict__ pos_out, uint64_t *__restrict__ anc_out) {
-    __shared__ int s_tok[kReqPerBlock][kWave];
-    __shared__ int s_par[kReqPerBlock][kWave];
-    __shared__ int s_rowret[kReqPerBlock][kWave];
+struct FlatIn {
+    // per lane, as draft node i = lane
+    bool isd;
+    int kp, dt, dp;
+    // per lane, as retrieval node t = lane
+    bool isr;
+    int rt, rp;
+    // uniform
+    int nk, R, root, base;
+};
+
+// Gear 3a: rows of the flattened hybrid tree.  Source lanes scatter their row
+// into the wave's LDS slices (stok/spar/srr: 64 ints each); lane f then owns
+// row f: token, parent row, depth and ancestor-or-self mask (pointer doubling).
+__device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &in, int *stok,
+                                             int *spar, int *srr, int32_t *tok_out, int32_t *par_out,
+                                             int32_t *dep_out, int32_t *pos_out, uint64_t *anc_out) {
     const int lane = lane_id();
-    const int w = threadIdx.x >> 6;
-    const int b = blockIdx.x * kReqPerBlock + w;
-    const bool live = b < B;
-    int *stok = s_tok[w];
-    int *spar = s_par[w];
-    int *srr = s_rowret[w];
     stok[lane] = -1;
     spar[lane] = -1;
     srr[lane] = 0;
-    __syncthreads();
-
-    const int nk = live ? n_keep[b] : 0;
-    const int R = live ? n_ret[b] : 0;
-    const bool isd = live && lane < Nd;
-    const int kp = isd ? keep[(size_t)b * Nd + lane] : 0;
-    const int dt = isd ? d_tok[(size_t)b * Nd + lane] : -1;
-    const int dp = (isd && layout != GRAFT_LAYOUT_CHAIN) ? d_parent[(size_t)b * Nd + lane] : -1;
-    const bool isr = live && lane < R && lane < r_out;
-    const int rt = isr ? ret_tok[(size_t)b * r_out + lane] : -1;
-    const int rp = isr ? ret_parent[(size_t)b * r_out + lane] : -1;
-    const uint64_t kmask = ballot(isd && kp);
-    const uint64_t dmask = ballot(isd);
-
+    wave_sync_lds();
+    const uint64_t kmask = ballot(in.isd && in.kp);
+    const uint64_t dmask = ballot(in.isd);
+    const int nk = in.nk;
     if (layout == GRAFT_LAYOUT_COMPACT) {
-        if (isd && kp) {
+        if (in.isd && in.kp) {
             const int row = 1 + lanes_below(kmask);
-            const int prow =
-                dp < 0 ? 0 : 1 + __popcll(kmask & ((dp >= 64) ? ~0ull : ((1ull << dp) - 1ull)));
+            const int dp = in.dp;
+            const int prow = dp < 0 ? 0 : 1 + __popcll(kmask & ((dp >= 64) ? ~0ull : ((1ull << dp) - 1ull)));
             if (row < T1) {
-                stok[row] = dt;
+                stok[row] = in.dt;
                 spar[row] = prow;
             }
         }
-        if (isr) {
+        if (in.isr) {
             const int row = 1 + nk + lane;
             if (row < T1) {
-                stok[row] = rt;
-                spar[row] = rp < 0 ? 0 : 1 + nk + rp;
+                stok[row] = in.rt;
+                spar[row] = in.rp < 0 ? 0 : 1 + nk + in.rp;
             }
         }
     } else if (layout == GRAFT_LAYOUT_IN_PLACE) {
         const uint64_t vmask = dmask & ~kmask;
-        const bool vac = isd && !kp;
+        const bool vac = in.isd && !in.kp;
         const int r_i = lanes_below(vmask);  // which retrieval node fills this slot
         if (vac && r_i < kWave) srr[r_i] = lane + 1;
-        __syncthreads();
-        const int rt_i = __shfl(rt, r_i < kWave ? r_i : 0);
-        const int rp_i = __shfl(rp, r_i < kWave ? r_i : 0);
-        if (isd && lane + 1 < T1) {
-            if (kp) {
-                stok[lane + 1] = dt;
-                spar[lane + 1] = dp < 0 ? 0 : dp + 1;
-            } else if (r_i < R) {
+        wave_sync_lds();
+        const int rt_i = __shfl(in.rt, r_i < kWave ? r_i : 0);
+        const int rp_i = __shfl(in.rp, r_i < kWave ? r_i : 0);
+        if (in.isd && lane + 1 < T1) {
+            if (in.kp) {
+                stok[lane + 1] = in.dt;
+                spar[lane + 1] = in.dp < 0 ? 0 : in.dp + 1;
+            } else if (r_i < in.R) {
                 stok[lane + 1] = rt_i;
                 spar[lane + 1] = (rp_i < 0 || rp_i >= kWave) ? 0 : srr[rp_i];
             }
         }
     } else {  // chain (TAIL)
-        if (isd && lane < nk && lane + 1 < T1) {
-            stok[lane + 1] = dt;
+        if (in.isd && lane < nk && lane + 1 < T1) {
+            stok[lane + 1] = in.dt;
             spar[lane + 1] = lane;
         }
-        if (isr) {
+        if (in.isr) {
             const int row = 1 + nk + lane;
             if (row < T1) {
-                stok[row] = rt;
+                stok[row] = in.rt;
                 spar[row] = row - 1;
             }
         }
     }
-    if (lane == 0 && live) {
-        stok[0] = root_tok[b];
+    if (lane == 0) {
+        stok[0] = in.root;
         spar[0] = -1;
     }
-    __syncthreads();
-    if (!live) return;
-
+    wave_sync_lds();
     const bool row_ok = lane < T1;
     const int t = row_ok ? stok[lane] : -1;
     const int p = row_ok ? spar[lane] : -1;
-    // ancestor-or-self mask and depth by pointer doubling along parent links
     int a = (row_ok && lane > 0) ? p : -1;
     uint64_t A = row_ok ? ((1ull << lane) | (a >= 0 ? (1ull << a) : 0ull)) : 0ull;
     int D = a >= 0 ? 1 : 0;
@@ -285,12 +224,196 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_flatten(
         }
     }
     if (row_ok) {
-        const size_t o = (size_t)b * T1 + lane;
-        tok_out[o] = t;
-        par_out[o] = lane == 0 ? -1 : p;
-        dep_out[o] = D;
-        pos_out[o] = base_pos[b] + D;
-        anc_out[o] = A;
+        tok_out[lane] = t;
+        par_out[lane] = lane == 0 ? -1 : p;
+        dep_out[lane] = D;
+        pos_out[lane] = in.base + D;
+        anc_out[lane] = A;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Standalone kernels (one wavefront per request).
+
+__global__ __launch_bounds__(kWave *kReqPerBlock) void k_prune(PruneKernelArgs a) {
+    const int lane = lane_id();
+    const int b = blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
+    if (b >= a.B) return;
+    const bool valid = lane < a.Nd;
+    const size_t o = (size_t)b * a.Nd + lane;
+    PruneOut r;
+    if (a.mode == GRAFT_MODE_TREE) {
+        const int par = valid ? a.parent[o] : -1;
+        const int lay = valid ? a.layer[o] : 0x7fffffff;
+        const float lp = valid ? a.score[o] : 0.0f;
+        r = prune_tree_wave(valid, par, lay, lp, a.Nd, a.cfg);
+        if (valid && a.cum_out) a.cum_out[o] = r.cum;
+    } else {
+        const float c = valid ? a.score[o] : 1.0f;
+        r = prune_tail_wave(valid, c, a.Nd, a.cfg.tail_thr);
+    }
+    if (valid) a.keep[o] = r.kept ? 1 : 0;
+    if (lane == 0) {
+        a.stage[b] = r.stage;
+        a.n_keep[b] = r.N;
+    }
+}
+
+__global__ __launch_bounds__(kWave *kReqPerBlock) void k_retrieve(RetrieveKernelArgs a) {
+    const int lane = lane_id();
+    const int b = blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
+    if (b >= a.B) return;
+    int R, val, rp;
+    if (a.mode == GRAFT_MODE_TREE) {
+        R = min(max(a.slots - a.n_keep[b], 0), a.tpl_size);
+        const bool act = lane < R;
+        const int tp = act ? a.tpl_parent[lane] : -1;
+        const int tr = act ? a.tpl_rank[lane] : 0;
+        const int td = act ? a.tpl_depth[lane] : 0;
+        val = retrieve_tree_wave(R, tp, tr, td, a.root_tok[b], a.table, a.V, a.k);
+        rp = act ? tp : -1;
+    } else {
+        const int p = min(max(a.n_keep[b], 0), a.Nd);
+        R = min(max(a.slots - p, 0), a.r_out);
+        const int x0 = (p <= 0) ? a.root_tok[b] : a.d_tok[(size_t)b * a.Nd + (p - 1)];
+        val = retrieve_tail_wave(R, x0, a.table, a.V, a.k);
+        rp = lane < R ? lane - 1 : -1;
+    }
+    if (lane < a.r_out) {
+        a.ret_tok[(size_t)b * a.r_out + lane] = lane < R ? val : -1;
+        a.ret_parent[(size_t)b * a.r_out + lane] = lane < R ? rp : -1;
+    }
+    if (lane == 0) a.n_ret[b] = R;
+}
+
+__global__ __launch_bounds__(kWave *kReqPerBlock) void k_flatten(FlattenKernelArgs a) {
+    __shared__ int s_tok[kReqPerBlock][kWave];
+    __shared__ int s_par[kReqPerBlock][kWave];
+    __shared__ int s_rowret[kReqPerBlock][kWave];
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    const int b = blockIdx.x * kReqPerBlock + w;
+    if (b >= a.B) return;
+    FlatIn in;
+    in.nk = a.n_keep[b];
+    in.R = a.n_ret[b];
+    in.root = a.root_tok[b];
+    in.base = a.base_pos[b];
+    in.isd = lane < a.Nd;
+    in.kp = in.isd ? a.keep[(size_t)b * a.Nd + lane] : 0;
+    in.dt = in.isd ? a.d_tok[(size_t)b * a.Nd + lane] : -1;
+    in.dp = (in.isd && a.layout != GRAFT_LAYOUT_CHAIN) ? a.d_parent[(size_t)b * a.Nd + lane] : -1;
+    in.isr = lane < in.R && lane < a.r_out;
+    in.rt = in.isr ? a.ret_tok[(size_t)b * a.r_out + lane] : -1;
+    in.rp = in.isr ? a.ret_parent[(size_t)b * a.r_out + lane] : -1;
+    const size_t o = (size_t)b * a.T1;
+    flatten_wave(a.layout, a.T1, in, s_tok[w], s_par[w], s_rowret[w], a.tok + o, a.parent + o,
+                 a.depth + o, a.pos_id + o, a.anc + o);
+}
+
+// ---------------------------------------------------------------------------------------
+// Fused build: one workgroup (2 wavefronts) per request.  TREE: wave 0 expands
+// the whole template from the root while wave 1 prunes; after one barrier wave
+// 0 keeps the first R = slots - n_keep template nodes and flattens.  TAIL:
+// wave 0 does all three (the chain starts from the last kept block token).
+__global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
+    __shared__ int s_ret[kWave];
+    __shared__ int s_keep[kWave];
+    __shared__ int s_misc[2];
+    __shared__ int s_tok[kWave], s_par[kWave], s_rowret[kWave];
+    const int lane = lane_id();
+    const int wv = threadIdx.x >> 6;
+    const int b = blockIdx.x;
+    const size_t od = (size_t)b * a.Nd + lane;
+    const bool isd = lane < a.Nd;
+    const int root = a.root_tok[b];
+
+    if (a.mode == GRAFT_MODE_TREE) {
+        if (wv == 0) {
+            const bool act = lane < a.tpl_size;
+            const int tp = act ? a.tpl_parent[lane] : -1;
+            const int tr = act ? a.tpl_rank[lane] : 0;
+            const int td = act ? a.tpl_depth[lane] : 0;
+            s_ret[lane] = retrieve_tree_wave(a.tpl_size, tp, tr, td, root, a.table, a.V, a.k);
+        } else {
+            const int par = isd ? a.d_parent[od] : -1;
+            const int lay = isd ? a.d_layer[od] : 0x7fffffff;
+            const float lp = isd ? a.d_score[od] : 0.0f;
+            const PruneOut r = prune_tree_wave(isd, par, lay, lp, a.Nd, a.cfg);
+            if (isd) {
+                a.keep[od] = r.kept ? 1 : 0;
+                if (a.cum_out) a.cum_out[od] = r.cum;
+            }
+            s_keep[lane] = r.kept ? 1 : 0;
+            if (lane == 0) {
+                s_misc[0] = r.stage;
+                s_misc[1] = r.N;
+            }
+        }
+        __syncthreads();
+        if (wv != 0) return;
+        const int nk = s_misc[1];
+        const int R = min(max(a.slots - nk, 0), a.tpl_size);
+        const bool isr = lane < R;
+        const int tp = isr ? a.tpl_parent[lane] : -1;
+        FlatIn in;
+        in.isd = isd;
+        in.kp = s_keep[lane];
+        in.dt = isd ? a.d_tok[od] : -1;
+        in.dp = isd ? a.d_parent[od] : -1;
+        in.isr = isr;
+        in.rt = isr ? s_ret[lane] : -1;
+        in.rp = tp;
+        in.nk = nk;
+        in.R = R;
+        in.root = root;
+        in.base = a.base_pos[b];
+        if (lane < a.r_out) {
+            a.ret_tok[(size_t)b * a.r_out + lane] = in.rt;
+            a.ret_parent[(size_t)b * a.r_out + lane] = isr ? tp : -1;
+        }
+        if (lane == 0) {
+            a.stage[b] = s_misc[0];
+            a.n_keep[b] = nk;
+            a.n_ret[b] = R;
+        }
+        const size_t o = (size_t)b * a.T1;
+        flatten_wave(a.layout, a.T1, in, s_tok, s_par, s_rowret, a.tok + o, a.parent + o, a.depth + o,
+                     a.pos_id + o, a.anc + o);
+    } else {
+        if (wv != 0) return;
+        const float c = isd ? a.d_score[od] : 1.0f;
+        const PruneOut r = prune_tail_wave(isd, c, a.Nd, a.cfg.tail_thr);
+        const int p = r.N;
+        const int dt = isd ? a.d_tok[od] : -1;
+        const int x0 = p <= 0 ? root : readlane_i32(dt, p - 1);
+        const int R = min(max(a.slots - p, 0), a.r_out);
+        const int val = retrieve_tail_wave(R, x0, a.table, a.V, a.k);
+        if (isd) a.keep[od] = r.kept ? 1 : 0;
+        FlatIn in;
+        in.isd = isd;
+        in.kp = r.kept ? 1 : 0;
+        in.dt = dt;
+        in.dp = -1;
+        in.isr = lane < R;
+        in.rt = lane < R ? val : -1;
+        in.rp = lane < R ? lane - 1 : -1;
+        in.nk = p;
+        in.R = R;
+        in.root = root;
+        in.base = a.base_pos[b];
+        if (lane < a.r_out) {
+            a.ret_tok[(size_t)b * a.r_out + lane] = in.rt;
+            a.ret_parent[(size_t)b * a.r_out + lane] = in.rp;
+        }
+        if (lane == 0) {
+            a.stage[b] = r.stage;
+            a.n_keep[b] = p;
+            a.n_ret[b] = R;
+        }
+        const size_t o = (size_t)b * a.T1;
+        flatten_wave(GRAFT_LAYOUT_CHAIN, a.T1, in, s_tok, s_par, s_rowret, a.tok + o, a.parent + o,
+                     a.depth + o, a.pos_id + o, a.anc + o);
     }
 }
 
@@ -298,44 +421,24 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_flatten(
 
 static inline int blocks_for(int B) { return (B + kReqPerBlock - 1) / kReqPerBlock; }
 
-void launch_prune(int B, int Nd, int mode, const int32_t *parent, const int32_t *layer,
-                  const float *score, const graft_prune_cfg &cfg, int32_t *stage, int32_t *n_keep,
-                  uint8_t *keep, float *cum_out, hipStream_t s) {
-    if (B <= 0) return;
-    if (mode == GRAFT_MODE_TREE)
-        hipLaunchKernelGGL(k_prune_tree, dim3(blocks_for(B)), dim3(kWave * kReqPerBlock), 0, s, B, Nd,
-                           parent, layer, score, cfg, stage, n_keep, keep, cum_out);
-    else
-        hipLaunchKernelGGL(k_prune_tail, dim3(blocks_for(B)), dim3(kWave * kReqPerBlock), 0, s, B, Nd,
-                           score, cfg.tail_thr, stage, n_keep, keep);
+void launch_prune(const PruneKernelArgs &a, hipStream_t s) {
+    if (a.B <= 0) return;
+    hipLaunchKernelGGL(k_prune, dim3(blocks_for(a.B)), dim3(kWave * kReqPerBlock), 0, s, a);
 }
 
-void launch_retrieve(int B, int V, int k, int mode, int slots, const int32_t *table,
-                     const int32_t *root_tok, const int32_t *n_keep, const int32_t *d_tok, int Nd,
-                     int tpl_size, const int32_t *tpl_parent, const int32_t *tpl_rank,
-                     const int32_t *tpl_depth, int32_t *ret_tok, int32_t *ret_parent,
-                     int32_t *n_ret, int r_out, hipStream_t s) {
-    if (B <= 0) return;
-    if (mode == GRAFT_MODE_TREE)
-        hipLaunchKernelGGL(k_retrieve_tree, dim3(blocks_for(B)), dim3(kWave * kReqPerBlock), 0, s, B,
-                           V, k, slots, table, root_tok, n_keep, tpl_size, tpl_parent, tpl_rank,
-                           tpl_depth, ret_tok, ret_parent, n_ret, r_out);
-    else
-        hipLaunchKernelGGL(k_retrieve_tail, dim3(blocks_for(B)), dim3(kWave * kReqPerBlock), 0, s, B,
-                           V, k, slots, table, root_tok, n_keep, d_tok, Nd, ret_tok, ret_parent,
-                           n_ret, r_out);
+void launch_retrieve(const RetrieveKernelArgs &a, hipStream_t s) {
+    if (a.B <= 0) return;
+    hipLaunchKernelGGL(k_retrieve, dim3(blocks_for(a.B)), dim3(kWave * kReqPerBlock), 0, s, a);
 }
 
-void launch_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
-                    const int32_t *base_pos, const int32_t *d_tok, const int32_t *d_parent,
-                    const uint8_t *keep, const int32_t *n_keep, const int32_t *ret_tok,
-                    const int32_t *ret_parent, const int32_t *n_ret, int r_out, int32_t *tok,
-                    int32_t *parent, int32_t *depth, int32_t *pos_id, uint64_t *anc,
-                    hipStream_t s) {
-    if (B <= 0) return;
-    hipLaunchKernelGGL(k_flatten, dim3(blocks_for(B)), dim3(kWave * kReqPerBlock), 0, s, B, Nd, T1,
-                       layout, root_tok, base_pos, d_tok, d_parent, keep, n_keep, ret_tok,
-                       ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc);
+void launch_flatten(const FlattenKernelArgs &a, hipStream_t s) {
+    if (a.B <= 0) return;
+    hipLaunchKernelGGL(k_flatten, dim3(blocks_for(a.B)), dim3(kWave * kReqPerBlock), 0, s, a);
+}
+
+void launch_build(const BuildKernelArgs &a, hipStream_t s) {
+    if (a.B <= 0) return;
+    hipLaunchKernelGGL(k_build_tree, dim3(a.B), dim3(2 * kWave), 0, s, a);
 }
 
 }  // namespace graft

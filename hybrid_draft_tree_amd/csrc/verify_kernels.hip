@@ -68,7 +68,9 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(int64_t n_rows, int V, i
                     for (int j = 0; j < k; ++j) table_prob[dst + j] = prob[src * k + j];
             }
         }
-        __threadfence();
+        // the next block may overwrite the same rows: order this block's stores first
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 }

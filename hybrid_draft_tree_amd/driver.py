@@ -10,7 +10,9 @@ in libgraft.so.  One ``GraftPipeline`` holds, for a batch of B requests:
 
 A decode step is ``build(draft)`` (prune -> retrieve -> flatten), the target
 forward that scores the flattened rows (outside this library), then
-``verify_update(logits)`` (top-k -> accept -> matrix update).  ``bonus`` is
+``verify_update(logits)`` (top-k -> accept -> matrix update).  By default each
+half is one launch (graft_build_hybrid_tree, graft_verify_update); with
+``fused=False`` the five separate entry points are used.  ``bonus`` is
 written straight into the root buffer and ``base_pos`` is advanced on the
 device, so consecutive steps need no host round trip.
 """
@@ -27,8 +29,9 @@ from . import _lib as L
 class GraftPipeline:
     def __init__(self, *, V, B, k=8, slots=60, mode="tree", layout="compact", dtype="bf16",
                  n_draft=60, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), keep=(8, 24, 40),
-                 tail_thr=0.5, tpl_width=8, tpl_depth=8, want_prob=False, device="cuda"):
+                 tail_thr=0.5, tpl_width=8, tpl_depth=8, want_prob=False, device="cuda", fused=True):
         L.load()
+        self.fused = bool(fused)
         self.V, self.B, self.k = int(V), int(B), int(k)
         self.mode = L.MODE_TREE if mode == "tree" else L.MODE_TAIL
         self.layout = L.LAYOUT[layout]
@@ -91,12 +94,13 @@ class GraftPipeline:
         self._ingest_ws = None
 
     @classmethod
-    def from_config(cls, cfg, want_prob=False, device="cuda"):
+    def from_config(cls, cfg, want_prob=False, device="cuda", fused=True):
         return cls(V=cfg.V, B=cfg.B, k=cfg.k,
                    slots=cfg.tail_block if cfg.mode == "tail" else cfg.slots,
                    mode=cfg.mode, layout=cfg.layout, dtype=cfg.dtype, n_draft=cfg.n_draft,
                    ckpt_layers=cfg.ckpt_layers, tau=cfg.tau, keep=cfg.keep, tail_thr=cfg.tail_thr,
-                   tpl_width=cfg.tpl_width, tpl_depth=cfg.tpl_depth, want_prob=want_prob, device=device)
+                   tpl_width=cfg.tpl_width, tpl_depth=cfg.tpl_depth, want_prob=want_prob, device=device,
+                   fused=fused)
 
     # ------------------------------------------------------------------ state
     def stream(self):
@@ -117,21 +121,40 @@ class GraftPipeline:
             self.d_score.copy_(torch.as_tensor(np.asarray(draft["conf"], np.float32)))
         self.d_tok.copy_(torch.as_tensor(np.asarray(draft["tok"], np.int32)))
 
-    def build_device(self):
-        """prune -> retrieve -> flatten on the draft already in the device buffers."""
+    def draft_buffers(self):
+        """A fresh set of device draft buffers shaped like the pipeline's own."""
+        return {"parent": torch.empty_like(self.d_parent), "layer": torch.empty_like(self.d_layer),
+                "score": torch.empty_like(self.d_score), "tok": torch.empty_like(self.d_tok)}
+
+    def build_device(self, bufs=None):
+        """prune -> retrieve -> flatten on a draft already on the device (the
+        pipeline's own buffers, or ``bufs`` from draft_buffers())."""
         s = self.stream()
         B, Nd, T1 = self.B, self.Nd, self.T1
-        L.graft_prune_select(B, Nd, self.mode, self.d_parent.data_ptr(), self.d_layer.data_ptr(),
-                             self.d_score.data_ptr(), self.cfg, self.stage.data_ptr(),
+        if bufs is None:
+            bufs = {"parent": self.d_parent, "layer": self.d_layer, "score": self.d_score, "tok": self.d_tok}
+        d_parent, d_layer, d_score, d_tok = bufs["parent"], bufs["layer"], bufs["score"], bufs["tok"]
+        if self.fused:
+            L.graft_build_hybrid_tree(
+                B, Nd, T1, self.mode, self.layout, self.slots, self.cfg, self.tpl, self.V, self.k,
+                self.table.data_ptr(), self.roots.data_ptr(), self.base_pos.data_ptr(), d_parent.data_ptr(),
+                d_layer.data_ptr(), d_score.data_ptr(), d_tok.data_ptr(), self.stage.data_ptr(),
+                self.n_keep.data_ptr(), self.keep.data_ptr(),
+                self.cum.data_ptr() if self.mode == L.MODE_TREE else None, self.ret_tok.data_ptr(),
+                self.ret_parent.data_ptr(), self.n_ret.data_ptr(), self.r_out, self.tok.data_ptr(),
+                self.parent.data_ptr(), self.depth.data_ptr(), self.pos_id.data_ptr(), self.anc.data_ptr(), s)
+            return
+        L.graft_prune_select(B, Nd, self.mode, d_parent.data_ptr(), d_layer.data_ptr(),
+                             d_score.data_ptr(), self.cfg, self.stage.data_ptr(),
                              self.n_keep.data_ptr(), self.keep.data_ptr(),
                              self.cum.data_ptr() if self.mode == L.MODE_TREE else None, s)
         L.graft_retrieve_expand(B, self.V, self.k, self.mode, self.slots, self.table.data_ptr(),
-                                self.roots.data_ptr(), self.n_keep.data_ptr(), self.d_tok.data_ptr(),
+                                self.roots.data_ptr(), self.n_keep.data_ptr(), d_tok.data_ptr(),
                                 Nd, self.tpl, self.cfg if self.mode == L.MODE_TREE else None,
                                 self.ret_tok.data_ptr(), self.ret_parent.data_ptr(),
                                 self.n_ret.data_ptr(), self.r_out, s)
         L.graft_build_tree_mask(B, Nd, T1, self.layout, self.roots.data_ptr(), self.base_pos.data_ptr(),
-                                self.d_tok.data_ptr(), self.d_parent.data_ptr(), self.keep.data_ptr(),
+                                d_tok.data_ptr(), d_parent.data_ptr(), self.keep.data_ptr(),
                                 self.n_keep.data_ptr(), self.ret_tok.data_ptr(),
                                 self.ret_parent.data_ptr(), self.n_ret.data_ptr(), self.r_out,
                                 self.tok.data_ptr(), self.parent.data_ptr(), self.depth.data_ptr(),
@@ -152,6 +175,15 @@ class GraftPipeline:
         """top-k -> accept -> matrix update for logits [B*T1, V] on the device."""
         s = self.stream()
         B, T1 = self.B, self.T1
+        if self.fused:
+            L.graft_verify_update(B, T1, self.V, self.k, self.dtype, logits.data_ptr(), self.tok.data_ptr(),
+                                  self.parent.data_ptr(), self.depth.data_ptr(), self.table.data_ptr(),
+                                  self.table_prob.data_ptr() if self.want_prob else None,
+                                  self.topk.data_ptr(), self.topk_prob.data_ptr() if self.want_prob else None,
+                                  self.accept_len.data_ptr(), self.accept_idx.data_ptr(), self.dmax,
+                                  self.roots.data_ptr(), self.base_pos.data_ptr(), self.ws.data_ptr(),
+                                  self.ws_bytes, s)
+            return
         L.graft_verify_accept(B, T1, self.V, self.k, self.dtype, logits.data_ptr(), self.tok.data_ptr(),
                               self.parent.data_ptr(), self.depth.data_ptr(), self.topk.data_ptr(),
                               self.topk_prob.data_ptr() if self.want_prob else None,

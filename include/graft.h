@@ -187,8 +187,37 @@ int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logit
                       int32_t *table, float *table_prob, int32_t *topk_out, void *ws,
                       size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes needed by graft_verify_accept / graft_update_topk for
- * n_rows rows of V logits (0 on invalid sizes).  Zero-fill it once after
+/* graft_build_hybrid_tree -- graft_prune_select, graft_retrieve_expand and
+ * graft_build_tree_mask in one launch (one workgroup per request; the
+ * retrieval chain runs in parallel with the pruning), with the same outputs
+ * and the same preconditions.  Requires T1 == slots + 1; mode TREE pairs with
+ * layout COMPACT or IN_PLACE, mode TAIL with layout CHAIN.  Section 二 (all
+ * three gears); section 七 for TAIL; section 四 for the in-place layout. */
+int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slots,
+                            const graft_prune_cfg *cfg, const graft_template *tpl, int V, int k,
+                            const int32_t *table, const int32_t *root_tok, const int32_t *base_pos,
+                            const int32_t *d_parent, const int32_t *d_layer, const float *d_score,
+                            const int32_t *d_tok, int32_t *stage, int32_t *n_keep, uint8_t *keep,
+                            float *cum_out, int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret,
+                            int r_out, int32_t *tok, int32_t *parent, int32_t *depth, int32_t *pos_id,
+                            uint64_t *anc, hipStream_t stream);
+
+/* graft_verify_update -- graft_verify_accept followed by
+ * graft_update_topk(row_tok = tok, topk_in = the top-k just computed) in one
+ * launch: the logits are read once and the matrix is updated in the same
+ * kernel (every row registers its token when it starts; each request, once
+ * accepted, writes the rows that are the last holder of their token in the
+ * batch).  table int32 [V, k] in/out; table_prob fp32 [V, k] (nullable;
+ * needs topk_prob).  Other arguments as for graft_verify_accept.  Section 二,
+ * gear 3; section 六 (online update). */
+int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logits, const int32_t *tok,
+                        const int32_t *parent, const int32_t *depth, int32_t *table, float *table_prob,
+                        int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
+                        int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Workspace bytes needed by graft_verify_accept / graft_verify_update /
+ * graft_update_topk for n_rows rows of V logits (0 on invalid sizes).  Zero-fill it once after
  * allocating it; calls leave it zero-filled. */
 size_t graft_workspace_bytes(int64_t n_rows, int V, int k, int dtype);
 

@@ -41,13 +41,13 @@ class HipBackend:
     """HIP path through the C-ABI; host copies of the small outputs are made for
     the synthetic generator and for comparison."""
 
-    def __init__(self, cfg, want_prob=False, device="cuda"):
+    def __init__(self, cfg, want_prob=False, device="cuda", fused=True):
         import torch
         from hybrid_draft_tree_amd.driver import GraftPipeline
         from synth.device import DeviceRows
         self.torch = torch
         self.cfg = cfg
-        self.p = GraftPipeline.from_config(cfg, want_prob=want_prob, device=device)
+        self.p = GraftPipeline.from_config(cfg, want_prob=want_prob, device=device, fused=fused)
         self.rows = None
         self._DeviceRows = DeviceRows
         self.want_prob = want_prob

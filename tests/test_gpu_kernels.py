@@ -428,3 +428,83 @@ def test_update_parity_collisions(n, ntok):
     want = table.copy()
     O.update(want, row_tok, tk)
     np.testing.assert_array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------- fused entry points
+
+def test_build_hybrid_tree_matches_oracle_tree():
+    rng = np.random.default_rng(30)
+    B, V = 37, 5000
+    par, lay, _ = TOPO
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    lp = _random_logp(rng, B)
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    base = rng.integers(0, 100000, size=B).astype(np.int32)
+    d_tok = rng.integers(0, V, size=(B, 60)).astype(np.int32)
+    tpl, keepalive, r_out = _tpl_dev(52)
+    cfg = L.prune_cfg(CFG["ckpt"], [float(np.float32(math.log(t))) for t in CFG["tau"]], CFG["keep"], 0.5)
+    for layout in ("compact", "in_place"):
+        ins = [_t(x, torch.int32) for x in (table, roots, base, P, Ly)]
+        sc, dt = _t(lp, torch.float32), _t(d_tok, torch.int32)
+        i32 = dict(dtype=torch.int32, device=DEV)
+        st, nk, nr = (torch.zeros(B, **i32) for _ in range(3))
+        kp = torch.zeros(B, 60, dtype=torch.uint8, device=DEV)
+        cum = torch.zeros(B, 60, dtype=torch.float32, device=DEV)
+        rt, rp = torch.zeros(B, r_out, **i32), torch.zeros(B, r_out, **i32)
+        tok, par_o, dep, pos = (torch.zeros(B, 61, **i32) for _ in range(4))
+        anc = torch.zeros(B, 61, dtype=torch.int64, device=DEV)
+        L.graft_build_hybrid_tree(B, 60, 61, L.MODE_TREE, L.LAYOUT[layout], 60, cfg, tpl, V, 8,
+                                  ins[0].data_ptr(), ins[1].data_ptr(), ins[2].data_ptr(), ins[3].data_ptr(),
+                                  ins[4].data_ptr(), sc.data_ptr(), dt.data_ptr(), st.data_ptr(), nk.data_ptr(),
+                                  kp.data_ptr(), cum.data_ptr(), rt.data_ptr(), rp.data_ptr(), nr.data_ptr(),
+                                  r_out, tok.data_ptr(), par_o.data_ptr(), dep.data_ptr(), pos.data_ptr(),
+                                  anc.data_ptr(), _s())
+        torch.cuda.synchronize()
+        pr = O.prune_tree(P, Ly, lp, want_cum=True)
+        ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, O.template(8, 8, 52))
+        fl = O.flatten(layout, 61, roots, base, d_tok, P, pr["keep"], pr["n_keep"], ret)
+        np.testing.assert_array_equal(st.cpu().numpy(), pr["stage"])
+        np.testing.assert_array_equal(nk.cpu().numpy(), pr["n_keep"])
+        np.testing.assert_array_equal(kp.cpu().numpy(), pr["keep"])
+        np.testing.assert_array_equal(cum.cpu().numpy().view(np.uint32), pr["cum"].view(np.uint32))
+        np.testing.assert_array_equal(nr.cpu().numpy(), ret["n_ret"])
+        np.testing.assert_array_equal(rt.cpu().numpy(), ret["ret_tok"])
+        np.testing.assert_array_equal(rp.cpu().numpy(), ret["ret_parent"])
+        for name, got in (("tok", tok), ("parent", par_o), ("depth", dep), ("pos_id", pos)):
+            np.testing.assert_array_equal(got.cpu().numpy(), fl[name], err_msg=(layout, name))
+        np.testing.assert_array_equal(anc.cpu().numpy().view(np.uint64), fl["anc"])
+
+
+def test_verify_update_matches_oracle_with_collisions():
+    rng = np.random.default_rng(31)
+    B, T1, V = 16, 61, 20000
+    tok, par, dep = _random_flat_trees(rng, B, T1, 40)     # 40 distinct tokens: many collisions
+    tok[3] = 7                                              # a whole request on one token
+    rows = _bf16(rng.standard_normal((B, T1, V)).astype(np.float32))
+    table0 = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    lg = _t(rows.view(np.int16)).view(torch.bfloat16)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    tb = _t(table0, torch.int32)
+    tk = torch.zeros(B, T1, 8, **i32)
+    al, bo, bp = torch.zeros(B, **i32), torch.zeros(B, **i32), torch.zeros(B, **i32)
+    ai = torch.zeros(B, T1 - 1, **i32)
+    t_, p_, d_ = (_t(x, torch.int32) for x in (tok, par, dep))
+    wsb = L.graft_workspace_bytes(B * T1, V, 8, L.DTYPE_BF16)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    want_tab = table0.copy()
+    for rep in range(3):        # repeated calls: the workspace must come back zeroed
+        L.graft_verify_update(B, T1, V, 8, L.DTYPE_BF16, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
+                              tb.data_ptr(), None, tk.data_ptr(), None, al.data_ptr(), ai.data_ptr(), T1 - 1,
+                              bo.data_ptr(), bp.data_ptr(), ws.data_ptr(), wsb, _s())
+        torch.cuda.synchronize()
+        want_tk = O.topk(rows.reshape(-1, V), 8, "bf16").reshape(B, T1, 8)
+        acc = O.accept(tok, par, want_tk[:, :, 0], T1 - 1)
+        O.update(want_tab, tok.reshape(-1), want_tk.reshape(-1, 8))
+        np.testing.assert_array_equal(tk.cpu().numpy(), want_tk)
+        np.testing.assert_array_equal(al.cpu().numpy(), acc["accept_len"])
+        np.testing.assert_array_equal(ai.cpu().numpy(), acc["accept_idx"])
+        np.testing.assert_array_equal(bo.cpu().numpy(), acc["bonus"])
+        np.testing.assert_array_equal(tb.cpu().numpy(), want_tab)
+        rows = _bf16(rng.standard_normal((B, T1, V)).astype(np.float32))
+        lg = _t(rows.view(np.int16)).view(torch.bfloat16)

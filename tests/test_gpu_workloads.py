@@ -25,8 +25,8 @@ KEYS_BUILD = ("stage", "n_keep", "keep", "n_ret", "ret_tok", "tok", "parent", "d
 KEYS_VERIFY = ("topk", "accept_len", "accept_idx", "bonus")
 
 
-def _compare_runs(cfg, n_steps, warmup, table_every=1):
-    ob, hb = OracleBackend(cfg), HipBackend(cfg)
+def _compare_runs(cfg, n_steps, warmup, table_every=1, fused=True, want_prob=False):
+    ob, hb = OracleBackend(cfg, want_prob=want_prob), HipBackend(cfg, want_prob=want_prob, fused=fused)
     wl_o, wl_h = R.Workload(cfg), R.Workload(cfg, pool=None)
     R.start(ob, wl_o)
     R.start(hb, wl_h)
@@ -65,18 +65,37 @@ def _small(cfg_id, **kw):
     return cfg.scaled(**d)
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "five_calls"])
 @pytest.mark.parametrize("cfg_id,kw,steps", [
     (1, {}, 60),                                   # toy, full V=32000 fp32
     (2, {}, 30),                                   # V=128256 bf16, B=1
     (3, {"V": 20000, "B": 16}, 12),                # in-place layout, batch collisions
     (5, {"V": 20000}, 20),                         # TAIL
 ])
-def test_lockstep_reduced(cfg_id, kw, steps):
+def test_lockstep_reduced(cfg_id, kw, steps, fused):
     cfg = _small(cfg_id, **kw)
-    st = _compare_runs(cfg, steps, warmup=cfg.warmup_steps)
+    st = _compare_runs(cfg, steps, warmup=cfg.warmup_steps, fused=fused)
     assert st["accepted"] > 0
     if cfg.mode == "tree":
         assert len(st["stages"]) >= 2
+
+
+def test_lockstep_with_probabilities():
+    """Probability outputs (fused softmax statistics) through whole steps: the
+    matrix's probability table and every top-k probability within 1e-5 relative."""
+    cfg = _small(3, V=30000, B=4)
+    ob, hb = OracleBackend(cfg, want_prob=True), HipBackend(cfg, want_prob=True)
+    wo, wh = R.Workload(cfg), R.Workload(cfg)
+    R.start(ob, wo)
+    R.start(hb, wh)
+    for s in range(4):
+        fo, ro = R.step(ob, wo, s)
+        fh, rh = R.step(hb, wh, s)
+        np.testing.assert_array_equal(rh["topk"], ro["topk"])
+        np.testing.assert_allclose(rh["topk_prob"], ro["topk_prob"], rtol=1e-5, atol=0)
+    np.testing.assert_array_equal(hb.get_table(), ob.get_table())
+    tp_h = hb.p.table_prob.cpu().numpy()
+    np.testing.assert_allclose(tp_h, ob.o.table_prob, rtol=1e-5, atol=0)
 
 
 def test_lockstep_ingest_reduced():
