@@ -74,7 +74,7 @@ struct TopkPlan {
     size_t stats_bytes = 0;
     size_t off_stats = 0;     // workspace offsets
     size_t off_counters = 0;  // row counters [n_rows], request counters [n_rows]
-    size_t off_occ = 0;       // last occurrence per token [V], registration counter, hand-offs [n_rows]
+    size_t off_occ = 0;       // last occurrence per token [V], one spare word, hand-offs [n_rows]
     size_t ws_bytes = 0;      // workspace bytes the kernel uses (all counters zero between calls)
 };
 
@@ -107,7 +107,6 @@ struct VerifyArgs {
     int32_t *table = nullptr;
     float *table_prob = nullptr;
     int32_t *last_occ = nullptr;   // [V] row+1 of the last row holding each token
-    uint32_t *reg_cnt = nullptr;   // rows registered
     uint32_t *handoff = nullptr;   // [B] accept-done / registration-done hand-off
     int B = 0;
 };

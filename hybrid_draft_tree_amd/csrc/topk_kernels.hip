@@ -327,29 +327,22 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
 
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6;
-    const int64_t w = (int64_t)blockIdx.x * kWavesPerBlockA + wv;
-    const int S = a.S;
-    Rank *scratch = s_merge[wv];
-    if (w >= a.n_rows * S) return;
-    const int64_t row = w / S;
-    const int split = (int)(w - row * S);
+    int64_t wg = blockIdx.x;
     if constexpr (ACCEPT) {
-        if (v.table && split == 0) {
-            // Register this row as a holder of its token (highest row wins the
-            // matrix row); the last row to register completes every request's
-            // hand-off.
-            if (lane == 0) {
-                const int t = v.tok[row];
-                if (t >= 0 && t < a.V)
-                    __hip_atomic_fetch_max(&v.last_occ[t], (int32_t)(row + 1), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-            }
-            publish();
-            uint32_t prev = 0;
-            if (lane == 0) prev = count_in(v.reg_cnt);
-            prev = (uint32_t)readlane_i32((int)prev, 0);
-            if (prev == (uint32_t)(a.n_rows - 1)) {
-                after_count();
+        if (v.table) {
+            // Workgroup 0 registers every row as a holder of its token (highest
+            // row wins the matrix row), then completes each request's hand-off.
+            // Kept off the streaming waves: no contended counter on their path.
+            if (blockIdx.x == 0) {
+                for (int64_t P = (int64_t)wv * kWave + lane; P < a.n_rows; P += kWave * kWavesPerBlockA) {
+                    const int t = v.tok[P];
+                    if (t >= 0 && t < a.V)
+                        __hip_atomic_fetch_max(&v.last_occ[t], (int32_t)(P + 1), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                }
+                publish();
+                __syncthreads();
+                if (wv != 0) return;
                 for (int b0 = 0; b0 < v.B; b0 += kWave) {
                     const int b = b0 + lane;
                     uint32_t old = 0;
@@ -358,14 +351,22 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
                     while (second) {
                         const int j = __ffsll((unsigned long long)second) - 1;
                         second &= second - 1;
+                        after_count();
                         update_request(v, a.V, a.k, a.topk, a.prob, b0 + j);
                         if (lane == 0) st_agent(&v.handoff[b0 + j], 0u);
                     }
                 }
-                if (lane == 0) st_agent(v.reg_cnt, 0u);
+                return;
             }
+            wg -= 1;
         }
     }
+    const int64_t w = wg * kWavesPerBlockA + wv;
+    const int S = a.S;
+    Rank *scratch = s_merge[wv];
+    if (w >= a.n_rows * S) return;
+    const int64_t row = w / S;
+    const int split = (int)(w - row * S);
     const int c0 = split * a.chunk;
     const int c1 = min(a.V, c0 + a.chunk);
     const char *rowp = (const char *)a.logits + (size_t)row * (size_t)a.V * ESZ;
@@ -554,7 +555,8 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
 template <typename TR>
 void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
     const int64_t waves = a.n_rows * a.S;
-    const dim3 grid((unsigned)((waves + kWavesPerBlockA - 1) / kWavesPerBlockA));
+    const int extra = (v && v->table) ? 1 : 0;  // the registration workgroup
+    const dim3 grid((unsigned)((waves + kWavesPerBlockA - 1) / kWavesPerBlockA + extra));
     const dim3 block(kWave * kWavesPerBlockA);
     const VerifyArgs vv = v ? *v : VerifyArgs{};
     const bool prob = a.prob != nullptr;
@@ -596,7 +598,7 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     p.partial_bytes = (size_t)n_rows * S * kTop * sizeof(uint64_t);
     p.stats_bytes = (size_t)n_rows * S * sizeof(float2);
     // workspace: [partials | stats | row counters, request counters |
-    //             last occurrence per token [V], registration counter, hand-offs]
+    //             last occurrence per token [V], (unused word), hand-offs [n_rows]]
     p.off_stats = (p.partial_bytes + 255) / 256 * 256;
     p.off_counters = p.off_stats + (p.stats_bytes + 255) / 256 * 256;
     p.off_occ = p.off_counters + ((size_t)n_rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
@@ -624,8 +626,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
         v = *verify;
         v.req_cnt = a.row_cnt + p.n_rows;
         v.last_occ = (int32_t *)((char *)ws + p.off_occ);
-        v.reg_cnt = (uint32_t *)(v.last_occ + p.V);
-        v.handoff = v.reg_cnt + 1;
+        v.handoff = (uint32_t *)(v.last_occ + p.V + 1);
         v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
     }
     if (dtype == GRAFT_DTYPE_BF16)
