@@ -68,14 +68,11 @@ void launch_build(const BuildKernelArgs &a, hipStream_t s);
 struct TopkPlan {
     int64_t n_rows = 0;
     int V = 0;
-    int splits = 1;     // wave ranges per row
-    int chunk = 0;      // elements per range (multiple of 8)
-    size_t partial_bytes = 0;
-    size_t stats_bytes = 0;
-    size_t off_stats = 0;     // workspace offsets
-    size_t off_counters = 0;  // row counters [n_rows], request counters [n_rows]
-    size_t off_occ = 0;       // last occurrence per token [V], one spare word, hand-offs [n_rows]
-    size_t ws_bytes = 0;      // workspace bytes the kernel uses (all counters zero between calls)
+    int splits = 1;           // wavefronts per row (one workgroup per row)
+    int chunk = 0;            // unused
+    size_t off_counters = 0;  // request counters [n_rows]
+    size_t off_occ = 0;       // last holder per token [V], one spare word, hand-offs [n_rows]
+    size_t ws_bytes = 0;      // workspace bytes the kernel uses (all zero between calls)
 };
 
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype);
@@ -83,10 +80,7 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype);
 struct TopkArgs {
     const void *logits;
     int64_t n_rows;
-    int V, S, chunk;
-    uint64_t *partials;
-    uint64_t *stats;   // (max, sum) fp32 pairs
-    uint32_t *row_cnt;
+    int V, S;
     int k;
     int32_t *topk;
     float *prob;

@@ -5,28 +5,33 @@
 // Order: value descending, ties -> lower id, -0 == +0.  The kernel is an HBM
 // stream: no MFMA (nothing is a contraction).
 //
-// Each wavefront owns a contiguous range of one row and streams it
-//   with 16-byte loads (8 bf16 or 4 fp32 per lane, U loads in flight).  A
-//   wave-uniform threshold -- the key of the wave's current 8th-best value --
-//   filters groups with a few packed integer ops; the rare groups that pass
-//   are compacted into LDS with a ballot, and merged into the wave's exact
-//   top-8 (8 rounds of wave-wide max) when 64 are pending.  The range's top-8
-//   goes to the workspace as 64-bit (value, id) ranks.
-// Epilogue: the last range of a row to finish merges the ranges' candidates
-//   into the final top-k (and combines online-softmax statistics); with the
-//   acceptance walk fused, the last row of a request to be merged runs the
-//   walk for that request.  One launch per call.
+// One workgroup per row, S wavefronts.  The row is cut into 1 KB blocks (64
+//   lanes x 16 bytes = 8 bf16 or 4 fp32 per lane); wavefront j reads blocks
+//   j, j+S, j+2S, ... so that the S waves of a row sweep it together (a
+//   contiguous front per row keeps HBM pages open), two blocks per batch with
+//   the next batch in flight.  A wave-uniform threshold -- the key of the
+//   wave's current 8th-best value -- filters each 16-byte group with a few
+//   packed integer ops; the rare groups that pass are compacted into LDS with a
+//   ballot and merged into the wave's exact top-8 (DPP wave maxima) when 64
+//   are pending.
+// Epilogue: the S waves meet at one barrier; wave 0 merges their candidates
+//   (and softmax statistics) from LDS into the row's top-k.  With the
+//   acceptance walk fused, the last row of a request to finish (device-scope
+//   counter) runs the walk for that request, then its share of the matrix
+//   update.  One launch per call.
 #include "device_utils.hpp"
 #include "launchers.hpp"
 
 namespace graft {
 namespace {
 
-constexpr int kWavesPerBlockA = 4;
-constexpr int kLoadsInFlight = 2;  // U: 16-byte loads per lane per batch
-template <int U>
-constexpr int kCapOf = kWave * (U + 1);  // pending groups per wave
+constexpr int kLoadsInFlight = 2;  // U: 1 KB blocks per wave per batch
+constexpr int kCap = kWave * (kLoadsInFlight + 1);  // pending groups per wave
 constexpr int kTop = 8;
+constexpr int kMaxWavesPerRow = 16;
+constexpr int kHeadPad = 8;  // local offsets below this are the row's unaligned head
+constexpr int kRowGroup = 8;  // rows per first-level completion counter
+constexpr int kMaxGroups = (64 + kRowGroup - 1) / kRowGroup;
 
 typedef short short2v __attribute__((ext_vector_type(2)));
 typedef int int4v __attribute__((ext_vector_type(4)));
@@ -50,7 +55,6 @@ __device__ __forceinline__ uint4 load16(const uint4 *p) {
 struct Bf16Traits {
     using Rank = uint32_t;
     static constexpr int kPerGroup = 8;
-    static constexpr int kMaxRange = 65536;  // offsets fit 16 bits
     __device__ static uint32_t elem(const uint4 &d, int e) {
         const uint32_t w = e < 2 ? d.x : e < 4 ? d.y : e < 6 ? d.z : d.w;
         return (e & 1) ? (w >> 16) : (w & 0xffffu);
@@ -64,10 +68,7 @@ struct Bf16Traits {
         return ((uint32_t)(bf16_key(raw) + 0x8000) << 16) | (0xffffu - (uint32_t)off);
     }
     __device__ static int32_t rank_key(Rank r) { return (int32_t)(r >> 16) - 0x8000; }
-    __device__ static uint64_t to_row_rank(Rank r, int col0) {
-        const int off = (int)(0xffffu - (r & 0xffffu));
-        return rank64(rank_key(r) * 65536, (uint32_t)(col0 + off));
-    }
+    __device__ static uint32_t local_off(Rank r) { return 0xffffu - (r & 0xffffu); }
     // Largest raw bit pattern of the group read as int16 (equals the largest key
     // whenever that is positive).
     __device__ static int raw_max(const uint4 &d) {
@@ -96,7 +97,6 @@ struct Bf16Traits {
 struct F32Traits {
     using Rank = uint64_t;
     static constexpr int kPerGroup = 4;
-    static constexpr int kMaxRange = 65536 * 4;  // group index fits 16 bits
     __device__ static uint32_t elem(const uint4 &d, int e) {
         return e == 0 ? d.x : e == 1 ? d.y : e == 2 ? d.z : d.w;
     }
@@ -107,9 +107,7 @@ struct F32Traits {
     __device__ static float value(uint32_t raw) { return __uint_as_float(raw); }
     __device__ static Rank make(uint32_t raw, int off) { return rank64(f32_key(raw), (uint32_t)off); }
     __device__ static int32_t rank_key(Rank r) { return rank64_key(r); }
-    __device__ static uint64_t to_row_rank(Rank r, int col0) {
-        return rank64(rank64_key(r), (uint32_t)col0 + rank64_id(r));
-    }
+    __device__ static uint32_t local_off(Rank r) { return rank64_id(r); }
     __device__ static int raw_max(const uint4 &d) {
         return max(max((int)d.x, (int)d.y), max((int)d.z, (int)d.w));
     }
@@ -205,39 +203,6 @@ struct SoftStats {
     }
 };
 
-// Merge the ranges' candidates of one row into its final top-k (+ softmax
-// probabilities), one wavefront.
-constexpr int kMaxPerLaneB = 4;  // S * 8 <= 256 candidates per row
-
-__device__ __forceinline__ void merge_row(const TopkArgs &a, int64_t row) {
-    const int lane = lane_id();
-    const int n = a.S * kTop;
-    uint64_t c[kMaxPerLaneB];
-#pragma unroll
-    for (int i = 0; i < kMaxPerLaneB; ++i) {
-        const int j = i * kWave + lane;
-        c[i] = j < n ? ld_agent(&a.partials[row * n + j]) : 0ull;
-    }
-    uint64_t top = 0;
-    merge_top8<uint64_t, kMaxPerLaneB>(c, top);
-    if (lane < a.k) st_agent(&a.topk[row * a.k + lane], top ? (int32_t)rank64_id(top) : -1);
-    if (a.prob) {
-        float2 sv = make_float2(-INFINITY, 0.0f);
-        if (lane < a.S) {
-            const uint64_t u = ld_agent(&a.stats[row * a.S + lane]);
-            sv = make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
-        }
-        const float M = wave_max_f32(sv.x);
-        const float s = (sv.x == -INFINITY) ? 0.0f : sv.y * __expf(sv.x - M);
-        const float Ssum = wave_sum_f32(s);
-        if (lane < a.k) {
-            const float x = key_to_f32(rank64_key(top));
-            const float pj = top ? __expf(x - M) / Ssum : 0.0f;
-            st_agent((int32_t *)&a.prob[row * a.k + lane], __float_as_int(pj));
-        }
-    }
-}
-
 // Strict greedy acceptance walk of request b (section 二, gear 3), one wavefront;
 // lane f is flattened row f.  A row is accepted iff every row on its path from
 // the root carries the greedy token of its parent row; the deepest accepted row
@@ -291,7 +256,7 @@ __device__ __forceinline__ void accept_walk(const VerifyArgs &v, int k, int32_t 
 // a row writes its top-k into the matrix row of its token iff it is the last
 // row of the whole batch holding that token (highest row wins), then clears
 // that token's registration.  Called once every row is registered and the
-// request's rows are merged.
+// request's rows are final.
 __device__ __forceinline__ void update_request(const VerifyArgs &v, int V, int k, int32_t *topk,
                                                const float *prob, int b) {
     const int lane = lane_id();
@@ -316,88 +281,120 @@ __device__ __forceinline__ bool handoff_second(const VerifyArgs &v, int b) {
     return prev == 1u;
 }
 
-template <typename TR, bool PROB, bool ACCEPT, bool NT, int U = kLoadsInFlight>
-__global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a, VerifyArgs v) {
+// Registration for the fused matrix update (workgroup 0 of the launch): every
+// row records itself as a holder of its token (atomic max of row+1), then the
+// hand-off of every request is completed.
+__device__ __forceinline__ void register_rows(const TopkArgs &a, const VerifyArgs &v) {
+    const int lane = lane_id();
+    const int wv = threadIdx.x >> 6;
+    const int nth = blockDim.x;
+    for (int64_t P = threadIdx.x; P < a.n_rows; P += nth) {
+        const int t = v.tok[P];
+        if (t >= 0 && t < a.V)
+            __hip_atomic_fetch_max(&v.last_occ[t], (int32_t)(P + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    publish();
+    __syncthreads();
+    if (wv != 0) return;
+    for (int b0 = 0; b0 < v.B; b0 += kWave) {
+        const int b = b0 + lane;
+        uint32_t old = 0;
+        if (b < v.B) old = count_in(&v.handoff[b]);
+        uint64_t second = ballot(b < v.B && old == 1u);
+        while (second) {
+            const int j = __ffsll((unsigned long long)second) - 1;
+            second &= second - 1;
+            after_count();
+            update_request(v, a.V, a.k, a.topk, a.prob, b0 + j);
+            if (lane == 0) st_agent(&v.handoff[b0 + j], 0u);
+        }
+    }
+}
+
+// Dynamic LDS layout of a row's workgroup (S waves).
+template <typename Rank>
+struct RowSmem {
+    static constexpr size_t kData = sizeof(uint4) * kCap;      // pending groups
+    static constexpr size_t kMerge = sizeof(Rank) * kWave;     // compaction scratch
+    static constexpr size_t kGidx = sizeof(uint16_t) * kCap;   // pending group indices
+    static constexpr size_t kPerWave = kData + kMerge + kGidx;
+    static size_t bytes(int S) {
+        return (size_t)S * kPerWave + (size_t)S * kTop * sizeof(uint64_t) + (size_t)S * sizeof(float2) + 16;
+    }
+};
+
+template <typename TR, bool PROB, bool ACCEPT, bool NT>
+__global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a, VerifyArgs v) {
     using Rank = typename TR::Rank;
+    using SM = RowSmem<Rank>;
+    constexpr int U = kLoadsInFlight;
     constexpr int EPG = TR::kPerGroup;
     constexpr int ESZ = 16 / EPG;
-    __shared__ uint4 s_data[kWavesPerBlockA][kCapOf<U>];
-    __shared__ uint16_t s_gidx[kWavesPerBlockA][kCapOf<U>];
-    __shared__ Rank s_merge[kWavesPerBlockA][kWave];
+    constexpr int BLK = kWave * EPG;  // elements per 1 KB block
+    extern __shared__ __align__(16) unsigned char smem[];
 
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6;
-    int64_t wg = blockIdx.x;
+    const int S = blockDim.x >> 6;
+    int64_t row = blockIdx.x;
     if constexpr (ACCEPT) {
         if (v.table) {
-            // Workgroup 0 registers every row as a holder of its token (highest
-            // row wins the matrix row), then completes each request's hand-off.
-            // Kept off the streaming waves: no contended counter on their path.
             if (blockIdx.x == 0) {
-                for (int64_t P = (int64_t)wv * kWave + lane; P < a.n_rows; P += kWave * kWavesPerBlockA) {
-                    const int t = v.tok[P];
-                    if (t >= 0 && t < a.V)
-                        __hip_atomic_fetch_max(&v.last_occ[t], (int32_t)(P + 1), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                }
-                publish();
-                __syncthreads();
-                if (wv != 0) return;
-                for (int b0 = 0; b0 < v.B; b0 += kWave) {
-                    const int b = b0 + lane;
-                    uint32_t old = 0;
-                    if (b < v.B) old = count_in(&v.handoff[b]);
-                    uint64_t second = ballot(b < v.B && old == 1u);
-                    while (second) {
-                        const int j = __ffsll((unsigned long long)second) - 1;
-                        second &= second - 1;
-                        after_count();
-                        update_request(v, a.V, a.k, a.topk, a.prob, b0 + j);
-                        if (lane == 0) st_agent(&v.handoff[b0 + j], 0u);
-                    }
-                }
+                register_rows(a, v);
                 return;
             }
-            wg -= 1;
+            row -= 1;
         }
     }
-    const int64_t w = wg * kWavesPerBlockA + wv;
-    const int S = a.S;
-    Rank *scratch = s_merge[wv];
-    if (w >= a.n_rows * S) return;
-    const int64_t row = w / S;
-    const int split = (int)(w - row * S);
-    const int c0 = split * a.chunk;
-    const int c1 = min(a.V, c0 + a.chunk);
-    const char *rowp = (const char *)a.logits + (size_t)row * (size_t)a.V * ESZ;
+    if (row >= a.n_rows) return;
 
-    // head (until 16-byte alignment), body (16-byte groups), tail
-    const uintptr_t a_addr = (uintptr_t)(rowp + (size_t)c0 * ESZ);
-    int head = (int)(((16u - (uint32_t)(a_addr & 15u)) & 15u) / ESZ);
-    head = min(head, c1 - c0);
-    const int a0 = c0 + head;
-    const int ng = (c1 - a0) / EPG;
-    const int a1 = a0 + ng * EPG;
-    const int ntail = c1 - a1;
+    uint4 *sd = (uint4 *)(smem + (size_t)wv * SM::kData);
+    Rank *scratch = (Rank *)(smem + (size_t)S * SM::kData + (size_t)wv * SM::kMerge);
+    uint16_t *sg = (uint16_t *)(smem + (size_t)S * (SM::kData + SM::kMerge) + (size_t)wv * SM::kGidx);
+    uint64_t *s_cand = (uint64_t *)(smem + (size_t)S * SM::kPerWave);
+    float2 *s_stat = (float2 *)(s_cand + (size_t)S * kTop);
+
+    const int V = a.V;
+    const char *rowp = (const char *)a.logits + (size_t)row * (size_t)V * ESZ;
+    // head (until 16-byte alignment), body of 16-byte groups in 1 KB blocks, tail
+    int head = (int)(((16u - (uint32_t)((uintptr_t)rowp & 15u)) & 15u) / ESZ);
+    head = min(head, V);
+    const int ng = (V - head) / EPG;
+    const int ntail = V - head - ng * EPG;
+    const int nblk = (ng + kWave - 1) / kWave;
+    const int kcount = nblk > wv ? (nblk - wv + S - 1) / S : 0;  // blocks of this wave
+    const uint4 *vp = (const uint4 *)(rowp + (size_t)head * ESZ);
+
+    // Local offsets (monotone in the element id for this wave): head elements
+    // 0..head-1 (wave 0), body kHeadPad + k*BLK + lane*EPG + e for the wave's
+    // k-th block, tail after the wave's body (wave 0).
+    auto global_id = [&](uint32_t off) -> uint32_t {
+        if (off < (uint32_t)kHeadPad) return off;
+        const uint32_t q = off - kHeadPad;
+        if (q < (uint32_t)kcount * BLK) return head + (wv + (q / BLK) * S) * BLK + q % BLK;
+        return head + ng * EPG + (q - (uint32_t)kcount * BLK);
+    };
 
     Rank top = 0;   // lanes 0..7: the wave's top-8, descending
     Rank kth = 0;   // the 8th best (uniform); 0 while fewer than 8 candidates
     int thr = INT_MIN;
     SoftStats st;
 
-    {  // head and tail elements: at most EPG-1 each
+    if (wv == 0) {  // head and tail elements: at most EPG-1 each
         Rank c[1] = {0};
         bool have = false;
-        int off = 0;
+        int off = 0, idx = 0;
         if (lane < head) {
             off = lane;
+            idx = lane;
             have = true;
         } else if (lane >= 16 && lane - 16 < ntail) {
-            off = (a1 - c0) + (lane - 16);
+            off = kHeadPad + kcount * BLK + (lane - 16);
+            idx = head + ng * EPG + (lane - 16);
             have = true;
         }
         if (have) {
-            const uint32_t raw = TR::load_scalar(rowp, c0 + off);
+            const uint32_t raw = TR::load_scalar(rowp, idx);
             c[0] = TR::make(raw, off);
             if constexpr (PROB) st.add(TR::value(raw));
         }
@@ -407,11 +404,7 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
         }
     }
 
-    const uint4 *vp = (const uint4 *)(rowp + (size_t)a0 * ESZ);
-    uint4 *sd = s_data[wv];
-    uint16_t *sg = s_gidx[wv];
     int count = 0;
-
     auto process = [&]() {
         for (int base = 0; base < count; base += kWave) {
             const int gi = base + lane;
@@ -419,7 +412,7 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
             bool any = false;
             if (gi < count) {
                 const uint4 d = sd[gi];
-                const int goff = head + (int)sg[gi] * EPG;
+                const int goff = kHeadPad + (int)sg[gi] * EPG;
 #pragma unroll
                 for (int e = 0; e < EPG; ++e) {
                     const Rank r = TR::make(TR::elem(d, e), goff + e);
@@ -436,22 +429,19 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
         thr = kth ? TR::rank_key(kth) : INT_MIN;
     };
 
-    // Software-pipelined stream: the next batch's loads are in flight while the
-    // current batch is filtered.  Loads are never predicated (indices past the
-    // range are clamped to its last group and the data ignored), so the
-    // compiler's wait counts only the older batch.
-    auto issue = [&](uint4 (&d)[U], int g0) {
+    // batch kk covers this wave's blocks kk .. kk+U-1; lane reads group
+    // (wv + (kk+u)*S)*64 + lane of the row body
+    auto issue = [&](uint4 (&d)[U], int kk) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int gi = min(g0 + u * kWave + lane, ng - 1);
+            const int gi = min((wv + (kk + u) * S) * kWave + lane, ng - 1);
             d[u] = load16<NT>(vp + gi);
         }
     };
-    auto filter = [&](const uint4 (&d)[U], int g0) {
+    auto filter = [&](const uint4 (&d)[U], int kk) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int gi = g0 + u * kWave + lane;
-            const bool inb = gi < ng;
+            const bool inb = (kk + u < kcount) && ((wv + (kk + u) * S) * kWave + lane < ng);
             if constexpr (PROB) {
                 if (inb) {
 #pragma unroll
@@ -464,29 +454,29 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
                 if (pass) {
                     const int pos = count + lanes_below(bal);
                     sd[pos] = d[u];
-                    sg[pos] = (uint16_t)gi;
+                    sg[pos] = (uint16_t)((kk + u) * kWave + lane);
                 }
                 count += __popcll(bal);
             }
         }
-        if (count > kCapOf<U> - kWave * U) {
+        if (count > kCap - kWave * U) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             process();
         }
     };
 
-    if (ng > 0) {
+    if (kcount > 0) {
         uint4 cur[U], nxt[U];
         issue(cur, 0);
         {
             // Seed the threshold: the 8th largest lane maximum of the first batch is a
-            // lower bound of the range's 8th best key when it is positive (8 distinct
+            // lower bound of the wave's 8th best key when it is positive (8 distinct
             // elements reach it), so the first batch is filtered like the rest.
             int m = TR::kRawMin;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (u * kWave + lane < ng) m = max(m, TR::raw_max(cur[u]));
+                if (u < kcount && (wv + u * S) * kWave + lane < ng) m = max(m, TR::raw_max(cur[u]));
             int m8 = TR::kRawMin;
 #pragma unroll
             for (int j = 0; j < kTop; ++j) {
@@ -496,14 +486,14 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
             }
             if (m8 >= 1 && m8 > thr) thr = m8;
         }
-        int g0 = 0;
-        for (; g0 + kWave * U < ng; g0 += kWave * U) {
-            issue(nxt, g0 + kWave * U);
-            filter(cur, g0);
+        int kk = 0;
+        for (; kk + U < kcount; kk += U) {
+            issue(nxt, kk + U);
+            filter(cur, kk);
 #pragma unroll
             for (int u = 0; u < U; ++u) cur[u] = nxt[u];
         }
-        filter(cur, g0);
+        filter(cur, kk);
     }
     if (count) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -511,42 +501,86 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
         process();
     }
 
-    // Publish this range's candidates.  The last range of a row to finish
-    // (device-scope counter) merges the row; with ACCEPT, the last row of a
-    // request to be merged runs that request's acceptance walk.  Counters are
-    // reset by the wave that consumed them, so the workspace is left zeroed.
-    if (lane < kTop) st_agent(&a.partials[w * kTop + lane], top ? TR::to_row_rank(top, c0) : 0ull);
+    // The row's S waves meet; wave 0 merges their candidates into the top-k.
+    if (lane < kTop) {
+        uint64_t r = 0;
+        if (top) r = rank64(TR::rank_key(top) * (sizeof(Rank) == 4 ? 65536 : 1),
+                            global_id(TR::local_off(top)));
+        s_cand[wv * kTop + lane] = r;
+    }
     if constexpr (PROB) {
         const float M = wave_max_f32(st.m);
         const float s = (st.m == -INFINITY) ? 0.0f : st.s * __expf(st.m - M);
         const float Ssum = wave_sum_f32(s);
-        if (lane == 0)
-            st_agent(&a.stats[w], ((uint64_t)__float_as_uint(Ssum) << 32) | __float_as_uint(M));
+        if (lane == 0) s_stat[wv] = make_float2(M, Ssum);
     }
-    publish();
-    uint32_t prev = 0;
-    if (lane == 0) prev = count_in(&a.row_cnt[row]);
-    prev = (uint32_t)readlane_i32((int)prev, 0);
-    if (prev != (uint32_t)(S - 1)) return;
-    after_count();
-    merge_row(a, row);
-    if (lane == 0) st_agent(&a.row_cnt[row], 0u);
+    __syncthreads();
+    if (wv != 0) return;
+    {
+        uint64_t c[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int j = i * kWave + lane;
+            c[i] = j < S * kTop ? s_cand[j] : 0ull;
+        }
+        uint64_t rtop = 0;
+        merge_top8<uint64_t, 2>(c, rtop);
+        if (lane < a.k) st_agent(&a.topk[row * a.k + lane], rtop ? (int32_t)rank64_id(rtop) : -1);
+        if (a.prob) {
+            const float2 sv = lane < S ? s_stat[lane] : make_float2(-INFINITY, 0.0f);
+            const float M = wave_max_f32(sv.x);
+            const float s = (sv.x == -INFINITY) ? 0.0f : sv.y * __expf(sv.x - M);
+            const float Ssum = wave_sum_f32(s);
+            if (lane < a.k) {
+                const float x = key_to_f32(rank64_key(rtop));
+                const float pj = rtop ? __expf(x - M) / Ssum : 0.0f;
+                st_agent((int32_t *)&a.prob[row * a.k + lane], __float_as_int(pj));
+            }
+        }
+    }
     if constexpr (ACCEPT) {
+        // The last row of request b to finish runs the request's acceptance walk,
+        // then (fused update) its share of the matrix update.  Counters are reset
+        // by the wave that consumed them, so the workspace is left zeroed.
+        // Two-level count (groups of kRowGroup rows, then groups) keeps the
+        // atomics on any one counter few: rows of a request finish together.
         const int b = (int)(row / v.T1);
+        const int f = (int)(row - (int64_t)b * v.T1);
+        const int grp = f / kRowGroup;
+        const int ngrp = (v.T1 + kRowGroup - 1) / kRowGroup;
+        const int gsize = min(kRowGroup, v.T1 - grp * kRowGroup);
+        uint32_t *gcnt = v.req_cnt + (size_t)v.B + (size_t)b * kMaxGroups + grp;
         publish();
-        uint32_t prev_r = 0;
-        if (lane == 0) prev_r = count_in(&v.req_cnt[b]);
-        prev_r = (uint32_t)readlane_i32((int)prev_r, 0);
-        if (prev_r != (uint32_t)(v.T1 - 1)) return;
+        uint32_t prev = 0;
+        if (lane == 0) prev = count_in(gcnt);
+        prev = (uint32_t)readlane_i32((int)prev, 0);
+        if (prev != (uint32_t)(gsize - 1)) return;
+        if (lane == 0) st_agent(gcnt, 0u);
+        after_count();
+        if (lane == 0) prev = count_in(&v.req_cnt[b]);
+        prev = (uint32_t)readlane_i32((int)prev, 0);
+        if (prev != (uint32_t)(ngrp - 1)) return;
         after_count();
         accept_walk(v, a.k, a.topk, b);
         if (lane == 0) st_agent(&v.req_cnt[b], 0u);
         if (v.table) {
-            publish();
-            if (handoff_second(v, b)) {
+            // Fast path: the registration workgroup already arrived (it finishes
+            // long before any request), so this wave runs the update and clears
+            // the hand-off word.  Otherwise the two-arrival hand-off decides.
+            int h = 0;
+            if (lane == 0) h = (int)ld_agent((const int32_t *)&v.handoff[b]);
+            h = readlane_i32(h, 0);
+            if (h == 1) {
                 after_count();
                 update_request(v, a.V, a.k, a.topk, a.prob, b);
                 if (lane == 0) st_agent(&v.handoff[b], 0u);
+            } else {
+                publish();
+                if (handoff_second(v, b)) {
+                    after_count();
+                    update_request(v, a.V, a.k, a.topk, a.prob, b);
+                    if (lane == 0) st_agent(&v.handoff[b], 0u);
+                }
             }
         }
     }
@@ -554,22 +588,23 @@ __global__ __launch_bounds__(kWave *kWavesPerBlockA) void k_topk_rows(TopkArgs a
 
 template <typename TR>
 void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
-    const int64_t waves = a.n_rows * a.S;
+    using Rank = typename TR::Rank;
     const int extra = (v && v->table) ? 1 : 0;  // the registration workgroup
-    const dim3 grid((unsigned)((waves + kWavesPerBlockA - 1) / kWavesPerBlockA + extra));
-    const dim3 block(kWave * kWavesPerBlockA);
+    const dim3 grid((unsigned)(a.n_rows + extra));
+    const dim3 block(kWave * a.S);
+    const size_t lds = RowSmem<Rank>::bytes(a.S);
     const VerifyArgs vv = v ? *v : VerifyArgs{};
     const bool prob = a.prob != nullptr;
     if (v) {
         if (prob)
-            hipLaunchKernelGGL((k_topk_rows<TR, true, true, true>), grid, block, 0, s, a, vv);
+            hipLaunchKernelGGL((k_topk_rows<TR, true, true, true>), grid, block, lds, s, a, vv);
         else
-            hipLaunchKernelGGL((k_topk_rows<TR, false, true, true>), grid, block, 0, s, a, vv);
+            hipLaunchKernelGGL((k_topk_rows<TR, false, true, true>), grid, block, lds, s, a, vv);
     } else {
         if (prob)
-            hipLaunchKernelGGL((k_topk_rows<TR, true, false, true>), grid, block, 0, s, a, vv);
+            hipLaunchKernelGGL((k_topk_rows<TR, true, false, true>), grid, block, lds, s, a, vv);
         else
-            hipLaunchKernelGGL((k_topk_rows<TR, false, false, true>), grid, block, 0, s, a, vv);
+            hipLaunchKernelGGL((k_topk_rows<TR, false, false, true>), grid, block, lds, s, a, vv);
     }
 }
 
@@ -579,29 +614,24 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     TopkPlan p;
     p.n_rows = n_rows;
     p.V = V;
-    const int max_range = dtype == GRAFT_DTYPE_BF16 ? Bf16Traits::kMaxRange : F32Traits::kMaxRange;
-    // Enough ranges to fill 256 CUs x 16 waves, each range >= 4096 elements,
-    // and at most 32 ranges per row (phase B holds 8 candidates per range).
-    const int64_t target_waves = 256 * 16;
-    int S = (int)((target_waves + n_rows - 1) / (n_rows > 0 ? n_rows : 1));
-    S = S < 1 ? 1 : S;
-    const int by_len = (V + 4095) / 4096;
-    if (S > by_len) S = by_len;
-    const int min_s = (V + max_range - 1) / max_range;
-    if (S < min_s) S = min_s;
-    if (S > 32) S = 32;
-    int chunk = (V + S - 1) / S;
-    chunk = (chunk + 7) / 8 * 8;
-    S = (V + chunk - 1) / chunk;
-    p.splits = S;
-    p.chunk = chunk;
-    p.partial_bytes = (size_t)n_rows * S * kTop * sizeof(uint64_t);
-    p.stats_bytes = (size_t)n_rows * S * sizeof(float2);
-    // workspace: [partials | stats | row counters, request counters |
-    //             last occurrence per token [V], (unused word), hand-offs [n_rows]]
-    p.off_stats = (p.partial_bytes + 255) / 256 * 256;
-    p.off_counters = p.off_stats + (p.stats_bytes + 255) / 256 * 256;
-    p.off_occ = p.off_counters + ((size_t)n_rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+    // S waves per row: about 4096 waves in flight over the chip (~16 per CU),
+    // at most 16 per row, and few enough blocks per wave that local offsets
+    // fit 16 bits (bf16: 127 blocks of 512 elements per wave).
+    const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
+    const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
+    const int64_t target_waves = 4096;
+    int64_t S = (target_waves + (n_rows > 0 ? n_rows : 1) - 1) / (n_rows > 0 ? n_rows : 1);
+    S = S < 1 ? 1 : (S > kMaxWavesPerRow ? kMaxWavesPerRow : S);
+    const int64_t smin = (nblk + 126) / 127;
+    if (S < smin) S = smin;
+    if (S > nblk && nblk > 0) S = nblk;
+    if (S < 1) S = 1;
+    p.splits = (int)S;
+    p.chunk = 0;
+    // workspace: [request counters [n_rows] + row-group counters [n_rows * kMaxGroups] |
+    //             last holder per token [V], spare, hand-offs [n_rows]]
+    p.off_counters = 0;
+    p.off_occ = ((size_t)n_rows * (1 + kMaxGroups) * sizeof(uint32_t) + 255) / 256 * 256;
     p.ws_bytes = p.off_occ + ((size_t)(V + 1 + n_rows) * sizeof(uint32_t) + 255) / 256 * 256;
     return p;
 }
@@ -614,17 +644,13 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     a.n_rows = p.n_rows;
     a.V = p.V;
     a.S = p.splits;
-    a.chunk = p.chunk;
-    a.partials = (uint64_t *)ws;
-    a.stats = (uint64_t *)((char *)ws + p.off_stats);
-    a.row_cnt = (uint32_t *)((char *)ws + p.off_counters);
     a.k = k;
     a.topk = topk;
     a.prob = prob;
     VerifyArgs v;
     if (verify) {
         v = *verify;
-        v.req_cnt = a.row_cnt + p.n_rows;
+        v.req_cnt = (uint32_t *)((char *)ws + p.off_counters);
         v.last_occ = (int32_t *)((char *)ws + p.off_occ);
         v.handoff = (uint32_t *)(v.last_occ + p.V + 1);
         v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
