@@ -77,6 +77,18 @@ struct Bf16Traits {
         return max((int)m.x, (int)m.y);
     }
     static constexpr int kRawMin = -32768;
+    // For a threshold thr >= 1: (thr-1) in both 16-bit halves, and the packed test
+    // "some element's raw bits, read as int16, exceed thr-1" -- exactly "some key
+    // >= thr", since keys >= 1 are positive values, whose bits order as int16.
+    __device__ static uint32_t splat_below(int thr) {
+        const uint32_t t = (uint32_t)(thr - 1) & 0xffffu;
+        return t | (t << 16);
+    }
+    __device__ static bool pass_positive(const uint4 &d, uint32_t t2) {
+        const short2v m = __builtin_elementwise_max(
+            __builtin_elementwise_max(as_s2(d.x), as_s2(d.y)), __builtin_elementwise_max(as_s2(d.z), as_s2(d.w)));
+        return as_u32(__builtin_elementwise_max(m, as_s2(t2))) != t2;
+    }
     // Superset filter: does any element of the group have key >= thr?
     __device__ static bool group_pass(const uint4 &d, int thr) {
         if (thr >= 1) {
@@ -112,6 +124,10 @@ struct F32Traits {
         return max(max((int)d.x, (int)d.y), max((int)d.z, (int)d.w));
     }
     static constexpr int kRawMin = INT_MIN;
+    __device__ static uint32_t splat_below(int thr) { return (uint32_t)thr; }
+    __device__ static bool pass_positive(const uint4 &d, uint32_t t) {
+        return max(max((int)d.x, (int)d.y), max((int)d.z, (int)d.w)) >= (int)t;
+    }
     __device__ static bool group_pass(const uint4 &d, int thr) {
         if (thr >= 1) {
             const int m = max(max((int)d.x, (int)d.y), max((int)d.z, (int)d.w));
@@ -334,7 +350,7 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int S = blockDim.x >> 6;
     int64_t row = blockIdx.x;
     if constexpr (ACCEPT) {
@@ -400,11 +416,12 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         }
         if (ballot(have)) {
             kth = merge_top8<Rank, 1>(c, top);
-            thr = kth ? TR::rank_key(kth) : INT_MIN;
+            thr = __builtin_amdgcn_readfirstlane(kth ? TR::rank_key(kth) : INT_MIN);
         }
     }
 
     int count = 0;
+    auto set_thr = [&](int t) { thr = __builtin_amdgcn_readfirstlane(t); };
     auto process = [&]() {
         for (int base = 0; base < count; base += kWave) {
             const int gi = base + lane;
@@ -426,19 +443,97 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
             if (ballot(any)) kth = merge_top8_compact<Rank, EPG>(c, top, scratch);
         }
         count = 0;
-        thr = kth ? TR::rank_key(kth) : INT_MIN;
+        set_thr(kth ? TR::rank_key(kth) : INT_MIN);
+    };
+    // Append the groups that pass (one per lane at most) to the pending buffer.
+    auto append = [&](const uint4 &d, bool pass, int kq) {
+        const uint64_t bal = ballot(pass);
+        if (bal) {
+            if (pass) {
+                const int pos = count + lanes_below(bal);
+                sd[pos] = d;
+                sg[pos] = (uint16_t)(kq * kWave + lane);
+            }
+            count += __popcll(bal);
+        }
+    };
+    auto maybe_process = [&]() {
+        if (__builtin_amdgcn_readfirstlane(count) > kCap - kWave * U) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            process();
+        }
     };
 
-    // batch kk covers this wave's blocks kk .. kk+U-1; lane reads group
-    // (wv + (kk+u)*S)*64 + lane of the row body
-    auto issue = [&](uint4 (&d)[U], int kk) {
+    // Steady state: this wave's complete blocks, U per batch, the next batch in
+    // flight.  Block (wv + k*S) starts at group (wv + k*S)*64: a wave-uniform
+    // base plus the lane, no per-lane bounds checks.
+    const int nfull = ng / kWave;  // complete 1 KB blocks of the row
+    const int kfull = nfull > wv ? (nfull - wv + S - 1) / S : 0;
+    auto issue_full = [&](uint4 (&d)[U], int kk) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) d[u] = load16<NT>(vp + (size_t)(wv + (kk + u) * S) * kWave + lane);
+    };
+    auto filter_full = [&](const uint4 (&d)[U], int kk) {
+        if constexpr (PROB) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < EPG; ++e) st.add(TR::value(TR::elem(d[u], e)));
+        }
+        const int thr_u = __builtin_amdgcn_readfirstlane(thr);
+        if (thr_u >= 1) {
+            const uint32_t t2 = TR::splat_below(thr_u);
+#pragma unroll
+            for (int u = 0; u < U; ++u) append(d[u], TR::pass_positive(d[u], t2), kk + u);
+        } else if (thr_u == INT_MIN) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) append(d[u], true, kk + u);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) append(d[u], TR::group_pass(d[u], thr), kk + u);
+        }
+        maybe_process();
+    };
+
+    int kk = 0;
+    if (kfull >= U) {
+        uint4 cur[U], nxt[U];
+        issue_full(cur, 0);
+        {
+            // Seed the threshold: the 8th largest lane maximum of the first batch is a
+            // lower bound of the wave's 8th best key when it is positive (8 distinct
+            // elements reach it), so the first batch is filtered like the rest.
+            int m = TR::kRawMin;
+#pragma unroll
+            for (int u = 0; u < U; ++u) m = max(m, TR::raw_max(cur[u]));
+            int m8 = TR::kRawMin;
+#pragma unroll
+            for (int j = 0; j < kTop; ++j) {
+                m8 = wave_max_i32(m);
+                const uint64_t own = ballot(m == m8);
+                if (lane == __ffsll((unsigned long long)own) - 1) m = TR::kRawMin;
+            }
+            if (m8 >= 1 && m8 > thr) set_thr(m8);
+        }
+        for (; kk + 2 * U <= kfull; kk += U) {
+            issue_full(nxt, kk + U);
+            filter_full(cur, kk);
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+        filter_full(cur, kk);
+        kk += U;
+    }
+    // Remaining blocks of this wave (fewer than U complete ones, and the row's
+    // partial last block if this wave owns it), with bounds checks.
+    for (; kk < kcount; kk += U) {
+        uint4 d[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int gi = min((wv + (kk + u) * S) * kWave + lane, ng - 1);
             d[u] = load16<NT>(vp + gi);
         }
-    };
-    auto filter = [&](const uint4 (&d)[U], int kk) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool inb = (kk + u < kcount) && ((wv + (kk + u) * S) * kWave + lane < ng);
@@ -448,52 +543,9 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
                     for (int e = 0; e < EPG; ++e) st.add(TR::value(TR::elem(d[u], e)));
                 }
             }
-            const bool pass = inb && (thr == INT_MIN || TR::group_pass(d[u], thr));
-            const uint64_t bal = ballot(pass);
-            if (bal) {
-                if (pass) {
-                    const int pos = count + lanes_below(bal);
-                    sd[pos] = d[u];
-                    sg[pos] = (uint16_t)((kk + u) * kWave + lane);
-                }
-                count += __popcll(bal);
-            }
+            append(d[u], inb && (thr == INT_MIN || TR::group_pass(d[u], thr)), kk + u);
         }
-        if (count > kCap - kWave * U) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            process();
-        }
-    };
-
-    if (kcount > 0) {
-        uint4 cur[U], nxt[U];
-        issue(cur, 0);
-        {
-            // Seed the threshold: the 8th largest lane maximum of the first batch is a
-            // lower bound of the wave's 8th best key when it is positive (8 distinct
-            // elements reach it), so the first batch is filtered like the rest.
-            int m = TR::kRawMin;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (u < kcount && (wv + u * S) * kWave + lane < ng) m = max(m, TR::raw_max(cur[u]));
-            int m8 = TR::kRawMin;
-#pragma unroll
-            for (int j = 0; j < kTop; ++j) {
-                m8 = wave_max_i32(m);
-                const uint64_t own = ballot(m == m8);
-                if (lane == __ffsll((unsigned long long)own) - 1) m = TR::kRawMin;
-            }
-            if (m8 >= 1 && m8 > thr) thr = m8;
-        }
-        int kk = 0;
-        for (; kk + U < kcount; kk += U) {
-            issue(nxt, kk + U);
-            filter(cur, kk);
-#pragma unroll
-            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-        }
-        filter(cur, kk);
+        maybe_process();
     }
     if (count) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
