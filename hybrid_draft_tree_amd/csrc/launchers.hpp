@@ -101,7 +101,7 @@ struct VerifyArgs {
     int32_t *table = nullptr;
     float *table_prob = nullptr;
     int32_t *last_occ = nullptr;   // [V] row+1 of the last row holding each token
-    uint32_t *handoff = nullptr;   // [B] accept-done / registration-done hand-off
+    uint32_t *handoff = nullptr;   // [n_rows] row-done / registration-done hand-off
     int B = 0;
 };
 

@@ -268,41 +268,47 @@ __device__ __forceinline__ void accept_walk(const VerifyArgs &v, int k, int32_t 
     }
 }
 
-// Matrix update for the rows of request b (one wavefront, lane f = row b*T1+f):
-// a row writes its top-k into the matrix row of its token iff it is the last
-// row of the whole batch holding that token (highest row wins), then clears
-// that token's registration.  Called once every row is registered and the
-// request's rows are final.
-__device__ __forceinline__ void update_request(const VerifyArgs &v, int V, int k, int32_t *topk,
-                                               const float *prob, int b) {
+// Matrix update (section 三): a row writes its top-k into the matrix row of its
+// token iff it is the last row of the whole batch holding that token (highest
+// row wins), then clears that token's registration.  Runs once every row of the
+// batch is registered; each row is updated by whichever of {the row's own
+// workgroup, the registration workgroup} arrives second at the row's hand-off
+// word, so neither waits for the other.
+
+// One row from registers (wave 0 of the row's workgroup): lanes j < k hold the
+// row's j-th id and probability.  t is the row's token (valid, uniform).
+__device__ __forceinline__ void update_row_regs(const VerifyArgs &v, int k, int64_t P, int t, int32_t id,
+                                                float pj, bool with_prob) {
     const int lane = lane_id();
-    if (lane >= v.T1) return;
-    const int64_t P = (int64_t)b * v.T1 + lane;
-    const int t = v.tok[P];
-    if (t < 0 || t >= V) return;
+    int occ = 0;
+    if (lane == 0) occ = ld_agent(&v.last_occ[t]);
+    occ = readlane_i32(occ, 0);
+    if (occ != (int32_t)(P + 1)) return;
+    if (lane < k) {
+        v.table[(size_t)t * k + lane] = id;
+        if (v.table_prob && with_prob) v.table_prob[(size_t)t * k + lane] = pj;
+    }
+    if (lane == 0) st_agent(&v.last_occ[t], 0);
+}
+
+// One row from the published top-k (one thread; the rare case of a row that
+// finished before the registration did).
+__device__ __forceinline__ void update_row_mem(const VerifyArgs &v, int k, const int32_t *topk,
+                                               const float *prob, int64_t P, int t) {
     if (ld_agent(&v.last_occ[t]) != (int32_t)(P + 1)) return;
     for (int j = 0; j < k; ++j) v.table[(size_t)t * k + j] = ld_agent(&topk[P * k + j]);
-    if (v.table_prob)
+    if (v.table_prob && prob)
         for (int j = 0; j < k; ++j)
             v.table_prob[(size_t)t * k + j] = __int_as_float(ld_agent((const int32_t *)&prob[P * k + j]));
     st_agent(&v.last_occ[t], 0);
 }
 
-// Hand-off between "request b accepted" and "every row registered": the second
-// of the two arrivals runs request b's update.  Returns true for the second.
-__device__ __forceinline__ bool handoff_second(const VerifyArgs &v, int b) {
-    uint32_t prev = 0;
-    if (lane_id() == 0) prev = count_in(&v.handoff[b]);
-    prev = (uint32_t)readlane_i32((int)prev, 0);
-    return prev == 1u;
-}
-
-// Registration for the fused matrix update (workgroup 0 of the launch): every
-// row records itself as a holder of its token (atomic max of row+1), then the
-// hand-off of every request is completed.
+// Registration (workgroup 0 of the launch): every row with a valid token
+// records itself as a holder of that token (atomic max of row+1); once all are
+// in, the workgroup arrives at every such row's hand-off word and updates the
+// rows that arrived first.
 __device__ __forceinline__ void register_rows(const TopkArgs &a, const VerifyArgs &v) {
-    const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    constexpr int kR = 4;  // hand-off arrivals in flight per thread
     const int nth = blockDim.x;
     for (int64_t P = threadIdx.x; P < a.n_rows; P += nth) {
         const int t = v.tok[P];
@@ -311,18 +317,23 @@ __device__ __forceinline__ void register_rows(const TopkArgs &a, const VerifyArg
     }
     publish();
     __syncthreads();
-    if (wv != 0) return;
-    for (int b0 = 0; b0 < v.B; b0 += kWave) {
-        const int b = b0 + lane;
-        uint32_t old = 0;
-        if (b < v.B) old = count_in(&v.handoff[b]);
-        uint64_t second = ballot(b < v.B && old == 1u);
-        while (second) {
-            const int j = __ffsll((unsigned long long)second) - 1;
-            second &= second - 1;
-            after_count();
-            update_request(v, a.V, a.k, a.topk, a.prob, b0 + j);
-            if (lane == 0) st_agent(&v.handoff[b0 + j], 0u);
+    for (int64_t P0 = threadIdx.x; P0 < a.n_rows; P0 += (int64_t)kR * nth) {
+        uint32_t old[kR];
+        int tk[kR];
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            const int64_t P = P0 + (int64_t)u * nth;
+            tk[u] = P < a.n_rows ? v.tok[P] : -1;
+            old[u] = (tk[u] >= 0 && tk[u] < a.V) ? count_in(&v.handoff[P]) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            if (old[u] == 1u) {
+                const int64_t P = P0 + (int64_t)u * nth;
+                after_count();
+                update_row_mem(v, a.k, a.topk, a.prob, P, tk[u]);
+                st_agent(&v.handoff[P], 0u);
+            }
         }
     }
 }
@@ -568,6 +579,8 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     }
     __syncthreads();
     if (wv != 0) return;
+    int32_t my_id = -1;  // lanes j < k: the row's j-th id and probability
+    float my_p = 0.0f;
     {
         uint64_t c[2];
 #pragma unroll
@@ -577,7 +590,8 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         }
         uint64_t rtop = 0;
         merge_top8<uint64_t, 2>(c, rtop);
-        if (lane < a.k) st_agent(&a.topk[row * a.k + lane], rtop ? (int32_t)rank64_id(rtop) : -1);
+        my_id = rtop ? (int32_t)rank64_id(rtop) : -1;
+        if (lane < a.k) st_agent(&a.topk[row * a.k + lane], my_id);
         if (a.prob) {
             const float2 sv = lane < S ? s_stat[lane] : make_float2(-INFINITY, 0.0f);
             const float M = wave_max_f32(sv.x);
@@ -585,27 +599,51 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
             const float Ssum = wave_sum_f32(s);
             if (lane < a.k) {
                 const float x = key_to_f32(rank64_key(rtop));
-                const float pj = rtop ? __expf(x - M) / Ssum : 0.0f;
-                st_agent((int32_t *)&a.prob[row * a.k + lane], __float_as_int(pj));
+                my_p = rtop ? __expf(x - M) / Ssum : 0.0f;
+                st_agent((int32_t *)&a.prob[row * a.k + lane], __float_as_int(my_p));
             }
         }
     }
     if constexpr (ACCEPT) {
-        // The last row of request b to finish runs the request's acceptance walk,
-        // then (fused update) its share of the matrix update.  Counters are reset
-        // by the wave that consumed them, so the workspace is left zeroed.
-        // Two-level count (groups of kRowGroup rows, then groups) keeps the
+        // The last row of request b to finish runs the request's acceptance walk.
+        // A two-level count (groups of kRowGroup rows, then groups) keeps the
         // atomics on any one counter few: rows of a request finish together.
+        // With the fused update each row also hands itself to the update (see
+        // register_rows); its hand-off word is read together with the first count.
+        // Counters are reset by the wave that consumed them, so the workspace is
+        // left zeroed.
         const int b = (int)(row / v.T1);
         const int f = (int)(row - (int64_t)b * v.T1);
         const int grp = f / kRowGroup;
         const int ngrp = (v.T1 + kRowGroup - 1) / kRowGroup;
         const int gsize = min(kRowGroup, v.T1 - grp * kRowGroup);
         uint32_t *gcnt = v.req_cnt + (size_t)v.B + (size_t)b * kMaxGroups + grp;
+        const int t = v.table ? __builtin_amdgcn_readfirstlane(v.tok[row]) : -1;
+        const bool upd = t >= 0 && t < a.V;
         publish();
         uint32_t prev = 0;
-        if (lane == 0) prev = count_in(gcnt);
+        int h = 0;
+        if (lane == 0) {
+            prev = count_in(gcnt);
+            if (upd) h = ld_agent((const int32_t *)&v.handoff[row]);
+        }
         prev = (uint32_t)readlane_i32((int)prev, 0);
+        h = readlane_i32(h, 0);
+        if (upd) {
+            // Fast path: the registration workgroup already arrived (it finishes long
+            // before the rows do); otherwise the second arrival updates the row.
+            bool mine = h == 1;
+            if (!mine) {
+                uint32_t o = 0;
+                if (lane == 0) o = count_in(&v.handoff[row]);
+                mine = readlane_i32((int)o, 0) == 1;
+            }
+            if (mine) {
+                after_count();
+                update_row_regs(v, a.k, row, t, my_id, my_p, a.prob != nullptr);
+                if (lane == 0) st_agent(&v.handoff[row], 0u);
+            }
+        }
         if (prev != (uint32_t)(gsize - 1)) return;
         if (lane == 0) st_agent(gcnt, 0u);
         after_count();
@@ -615,26 +653,6 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         after_count();
         accept_walk(v, a.k, a.topk, b);
         if (lane == 0) st_agent(&v.req_cnt[b], 0u);
-        if (v.table) {
-            // Fast path: the registration workgroup already arrived (it finishes
-            // long before any request), so this wave runs the update and clears
-            // the hand-off word.  Otherwise the two-arrival hand-off decides.
-            int h = 0;
-            if (lane == 0) h = (int)ld_agent((const int32_t *)&v.handoff[b]);
-            h = readlane_i32(h, 0);
-            if (h == 1) {
-                after_count();
-                update_request(v, a.V, a.k, a.topk, a.prob, b);
-                if (lane == 0) st_agent(&v.handoff[b], 0u);
-            } else {
-                publish();
-                if (handoff_second(v, b)) {
-                    after_count();
-                    update_request(v, a.V, a.k, a.topk, a.prob, b);
-                    if (lane == 0) st_agent(&v.handoff[b], 0u);
-                }
-            }
-        }
     }
 }
 
