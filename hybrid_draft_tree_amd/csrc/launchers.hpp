@@ -70,7 +70,7 @@ struct TopkPlan {
     int V = 0;
     int splits = 1;           // wavefronts per row (one workgroup per row)
     int chunk = 0;            // unused
-    size_t off_counters = 0;  // request counters [n_rows]
+    size_t off_counters = 0;  // completion words [n_rows]
     size_t off_occ = 0;       // last holder per token [V], one spare word, hand-offs [n_rows]
     size_t ws_bytes = 0;      // workspace bytes the kernel uses (all zero between calls)
 };
@@ -96,13 +96,14 @@ struct VerifyArgs {
     int dmax = 0;
     int32_t *bonus = nullptr;
     int32_t *base_pos_io = nullptr;
-    uint32_t *req_cnt = nullptr;
+    int32_t *done = nullptr;       // [n_rows] completion words (greedy token + 1), zero between calls
     // fused matrix update (table != nullptr)
     int32_t *table = nullptr;
     float *table_prob = nullptr;
     int32_t *last_occ = nullptr;   // [V] row+1 of the last row holding each token
     uint32_t *handoff = nullptr;   // [n_rows] row-done / registration-done hand-off
     int B = 0;
+    int ncoord = 0;                // coordinator workgroups (one wavefront per request)
 };
 
 // Row-wise top-k of logits [n_rows, V] into topk [n_rows, k] (+ probabilities);

@@ -30,8 +30,7 @@ constexpr int kCap = kWave * (kLoadsInFlight + 1);  // pending groups per wave
 constexpr int kTop = 8;
 constexpr int kMaxWavesPerRow = 16;
 constexpr int kHeadPad = 8;  // local offsets below this are the row's unaligned head
-constexpr int kRowGroup = 8;  // rows per first-level completion counter
-constexpr int kMaxGroups = (64 + kRowGroup - 1) / kRowGroup;
+constexpr uint64_t kSpinTicks = 100000000ull;  // coordinator gives up after ~1 s (100 MHz clock)
 
 typedef short short2v __attribute__((ext_vector_type(2)));
 typedef int int4v __attribute__((ext_vector_type(4)));
@@ -220,18 +219,15 @@ struct SoftStats {
 };
 
 // Strict greedy acceptance walk of request b (section 二, gear 3), one wavefront;
-// lane f is flattened row f.  A row is accepted iff every row on its path from
-// the root carries the greedy token of its parent row; the deepest accepted row
-// wins, ties -> lowest row.
-__device__ __forceinline__ void accept_walk(const VerifyArgs &v, int k, int32_t *topk, int b) {
+// lane f is flattened row f with its greedy token g, token t, parent row p and
+// depth d.  A row is accepted iff every row on its path from the root carries
+// the greedy token of its parent row; the deepest accepted row wins, ties ->
+// lowest row.
+__device__ __forceinline__ void accept_walk(const VerifyArgs &v, int b, int g, int t, int p, int d) {
     const int lane = lane_id();
     const int T1 = v.T1;
     const bool row = lane < T1;
-    const size_t o = (size_t)b * T1 + lane;
-    const int g = row ? ld_agent(&topk[o * k]) : -1;
-    const int t = row ? v.tok[o] : -1;
-    const int p = (row && lane > 0) ? v.parent[o] : -1;
-    const int d = row ? v.depth[o] : 0;
+    if (!row || lane == 0) p = -1;
     const int gp = __shfl(g, p >= 0 ? p : lane);
     bool ok = row && (lane == 0 || (p >= 0 && t == gp));
     // AND of the edge checks along the path and the ancestor-or-self mask, by
@@ -303,7 +299,7 @@ __device__ __forceinline__ void update_row_mem(const VerifyArgs &v, int k, const
     st_agent(&v.last_occ[t], 0);
 }
 
-// Registration (workgroup 0 of the launch): every row with a valid token
+// Registration (fused update only): every row with a valid token
 // records itself as a holder of that token (atomic max of row+1); once all are
 // in, the workgroup arrives at every such row's hand-off word and updates the
 // rows that arrived first.
@@ -338,6 +334,47 @@ __device__ __forceinline__ void register_rows(const TopkArgs &a, const VerifyArg
     }
 }
 
+// Coordinators (the first v.ncoord workgroups of a verify launch, one wavefront
+// per request; nothing waits on them, so they cannot hold up the rows).  The
+// first one registers the rows' tokens for the fused update.  Row P publishes
+// (greedy token + 1) into done[P], zero meaning "not yet"; wavefront w watches
+// request w (one load per unfinished row per poll, no atomics) and runs its
+// acceptance walk as soon as all its rows are in, then clears the words.  A
+// watch that exceeds kSpinTicks reports accept_len = -1 and stops.
+__device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &v, int cw) {
+    if (cw == 0 && v.table) register_rows(a, v);
+    const int lane = lane_id();
+    const int S = blockDim.x >> 6;
+    const int T1 = v.T1;
+    const bool row = lane < T1;
+    for (int b = cw * S + (int)(threadIdx.x >> 6); b < v.B; b += v.ncoord * S) {
+        const size_t o = (size_t)b * T1 + lane;
+        int t = -1, p = -1, d = 0, g = 1;
+        if (row) {
+            t = v.tok[o];
+            p = v.parent[o];
+            d = v.depth[o];
+            g = 0;
+        }
+        const uint64_t t0 = wall_clock64();
+        bool ok = true;
+        while (true) {
+            if (g == 0) g = ld_agent(&v.done[o]);
+            if (!ballot(g == 0)) break;
+            if (wall_clock64() - t0 > kSpinTicks) {
+                ok = false;
+                break;
+            }
+        }
+        if (!ok) {
+            if (lane == 0) v.accept_len[b] = -1;
+            continue;
+        }
+        accept_walk(v, b, g - 1, t, p, d);
+        if (row) st_agent(&v.done[o], 0);
+    }
+}
+
 // Dynamic LDS layout of a row's workgroup (S waves).
 template <typename Rank>
 struct RowSmem {
@@ -345,8 +382,12 @@ struct RowSmem {
     static constexpr size_t kMerge = sizeof(Rank) * kWave;     // compaction scratch
     static constexpr size_t kGidx = sizeof(uint16_t) * kCap;   // pending group indices
     static constexpr size_t kPerWave = kData + kMerge + kGidx;
+    // row tail: the waves' top-8 (S*kTop u64, at least one wavefront's worth), the
+    // row's top-8 (u64), per-wave 8th best keys (int), softmax statistics (float2)
+    __host__ __device__ static size_t cand_entries(int S) { return (size_t)(S * kTop > kWave ? S * kTop : kWave); }
     static size_t bytes(int S) {
-        return (size_t)S * kPerWave + (size_t)S * kTop * sizeof(uint64_t) + (size_t)S * sizeof(float2) + 16;
+        return (size_t)S * kPerWave + (cand_entries(S) + kTop) * sizeof(uint64_t) +
+               (size_t)S * (sizeof(int) + sizeof(float2)) + 16;
     }
 };
 
@@ -365,13 +406,11 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     const int S = blockDim.x >> 6;
     int64_t row = blockIdx.x;
     if constexpr (ACCEPT) {
-        if (v.table) {
-            if (blockIdx.x == 0) {
-                register_rows(a, v);
-                return;
-            }
-            row -= 1;
+        if (row < v.ncoord) {
+            coordinate(a, v, (int)row);
+            return;
         }
+        row -= v.ncoord;
     }
     if (row >= a.n_rows) return;
 
@@ -379,7 +418,9 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     Rank *scratch = (Rank *)(smem + (size_t)S * SM::kData + (size_t)wv * SM::kMerge);
     uint16_t *sg = (uint16_t *)(smem + (size_t)S * (SM::kData + SM::kMerge) + (size_t)wv * SM::kGidx);
     uint64_t *s_cand = (uint64_t *)(smem + (size_t)S * SM::kPerWave);
-    float2 *s_stat = (float2 *)(s_cand + (size_t)S * kTop);
+    uint64_t *s_top = s_cand + SM::cand_entries(S);
+    float2 *s_stat = (float2 *)(s_top + kTop);
+    int *s_kth = (int *)(s_stat + S);
 
     const int V = a.V;
     const char *rowp = (const char *)a.logits + (size_t)row * (size_t)V * ESZ;
@@ -564,13 +605,19 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         process();
     }
 
-    // The row's S waves meet; wave 0 merges their candidates into the top-k.
+    // The row's S waves meet: each publishes its exact top-8 (row ranks) and its
+    // 8th best key.  Every wave holds 8 elements at or above its 8th best key, so
+    // the row's 8th best key is at least T = the largest of these; wave 0 keeps
+    // the entries with key >= T (typically a dozen) and picks the 8 best by
+    // counting, for each, the entries that rank above it.  Massive ties at T
+    // (more than one wavefront of entries) take the full merge instead.
+    constexpr int kScale = sizeof(Rank) == 4 ? 65536 : 1;  // wave key -> fp32 key
     if (lane < kTop) {
         uint64_t r = 0;
-        if (top) r = rank64(TR::rank_key(top) * (sizeof(Rank) == 4 ? 65536 : 1),
-                            global_id(TR::local_off(top)));
+        if (top) r = rank64(TR::rank_key(top) * kScale, global_id(TR::local_off(top)));
         s_cand[wv * kTop + lane] = r;
     }
+    if (lane == 0) s_kth[wv] = kth ? TR::rank_key(kth) * kScale : INT_MIN;
     if constexpr (PROB) {
         const float M = wave_max_f32(st.m);
         const float s = (st.m == -INFINITY) ? 0.0f : st.s * __expf(st.m - M);
@@ -579,17 +626,51 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     }
     __syncthreads();
     if (wv != 0) return;
-    int32_t my_id = -1;  // lanes j < k: the row's j-th id and probability
-    float my_p = 0.0f;
+    uint64_t rtop = 0;  // lanes 0..7: the row's top-8 (row ranks), descending
     {
+        int T = INT_MIN;
+        for (int w = 0; w < S; ++w) T = max(T, s_kth[w]);
         uint64_t c[2];
+        bool keep[2];
+        uint64_t bal[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int j = i * kWave + lane;
             c[i] = j < S * kTop ? s_cand[j] : 0ull;
+            keep[i] = c[i] != 0ull && rank64_key(c[i]) >= T;
+            bal[i] = ballot(keep[i]);
         }
-        uint64_t rtop = 0;
-        merge_top8<uint64_t, 2>(c, rtop);
+        const int n0 = __popcll(bal[0]);
+        const int ncand = n0 + __popcll(bal[1]);
+        if (ncand <= kWave) {
+            // compact the kept entries to lanes 0..ncand-1 (s_cand is wave 0's now)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            if (keep[0]) s_cand[lanes_below(bal[0])] = c[0];
+            if (keep[1]) s_cand[n0 + lanes_below(bal[1])] = c[1];
+            if (lane < kTop) s_top[lane] = 0ull;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const uint64_t x = lane < ncand ? s_cand[lane] : 0ull;
+            int above = 0;
+            for (int j = 0; j < ncand; ++j) {
+                const uint32_t lo = (uint32_t)readlane_i32((int)(uint32_t)x, j);
+                const uint32_t hi = (uint32_t)readlane_i32((int)(uint32_t)(x >> 32), j);
+                above += (((uint64_t)hi << 32) | lo) > x ? 1 : 0;
+            }
+            if (lane < ncand && above < kTop) s_top[above] = x;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            rtop = lane < kTop ? s_top[lane] : 0ull;
+        } else {
+            merge_top8<uint64_t, 2>(c, rtop);
+        }
+    }
+    int32_t my_id = -1;  // lanes j < k: the row's j-th id and probability
+    float my_p = 0.0f;
+    {
         my_id = rtop ? (int32_t)rank64_id(rtop) : -1;
         if (lane < a.k) st_agent(&a.topk[row * a.k + lane], my_id);
         if (a.prob) {
@@ -605,35 +686,18 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         }
     }
     if constexpr (ACCEPT) {
-        // The last row of request b to finish runs the request's acceptance walk.
-        // A two-level count (groups of kRowGroup rows, then groups) keeps the
-        // atomics on any one counter few: rows of a request finish together.
-        // With the fused update each row also hands itself to the update (see
-        // register_rows); its hand-off word is read together with the first count.
-        // Counters are reset by the wave that consumed them, so the workspace is
-        // left zeroed.
-        const int b = (int)(row / v.T1);
-        const int f = (int)(row - (int64_t)b * v.T1);
-        const int grp = f / kRowGroup;
-        const int ngrp = (v.T1 + kRowGroup - 1) / kRowGroup;
-        const int gsize = min(kRowGroup, v.T1 - grp * kRowGroup);
-        uint32_t *gcnt = v.req_cnt + (size_t)v.B + (size_t)b * kMaxGroups + grp;
+        // Completion word for the coordinator: greedy token + 1 (lane 0 holds it).
+        if (lane == 0) st_agent(&v.done[row], my_id + 1);
+        // Fused update: hand the row to the update.  Fast path: the registration
+        // already arrived (it finishes long before the rows do); otherwise the
+        // second arrival at the row's hand-off word updates the row.
         const int t = v.table ? __builtin_amdgcn_readfirstlane(v.tok[row]) : -1;
-        const bool upd = t >= 0 && t < a.V;
-        publish();
-        uint32_t prev = 0;
-        int h = 0;
-        if (lane == 0) {
-            prev = count_in(gcnt);
-            if (upd) h = ld_agent((const int32_t *)&v.handoff[row]);
-        }
-        prev = (uint32_t)readlane_i32((int)prev, 0);
-        h = readlane_i32(h, 0);
-        if (upd) {
-            // Fast path: the registration workgroup already arrived (it finishes long
-            // before the rows do); otherwise the second arrival updates the row.
-            bool mine = h == 1;
+        if (t >= 0 && t < a.V) {
+            int h = 0;
+            if (lane == 0) h = ld_agent((const int32_t *)&v.handoff[row]);
+            bool mine = readlane_i32(h, 0) == 1;
             if (!mine) {
+                publish();
                 uint32_t o = 0;
                 if (lane == 0) o = count_in(&v.handoff[row]);
                 mine = readlane_i32((int)o, 0) == 1;
@@ -644,22 +708,13 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
                 if (lane == 0) st_agent(&v.handoff[row], 0u);
             }
         }
-        if (prev != (uint32_t)(gsize - 1)) return;
-        if (lane == 0) st_agent(gcnt, 0u);
-        after_count();
-        if (lane == 0) prev = count_in(&v.req_cnt[b]);
-        prev = (uint32_t)readlane_i32((int)prev, 0);
-        if (prev != (uint32_t)(ngrp - 1)) return;
-        after_count();
-        accept_walk(v, a.k, a.topk, b);
-        if (lane == 0) st_agent(&v.req_cnt[b], 0u);
     }
 }
 
 template <typename TR>
 void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
     using Rank = typename TR::Rank;
-    const int extra = (v && v->table) ? 1 : 0;  // the registration workgroup
+    const int extra = v ? v->ncoord : 0;  // the coordinator workgroups
     const dim3 grid((unsigned)(a.n_rows + extra));
     const dim3 block(kWave * a.S);
     const size_t lds = RowSmem<Rank>::bytes(a.S);
@@ -698,10 +753,10 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     if (S < 1) S = 1;
     p.splits = (int)S;
     p.chunk = 0;
-    // workspace: [request counters [n_rows] + row-group counters [n_rows * kMaxGroups] |
-    //             last holder per token [V], spare, hand-offs [n_rows]]
+    // workspace: [completion words [n_rows] | last holder per token [V], spare,
+    //             hand-offs [n_rows]]
     p.off_counters = 0;
-    p.off_occ = ((size_t)n_rows * (1 + kMaxGroups) * sizeof(uint32_t) + 255) / 256 * 256;
+    p.off_occ = ((size_t)n_rows * sizeof(int32_t) + 255) / 256 * 256;
     p.ws_bytes = p.off_occ + ((size_t)(V + 1 + n_rows) * sizeof(uint32_t) + 255) / 256 * 256;
     return p;
 }
@@ -720,10 +775,11 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     VerifyArgs v;
     if (verify) {
         v = *verify;
-        v.req_cnt = (uint32_t *)((char *)ws + p.off_counters);
+        v.done = (int32_t *)((char *)ws + p.off_counters);
         v.last_occ = (int32_t *)((char *)ws + p.off_occ);
         v.handoff = (uint32_t *)(v.last_occ + p.V + 1);
         v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
+        v.ncoord = (v.B + p.splits - 1) / p.splits;  // one wavefront per request
     }
     if (dtype == GRAFT_DTYPE_BF16)
         launch_rows<Bf16Traits>(a, verify ? &v : nullptr, s);

@@ -161,8 +161,12 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
  * tok, parent, depth: int32 [B, T1] from graft_build_tree_mask.  logits must
  * be 16-byte aligned.  ws: zero-filled device workspace (256-byte aligned) of
  * at least graft_workspace_bytes(B*T1, V, k, dtype) bytes.  One kernel launch:
- * the acceptance walk runs in the top-k kernel's epilogue.
- * Requires 1 <= T1 <= 64, 1 <= k <= 8, k <= V, dmax >= 0. */
+ * one workgroup per row computes the top-k and publishes the row's greedy
+ * token; a coordinating workgroup in the same launch runs each request's
+ * acceptance walk as soon as all its rows are in.  accept_len[b] == -1 reports
+ * a coordinator that gave up waiting (about a second; never in normal
+ * operation): the outputs are then invalid and the workspace must be
+ * zero-filled again.  Requires 1 <= T1 <= 64, 1 <= k <= 8, k <= V, dmax >= 0. */
 int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logits,
                         const int32_t *tok, const int32_t *parent, const int32_t *depth,
                         int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
@@ -205,11 +209,12 @@ int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slo
 /* graft_verify_update -- graft_verify_accept followed by
  * graft_update_topk(row_tok = tok, topk_in = the top-k just computed) in one
  * launch: the logits are read once and the matrix is updated in the same
- * kernel (every row registers its token when it starts; each request, once
- * accepted, writes the rows that are the last holder of their token in the
- * batch).  table int32 [V, k] in/out; table_prob fp32 [V, k] (nullable;
- * needs topk_prob).  Other arguments as for graft_verify_accept.  Section 二,
- * gear 3; section 六 (online update). */
+ * kernel (the coordinating workgroup registers every row's token first; each
+ * row, once its top-k is known, writes it into the matrix row of its token if
+ * it is the last holder of that token in the batch).  table int32 [V, k]
+ * in/out; table_prob fp32 [V, k] (nullable; needs topk_prob).  Other
+ * arguments and the accept_len == -1 report as for graft_verify_accept.
+ * Section 二, gear 3; section 六 (online update). */
 int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logits, const int32_t *tok,
                         const int32_t *parent, const int32_t *depth, int32_t *table, float *table_prob,
                         int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
