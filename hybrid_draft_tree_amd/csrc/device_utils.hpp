@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <climits>
 
 namespace graft {
 
@@ -23,7 +24,10 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 // half-rows, rows, then rows 0+1 and 2+3 via row broadcasts; lane 63 ends up with
 // the full result, read back as a wave-uniform value.  The mirror steps pair each
 // lane with a distinct partner, so the sequence is valid for max and for sum.
-#define GRAFT_DPP(v, ctrl, rmask) __builtin_amdgcn_update_dpp((v), (v), (ctrl), (rmask), 0xf, false)
+// Lanes a step leaves out (row mask) take `id`; with the operation's identity
+// there the compiler folds each step into one DPP-modified ALU instruction.
+#define GRAFT_DPP_ID(id, v, ctrl, rmask) __builtin_amdgcn_update_dpp((id), (v), (ctrl), (rmask), 0xf, false)
+#define GRAFT_DPP(v, ctrl, rmask) GRAFT_DPP_ID((v), (v), (ctrl), (rmask))
 constexpr int kDppXor1 = 0xb1;      // quad_perm(1,0,3,2)
 constexpr int kDppXor2 = 0x4e;      // quad_perm(2,3,0,1)
 constexpr int kDppHalfMirror = 0x141;
@@ -42,12 +46,24 @@ __device__ __forceinline__ int dpp_reduce_i32(int v, Op op) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Same with the operation's identity for the left-out lanes (integer max).
+template <typename Op>
+__device__ __forceinline__ int dpp_reduce_id_i32(int v, int id, Op op) {
+    v = op(v, GRAFT_DPP_ID(id, v, kDppXor1, 0xf));
+    v = op(v, GRAFT_DPP_ID(id, v, kDppXor2, 0xf));
+    v = op(v, GRAFT_DPP_ID(id, v, kDppHalfMirror, 0xf));
+    v = op(v, GRAFT_DPP_ID(id, v, kDppMirror, 0xf));
+    v = op(v, GRAFT_DPP_ID(id, v, kDppBcast15, 0xa));
+    v = op(v, GRAFT_DPP_ID(id, v, kDppBcast31, 0xc));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    return (uint32_t)dpp_reduce_i32((int)v, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
+    return (uint32_t)dpp_reduce_id_i32((int)v, 0, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
 }
 
 __device__ __forceinline__ int wave_max_i32(int v) {
-    return dpp_reduce_i32(v, [](int a, int b) { return max(a, b); });
+    return dpp_reduce_id_i32(v, INT_MIN, [](int a, int b) { return max(a, b); });
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
