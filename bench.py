@@ -38,7 +38,9 @@ if ROOT not in sys.path:
 METRIC = "Graft steps/sec at batch 16, V=151936, 60 slots; achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "topk_rows_b16_v151936_pmc.json")
-KERNEL_SRC = os.path.join(ROOT, "hybrid_draft_tree_amd", "csrc", "topk_kernels.hip")
+# sources the dominant kernel is compiled from (the counter summary is valid for them only)
+KERNEL_SRCS = [os.path.join(ROOT, "hybrid_draft_tree_amd", "csrc", f)
+               for f in ("topk_kernels.hip", "device_utils.hpp", "launchers.hpp")]
 
 
 def parse():
@@ -89,8 +91,11 @@ class _Adapter:
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(bytes_alg):
