@@ -23,25 +23,6 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Depth below the root of every node, by pointer doubling over parent links
-// (parent < 0 = child of the root, depth 1).  Invalid lanes report 0.
-__device__ __forceinline__ int node_depth(int par, bool valid) {
-    const int lane = lane_id();
-    int a = valid ? par : -1;
-    int d = valid ? 1 : 0;
-#pragma unroll
-    for (int r = 0; r < 6; ++r) {
-        const int src = a >= 0 ? a : lane;
-        const int da = __shfl(d, src);
-        const int aa = __shfl(a, src);
-        if (a >= 0) {
-            d += da;
-            a = aa;
-        }
-    }
-    return d;
-}
-
 struct PruneOut {
     int stage;   // uniform
     int N;       // uniform: kept draft nodes
@@ -56,20 +37,31 @@ struct PruneOut {
 __device__ __forceinline__ PruneOut prune_tree_wave(bool valid, int par, int lay, float lp, int Nd,
                                                    const graft_prune_cfg &cfg) {
     const int lane = lane_id();
-    const int dep = node_depth(par, valid);
-    const int maxd = wave_max_i32(dep);
-    float cum = 0.0f;
-    for (int d = 1; d <= maxd; ++d) {
-        const float pc = __shfl(cum, par >= 0 ? par : lane);
-        if (valid && dep == d) cum = (par >= 0 ? pc : 0.0f) + lp;
+    // one level per pass: a node is done once its parent is (root children first)
+    bool done = valid && par < 0;
+    float cum = done ? 0.0f + lp : 0.0f;
+    uint64_t todo = ballot(valid && !done);
+    while (todo) {
+        const int src = par >= 0 ? par : lane;
+        const float pc = __shfl(cum, src);
+        const int pd = __shfl((int)done, src);
+        if (valid && !done && par >= 0 && pd) {
+            cum = pc + lp;
+            done = true;
+        }
+        const uint64_t left = ballot(valid && !done);
+        if (left == todo) break;  // a parent link that never resolves (bad input)
+        todo = left;
     }
+    // order-preserving integer keys (-0 == +0): integer max and compares
+    const int key = f32_key(__float_as_uint(cum));
     int st = 3;
     for (int s = 0; s < 3; ++s) {
         const int c = cfg.ckpt_layer[s];
         const int on = __popcll(ballot(valid && lay == c));
         const int upto = __popcll(ballot(valid && lay <= c));
-        const float best = wave_max_f32((valid && lay == c) ? cum : -INFINITY);
-        if (on > 0 && upto >= cfg.keep[s] && best < cfg.log_thr[s]) {
+        const int best = wave_max_i32((valid && lay == c) ? key : INT_MIN);
+        if (on > 0 && upto >= cfg.keep[s] && best < f32_key(__float_as_uint(cfg.log_thr[s]))) {
             st = s;
             break;
         }
@@ -77,14 +69,20 @@ __device__ __forceinline__ PruneOut prune_tree_wave(bool valid, int par, int lay
     const int N = st < 3 ? cfg.keep[st] : Nd;
     const int climit = st < 3 ? cfg.ckpt_layer[st] : 0x7fffffff;
     const bool elig = valid && lay <= climit;
-    const uint64_t emask = ballot(elig);
-    int rank = 0;
-    for (int j = 0; j < Nd; ++j) {
-        const float cj = readlane_f32(cum, j);
-        const bool ej = (emask >> j) & 1ull;
-        rank += (ej && (cj > cum || (cj == cum && j < lane))) ? 1 : 0;
+    // T = the N-th largest key among the eligible nodes (bitwise search on the
+    // unsigned image of the key); keep every node above T and, of the nodes at
+    // T, the lowest-indexed ones up to N
+    const uint32_t u = (uint32_t)key ^ 0x80000000u;
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        if (__popcll(ballot(elig && u >= cand)) >= N) T = cand;
     }
-    return {st, N, elig && rank < N, cum};
+    const uint64_t gt = ballot(elig && u > T);
+    const uint64_t eq = ballot(elig && u == T);
+    const int need = N - __popcll(gt);
+    const bool kept = elig && (u > T || (u == T && lanes_below(eq) < need));
+    return {st, N, kept, cum};
 }
 
 // TAIL (section 七): the longest prefix of the block with confidence >= thr.
@@ -210,19 +208,17 @@ __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &i
     const int p = row_ok ? spar[lane] : -1;
     int a = (row_ok && lane > 0) ? p : -1;
     uint64_t A = row_ok ? ((1ull << lane) | (a >= 0 ? (1ull << a) : 0ull)) : 0ull;
-    int D = a >= 0 ? 1 : 0;
 #pragma unroll
     for (int r = 0; r < 6; ++r) {
         const int src = a >= 0 ? a : lane;
         const uint64_t Aa = shfl_u64(A, src);
-        const int Da = __shfl(D, src);
         const int aa = __shfl(a, src);
         if (a >= 0) {
             A |= Aa;
-            D += Da;
             a = aa;
         }
     }
+    const int D = __popcll(A) - 1;  // ancestors of the row (root: 0)
     if (row_ok) {
         tok_out[lane] = t;
         par_out[lane] = lane == 0 ? -1 : p;
@@ -329,11 +325,19 @@ __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
     const int root = a.root_tok[b];
 
     if (a.mode == GRAFT_MODE_TREE) {
+        // wave 0's flatten inputs, loaded up front so they are not a round trip after the barrier
+        int dt0 = -1, dp0 = -1, base0 = 0, tp0 = -1;
         if (wv == 0) {
             const bool act = lane < a.tpl_size;
             const int tp = act ? a.tpl_parent[lane] : -1;
+            tp0 = tp;
             const int tr = act ? a.tpl_rank[lane] : 0;
             const int td = act ? a.tpl_depth[lane] : 0;
+            if (isd) {
+                dt0 = a.d_tok[od];
+                dp0 = a.d_parent[od];
+            }
+            base0 = a.base_pos[b];
             s_ret[lane] = retrieve_tree_wave(a.tpl_size, tp, tr, td, root, a.table, a.V, a.k);
         } else {
             const int par = isd ? a.d_parent[od] : -1;
@@ -355,19 +359,19 @@ __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
         const int nk = s_misc[1];
         const int R = min(max(a.slots - nk, 0), a.tpl_size);
         const bool isr = lane < R;
-        const int tp = isr ? a.tpl_parent[lane] : -1;
+        const int tp = isr ? tp0 : -1;
         FlatIn in;
         in.isd = isd;
         in.kp = s_keep[lane];
-        in.dt = isd ? a.d_tok[od] : -1;
-        in.dp = isd ? a.d_parent[od] : -1;
+        in.dt = dt0;
+        in.dp = dp0;
         in.isr = isr;
         in.rt = isr ? s_ret[lane] : -1;
         in.rp = tp;
         in.nk = nk;
         in.R = R;
         in.root = root;
-        in.base = a.base_pos[b];
+        in.base = base0;
         if (lane < a.r_out) {
             a.ret_tok[(size_t)b * a.r_out + lane] = in.rt;
             a.ret_parent[(size_t)b * a.r_out + lane] = isr ? tp : -1;
