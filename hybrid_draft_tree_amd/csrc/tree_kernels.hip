@@ -95,9 +95,12 @@ __device__ __forceinline__ PruneOut prune_tail_wave(bool valid, float conf, int 
 
 // Gear 2 (TREE): template node t (lane t < R) reads one entry of the matrix row
 // of its parent's token (the root's for root children); depth levels are
-// dependent gathers.  Returns the node's token (-1 for lanes >= R).
-__device__ __forceinline__ int retrieve_tree_wave(int R, int tp, int tr, int td, int root,
-                                                  const int32_t *__restrict__ table, int V, int k) {
+// dependent gathers.  Returns the node's token (-1 for lanes >= R, and for a
+// node below an out-of-range token or rank).
+//
+// Level by level, each node reading its parent's token across lanes: any depth.
+__device__ __forceinline__ int retrieve_tree_levels(int R, int tp, int tr, int td, int root,
+                                                    const int32_t *__restrict__ table, int V, int k) {
     const int lane = lane_id();
     const bool act = lane < R;
     const int maxd = wave_max_i32(act ? td : 0);
@@ -109,6 +112,45 @@ __device__ __forceinline__ int retrieve_tree_wave(int R, int tp, int tr, int td,
             val = (src >= 0 && src < V && tr >= 0 && tr < k) ? table[(size_t)src * k + tr] : -1;
     }
     return act ? val : -1;
+}
+
+constexpr int kPathLevels = 21;  // 3-bit ranks in a 64-bit path code
+
+// Same result with no cross-lane step between the dependent gathers: every
+// node walks its own path from the root (nodes sharing a prefix read the same
+// matrix entries).  The ranks along the path are packed 3 bits per depth by
+// pointer doubling over the template's parent links before the first gather.
+// Needs depth <= kPathLevels (ranks < 8 always hold: k <= 8).
+__device__ __forceinline__ int retrieve_tree_wave(int R, int tp, int tr, int td, int root,
+                                                  const int32_t *__restrict__ table, int V, int k) {
+    const int lane = lane_id();
+    const bool act = lane < R;
+    const int maxd = wave_max_i32(act ? td : 0);
+    if (maxd > kPathLevels) return retrieve_tree_levels(R, tp, tr, td, root, table, V, k);
+    const bool own_ok = tr >= 0 && tr < k && td >= 1;
+    uint64_t P = (act && own_ok) ? ((uint64_t)tr << (3 * (td - 1))) : 0ull;
+    int bad = (act && !own_ok) ? 1 : 0;  // some rank on the path is out of range
+    int a = act ? tp : -1;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+        const int src = a >= 0 ? a : lane;
+        const uint64_t Pa = shfl_u64(P, src);
+        const int ba = __shfl(bad, src);
+        const int aa = __shfl(a, src);
+        if (a >= 0) {
+            P |= Pa;
+            bad |= ba;
+            a = aa;
+        }
+    }
+    int x = root;
+    for (int d = 1; d <= maxd; ++d) {
+        if (act && d <= td) {
+            const int r = (int)((P >> (3 * (d - 1))) & 7ull);
+            x = (x >= 0 && x < V) ? table[(size_t)x * k + r] : -1;
+        }
+    }
+    return (act && !bad) ? x : -1;
 }
 
 // TAIL: chain of rank-0 successors x <- M[x][0], R steps from x0; lane t gets
@@ -140,13 +182,18 @@ struct FlatIn {
 // Gear 3a: rows of the flattened hybrid tree.  Source lanes scatter their row
 // into the wave's LDS slices (stok/spar/srr: 64 ints each); lane f then owns
 // row f: token, parent row, depth and ancestor-or-self mask (pointer doubling).
+// The structure does not depend on the retrieved tokens: with `srowtpl` (an LDS
+// slice) the template node held by each row (or -1) is recorded there and the
+// tokens of those rows are left for the caller to store.
 __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &in, int *stok,
-                                             int *spar, int *srr, int32_t *tok_out, int32_t *par_out,
-                                             int32_t *dep_out, int32_t *pos_out, uint64_t *anc_out) {
+                                             int *spar, int *srr, int *srowtpl, int32_t *tok_out,
+                                             int32_t *par_out, int32_t *dep_out, int32_t *pos_out,
+                                             uint64_t *anc_out) {
     const int lane = lane_id();
     stok[lane] = -1;
     spar[lane] = -1;
     srr[lane] = 0;
+    if (srowtpl) srowtpl[lane] = -1;
     wave_sync_lds();
     const uint64_t kmask = ballot(in.isd && in.kp);
     const uint64_t dmask = ballot(in.isd);
@@ -166,6 +213,7 @@ __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &i
             if (row < T1) {
                 stok[row] = in.rt;
                 spar[row] = in.rp < 0 ? 0 : 1 + nk + in.rp;
+                if (srowtpl) srowtpl[row] = lane;
             }
         }
     } else if (layout == GRAFT_LAYOUT_IN_PLACE) {
@@ -183,6 +231,7 @@ __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &i
             } else if (r_i < in.R) {
                 stok[lane + 1] = rt_i;
                 spar[lane + 1] = (rp_i < 0 || rp_i >= kWave) ? 0 : srr[rp_i];
+                if (srowtpl) srowtpl[lane + 1] = r_i;
             }
         }
     } else {  // chain (TAIL)
@@ -195,6 +244,7 @@ __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &i
             if (row < T1) {
                 stok[row] = in.rt;
                 spar[row] = row - 1;
+                if (srowtpl) srowtpl[row] = lane;
             }
         }
     }
@@ -220,7 +270,7 @@ __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &i
     }
     const int D = __popcll(A) - 1;  // ancestors of the row (root: 0)
     if (row_ok) {
-        tok_out[lane] = t;
+        if (!srowtpl || srowtpl[lane] < 0) tok_out[lane] = t;
         par_out[lane] = lane == 0 ? -1 : p;
         dep_out[lane] = D;
         pos_out[lane] = in.base + D;
@@ -303,7 +353,7 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_flatten(FlattenKernelAr
     in.rt = in.isr ? a.ret_tok[(size_t)b * a.r_out + lane] : -1;
     in.rp = in.isr ? a.ret_parent[(size_t)b * a.r_out + lane] : -1;
     const size_t o = (size_t)b * a.T1;
-    flatten_wave(a.layout, a.T1, in, s_tok[w], s_par[w], s_rowret[w], a.tok + o, a.parent + o,
+    flatten_wave(a.layout, a.T1, in, s_tok[w], s_par[w], s_rowret[w], nullptr, a.tok + o, a.parent + o,
                  a.depth + o, a.pos_id + o, a.anc + o);
 }
 
@@ -313,10 +363,8 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_flatten(FlattenKernelAr
 // 0 keeps the first R = slots - n_keep template nodes and flattens.  TAIL:
 // wave 0 does all three (the chain starts from the last kept block token).
 __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
-    __shared__ int s_ret[kWave];
-    __shared__ int s_keep[kWave];
-    __shared__ int s_misc[2];
-    __shared__ int s_tok[kWave], s_par[kWave], s_rowret[kWave];
+    __shared__ int s_misc[1];
+    __shared__ int s_tok[kWave], s_par[kWave], s_rowret[kWave], s_rowtpl[kWave];
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6;
     const int b = blockIdx.x;
@@ -325,65 +373,62 @@ __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
     const int root = a.root_tok[b];
 
     if (a.mode == GRAFT_MODE_TREE) {
-        // wave 0's flatten inputs, loaded up front so they are not a round trip after the barrier
-        int dt0 = -1, dp0 = -1, base0 = 0, tp0 = -1;
+        const bool act = lane < a.tpl_size;
+        const int tp = act ? a.tpl_parent[lane] : -1;
+        int val = -1;
         if (wv == 0) {
-            const bool act = lane < a.tpl_size;
-            const int tp = act ? a.tpl_parent[lane] : -1;
-            tp0 = tp;
+            // wave 0: the whole template from the root (the budget R is not known yet)
             const int tr = act ? a.tpl_rank[lane] : 0;
             const int td = act ? a.tpl_depth[lane] : 0;
-            if (isd) {
-                dt0 = a.d_tok[od];
-                dp0 = a.d_parent[od];
-            }
-            base0 = a.base_pos[b];
-            s_ret[lane] = retrieve_tree_wave(a.tpl_size, tp, tr, td, root, a.table, a.V, a.k);
+            val = retrieve_tree_wave(a.tpl_size, tp, tr, td, root, a.table, a.V, a.k);
         } else {
+            // wave 1: prune, then the whole tree structure, which does not depend on
+            // the retrieved tokens (rows, parents, depths, positions, masks, draft
+            // and root tokens); the retrieval rows are recorded in s_rowtpl
             const int par = isd ? a.d_parent[od] : -1;
             const int lay = isd ? a.d_layer[od] : 0x7fffffff;
             const float lp = isd ? a.d_score[od] : 0.0f;
+            const int dt = isd ? a.d_tok[od] : -1;
+            const int base = a.base_pos[b];
             const PruneOut r = prune_tree_wave(isd, par, lay, lp, a.Nd, a.cfg);
             if (isd) {
                 a.keep[od] = r.kept ? 1 : 0;
                 if (a.cum_out) a.cum_out[od] = r.cum;
             }
-            s_keep[lane] = r.kept ? 1 : 0;
+            const int nk = r.N;
+            const int R = min(max(a.slots - nk, 0), a.tpl_size);
+            const bool isr = lane < R;
+            FlatIn in;
+            in.isd = isd;
+            in.kp = r.kept ? 1 : 0;
+            in.dt = dt;
+            in.dp = par;
+            in.isr = isr;
+            in.rt = -1;
+            in.rp = isr ? tp : -1;
+            in.nk = nk;
+            in.R = R;
+            in.root = root;
+            in.base = base;
+            if (lane < a.r_out) a.ret_parent[(size_t)b * a.r_out + lane] = isr ? tp : -1;
             if (lane == 0) {
-                s_misc[0] = r.stage;
-                s_misc[1] = r.N;
+                a.stage[b] = r.stage;
+                a.n_keep[b] = nk;
+                a.n_ret[b] = R;
+                s_misc[0] = R;
             }
+            const size_t o = (size_t)b * a.T1;
+            flatten_wave(a.layout, a.T1, in, s_tok, s_par, s_rowret, s_rowtpl, a.tok + o, a.parent + o,
+                         a.depth + o, a.pos_id + o, a.anc + o);
         }
         __syncthreads();
         if (wv != 0) return;
-        const int nk = s_misc[1];
-        const int R = min(max(a.slots - nk, 0), a.tpl_size);
-        const bool isr = lane < R;
-        const int tp = isr ? tp0 : -1;
-        FlatIn in;
-        in.isd = isd;
-        in.kp = s_keep[lane];
-        in.dt = dt0;
-        in.dp = dp0;
-        in.isr = isr;
-        in.rt = isr ? s_ret[lane] : -1;
-        in.rp = tp;
-        in.nk = nk;
-        in.R = R;
-        in.root = root;
-        in.base = base0;
-        if (lane < a.r_out) {
-            a.ret_tok[(size_t)b * a.r_out + lane] = in.rt;
-            a.ret_parent[(size_t)b * a.r_out + lane] = isr ? tp : -1;
-        }
-        if (lane == 0) {
-            a.stage[b] = s_misc[0];
-            a.n_keep[b] = nk;
-            a.n_ret[b] = R;
-        }
-        const size_t o = (size_t)b * a.T1;
-        flatten_wave(a.layout, a.T1, in, s_tok, s_par, s_rowret, a.tok + o, a.parent + o, a.depth + o,
-                     a.pos_id + o, a.anc + o);
+        // wave 0: the first R retrieved tokens, into ret_tok and the rows holding them
+        const int R = s_misc[0];
+        if (lane < a.r_out) a.ret_tok[(size_t)b * a.r_out + lane] = lane < R ? val : -1;
+        const int tn = lane < a.T1 ? s_rowtpl[lane] : -1;
+        const int tv = __shfl(val, tn >= 0 ? tn : lane);
+        if (tn >= 0) a.tok[(size_t)b * a.T1 + lane] = tv;
     } else {
         if (wv != 0) return;
         const float c = isd ? a.d_score[od] : 1.0f;
@@ -416,7 +461,7 @@ __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
             a.n_ret[b] = R;
         }
         const size_t o = (size_t)b * a.T1;
-        flatten_wave(GRAFT_LAYOUT_CHAIN, a.T1, in, s_tok, s_par, s_rowret, a.tok + o, a.parent + o,
+        flatten_wave(GRAFT_LAYOUT_CHAIN, a.T1, in, s_tok, s_par, s_rowret, nullptr, a.tok + o, a.parent + o,
                      a.depth + o, a.pos_id + o, a.anc + o);
     }
 }
