@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     // Local offsets (monotone in the element id for this wave): head elements
     // 0..head-1 (wave 0), body kHeadPad + k*BLK + lane*EPG + e for the wave's
     // k-th block, tail after the wave's body (wave 0).
-    auto global_id = [&](uint32_t off) -> uint32_t {
+    auto global_id = [&](uint32_t off) __attribute__((always_inline)) -> uint32_t {
         if (off < (uint32_t)kHeadPad) return off;
         const uint32_t q = off - kHeadPad;
         if (q < (uint32_t)kcount * BLK) return head + (wv + (q / BLK) * S) * BLK + q % BLK;
@@ -473,8 +473,8 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     }
 
     int count = 0;
-    auto set_thr = [&](int t) { thr = __builtin_amdgcn_readfirstlane(t); };
-    auto process = [&]() {
+    auto set_thr = [&](int t) __attribute__((always_inline)) { thr = __builtin_amdgcn_readfirstlane(t); };
+    auto process = [&]() __attribute__((always_inline)) {
         for (int base = 0; base < count; base += kWave) {
             const int gi = base + lane;
             Rank c[EPG];
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         set_thr(kth ? TR::rank_key(kth) : INT_MIN);
     };
     // Append the groups that pass (one per lane at most) to the pending buffer.
-    auto append = [&](const uint4 &d, bool pass, int kq) {
+    auto append = [&](const uint4 &d, bool pass, int kq) __attribute__((always_inline)) {
         const uint64_t bal = ballot(pass);
         if (bal) {
             if (pass) {
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
             count += __popcll(bal);
         }
     };
-    auto maybe_process = [&]() {
+    auto maybe_process = [&]() __attribute__((always_inline)) {
         if (__builtin_amdgcn_readfirstlane(count) > kCap - kWave * U) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -522,11 +522,11 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     // base plus the lane, no per-lane bounds checks.
     const int nfull = ng / kWave;  // complete 1 KB blocks of the row
     const int kfull = nfull > wv ? (nfull - wv + S - 1) / S : 0;
-    auto issue_full = [&](uint4 (&d)[U], int kk) {
+    auto issue_full = [&](uint4 (&d)[U], int kk) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) d[u] = load16<NT>(vp + (size_t)(wv + (kk + u) * S) * kWave + lane);
     };
-    auto filter_full = [&](const uint4 (&d)[U], int kk) {
+    auto filter_full = [&](const uint4 (&d)[U], int kk) __attribute__((always_inline)) {
         if constexpr (PROB) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
