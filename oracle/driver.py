@@ -58,7 +58,7 @@ class OracleGraft:
         return out
 
     # -- verify + update ----------------------------------------------------
-    def verify_update(self, logits, want_prob=False):
+    def verify_update(self, logits, want_prob=False, want_coverage=False):
         cfg = self.cfg
         B, T1, k = cfg.B, cfg.rows_per_request, cfg.k
         Dmax = T1 - 1
@@ -73,12 +73,16 @@ class OracleGraft:
             self.table_prob = np.zeros((cfg.V, k), np.float32)
         O.update(self.table, fl["tok"].reshape(-1), tk.reshape(-1, k),
                  prob if want_prob else None, self.table_prob if want_prob else None)
-        self.roots = acc["bonus"].copy()
-        self.base_pos = self.base_pos + acc["accept_len"] + 1
         out = dict(acc)
         out["topk"] = tk
         if want_prob:
             out["topk_prob"] = prob.reshape(B, T1, k)
+        if want_coverage:
+            # coverage gain of the tree just verified (section 三), fp64
+            out["coverage"] = O.coverage_gain(logits.reshape(B, T1, cfg.V), fl["tok"], fl["parent"],
+                                              fl["row_src"], cfg.dtype)
+        self.roots = acc["bonus"].copy()
+        self.base_pos = self.base_pos + acc["accept_len"] + 1
         return out
 
     # -- prompt ingest (long-context section) --------------------------------

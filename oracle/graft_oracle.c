@@ -234,12 +234,14 @@ int oracle_retrieve_tail(int B, int V, int k, const int32_t *table, const int32_
 /*   2 chain   : TAIL: kept block prefix, then the retrieval chain.          */
 /* depth[f] = depth[parent]+1; pos_id = base_pos + depth; anc[f] has bit g   */
 /* set iff row g is an ancestor of row f or f itself (root included).        */
+/* row_src (optional): where each row comes from -- 0 root, 1 kept draft     */
+/* node, 2 retrieval node, 3 unfilled.                                       */
 /* ------------------------------------------------------------------------- */
 int oracle_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
                    const int32_t *base_pos, const int32_t *d_tok, const int32_t *d_parent,
                    const uint8_t *keep, const int32_t *n_keep, int Rmax, const int32_t *ret_tok,
                    const int32_t *ret_parent, const int32_t *n_ret, int32_t *tok, int32_t *parent,
-                   int32_t *depth, int32_t *pos_id, uint64_t *anc) {
+                   int32_t *depth, int32_t *pos_id, uint64_t *anc, uint8_t *row_src) {
     if (T1 > 64) return -1;
     int *row_of_draft = (int *)malloc(sizeof(int) * (size_t)(Nd > 0 ? Nd : 1));
     int *row_of_ret = (int *)malloc(sizeof(int) * (size_t)(Rmax > 0 ? Rmax : 1));
@@ -253,12 +255,15 @@ int oracle_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
         const int32_t *rt = ret_tok + (size_t)b * Rmax;
         const int32_t *rp = ret_parent + (size_t)b * Rmax;
         int R = n_ret[b];
+        uint8_t *sr = row_src ? row_src + (size_t)b * T1 : NULL;
         for (int f = 0; f < T1; ++f) {
             tk[f] = -1;
             pa[f] = -1;
+            if (sr) sr[f] = 3;
         }
         tk[0] = root_tok[b];
         pa[0] = -1;
+        if (sr) sr[0] = 0;
         int used = 1;
         if (layout == 0) {
             for (int i = 0; i < Nd; ++i) {
@@ -267,12 +272,14 @@ int oracle_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
                 row_of_draft[i] = used;
                 tk[used] = dt[i];
                 pa[used] = (dp[i] < 0) ? 0 : row_of_draft[dp[i]];
+                if (sr) sr[used] = 1;
                 used++;
             }
             for (int t = 0; t < R; ++t) {
                 row_of_ret[t] = used;
                 tk[used] = rt[t];
                 pa[used] = (rp[t] < 0) ? 0 : row_of_ret[rp[t]];
+                if (sr) sr[used] = 2;
                 used++;
             }
         } else if (layout == 1) {
@@ -282,11 +289,13 @@ int oracle_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
                 if (kp[i]) {
                     tk[f] = dt[i];
                     pa[f] = (dp[i] < 0) ? 0 : dp[i] + 1;
+                    if (sr) sr[f] = 1;
                 } else {
                     if (t >= R) return -3;
                     row_of_ret[t] = f;
                     tk[f] = rt[t];
                     pa[f] = (rp[t] < 0) ? 0 : row_of_ret[rp[t]];
+                    if (sr) sr[f] = 2;
                     t++;
                 }
             }
@@ -297,11 +306,13 @@ int oracle_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
             for (int i = 0; i < p; ++i) {
                 tk[used] = dt[i];
                 pa[used] = used - 1;
+                if (sr) sr[used] = 1;
                 used++;
             }
             for (int t = 0; t < R; ++t) {
                 tk[used] = rt[t];
                 pa[used] = used - 1;
+                if (sr) sr[used] = 2;
                 used++;
             }
         } else {
@@ -442,5 +453,76 @@ int oracle_update(int64_t n_rows, int V, int k, const int32_t *row_tok, const in
             if (prob && table_prob) table_prob[(size_t)x * k + j] = (float)prob[P * k + j];
         }
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Softmax statistics of a row, fp64: stats[2r] = max value, stats[2r+1] =   */
+/* sum over the row of exp(value - max).                                      */
+/* ------------------------------------------------------------------------- */
+int oracle_row_stats(int64_t n_rows, int V, int dtype, const void *logits, double *stats) {
+    const size_t esz = dtype == ODT_BF16 ? 2 : 4;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const void *row = (const char *)logits + (size_t)r * (size_t)V * esz;
+        double m = -INFINITY;
+        for (int i = 0; i < V; ++i) {
+            double x = elem(row, dtype, i);
+            if (x > m) m = x;
+        }
+        double sum = 0.0;
+        for (int i = 0; i < V; ++i) sum += exp(elem(row, dtype, i) - m);
+        stats[2 * r] = m;
+        stats[2 * r + 1] = sum;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Coverage gain (section 三): what the grafted candidates add where pruning  */
+/* cut.  Reading: at every row v that has retrieval children, the target's   */
+/* probability mass -- softmax of row v's logits, fp64 -- of the SET of      */
+/* retrieval-child tokens of v that are not the token of a kept draft child */
+/* of v (each token once); summed over the rows v of a request.  It is       */
+/* positive as soon as one such token has nonzero probability.               */
+/* tok, parent, row_src as produced by oracle_flatten; gain[B] fp64.         */
+/* ------------------------------------------------------------------------- */
+int oracle_coverage_gain(int B, int T1, int V, int dtype, const void *logits, const int32_t *tok,
+                         const int32_t *parent, const uint8_t *row_src, double *gain) {
+    const size_t esz = dtype == ODT_BF16 ? 2 : 4;
+    int32_t *fresh = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T1 > 0 ? T1 : 1));
+    if (!fresh) return -1;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *tk = tok + (size_t)b * T1;
+        const int32_t *pa = parent + (size_t)b * T1;
+        const uint8_t *sr = row_src + (size_t)b * T1;
+        double g = 0.0;
+        for (int v = 0; v < T1; ++v) {
+            int nf = 0;
+            for (int c = 0; c < T1; ++c) {
+                if (pa[c] != v || sr[c] != 2) continue;
+                int x = tk[c];
+                if (x < 0 || x >= V) continue;
+                int seen = 0;
+                for (int d = 0; d < T1; ++d)
+                    if (pa[d] == v && sr[d] == 1 && tk[d] == x) seen = 1;
+                for (int j = 0; j < nf; ++j)
+                    if (fresh[j] == x) seen = 1;
+                if (!seen) fresh[nf++] = x;
+            }
+            if (nf == 0) continue;
+            const void *row = (const char *)logits + ((size_t)b * T1 + v) * (size_t)V * esz;
+            double m = -INFINITY;
+            for (int i = 0; i < V; ++i) {
+                double x = elem(row, dtype, i);
+                if (x > m) m = x;
+            }
+            double sum = 0.0;
+            for (int i = 0; i < V; ++i) sum += exp(elem(row, dtype, i) - m);
+            for (int j = 0; j < nf; ++j) g += exp(elem(row, dtype, fresh[j]) - m) / sum;
+        }
+        gain[b] = g;
+    }
+    free(fresh);
     return 0;
 }

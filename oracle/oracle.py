@@ -17,6 +17,7 @@ _LIB = None
 DT_F32 = 0
 DT_BF16 = 1
 LAYOUTS = {"compact": 0, "in_place": 1, "chain": 2}
+ROW_ROOT, ROW_DRAFT, ROW_RETRIEVED, ROW_EMPTY = 0, 1, 2, 3
 
 
 def lib():
@@ -35,7 +36,9 @@ def lib():
                                            C.c_int, P, P, P]
         L.oracle_retrieve_tail.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, C.c_int, P, P, P]
         L.oracle_flatten.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P, P, P, C.c_int,
-                                     P, P, P, P, P, P, P, P]
+                                     P, P, P, P, P, P, P, P, P]
+        L.oracle_row_stats.argtypes = [C.c_int64, C.c_int, C.c_int, P, P]
+        L.oracle_coverage_gain.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P, P]
         L.oracle_topk.argtypes = [C.c_int64, C.c_int, C.c_int, C.c_int, P, P, P]
         L.oracle_accept.argtypes = [C.c_int, C.c_int, P, P, P, C.c_int, P, P, P]
         L.oracle_update.argtypes = [C.c_int64, C.c_int, C.c_int, P, P, P, P, P]
@@ -151,11 +154,43 @@ def flatten(layout, T1, root_tok, base_pos, d_tok, d_parent, keep, n_keep, ret):
     dep = np.zeros((B, T1), np.int32)
     pos = np.zeros((B, T1), np.int32)
     anc = np.zeros((B, T1), np.uint64)
+    src = np.zeros((B, T1), np.uint8)
     rc = lib().oracle_flatten(B, Nd, T1, LAYOUTS[layout], _p(_i32(root_tok)), _p(_i32(base_pos)),
                               _p(d_tok), _p(d_parent), _p(keep), _p(_i32(n_keep)), Rmax, _p(rt), _p(rp),
-                              _p(_i32(ret["n_ret"])), _p(tok), _p(par), _p(dep), _p(pos), _p(anc))
+                              _p(_i32(ret["n_ret"])), _p(tok), _p(par), _p(dep), _p(pos), _p(anc), _p(src))
     _check(rc, "flatten")
-    return {"tok": tok, "parent": par, "depth": dep, "pos_id": pos, "anc": anc}
+    return {"tok": tok, "parent": par, "depth": dep, "pos_id": pos, "anc": anc, "row_src": src}
+
+
+def _logits(a, dtype):
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return a.view(np.uint16), DT_BF16
+    return a.view(np.float32), DT_F32
+
+
+def row_stats(logits, dtype="bf16"):
+    """fp64 softmax statistics per row: [..., 2] = (max value, sum of exp(value - max))."""
+    a, dt = _logits(logits, dtype)
+    V = a.shape[-1]
+    n = a.size // V
+    out = np.zeros((n, 2), np.float64)
+    _check(lib().oracle_row_stats(n, V, dt, _p(a), _p(out)), "row_stats")
+    return out.reshape(a.shape[:-1] + (2,))
+
+
+def coverage_gain(logits, tok, parent, row_src, dtype="bf16"):
+    """fp64 coverage gain per request; logits [B, T1, V], tree arrays [B, T1]."""
+    a, dt = _logits(logits, dtype)
+    tok, parent = _i32(tok), _i32(parent)
+    B, T1 = tok.shape
+    V = a.shape[-1]
+    assert a.size == B * T1 * V
+    src = np.ascontiguousarray(row_src, np.uint8)
+    out = np.zeros(B, np.float64)
+    _check(lib().oracle_coverage_gain(B, T1, V, dt, _p(a), _p(tok), _p(parent), _p(src), _p(out)),
+           "coverage_gain")
+    return out
 
 
 def topk(logits, k=8, dtype="bf16", want_prob=False):
