@@ -209,7 +209,7 @@ def main():
     def verify_call(i):
         L.graft_verify_update(B, T1, V, k, pipe.dtype, pool_logits[i % P].data_ptr(), pipe.tok.data_ptr(),
                               pipe.parent.data_ptr(), pipe.depth.data_ptr(), pipe.table.data_ptr(), None,
-                              pipe.topk.data_ptr(), None, pipe.accept_len.data_ptr(), pipe.accept_idx.data_ptr(),
+                              pipe.topk.data_ptr(), None, None, pipe.accept_len.data_ptr(), pipe.accept_idx.data_ptr(),
                               pipe.dmax, pipe.roots.data_ptr(), None, pipe.ws.data_ptr(), pipe.ws_bytes,
                               stream.cuda_stream)
 

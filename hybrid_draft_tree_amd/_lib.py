@@ -23,13 +23,14 @@ DTYPE_BF16 = 1
 MODE_TREE = 0
 MODE_TAIL = 1
 LAYOUT = {"compact": 0, "in_place": 1, "chain": 2}
+ROW_ROOT, ROW_DRAFT, ROW_RETRIEVED, ROW_EMPTY = 0, 1, 2, 3
 MAX_ROWS = 64
 MAX_K = 8
 
 EXPORTS = (
     "graft_prune_select", "graft_template_master", "graft_retrieve_expand",
     "graft_build_tree_mask", "graft_verify_accept", "graft_update_topk",
-    "graft_build_hybrid_tree", "graft_verify_update",
+    "graft_build_hybrid_tree", "graft_verify_update", "graft_coverage_gain",
     "graft_workspace_bytes", "graft_status_string",
 )
 
@@ -68,12 +69,13 @@ def load():
     L.graft_template_master.argtypes = [I, I, I, P, P, P]
     L.graft_retrieve_expand.argtypes = [I, I, I, I, I, P, P, P, P, I, C.POINTER(Template),
                                         C.POINTER(PruneCfg), P, P, P, I, P]
-    L.graft_build_tree_mask.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P]
-    L.graft_verify_accept.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
+    L.graft_build_tree_mask.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P]
+    L.graft_verify_accept.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
     L.graft_update_topk.argtypes = [I64, I, I, I, P, P, P, P, P, P, P, P, S, P]
     L.graft_build_hybrid_tree.argtypes = [I, I, I, I, I, I, C.POINTER(PruneCfg), C.POINTER(Template), I, I,
-                                          P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P]
-    L.graft_verify_update.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
+                                          P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P]
+    L.graft_verify_update.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
+    L.graft_coverage_gain.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
     L.graft_workspace_bytes.argtypes = [I64, I, I, I]
     L.graft_workspace_bytes.restype = S
     L.graft_status_string.argtypes = [I]
@@ -124,17 +126,18 @@ def graft_retrieve_expand(B, V, k, mode, slots, table, root_tok, n_keep, d_tok, 
 
 
 def graft_build_tree_mask(B, Nd, T1, layout, root_tok, base_pos, d_tok, d_parent, keep, n_keep,
-                          ret_tok, ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, stream):
+                          ret_tok, ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, row_src,
+                          stream):
     return _chk("graft_build_tree_mask", load().graft_build_tree_mask(
         B, Nd, T1, layout, root_tok, base_pos, d_tok, d_parent, keep, n_keep, ret_tok, ret_parent,
-        n_ret, r_out, tok, parent, depth, pos_id, anc, stream))
+        n_ret, r_out, tok, parent, depth, pos_id, anc, row_src, stream))
 
 
-def graft_verify_accept(B, T1, V, k, dtype, logits, tok, parent, depth, topk, topk_prob,
+def graft_verify_accept(B, T1, V, k, dtype, logits, tok, parent, depth, topk, topk_prob, row_stats,
                         accept_len, accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream):
     return _chk("graft_verify_accept", load().graft_verify_accept(
-        B, T1, V, k, dtype, logits, tok, parent, depth, topk, topk_prob, accept_len, accept_idx,
-        dmax, bonus, base_pos_io, ws, ws_bytes, stream))
+        B, T1, V, k, dtype, logits, tok, parent, depth, topk, topk_prob, row_stats, accept_len,
+        accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream))
 
 
 def graft_update_topk(n_rows, V, k, dtype, logits, topk_in, prob_in, row_tok, table, table_prob,
@@ -146,18 +149,23 @@ def graft_update_topk(n_rows, V, k, dtype, logits, topk_in, prob_in, row_tok, ta
 
 def graft_build_hybrid_tree(B, Nd, T1, mode, layout, slots, cfg, tpl, V, k, table, root_tok, base_pos,
                             d_parent, d_layer, d_score, d_tok, stage, n_keep, keep, cum_out, ret_tok,
-                            ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, stream):
+                            ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, row_src, stream):
     return _chk("graft_build_hybrid_tree", load().graft_build_hybrid_tree(
         B, Nd, T1, mode, layout, slots, C.byref(cfg), C.byref(tpl) if tpl is not None else None, V, k,
         table, root_tok, base_pos, d_parent, d_layer, d_score, d_tok, stage, n_keep, keep, cum_out,
-        ret_tok, ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, stream))
+        ret_tok, ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, row_src, stream))
 
 
 def graft_verify_update(B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob,
-                        accept_len, accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream):
+                        row_stats, accept_len, accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream):
     return _chk("graft_verify_update", load().graft_verify_update(
-        B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob, accept_len,
-        accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream))
+        B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob, row_stats,
+        accept_len, accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream))
+
+
+def graft_coverage_gain(B, T1, V, dtype, logits, tok, parent, row_src, row_stats, gain, stream):
+    return _chk("graft_coverage_gain", load().graft_coverage_gain(
+        B, T1, V, dtype, logits, tok, parent, row_src, row_stats, gain, stream))
 
 
 def graft_workspace_bytes(n_rows, V, k, dtype):

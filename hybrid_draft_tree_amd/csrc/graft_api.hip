@@ -141,7 +141,7 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
                           const uint8_t *keep, const int32_t *n_keep, const int32_t *ret_tok,
                           const int32_t *ret_parent, const int32_t *n_ret, int r_out, int32_t *tok,
                           int32_t *parent, int32_t *depth, int32_t *pos_id, uint64_t *anc,
-                          hipStream_t stream) {
+                          uint8_t *row_src, hipStream_t stream) {
     if (layout != GRAFT_LAYOUT_COMPACT && layout != GRAFT_LAYOUT_IN_PLACE &&
         layout != GRAFT_LAYOUT_CHAIN)
         return GRAFT_EUNSUPPORTED;
@@ -156,7 +156,7 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
     if (layout != GRAFT_LAYOUT_CHAIN && !d_parent) return GRAFT_EINVAL;
     if (!aligned(anc, 8)) return GRAFT_EINVAL;
     FlattenKernelArgs a{B, Nd, T1, layout, root_tok, base_pos, d_tok, d_parent, keep, n_keep, ret_tok,
-                        ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc};
+                        ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, row_src};
     launch_flatten(a, stream);
     return launch_status();
 }
@@ -168,7 +168,7 @@ int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slo
                             const int32_t *d_tok, int32_t *stage, int32_t *n_keep, uint8_t *keep,
                             float *cum_out, int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret,
                             int r_out, int32_t *tok, int32_t *parent, int32_t *depth, int32_t *pos_id,
-                            uint64_t *anc, hipStream_t stream) {
+                            uint64_t *anc, uint8_t *row_src, hipStream_t stream) {
     if (mode != GRAFT_MODE_TREE && mode != GRAFT_MODE_TAIL) return GRAFT_EUNSUPPORTED;
     if (layout != GRAFT_LAYOUT_COMPACT && layout != GRAFT_LAYOUT_IN_PLACE && layout != GRAFT_LAYOUT_CHAIN)
         return GRAFT_EUNSUPPORTED;
@@ -228,15 +228,16 @@ int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slo
     a.depth = depth;
     a.pos_id = pos_id;
     a.anc = anc;
+    a.row_src = row_src;
     launch_build(a, stream);
     return launch_status();
 }
 
 int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logits, const int32_t *tok,
                         const int32_t *parent, const int32_t *depth, int32_t *table, float *table_prob,
-                        int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
-                        int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws, size_t ws_bytes,
-                        hipStream_t stream) {
+                        int32_t *topk, float *topk_prob, float *row_stats, int32_t *accept_len,
+                        int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws,
+                        size_t ws_bytes, hipStream_t stream) {
     if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
     if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || k < 1 || k > GRAFT_MAX_K || k > V ||
         dmax < 0)
@@ -245,7 +246,7 @@ int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logi
     if (!logits || !tok || !parent || !depth || !table || !topk || !accept_len || !bonus ||
         (dmax > 0 && !accept_idx) || !ws || (table_prob && !topk_prob))
         return GRAFT_EINVAL;
-    if (!aligned(logits, 16) || !aligned(ws, 256)) return GRAFT_EINVAL;
+    if (!aligned(logits, 16) || !aligned(ws, 256) || !aligned(row_stats, 8)) return GRAFT_EINVAL;
     const int64_t n_rows = (int64_t)B * T1;
     const WsLayout L = ws_layout(n_rows, V, k, dtype);
     if (ws_bytes < L.total) return GRAFT_EINVAL;
@@ -261,15 +262,15 @@ int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logi
     v.base_pos_io = base_pos_io;
     v.table = table;
     v.table_prob = table_prob;
-    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, ws, &v, stream);
+    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, row_stats, ws, &v, stream);
     return launch_status();
 }
 
 int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logits,
                         const int32_t *tok, const int32_t *parent, const int32_t *depth,
-                        int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
-                        int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws, size_t ws_bytes,
-                        hipStream_t stream) {
+                        int32_t *topk, float *topk_prob, float *row_stats, int32_t *accept_len,
+                        int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws,
+                        size_t ws_bytes, hipStream_t stream) {
     if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
     if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || k < 1 || k > GRAFT_MAX_K || k > V ||
         dmax < 0)
@@ -278,7 +279,7 @@ int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logi
     if (!logits || !tok || !parent || !depth || !topk || !accept_len || !bonus ||
         (dmax > 0 && !accept_idx) || !ws)
         return GRAFT_EINVAL;
-    if (!aligned(logits, 16) || !aligned(ws, 256)) return GRAFT_EINVAL;
+    if (!aligned(logits, 16) || !aligned(ws, 256) || !aligned(row_stats, 8)) return GRAFT_EINVAL;
     const int64_t n_rows = (int64_t)B * T1;
     const WsLayout L = ws_layout(n_rows, V, k, dtype);
     if (ws_bytes < L.total) return GRAFT_EINVAL;
@@ -292,7 +293,7 @@ int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logi
     v.dmax = dmax;
     v.bonus = bonus;
     v.base_pos_io = base_pos_io;
-    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, ws, &v, stream);
+    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, row_stats, ws, &v, stream);
     return launch_status();
 }
 
@@ -312,13 +313,26 @@ int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logit
         if (ws_bytes < L.total) return GRAFT_EINVAL;
         int32_t *tk_ws = topk_out ? topk_out : (int32_t *)((char *)ws + L.off_topk);
         float *pr_ws = table_prob ? (float *)((char *)ws + L.off_prob) : nullptr;
-        launch_topk(L.plan, dtype, logits, k, tk_ws, pr_ws, ws, nullptr, stream);
+        launch_topk(L.plan, dtype, logits, k, tk_ws, pr_ws, nullptr, ws, nullptr, stream);
         tk = tk_ws;
         pr = pr_ws;
     } else if (table_prob && !prob_in) {
         return GRAFT_EINVAL;
     }
     launch_update(n_rows, V, k, tk, table_prob ? pr : nullptr, row_tok, table, table_prob, stream);
+    return launch_status();
+}
+
+int graft_coverage_gain(int B, int T1, int V, int dtype, const void *logits, const int32_t *tok,
+                        const int32_t *parent, const uint8_t *row_src, const float *row_stats,
+                        float *gain, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
+    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1) return GRAFT_EINVAL;
+    if (B == 0) return GRAFT_OK;
+    if (!logits || !tok || !parent || !row_src || !row_stats || !gain) return GRAFT_EINVAL;
+    if (!aligned(row_stats, 8)) return GRAFT_EINVAL;
+    CoverageArgs a{B, T1, V, dtype, logits, tok, parent, row_src, row_stats, gain};
+    launch_coverage(a, stream);
     return launch_status();
 }
 

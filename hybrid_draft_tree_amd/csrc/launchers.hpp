@@ -39,6 +39,7 @@ struct FlattenKernelArgs {
     int r_out;
     int32_t *tok, *parent, *depth, *pos_id;
     uint64_t *anc;
+    uint8_t *row_src;  // nullable
 };
 
 struct BuildKernelArgs {
@@ -57,6 +58,7 @@ struct BuildKernelArgs {
     int r_out;
     int32_t *tok, *parent, *depth, *pos_id;
     uint64_t *anc;
+    uint8_t *row_src;  // nullable
 };
 
 void launch_prune(const PruneKernelArgs &a, hipStream_t s);
@@ -83,7 +85,8 @@ struct TopkArgs {
     int V, S;
     int k;
     int32_t *topk;
-    float *prob;
+    float *prob;   // nullable: softmax probability of each top-k id
+    float *stats;  // nullable: per row (largest value, sum of exp(value - largest))
 };
 
 struct VerifyArgs {
@@ -111,10 +114,21 @@ struct VerifyArgs {
 // runs in the same launch, and with verify->table the matrix update too.  The
 // workspace counters must be zero on entry and are zero again on exit.
 void launch_topk(const TopkPlan &plan, int dtype, const void *logits, int k, int32_t *topk,
-                 float *prob, void *ws, const VerifyArgs *verify, hipStream_t s);
+                 float *prob, float *stats, void *ws, const VerifyArgs *verify, hipStream_t s);
 
 // ---- matrix update (verify_kernels.hip) ---------------------------------------------
 void launch_update(int64_t n_rows, int V, int k, const int32_t *topk, const float *prob,
                    const int32_t *row_tok, int32_t *table, float *table_prob, hipStream_t s);
+
+// ---- coverage gain (verify_kernels.hip) ---------------------------------------------
+struct CoverageArgs {
+    int B, T1, V, dtype;
+    const void *logits;
+    const int32_t *tok, *parent;
+    const uint8_t *row_src;
+    const float *row_stats;
+    float *gain;
+};
+void launch_coverage(const CoverageArgs &a, hipStream_t s);
 
 }  // namespace graft

@@ -673,12 +673,13 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     {
         my_id = rtop ? (int32_t)rank64_id(rtop) : -1;
         if (lane < a.k) st_agent(&a.topk[row * a.k + lane], my_id);
-        if (a.prob) {
+        if (PROB) {
             const float2 sv = lane < S ? s_stat[lane] : make_float2(-INFINITY, 0.0f);
             const float M = wave_max_f32(sv.x);
             const float s = (sv.x == -INFINITY) ? 0.0f : sv.y * __expf(sv.x - M);
             const float Ssum = wave_sum_f32(s);
-            if (lane < a.k) {
+            if (a.stats && lane == 0) *(float2 *)&a.stats[row * 2] = make_float2(M, Ssum);
+            if (a.prob && lane < a.k) {
                 const float x = key_to_f32(rank64_key(rtop));
                 my_p = rtop ? __expf(x - M) / Ssum : 0.0f;
                 st_agent((int32_t *)&a.prob[row * a.k + lane], __float_as_int(my_p));
@@ -719,7 +720,7 @@ void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
     const dim3 block(kWave * a.S);
     const size_t lds = RowSmem<Rank>::bytes(a.S);
     const VerifyArgs vv = v ? *v : VerifyArgs{};
-    const bool prob = a.prob != nullptr;
+    const bool prob = a.prob != nullptr || a.stats != nullptr;  // softmax statistics wanted
     if (v) {
         if (prob)
             hipLaunchKernelGGL((k_topk_rows<TR, true, true, true>), grid, block, lds, s, a, vv);
@@ -762,7 +763,7 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
 }
 
 void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_t *topk,
-                 float *prob, void *ws, const VerifyArgs *verify, hipStream_t s) {
+                 float *prob, float *stats, void *ws, const VerifyArgs *verify, hipStream_t s) {
     if (p.n_rows <= 0) return;
     TopkArgs a;
     a.logits = logits;
@@ -772,6 +773,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     a.k = k;
     a.topk = topk;
     a.prob = prob;
+    a.stats = stats;
     VerifyArgs v;
     if (verify) {
         v = *verify;

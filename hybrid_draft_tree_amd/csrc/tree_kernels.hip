@@ -182,16 +182,20 @@ struct FlatIn {
 // Gear 3a: rows of the flattened hybrid tree.  Source lanes scatter their row
 // into the wave's LDS slices (stok/spar/srr: 64 ints each); lane f then owns
 // row f: token, parent row, depth and ancestor-or-self mask (pointer doubling).
-// The structure does not depend on the retrieved tokens: with `srowtpl` (an LDS
-// slice) the template node held by each row (or -1) is recorded there and the
-// tokens of those rows are left for the caller to store.
+// spar holds (parent row + 1) | (row source << 8), so an unfilled row reads as
+// parent -1, source GRAFT_ROW_EMPTY.  The structure does not depend on the
+// retrieved tokens: with `srowtpl` (an LDS slice) the template node held by each
+// row (or -1) is recorded there and the tokens of those rows are left for the
+// caller to store.  src_out (nullable) receives the row sources.
+__device__ __forceinline__ int flat_link(int prow, int src) { return (prow + 1) | (src << 8); }
+
 __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &in, int *stok,
                                              int *spar, int *srr, int *srowtpl, int32_t *tok_out,
                                              int32_t *par_out, int32_t *dep_out, int32_t *pos_out,
-                                             uint64_t *anc_out) {
+                                             uint64_t *anc_out, uint8_t *src_out) {
     const int lane = lane_id();
     stok[lane] = -1;
-    spar[lane] = -1;
+    spar[lane] = flat_link(-1, GRAFT_ROW_EMPTY);
     srr[lane] = 0;
     if (srowtpl) srowtpl[lane] = -1;
     wave_sync_lds();
@@ -205,14 +209,14 @@ __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &i
             const int prow = dp < 0 ? 0 : 1 + __popcll(kmask & ((dp >= 64) ? ~0ull : ((1ull << dp) - 1ull)));
             if (row < T1) {
                 stok[row] = in.dt;
-                spar[row] = prow;
+                spar[row] = flat_link(prow, GRAFT_ROW_DRAFT);
             }
         }
         if (in.isr) {
             const int row = 1 + nk + lane;
             if (row < T1) {
                 stok[row] = in.rt;
-                spar[row] = in.rp < 0 ? 0 : 1 + nk + in.rp;
+                spar[row] = flat_link(in.rp < 0 ? 0 : 1 + nk + in.rp, GRAFT_ROW_RETRIEVED);
                 if (srowtpl) srowtpl[row] = lane;
             }
         }
@@ -227,35 +231,36 @@ __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &i
         if (in.isd && lane + 1 < T1) {
             if (in.kp) {
                 stok[lane + 1] = in.dt;
-                spar[lane + 1] = in.dp < 0 ? 0 : in.dp + 1;
+                spar[lane + 1] = flat_link(in.dp < 0 ? 0 : in.dp + 1, GRAFT_ROW_DRAFT);
             } else if (r_i < in.R) {
                 stok[lane + 1] = rt_i;
-                spar[lane + 1] = (rp_i < 0 || rp_i >= kWave) ? 0 : srr[rp_i];
+                spar[lane + 1] = flat_link((rp_i < 0 || rp_i >= kWave) ? 0 : srr[rp_i], GRAFT_ROW_RETRIEVED);
                 if (srowtpl) srowtpl[lane + 1] = r_i;
             }
         }
     } else {  // chain (TAIL)
         if (in.isd && lane < nk && lane + 1 < T1) {
             stok[lane + 1] = in.dt;
-            spar[lane + 1] = lane;
+            spar[lane + 1] = flat_link(lane, GRAFT_ROW_DRAFT);
         }
         if (in.isr) {
             const int row = 1 + nk + lane;
             if (row < T1) {
                 stok[row] = in.rt;
-                spar[row] = row - 1;
+                spar[row] = flat_link(row - 1, GRAFT_ROW_RETRIEVED);
                 if (srowtpl) srowtpl[row] = lane;
             }
         }
     }
     if (lane == 0) {
         stok[0] = in.root;
-        spar[0] = -1;
+        spar[0] = flat_link(-1, GRAFT_ROW_ROOT);
     }
     wave_sync_lds();
     const bool row_ok = lane < T1;
     const int t = row_ok ? stok[lane] : -1;
-    const int p = row_ok ? spar[lane] : -1;
+    const int link = row_ok ? spar[lane] : flat_link(-1, GRAFT_ROW_EMPTY);
+    const int p = (link & 0xff) - 1;
     int a = (row_ok && lane > 0) ? p : -1;
     uint64_t A = row_ok ? ((1ull << lane) | (a >= 0 ? (1ull << a) : 0ull)) : 0ull;
 #pragma unroll
@@ -275,6 +280,7 @@ __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &i
         dep_out[lane] = D;
         pos_out[lane] = in.base + D;
         anc_out[lane] = A;
+        if (src_out) src_out[lane] = (uint8_t)(link >> 8);
     }
 }
 
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_flatten(FlattenKernelAr
     in.rp = in.isr ? a.ret_parent[(size_t)b * a.r_out + lane] : -1;
     const size_t o = (size_t)b * a.T1;
     flatten_wave(a.layout, a.T1, in, s_tok[w], s_par[w], s_rowret[w], nullptr, a.tok + o, a.parent + o,
-                 a.depth + o, a.pos_id + o, a.anc + o);
+                 a.depth + o, a.pos_id + o, a.anc + o, a.row_src ? a.row_src + o : nullptr);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -419,7 +425,7 @@ __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
             }
             const size_t o = (size_t)b * a.T1;
             flatten_wave(a.layout, a.T1, in, s_tok, s_par, s_rowret, s_rowtpl, a.tok + o, a.parent + o,
-                         a.depth + o, a.pos_id + o, a.anc + o);
+                         a.depth + o, a.pos_id + o, a.anc + o, a.row_src ? a.row_src + o : nullptr);
         }
         __syncthreads();
         if (wv != 0) return;
@@ -462,7 +468,7 @@ __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
         }
         const size_t o = (size_t)b * a.T1;
         flatten_wave(GRAFT_LAYOUT_CHAIN, a.T1, in, s_tok, s_par, s_rowret, nullptr, a.tok + o, a.parent + o,
-                     a.depth + o, a.pos_id + o, a.anc + o);
+                     a.depth + o, a.pos_id + o, a.anc + o, a.row_src ? a.row_src + o : nullptr);
     }
 }
 

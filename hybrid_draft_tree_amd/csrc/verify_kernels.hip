@@ -1,7 +1,9 @@
 // Online update of the continuation matrix (section 二, gear 3 of the news
 // write-up of arXiv 2605.20104): the target's top-k at every verified position,
-// accepted or rejected, overwrites the row of that position's input token.  The
-// acceptance walk lives in the top-k kernel's epilogue (topk_kernels.hip).
+// accepted or rejected, overwrites the row of that position's input token (this
+// kernel serves the prompt ingest and the separate-call path; the fused verify
+// launch updates the matrix itself, topk_kernels.hip).  Also the coverage-gain
+// diagnostic of section 三.
 #include "device_utils.hpp"
 #include "launchers.hpp"
 
@@ -75,7 +77,53 @@ __global__ __launch_bounds__(kUpdThreads) void k_update(int64_t n_rows, int V, i
     }
 }
 
+// Coverage gain (section 三 of the news write-up): for each request (one
+// wavefront, lane c = row c), the retrieved rows whose token is new under their
+// parent row v -- no kept draft sibling carries it, no earlier retrieved sibling
+// either -- add the target's softmax probability of that token at row v, from
+// the row's logit and its softmax statistics (largest value, normaliser).
+constexpr int kCovReqPerBlock = 4;
+
+__global__ __launch_bounds__(kWave *kCovReqPerBlock) void k_coverage(CoverageArgs a) {
+    const int lane = lane_id();
+    const int b = blockIdx.x * kCovReqPerBlock + (int)(threadIdx.x >> 6);
+    if (b >= a.B) return;
+    const int T1 = a.T1;
+    const bool row = lane < T1;
+    const size_t o = (size_t)b * T1 + lane;
+    const int src = row ? (int)a.row_src[o] : GRAFT_ROW_EMPTY;
+    const int t = row ? a.tok[o] : -1;
+    const int v = row ? a.parent[o] : -1;
+    const bool ret = src == GRAFT_ROW_RETRIEVED && v >= 0 && v < T1 && t >= 0 && t < a.V;
+    bool dup = false;
+    for (int d = 0; d < T1; ++d) {
+        const int sd = readlane_i32(src, d);
+        const int td = readlane_i32(t, d);
+        const int vd = readlane_i32(v, d);
+        dup |= vd == v && td == t &&
+               (sd == GRAFT_ROW_DRAFT || (sd == GRAFT_ROW_RETRIEVED && d < lane));
+    }
+    float p = 0.0f;
+    if (ret && !dup) {
+        const size_t r = (size_t)b * T1 + v;
+        const float2 st = *(const float2 *)&a.row_stats[2 * r];
+        const size_t i = r * (size_t)a.V + t;
+        const float x = a.dtype == GRAFT_DTYPE_BF16
+                            ? __uint_as_float((uint32_t)((const uint16_t *)a.logits)[i] << 16)
+                            : ((const float *)a.logits)[i];
+        p = expf(x - st.x) / st.y;
+    }
+    const float g = wave_sum_f32(p);
+    if (lane == 0) a.gain[b] = g;
+}
+
 }  // namespace
+
+void launch_coverage(const CoverageArgs &a, hipStream_t s) {
+    if (a.B <= 0) return;
+    const int blocks = (a.B + kCovReqPerBlock - 1) / kCovReqPerBlock;
+    hipLaunchKernelGGL(k_coverage, dim3(blocks), dim3(kWave * kCovReqPerBlock), 0, s, a);
+}
 
 void launch_update(int64_t n_rows, int V, int k, const int32_t *topk, const float *prob,
                    const int32_t *row_tok, int32_t *table, float *table_prob, hipStream_t s) {

@@ -15,6 +15,10 @@ half is one launch (graft_build_hybrid_tree, graft_verify_update); with
 ``fused=False`` the five separate entry points are used.  ``bonus`` is
 written straight into the root buffer and ``base_pos`` is advanced on the
 device, so consecutive steps need no host round trip.
+
+With ``want_coverage`` the build also records each row's source (root, draft,
+retrieved), verification exports every row's softmax statistics, and
+``verify_update`` adds the coverage gain per request (graft_coverage_gain).
 """
 from __future__ import annotations
 
@@ -29,7 +33,8 @@ from . import _lib as L
 class GraftPipeline:
     def __init__(self, *, V, B, k=8, slots=60, mode="tree", layout="compact", dtype="bf16",
                  n_draft=60, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), keep=(8, 24, 40),
-                 tail_thr=0.5, tpl_width=8, tpl_depth=8, want_prob=False, device="cuda", fused=True):
+                 tail_thr=0.5, tpl_width=8, tpl_depth=8, want_prob=False, want_coverage=False,
+                 device="cuda", fused=True):
         L.load()
         self.fused = bool(fused)
         self.V, self.B, self.k = int(V), int(B), int(k)
@@ -41,6 +46,7 @@ class GraftPipeline:
         self.T1 = self.slots + 1
         self.dmax = self.T1 - 1
         self.want_prob = bool(want_prob)
+        self.want_coverage = bool(want_coverage)
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
@@ -84,6 +90,9 @@ class GraftPipeline:
         self.depth = torch.zeros(B, T1, **i32)
         self.pos_id = torch.zeros(B, T1, **i32)
         self.anc = torch.zeros(B, T1, dtype=torch.int64, device=dev)
+        self.row_src = torch.zeros(B, T1, dtype=torch.uint8, device=dev) if want_coverage else None
+        self.row_stats = torch.zeros(B, T1, 2, dtype=torch.float32, device=dev) if want_coverage else None
+        self.gain = torch.zeros(B, dtype=torch.float32, device=dev) if want_coverage else None
 
         self.topk = torch.zeros(B, T1, self.k, **i32)
         self.topk_prob = torch.zeros(B, T1, self.k, dtype=torch.float32, device=dev) if want_prob else None
@@ -94,13 +103,13 @@ class GraftPipeline:
         self._ingest_ws = None
 
     @classmethod
-    def from_config(cls, cfg, want_prob=False, device="cuda", fused=True):
+    def from_config(cls, cfg, want_prob=False, want_coverage=False, device="cuda", fused=True):
         return cls(V=cfg.V, B=cfg.B, k=cfg.k,
                    slots=cfg.tail_block if cfg.mode == "tail" else cfg.slots,
                    mode=cfg.mode, layout=cfg.layout, dtype=cfg.dtype, n_draft=cfg.n_draft,
                    ckpt_layers=cfg.ckpt_layers, tau=cfg.tau, keep=cfg.keep, tail_thr=cfg.tail_thr,
-                   tpl_width=cfg.tpl_width, tpl_depth=cfg.tpl_depth, want_prob=want_prob, device=device,
-                   fused=fused)
+                   tpl_width=cfg.tpl_width, tpl_depth=cfg.tpl_depth, want_prob=want_prob,
+                   want_coverage=want_coverage, device=device, fused=fused)
 
     # ------------------------------------------------------------------ state
     def stream(self):
@@ -142,7 +151,8 @@ class GraftPipeline:
                 self.n_keep.data_ptr(), self.keep.data_ptr(),
                 self.cum.data_ptr() if self.mode == L.MODE_TREE else None, self.ret_tok.data_ptr(),
                 self.ret_parent.data_ptr(), self.n_ret.data_ptr(), self.r_out, self.tok.data_ptr(),
-                self.parent.data_ptr(), self.depth.data_ptr(), self.pos_id.data_ptr(), self.anc.data_ptr(), s)
+                self.parent.data_ptr(), self.depth.data_ptr(), self.pos_id.data_ptr(), self.anc.data_ptr(),
+                self._ptr(self.row_src), s)
             return
         L.graft_prune_select(B, Nd, self.mode, d_parent.data_ptr(), d_layer.data_ptr(),
                              d_score.data_ptr(), self.cfg, self.stage.data_ptr(),
@@ -158,7 +168,7 @@ class GraftPipeline:
                                 self.n_keep.data_ptr(), self.ret_tok.data_ptr(),
                                 self.ret_parent.data_ptr(), self.n_ret.data_ptr(), self.r_out,
                                 self.tok.data_ptr(), self.parent.data_ptr(), self.depth.data_ptr(),
-                                self.pos_id.data_ptr(), self.anc.data_ptr(), s)
+                                self.pos_id.data_ptr(), self.anc.data_ptr(), self._ptr(self.row_src), s)
 
     def build(self, draft):
         self.load_draft(draft)
@@ -168,7 +178,13 @@ class GraftPipeline:
                "depth": self.depth, "pos_id": self.pos_id, "anc": self.anc}
         if self.mode == L.MODE_TREE:
             out["cum"] = self.cum
+        if self.want_coverage:
+            out["row_src"] = self.row_src
         return out
+
+    @staticmethod
+    def _ptr(t):
+        return None if t is None else t.data_ptr()
 
     # ------------------------------------------------------------------ verify + update
     def verify_update_device(self, logits):
@@ -180,20 +196,29 @@ class GraftPipeline:
                                   self.parent.data_ptr(), self.depth.data_ptr(), self.table.data_ptr(),
                                   self.table_prob.data_ptr() if self.want_prob else None,
                                   self.topk.data_ptr(), self.topk_prob.data_ptr() if self.want_prob else None,
-                                  self.accept_len.data_ptr(), self.accept_idx.data_ptr(), self.dmax,
-                                  self.roots.data_ptr(), self.base_pos.data_ptr(), self.ws.data_ptr(),
-                                  self.ws_bytes, s)
+                                  self._ptr(self.row_stats), self.accept_len.data_ptr(),
+                                  self.accept_idx.data_ptr(), self.dmax, self.roots.data_ptr(),
+                                  self.base_pos.data_ptr(), self.ws.data_ptr(), self.ws_bytes, s)
+            self._coverage(logits, s)
             return
         L.graft_verify_accept(B, T1, self.V, self.k, self.dtype, logits.data_ptr(), self.tok.data_ptr(),
                               self.parent.data_ptr(), self.depth.data_ptr(), self.topk.data_ptr(),
                               self.topk_prob.data_ptr() if self.want_prob else None,
-                              self.accept_len.data_ptr(), self.accept_idx.data_ptr(), self.dmax,
-                              self.roots.data_ptr(), self.base_pos.data_ptr(), self.ws.data_ptr(),
-                              self.ws_bytes, s)
+                              self._ptr(self.row_stats), self.accept_len.data_ptr(),
+                              self.accept_idx.data_ptr(), self.dmax, self.roots.data_ptr(),
+                              self.base_pos.data_ptr(), self.ws.data_ptr(), self.ws_bytes, s)
+        self._coverage(logits, s)
         L.graft_update_topk(B * T1, self.V, self.k, self.dtype, None, self.topk.data_ptr(),
                             self.topk_prob.data_ptr() if self.want_prob else None, self.tok.data_ptr(),
                             self.table.data_ptr(), self.table_prob.data_ptr() if self.want_prob else None,
                             None, None, 0, s)
+
+    def _coverage(self, logits, s):
+        if not self.want_coverage:
+            return
+        L.graft_coverage_gain(self.B, self.T1, self.V, self.dtype, logits.data_ptr(), self.tok.data_ptr(),
+                              self.parent.data_ptr(), self.row_src.data_ptr(), self.row_stats.data_ptr(),
+                              self.gain.data_ptr(), s)
 
     def verify_update(self, logits):
         self._check_logits(logits, self.B * self.T1)
@@ -202,6 +227,9 @@ class GraftPipeline:
                "topk": self.topk, "base_pos": self.base_pos}
         if self.want_prob:
             out["topk_prob"] = self.topk_prob
+        if self.want_coverage:
+            out["coverage"] = self.gain
+            out["row_stats"] = self.row_stats
         return out
 
     # ------------------------------------------------------------------ prompt ingest

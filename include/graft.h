@@ -16,7 +16,7 @@
  *    "host".  The library never allocates, frees or retains them.  Scratch
  *    comes from a caller workspace sized by graft_workspace_bytes(): it must
  *    be zero-filled once after allocation; every call leaves it zero-filled
- *    again (its completion counters are reset by the kernel that used them).
+ *    again (its completion words are cleared by the kernel that used them).
  *    Calls that share one workspace must be ordered (same stream).
  *  - Work is enqueued asynchronously on `stream`; nothing is synchronised.
  *    Calls on different streams touching disjoint buffers are independent.
@@ -26,7 +26,8 @@
  *  - Device-side data preconditions (token ids in [0, V), parents before
  *    children, log-probs finite) are the caller's; no NaN is handled.
  *  - Row-major layouts throughout; "[B, T1]" means B*T1 contiguous elements.
- *  - The continuation matrix is int32 [V, k]; only graft_update_topk writes it.
+ *  - The continuation matrix is int32 [V, k]; only graft_update_topk and
+ *    graft_verify_update write it.
  */
 #ifndef GRAFT_H
 #define GRAFT_H
@@ -54,6 +55,12 @@ extern "C" {
 #define GRAFT_LAYOUT_COMPACT 0  /* root, kept draft nodes ascending, retrieval in template order */
 #define GRAFT_LAYOUT_IN_PLACE 1 /* static slots: draft slot i -> row i+1, vacated rows take retrieval */
 #define GRAFT_LAYOUT_CHAIN 2    /* TAIL: root, kept block prefix, retrieval chain */
+
+/* row_src codes: where a flattened row comes from */
+#define GRAFT_ROW_ROOT 0      /* row 0: the last committed token */
+#define GRAFT_ROW_DRAFT 1     /* a kept draft node */
+#define GRAFT_ROW_RETRIEVED 2 /* a node grafted from the continuation matrix */
+#define GRAFT_ROW_EMPTY 3     /* a slot nothing was placed in (token -1) */
 
 #define GRAFT_MAX_ROWS 64 /* rows per request (root + candidate slots); one wavefront */
 #define GRAFT_MAX_K 8     /* successors per matrix row */
@@ -139,13 +146,15 @@ int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_
  * n_ret int32 [B].  n_keep + n_ret must equal T1 - 1 per request.
  * Outputs [B, T1]: tok, parent (-1 at the root), depth, pos_id = base_pos +
  * depth (int32), anc (uint64: bit g set iff row g is an ancestor of the row or
- * the row itself).  Requires 2 <= T1 <= 64, Nd <= 64, r_out <= 64. */
+ * the row itself), row_src (uint8, nullable: GRAFT_ROW_* of every row, the
+ * input of graft_coverage_gain).  Requires 2 <= T1 <= 64, Nd <= 64,
+ * r_out <= 64. */
 int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root_tok,
                           const int32_t *base_pos, const int32_t *d_tok, const int32_t *d_parent,
                           const uint8_t *keep, const int32_t *n_keep, const int32_t *ret_tok,
                           const int32_t *ret_parent, const int32_t *n_ret, int r_out, int32_t *tok,
                           int32_t *parent, int32_t *depth, int32_t *pos_id, uint64_t *anc,
-                          hipStream_t stream);
+                          uint8_t *row_src, hipStream_t stream);
 
 /* graft_verify_accept -- section 二, gear 3: strict greedy verification.
  * Row-wise top-k of logits [B, T1, V] (value descending, ties -> lower id,
@@ -154,7 +163,9 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
  * carries the token g of its parent row; the deepest accepted row wins, ties
  * -> lowest row.  Outputs: topk int32 [B, T1, k]; topk_prob fp32 [B, T1, k]
  * (nullable: softmax probability of each top-k id); accept_len int32 [B]
- * (candidate tokens accepted, root excluded); accept_idx int32 [B, dmax]
+ * (candidate tokens accepted, root excluded); row_stats fp32 [B, T1, 2]
+ * (nullable: per row the largest logit and the sum of exp(logit - largest),
+ * the softmax normaliser, for graft_coverage_gain); accept_idx int32 [B, dmax]
  * (rows of the accepted path from depth 1, -1 padded); bonus int32 [B] (g at
  * the accepted row: the next root; `bonus` may alias the root buffer of the
  * next step); base_pos_io int32 [B] (nullable; += accept_len + 1).
@@ -169,7 +180,8 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
  * zero-filled again.  Requires 1 <= T1 <= 64, 1 <= k <= 8, k <= V, dmax >= 0. */
 int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logits,
                         const int32_t *tok, const int32_t *parent, const int32_t *depth,
-                        int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
+                        int32_t *topk, float *topk_prob, float *row_stats, int32_t *accept_len,
+                        int32_t *accept_idx,
                         int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws, size_t ws_bytes,
                         hipStream_t stream);
 
@@ -204,7 +216,7 @@ int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slo
                             const int32_t *d_tok, int32_t *stage, int32_t *n_keep, uint8_t *keep,
                             float *cum_out, int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret,
                             int r_out, int32_t *tok, int32_t *parent, int32_t *depth, int32_t *pos_id,
-                            uint64_t *anc, hipStream_t stream);
+                            uint64_t *anc, uint8_t *row_src, hipStream_t stream);
 
 /* graft_verify_update -- graft_verify_accept followed by
  * graft_update_topk(row_tok = tok, topk_in = the top-k just computed) in one
@@ -217,9 +229,24 @@ int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slo
  * Section 二, gear 3; section 六 (online update). */
 int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logits, const int32_t *tok,
                         const int32_t *parent, const int32_t *depth, int32_t *table, float *table_prob,
-                        int32_t *topk, float *topk_prob, int32_t *accept_len, int32_t *accept_idx,
+                        int32_t *topk, float *topk_prob, float *row_stats, int32_t *accept_len,
+                        int32_t *accept_idx,
                         int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws, size_t ws_bytes,
                         hipStream_t stream);
+
+/* graft_coverage_gain -- section 三: what the grafted candidates add where
+ * pruning cut.  For every row v of a request that has retrieved children, the
+ * target's softmax probability (row v's logits) of the set of retrieved child
+ * tokens that no kept draft child of v already carries (each token once, ids
+ * outside [0, V) skipped), summed over v: gain fp32 [B].  Positive as soon as
+ * one such token has nonzero probability; 0 when nothing was retrieved.
+ * logits [B, T1, V] as verified; tok, parent, row_src [B, T1] from the build;
+ * row_stats [B, T1, 2] from graft_verify_accept / graft_verify_update on the
+ * same logits (so only the retrieved entries are read here).  One wavefront
+ * per request, one launch.  Requires 1 <= T1 <= 64. */
+int graft_coverage_gain(int B, int T1, int V, int dtype, const void *logits, const int32_t *tok,
+                        const int32_t *parent, const uint8_t *row_src, const float *row_stats,
+                        float *gain, hipStream_t stream);
 
 /* Workspace bytes needed by graft_verify_accept / graft_verify_update /
  * graft_update_topk for n_rows rows of V logits (0 on invalid sizes).  Zero-fill it once after

@@ -8,11 +8,12 @@ from synth import generators as G
 
 
 class OracleBackend:
-    def __init__(self, cfg, want_prob=False):
+    def __init__(self, cfg, want_prob=False, want_coverage=False):
         from oracle.driver import OracleGraft
         self.o = OracleGraft(cfg)
         self.cfg = cfg
         self.want_prob = want_prob
+        self.want_coverage = want_coverage
 
     def set_roots(self, roots, base_pos):
         self.o.set_roots(roots, base_pos)
@@ -31,7 +32,7 @@ class OracleBackend:
         return rows if self.cfg.dtype == "bf16" else rows.view(np.float32)
 
     def verify_update(self, rows):
-        return self.o.verify_update(rows, want_prob=self.want_prob)
+        return self.o.verify_update(rows, want_prob=self.want_prob, want_coverage=self.want_coverage)
 
     def ingest_chunk(self, row_tok, rows):
         return self.o.ingest_chunk(row_tok, rows)
@@ -41,13 +42,14 @@ class HipBackend:
     """HIP path through the C-ABI; host copies of the small outputs are made for
     the synthetic generator and for comparison."""
 
-    def __init__(self, cfg, want_prob=False, device="cuda", fused=True):
+    def __init__(self, cfg, want_prob=False, device="cuda", fused=True, want_coverage=False):
         import torch
         from hybrid_draft_tree_amd.driver import GraftPipeline
         from synth.device import DeviceRows
         self.torch = torch
         self.cfg = cfg
-        self.p = GraftPipeline.from_config(cfg, want_prob=want_prob, device=device, fused=fused)
+        self.p = GraftPipeline.from_config(cfg, want_prob=want_prob, want_coverage=want_coverage,
+                                           device=device, fused=fused)
         self.rows = None
         self._DeviceRows = DeviceRows
         self.want_prob = want_prob

@@ -284,14 +284,15 @@ def gpu_flatten(layout, T1, roots, base, d_tok, d_parent, keep, n_keep, ret):
     rt, rp, nr = (_t(ret[k], torch.int32) for k in ("ret_tok", "ret_parent", "n_ret"))
     outs = [torch.zeros(B, T1, dtype=torch.int32, device=DEV) for _ in range(4)]
     anc = torch.zeros(B, T1, dtype=torch.int64, device=DEV)
+    src = torch.full((B, T1), 99, dtype=torch.uint8, device=DEV)
     L.graft_build_tree_mask(B, Nd, T1, L.LAYOUT[layout], args[0].data_ptr(), args[1].data_ptr(),
                             args[2].data_ptr(), args[3].data_ptr(), kp.data_ptr(), nk.data_ptr(),
                             rt.data_ptr(), rp.data_ptr(), nr.data_ptr(), r_out,
-                            *[o.data_ptr() for o in outs], anc.data_ptr(), _s())
+                            *[o.data_ptr() for o in outs], anc.data_ptr(), src.data_ptr(), _s())
     torch.cuda.synchronize()
     res = [o.cpu().numpy() for o in outs]
     return {"tok": res[0], "parent": res[1], "depth": res[2], "pos_id": res[3],
-            "anc": anc.cpu().numpy().view(np.uint64)}
+            "anc": anc.cpu().numpy().view(np.uint64), "row_src": src.cpu().numpy()}
 
 
 @pytest.mark.parametrize("layout", ["compact", "in_place"])
@@ -310,7 +311,7 @@ def test_flatten_tree_parity(layout):
     base = rng.integers(0, 100000, size=B).astype(np.int32)
     got = gpu_flatten(layout, 61, roots, base, d_tok, P, pr["keep"], pr["n_keep"], ret)
     want = O.flatten(layout, 61, roots, base, d_tok, P, pr["keep"], pr["n_keep"], ret)
-    for key in ("tok", "parent", "depth", "pos_id", "anc"):
+    for key in ("tok", "parent", "depth", "pos_id", "anc", "row_src"):
         np.testing.assert_array_equal(got[key], want[key], err_msg=key)
 
 
@@ -330,7 +331,7 @@ def test_flatten_chain_parity():
     dpar = np.tile(np.arange(-1, 15, dtype=np.int32), (B, 1))
     got = gpu_flatten("chain", 17, roots, base, d_tok, dpar, pr["keep"], pr["n_keep"], ret)
     want = O.flatten("chain", 17, roots, base, d_tok, dpar, pr["keep"], pr["n_keep"], ret)
-    for key in ("tok", "parent", "depth", "pos_id", "anc"):
+    for key in ("tok", "parent", "depth", "pos_id", "anc", "row_src"):
         np.testing.assert_array_equal(got[key], want[key], err_msg=key)
 
 
@@ -351,7 +352,7 @@ def gpu_verify(rows, tok, parent, depth, k=8, dtype="bf16", want_prob=False, bas
     wsb = L.graft_workspace_bytes(B * T1, V, k, dt)
     ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     L.graft_verify_accept(B, T1, V, k, dt, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
-                          tk.data_ptr(), pr.data_ptr() if want_prob else None, al.data_ptr(), ai.data_ptr(),
+                          tk.data_ptr(), pr.data_ptr() if want_prob else None, None, al.data_ptr(), ai.data_ptr(),
                           T1 - 1, bo.data_ptr(), bp.data_ptr(), ws.data_ptr(), wsb, _s())
     torch.cuda.synchronize()
     out = {"topk": tk.cpu().numpy(), "accept_len": al.cpu().numpy(), "accept_idx": ai.cpu().numpy(),
@@ -454,12 +455,13 @@ def test_build_hybrid_tree_matches_oracle_tree():
         rt, rp = torch.zeros(B, r_out, **i32), torch.zeros(B, r_out, **i32)
         tok, par_o, dep, pos = (torch.zeros(B, 61, **i32) for _ in range(4))
         anc = torch.zeros(B, 61, dtype=torch.int64, device=DEV)
+        src = torch.full((B, 61), 99, dtype=torch.uint8, device=DEV)
         L.graft_build_hybrid_tree(B, 60, 61, L.MODE_TREE, L.LAYOUT[layout], 60, cfg, tpl, V, 8,
                                   ins[0].data_ptr(), ins[1].data_ptr(), ins[2].data_ptr(), ins[3].data_ptr(),
                                   ins[4].data_ptr(), sc.data_ptr(), dt.data_ptr(), st.data_ptr(), nk.data_ptr(),
                                   kp.data_ptr(), cum.data_ptr(), rt.data_ptr(), rp.data_ptr(), nr.data_ptr(),
                                   r_out, tok.data_ptr(), par_o.data_ptr(), dep.data_ptr(), pos.data_ptr(),
-                                  anc.data_ptr(), _s())
+                                  anc.data_ptr(), src.data_ptr(), _s())
         torch.cuda.synchronize()
         pr = O.prune_tree(P, Ly, lp, want_cum=True)
         ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, O.template(8, 8, 52))
@@ -474,6 +476,7 @@ def test_build_hybrid_tree_matches_oracle_tree():
         for name, got in (("tok", tok), ("parent", par_o), ("depth", dep), ("pos_id", pos)):
             np.testing.assert_array_equal(got.cpu().numpy(), fl[name], err_msg=(layout, name))
         np.testing.assert_array_equal(anc.cpu().numpy().view(np.uint64), fl["anc"])
+        np.testing.assert_array_equal(src.cpu().numpy(), fl["row_src"])
 
 
 def test_verify_update_matches_oracle_with_collisions():
@@ -495,7 +498,7 @@ def test_verify_update_matches_oracle_with_collisions():
     want_tab = table0.copy()
     for rep in range(3):        # repeated calls: the workspace must come back zeroed
         L.graft_verify_update(B, T1, V, 8, L.DTYPE_BF16, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
-                              tb.data_ptr(), None, tk.data_ptr(), None, al.data_ptr(), ai.data_ptr(), T1 - 1,
+                              tb.data_ptr(), None, tk.data_ptr(), None, None, al.data_ptr(), ai.data_ptr(), T1 - 1,
                               bo.data_ptr(), bp.data_ptr(), ws.data_ptr(), wsb, _s())
         torch.cuda.synchronize()
         want_tk = O.topk(rows.reshape(-1, V), 8, "bf16").reshape(B, T1, 8)
@@ -508,3 +511,94 @@ def test_verify_update_matches_oracle_with_collisions():
         np.testing.assert_array_equal(tb.cpu().numpy(), want_tab)
         rows = _bf16(rng.standard_normal((B, T1, V)).astype(np.float32))
         lg = _t(rows.view(np.int16)).view(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------- coverage gain
+
+def _coverage_case(rng, B, T1, V, layout, dtype):
+    """Oracle-built hybrid trees (row sources included) and random logits."""
+    par, lay, _ = TOPO
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    lp = _random_logp(rng, B)
+    pr = O.prune_tree(P, Ly, lp)
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, O.template(8, 8, 52))
+    d_tok = rng.integers(0, V, size=(B, 60)).astype(np.int32)
+    # make some retrieved tokens repeat a kept draft sibling at the root
+    d_tok[:, :8] = np.where(rng.random((B, 8)) < 0.3, table[roots][:, :8], d_tok[:, :8])
+    fl = O.flatten(layout, T1, roots, np.zeros(B, np.int32), d_tok, P, pr["keep"], pr["n_keep"], ret)
+    z = (rng.standard_normal((B, T1, V)) * 2.5).astype(np.float32)
+    rows = _bf16(z) if dtype == "bf16" else z
+    return fl, rows, pr
+
+
+@pytest.mark.parametrize("dtype,layout", [("bf16", "in_place"), ("bf16", "compact"), ("f32", "compact")])
+def test_row_stats_and_coverage_gain(dtype, layout):
+    """Row softmax statistics from the verify launch (largest value exact, the
+    normaliser within 1e-5 relative of fp64) and graft_coverage_gain from them,
+    within 1e-5 relative of the fp64 oracle; requests that retrieved nothing
+    give exactly 0."""
+    rng = np.random.default_rng(40 if dtype == "bf16" else 41)
+    B, T1, V = 12, 61, 30011
+    fl, rows, pr = _coverage_case(rng, B, T1, V, layout, dtype)
+    lg = _t(rows.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else _t(rows)
+    dt = L.DTYPE_BF16 if dtype == "bf16" else L.DTYPE_F32
+    i32 = dict(dtype=torch.int32, device=DEV)
+    tk = torch.zeros(B, T1, 8, **i32)
+    stats = torch.zeros(B, T1, 2, dtype=torch.float32, device=DEV)
+    al, bo = torch.zeros(B, **i32), torch.zeros(B, **i32)
+    ai = torch.zeros(B, T1 - 1, **i32)
+    t_, p_, d_ = (_t(fl[x], torch.int32) for x in ("tok", "parent", "depth"))
+    src = _t(fl["row_src"], torch.uint8)
+    wsb = L.graft_workspace_bytes(B * T1, V, 8, dt)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    L.graft_verify_accept(B, T1, V, 8, dt, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
+                          tk.data_ptr(), None, stats.data_ptr(), al.data_ptr(), ai.data_ptr(), T1 - 1,
+                          bo.data_ptr(), None, ws.data_ptr(), wsb, _s())
+    gain = torch.full((B,), -1.0, dtype=torch.float32, device=DEV)
+    L.graft_coverage_gain(B, T1, V, dt, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), src.data_ptr(),
+                          stats.data_ptr(), gain.data_ptr(), _s())
+    torch.cuda.synchronize()
+    want_st = O.row_stats(rows, dtype)
+    got_st = stats.cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(got_st[..., 0], want_st[..., 0])
+    np.testing.assert_allclose(got_st[..., 1], want_st[..., 1], rtol=1e-5, atol=0)
+    want = O.coverage_gain(rows, fl["tok"], fl["parent"], fl["row_src"], dtype)
+    got = gain.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=0)
+    assert (want[pr["stage"] == 3] == 0).all()
+    assert (want[pr["stage"] < 3] > 0).all()
+    # the top-k is unchanged by asking for the statistics
+    np.testing.assert_array_equal(tk.cpu().numpy(), O.topk(rows.reshape(-1, V), 8, dtype).reshape(B, T1, 8))
+
+
+def test_coverage_gain_hand_tree_closed_form():
+    """All-equal rows: every new token is worth exactly 1/V (fp32 1/V within 1e-6);
+    duplicates of a draft sibling or of an earlier retrieved sibling add nothing."""
+    V = 4096
+    rows_spec = [(100, -1, 0), (5, 0, 1), (5, 0, 2), (7, 0, 2), (9, 3, 2), (7, 0, 2), (V + 3, 0, 2)]
+    T1 = len(rows_spec)
+    tok = np.array([[r[0] for r in rows_spec]], np.int32)
+    par = np.array([[r[1] for r in rows_spec]], np.int32)
+    src = np.array([[r[2] for r in rows_spec]], np.uint8)
+    rows = np.full((1, T1, V), 0x3F80, np.uint16)       # bf16 1.0 everywhere
+    lg = _t(rows.view(np.int16)).view(torch.bfloat16)
+    stats = torch.zeros(1, T1, 2, dtype=torch.float32, device=DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    tk, al, bo = torch.zeros(1, T1, 8, **i32), torch.zeros(1, **i32), torch.zeros(1, **i32)
+    ai = torch.zeros(1, T1 - 1, **i32)
+    t_, p_ = _t(tok, torch.int32), _t(par, torch.int32)
+    d_ = _t(np.array([[0, 1, 1, 1, 2, 1, 1]], np.int32), torch.int32)
+    wsb = L.graft_workspace_bytes(T1, V, 8, L.DTYPE_BF16)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    L.graft_verify_accept(1, T1, V, 8, L.DTYPE_BF16, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
+                          tk.data_ptr(), None, stats.data_ptr(), al.data_ptr(), ai.data_ptr(), T1 - 1,
+                          bo.data_ptr(), None, ws.data_ptr(), wsb, _s())
+    gain = torch.zeros(1, dtype=torch.float32, device=DEV)
+    s_ = _t(src, torch.uint8)
+    L.graft_coverage_gain(1, T1, V, L.DTYPE_BF16, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), s_.data_ptr(),
+                          stats.data_ptr(), gain.data_ptr(), _s())
+    torch.cuda.synchronize()
+    assert abs(float(gain.item()) - 2.0 / V) <= 1e-6 * (2.0 / V)
+    assert float(O.coverage_gain(rows, tok, par, src, "bf16")[0]) == pytest.approx(2.0 / V, rel=1e-14)

@@ -98,6 +98,32 @@ def test_lockstep_with_probabilities():
     np.testing.assert_allclose(tp_h, ob.o.table_prob, rtol=1e-5, atol=0)
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "five_calls"])
+def test_lockstep_coverage_gain(fused):
+    """The coverage-gain diagnostic through whole steps (row sources from the
+    build, softmax statistics from the verify launch): within 1e-5 relative of
+    the oracle's fp64 gain every step, exactly 0 where nothing was retrieved."""
+    cfg = _small(3, V=30000, B=8)
+    ob, hb = OracleBackend(cfg, want_coverage=True), HipBackend(cfg, want_coverage=True, fused=fused)
+    wo, wh = R.Workload(cfg), R.Workload(cfg)
+    R.start(ob, wo)
+    R.start(hb, wh)
+    seen_pos = seen_zero = False
+    for s in range(cfg.warmup_steps + 6):
+        off = G.WARMUP_STREAM_OFFSET if s < cfg.warmup_steps else 0
+        idx = s if s < cfg.warmup_steps else s - cfg.warmup_steps
+        fo, ro = R.step(ob, wo, idx, off)
+        fh, rh = R.step(hb, wh, idx, off)
+        np.testing.assert_array_equal(fh["row_src"], fo["row_src"], err_msg="step %d" % s)
+        np.testing.assert_array_equal(rh["topk"], ro["topk"])
+        np.testing.assert_allclose(rh["coverage"], ro["coverage"], rtol=1e-5, atol=0, err_msg="step %d" % s)
+        seen_pos |= bool((ro["coverage"] > 0).any())
+        seen_zero |= bool((np.asarray(fo["n_ret"]) == 0).any())
+        assert (ro["coverage"][np.asarray(fo["n_ret"]) == 0] == 0).all()
+    assert seen_pos
+    np.testing.assert_array_equal(hb.get_table(), ob.get_table())
+
+
 def test_lockstep_ingest_reduced():
     cfg = _small(4, V=30000, prompt_len=5000, ingest_chunk=1024)
     st = _compare_runs(cfg, 10, warmup=0)

@@ -66,18 +66,25 @@ def test_host_validation_rejects_without_launch():
     P = 0x1000  # never dereferenced: every call below fails validation first
     # unsupported mode / layout / dtype
     assert lib.graft_prune_select(1, 60, 7, P, P, P, ctypes.byref(cfg), P, P, P, None, None) == L.GRAFT_EUNSUPPORTED
-    assert lib.graft_build_tree_mask(1, 60, 61, 9, *([P] * 9), 52, *([P] * 5), None) == L.GRAFT_EUNSUPPORTED
-    assert lib.graft_verify_accept(1, 61, 100, 8, 5, *([P] * 8), 60, P, None, P, 1 << 20, None) == L.GRAFT_EUNSUPPORTED
+    assert lib.graft_build_tree_mask(1, 60, 61, 9, *([P] * 9), 52, *([P] * 5), None, None) == L.GRAFT_EUNSUPPORTED
+    assert lib.graft_verify_accept(1, 61, 100, 8, 5, *([P] * 9), 60, P, None, P, 1 << 20, None) == L.GRAFT_EUNSUPPORTED
     # bad sizes
     assert lib.graft_prune_select(1, 65, 0, P, P, P, ctypes.byref(cfg), P, P, P, None, None) == L.GRAFT_EINVAL
     assert lib.graft_prune_select(1, 0, 0, P, P, P, ctypes.byref(cfg), P, P, P, None, None) == L.GRAFT_EINVAL
     bad = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 70), 0.5)
     assert lib.graft_prune_select(1, 60, 0, P, P, P, ctypes.byref(bad), P, P, P, None, None) == L.GRAFT_EINVAL
-    assert lib.graft_build_tree_mask(1, 60, 65, 0, *([P] * 9), 52, *([P] * 5), None) == L.GRAFT_EINVAL
-    assert lib.graft_build_tree_mask(1, 60, 60, 1, *([P] * 9), 52, *([P] * 5), None) == L.GRAFT_EINVAL  # in-place needs T1 = Nd + 1
-    assert lib.graft_verify_accept(1, 61, 100, 9, 1, *([P] * 8), 60, P, None, P, 1 << 20, None) == L.GRAFT_EINVAL
-    assert lib.graft_verify_accept(1, 61, 100, 8, 1, P + 2, *([P] * 7), 60, P, None, P, 1 << 20, None) == L.GRAFT_EINVAL  # misaligned logits
-    assert lib.graft_verify_accept(1, 61, 100, 8, 1, *([P] * 8), 60, P, None, P, 16, None) == L.GRAFT_EINVAL  # workspace too small
+    assert lib.graft_build_tree_mask(1, 60, 65, 0, *([P] * 9), 52, *([P] * 5), None, None) == L.GRAFT_EINVAL
+    assert lib.graft_build_tree_mask(1, 60, 60, 1, *([P] * 9), 52, *([P] * 5), None, None) == L.GRAFT_EINVAL  # in-place needs T1 = Nd + 1
+    assert lib.graft_verify_accept(1, 61, 100, 9, 1, *([P] * 9), 60, P, None, P, 1 << 20, None) == L.GRAFT_EINVAL
+    assert lib.graft_verify_accept(1, 61, 100, 8, 1, P + 2, *([P] * 8), 60, P, None, P, 1 << 20, None) == L.GRAFT_EINVAL  # misaligned logits
+    assert lib.graft_verify_accept(1, 61, 100, 8, 1, *([P] * 9), 60, P, None, P, 16, None) == L.GRAFT_EINVAL  # workspace too small
+    assert lib.graft_verify_accept(1, 61, 100, 8, 1, *([P] * 6), P + 4, P, P, 60, P, None, P, 1 << 20,
+                                   None) == L.GRAFT_EINVAL  # misaligned row_stats
+    assert lib.graft_coverage_gain(1, 65, 100, 1, *([P] * 6), None) == L.GRAFT_EINVAL
+    assert lib.graft_coverage_gain(1, 61, 100, 7, *([P] * 6), None) == L.GRAFT_EUNSUPPORTED
+    assert lib.graft_coverage_gain(1, 61, 100, 1, P, P, P, P, P + 4, P, None) == L.GRAFT_EINVAL
+    assert lib.graft_coverage_gain(1, 61, 100, 1, P, P, P, None, P, P, None) == L.GRAFT_EINVAL
+    assert lib.graft_coverage_gain(0, 61, 100, 1, *([None] * 6), None) == 0
     # null pointers
     assert lib.graft_prune_select(1, 60, 0, None, P, P, ctypes.byref(cfg), P, P, P, None, None) == L.GRAFT_EINVAL
     assert lib.graft_update_topk(10, 100, 8, 1, None, None, None, P, P, None, None, P, 1 << 20, None) == L.GRAFT_EINVAL
