@@ -232,6 +232,51 @@ def main():
     traffic, tnote = load_traffic(alg_bytes)
     log("dominant kernel: mean %.2f us, median %.2f us, %.0f GB/s algorithmic" % (k_ms * 1e3, k_med * 1e3, achieved))
 
+    # ---------------- coverage-gain diagnostic (outside the step) ----------------
+    # The verify launch with per-row softmax statistics, then graft_coverage_gain,
+    # on pool step 0 rebuilt with row sources.
+    row_src = torch.zeros(B, T1, dtype=torch.uint8, device=dev)
+    row_stats = torch.zeros(B, T1, 2, dtype=torch.float32, device=dev)
+    gain = torch.zeros(B, dtype=torch.float32, device=dev)
+    pipe.row_src = row_src
+    pipe.build_device(pool_drafts[0])
+    pipe.row_src = None
+
+    def verify_stats_call(i):
+        L.graft_verify_update(B, T1, V, k, pipe.dtype, pool_logits[i % P].data_ptr(), pipe.tok.data_ptr(),
+                              pipe.parent.data_ptr(), pipe.depth.data_ptr(), pipe.table.data_ptr(), None,
+                              pipe.topk.data_ptr(), None, row_stats.data_ptr(), pipe.accept_len.data_ptr(),
+                              pipe.accept_idx.data_ptr(), pipe.dmax, pipe.bonus_scratch.data_ptr(), None,
+                              pipe.ws.data_ptr(), pipe.ws_bytes, stream.cuda_stream)
+
+    def coverage_call(i):
+        L.graft_coverage_gain(B, T1, V, pipe.dtype, pool_logits[0].data_ptr(), pipe.tok.data_ptr(),
+                              pipe.parent.data_ptr(), row_src.data_ptr(), row_stats.data_ptr(),
+                              gain.data_ptr(), stream.cuda_stream)
+
+    def time_calls(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(min(n, 4)):
+            fn(i)
+        torch.cuda.synchronize()
+        for i in range(n):
+            a, b = ev[i]
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / n
+
+    pipe.bonus_scratch = torch.zeros(B, dtype=torch.int32, device=dev)  # roots stay untouched
+    vs_ms = time_calls(verify_stats_call, 52)
+    verify_stats_call(0)  # statistics of pool step 0 for the coverage launch
+    cov_ms = time_calls(coverage_call, 50)
+    gain_mean = float(gain.mean().item())
+    n_ret_mean = float(pipe.n_ret.float().mean().item())
+    log("coverage diagnostic: verify with row statistics %.2f us (+%.2f us), coverage launch %.2f us, "
+        "mean gain %.4f over %.1f retrieved rows/request" % (vs_ms * 1e3, (vs_ms - k_ms) * 1e3, cov_ms * 1e3,
+                                                              gain_mean, n_ret_mean))
+
     copy_gbps = None
     if args.copy_calib:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -291,6 +336,12 @@ def main():
                    "pool_steps": P, "hip_graph": not args.no_graph},
         "step_hbm_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "coverage_diagnostic": {"verify_with_row_stats_us": round(vs_ms * 1e3, 3),
+                                "row_stats_overhead_us": round((vs_ms - k_ms) * 1e3, 3),
+                                "coverage_kernel_us": round(cov_ms * 1e3, 3),
+                                "mean_gain": round(gain_mean, 6),
+                                "note": "outside the timed step; pool step 0's draft rebuilt with row "
+                                        "sources against the evolved matrix"},
         "roofline": {"kernel": "k_topk_rows (graft_verify_update: row-wise top-k + acceptance walk + matrix update)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,

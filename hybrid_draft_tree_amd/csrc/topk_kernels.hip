@@ -206,17 +206,43 @@ __device__ __forceinline__ Rank merge_top8_compact(Rank (&c)[N], Rank &top, Rank
     return kth;
 }
 
+// Per-lane online softmax statistics: running maximum m and sum of exp(x - m).
+// Values arrive in batches: one rescale when a batch raises the maximum, then
+// one subtract, exponential and add per value (no per-value branch).  While
+// the maximum is still -inf every value so far is -inf and adds nothing.
 struct SoftStats {
     float m = -INFINITY;
     float s = 0.0f;
-    __device__ void add(float v) {
-        if (v > m) {
-            s = (m == -INFINITY) ? 0.0f : s * __expf(m - v);
-            m = v;
+    template <int N>
+    __device__ __forceinline__ void add_batch(const float (&x)[N]) {
+        float mb = x[0];
+#pragma unroll
+        for (int i = 1; i < N; ++i) mb = fmaxf(mb, x[i]);
+        if (mb > m) {
+            s = (m == -INFINITY) ? 0.0f : s * __expf(m - mb);
+            m = mb;
         }
-        s += __expf(v - m);
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) s += __expf(x[i] - m);
+        }
+    }
+    __device__ __forceinline__ void add(float v) {
+        const float x[1] = {v};
+        add_batch<1>(x);
     }
 };
+
+template <typename TR, int U>
+__device__ __forceinline__ void add_groups(SoftStats &st, const uint4 (&d)[U]) {
+    constexpr int EPG = TR::kPerGroup;
+    float x[U * EPG];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < EPG; ++e) x[u * EPG + e] = TR::value(TR::elem(d[u], e));
+    st.add_batch<U * EPG>(x);
+}
 
 // Strict greedy acceptance walk of request b (section 二, gear 3), one wavefront;
 // lane f is flattened row f with its greedy token g, token t, parent row p and
@@ -527,12 +553,7 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         for (int u = 0; u < U; ++u) d[u] = load16<NT>(vp + (size_t)(wv + (kk + u) * S) * kWave + lane);
     };
     auto filter_full = [&](const uint4 (&d)[U], int kk) __attribute__((always_inline)) {
-        if constexpr (PROB) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < EPG; ++e) st.add(TR::value(TR::elem(d[u], e)));
-        }
+        if constexpr (PROB) add_groups<TR, U>(st, d);
         const int thr_u = __builtin_amdgcn_readfirstlane(thr);
         if (thr_u >= 1) {
             const uint32_t t2 = TR::splat_below(thr_u);
@@ -591,8 +612,8 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
             const bool inb = (kk + u < kcount) && ((wv + (kk + u) * S) * kWave + lane < ng);
             if constexpr (PROB) {
                 if (inb) {
-#pragma unroll
-                    for (int e = 0; e < EPG; ++e) st.add(TR::value(TR::elem(d[u], e)));
+                    const uint4 one[1] = {d[u]};
+                    add_groups<TR, 1>(st, one);
                 }
             }
             append(d[u], inb && (thr == INT_MIN || TR::group_pass(d[u], thr)), kk + u);

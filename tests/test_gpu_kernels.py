@@ -109,6 +109,9 @@ def test_topk_prob_parity():
     V = 151936
     z = (rng.standard_normal((12, V)) * 2.0).astype(np.float32)
     z[0] = 0.0
+    z[1, :1000] = -np.inf            # masked prefix: the first batches hold only -inf
+    z[2] = -np.inf                   # one finite entry: probability 1
+    z[2, 77777] = 1.5
     rows = _bf16(z)
     tk, tprob, table = gpu_topk(rows, 8, "bf16", want_prob=True)
     want_tk, want_p = O.topk(rows, 8, "bf16", want_prob=True)
