@@ -181,8 +181,10 @@ int oracle_retrieve_tree(int B, int V, int k, const int32_t *table, const int32_
                          const int32_t *tpl_rank, int Rmax_out, int32_t *ret_tok,
                          int32_t *ret_parent, int32_t *n_ret) {
     for (int b = 0; b < B; ++b) {
+        /* the freed slots, as far as the template reaches (the rest stay empty) */
         int R = slots - n_keep[b];
-        if (R < 0 || R > Rtpl || R > Rmax_out) return -1;
+        if (R > Rtpl) R = Rtpl;
+        if (R < 0 || R > Rmax_out) return -1;
         int32_t *rt = ret_tok + (size_t)b * Rmax_out;
         int32_t *rp = ret_parent + (size_t)b * Rmax_out;
         for (int t = 0; t < Rmax_out; ++t) {
@@ -198,6 +200,69 @@ int oracle_retrieve_tree(int B, int V, int k, const int32_t *table, const int32_
         n_ret[b] = R;
     }
     return 0;
+}
+
+/* Branching template (the asymmetric shape of section 二 gear 2, after Token  */
+/* Recycling: better-ranked successors get more children and reach deeper).  */
+/* Reading: a node is a path of ranks (r_1..r_d), 1 <= d <= D, each r < W;   */
+/* its cost is d*den + num*(r_1+..+r_d) (beta = num/den >= 0 charges worse   */
+/* ranks); the master order is ascending (cost, d, ranks lexicographic) and  */
+/* a budget R takes its first R nodes.  A child costs more than its parent,  */
+/* so every prefix is a tree.  Plain best-first expansion: the frontier is    */
+/* scanned for its minimum each time.  Returns the number of nodes written.  */
+#define OT_MAXD 64
+typedef struct {
+    long long cost;
+    int d;
+    int parent;           /* index in the order, -1 for root children */
+    int path[OT_MAXD];
+} ot_node;
+
+static int ot_before(const ot_node *a, const ot_node *b) {
+    if (a->cost != b->cost) return a->cost < b->cost;
+    if (a->d != b->d) return a->d < b->d;
+    for (int i = 0; i < a->d; ++i)
+        if (a->path[i] != b->path[i]) return a->path[i] < b->path[i];
+    return 0;
+}
+
+int oracle_template_branching(int W, int D, int num, int den, int Rmax, int32_t *parent,
+                              int32_t *rank, int32_t *depth) {
+    if (W < 1 || D < 1 || D > OT_MAXD || num < 0 || den < 1 || Rmax < 0) return -1;
+    int cap = W + Rmax * W;
+    ot_node *fr = (ot_node *)malloc(sizeof(ot_node) * (size_t)cap);
+    if (!fr) return -1;
+    int nf = 0, n = 0;
+    for (int j = 0; j < W; ++j) {
+        fr[nf].cost = (long long)den + (long long)num * j;
+        fr[nf].d = 1;
+        fr[nf].parent = -1;
+        fr[nf].path[0] = j;
+        nf++;
+    }
+    while (n < Rmax && nf > 0) {
+        int best = 0;
+        for (int i = 1; i < nf; ++i)
+            if (ot_before(&fr[i], &fr[best])) best = i;
+        ot_node cur = fr[best];
+        fr[best] = fr[--nf];
+        parent[n] = cur.parent;
+        rank[n] = cur.path[cur.d - 1];
+        depth[n] = cur.d;
+        if (cur.d < D) {
+            for (int j = 0; j < W && nf < cap; ++j) {
+                ot_node c = cur;
+                c.d = cur.d + 1;
+                c.path[cur.d] = j;
+                c.cost = cur.cost + den + (long long)num * j;
+                c.parent = n;
+                fr[nf++] = c;
+            }
+        }
+        n++;
+    }
+    free(fr);
+    return n;
 }
 
 /* TAIL retrieval: a chain of rank-0 successors x <- M[x][0], L - p steps long, */
@@ -235,7 +300,9 @@ int oracle_retrieve_tail(int B, int V, int k, const int32_t *table, const int32_
 /* depth[f] = depth[parent]+1; pos_id = base_pos + depth; anc[f] has bit g   */
 /* set iff row g is an ancestor of row f or f itself (root included).        */
 /* row_src (optional): where each row comes from -- 0 root, 1 kept draft     */
-/* node, 2 retrieval node, 3 unfilled.                                       */
+/* node, 2 retrieval node, 3 unfilled.  A row nothing is placed in (freed    */
+/* slots beyond a small template) is empty: token -1, parent -1, depth 0,    */
+/* its mask only itself.                                                     */
 /* ------------------------------------------------------------------------- */
 int oracle_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
                    const int32_t *base_pos, const int32_t *d_tok, const int32_t *d_parent,
@@ -291,7 +358,7 @@ int oracle_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
                     pa[f] = (dp[i] < 0) ? 0 : dp[i] + 1;
                     if (sr) sr[f] = 1;
                 } else {
-                    if (t >= R) return -3;
+                    if (t >= R) continue; /* freed slot the template does not reach: empty */
                     row_of_ret[t] = f;
                     tk[f] = rt[t];
                     pa[f] = (rp[t] < 0) ? 0 : row_of_ret[rp[t]];
@@ -318,7 +385,7 @@ int oracle_flatten(int B, int Nd, int T1, int layout, const int32_t *root_tok,
         } else {
             return -1;
         }
-        if (used != T1) return -3;
+        if (used > T1) return -3; /* rows past `used` stay empty */
         for (int f = 0; f < T1; ++f) {
             int d = 0;
             uint64_t a = 0;

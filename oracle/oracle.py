@@ -32,6 +32,7 @@ def lib():
         L.oracle_prune_tree.argtypes = [C.c_int, C.c_int, P, P, P, P, P, P, P, P, P, P]
         L.oracle_prune_tail.argtypes = [C.c_int, C.c_int, P, C.c_float, P, P, P]
         L.oracle_template.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P]
+        L.oracle_template_branching.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P]
         L.oracle_retrieve_tree.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, C.c_int, C.c_int, P, P,
                                            C.c_int, P, P, P]
         L.oracle_retrieve_tail.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, C.c_int, P, P, P]
@@ -108,6 +109,18 @@ def template(W=8, D=8, Rmax=52):
     n = lib().oracle_template(W, D, Rmax, _p(par), _p(rank), _p(dep))
     if n < 0:
         raise RuntimeError("oracle template failed")
+    return {"parent": par[:n], "rank": rank[:n], "depth": dep[:n]}
+
+
+def template_branching(W=8, D=8, beta=(1, 1), Rmax=52):
+    """Branching template: rank paths ordered by d*den + num*sum(ranks), beta = num/den."""
+    num, den = beta
+    par = np.zeros(max(Rmax, 1), np.int32)
+    rank = np.zeros(max(Rmax, 1), np.int32)
+    dep = np.zeros(max(Rmax, 1), np.int32)
+    n = lib().oracle_template_branching(W, D, num, den, Rmax, _p(par), _p(rank), _p(dep))
+    if n < 0:
+        raise RuntimeError("oracle branching template failed")
     return {"parent": par[:n], "rank": rank[:n], "depth": dep[:n]}
 
 
