@@ -28,7 +28,7 @@ MAX_ROWS = 64
 MAX_K = 8
 
 EXPORTS = (
-    "graft_prune_select", "graft_template_master", "graft_retrieve_expand",
+    "graft_prune_select", "graft_template_master", "graft_template_branching", "graft_retrieve_expand",
     "graft_build_tree_mask", "graft_verify_accept", "graft_update_topk",
     "graft_build_hybrid_tree", "graft_verify_update", "graft_coverage_gain",
     "graft_workspace_bytes", "graft_status_string",
@@ -67,6 +67,7 @@ def load():
     P, I, I64, S = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
     L.graft_prune_select.argtypes = [I, I, I, P, P, P, C.POINTER(PruneCfg), P, P, P, P, P]
     L.graft_template_master.argtypes = [I, I, I, P, P, P]
+    L.graft_template_branching.argtypes = [I, I, I, I, I, P, P, P]
     L.graft_retrieve_expand.argtypes = [I, I, I, I, I, P, P, P, P, I, C.POINTER(Template),
                                         C.POINTER(PruneCfg), P, P, P, I, P]
     L.graft_build_tree_mask.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P]
@@ -114,6 +115,16 @@ def graft_template_master(width, depth, cap):
     rk = (C.c_int32 * max(cap, 1))()
     dp = (C.c_int32 * max(cap, 1))()
     n = _chk("graft_template_master", load().graft_template_master(width, depth, cap, par, rk, dp))
+    return list(par[:n]), list(rk[:n]), list(dp[:n])
+
+
+def graft_template_branching(width, depth, beta_num, beta_den, cap):
+    """Returns (parent, rank, depth) host lists of the branching template's master order."""
+    par = (C.c_int32 * max(cap, 1))()
+    rk = (C.c_int32 * max(cap, 1))()
+    dp = (C.c_int32 * max(cap, 1))()
+    n = _chk("graft_template_branching",
+             load().graft_template_branching(width, depth, beta_num, beta_den, cap, par, rk, dp))
     return list(par[:n]), list(rk[:n]), list(dp[:n])
 
 

@@ -104,6 +104,46 @@ int graft_template_master(int width, int depth, int cap, int32_t *parent, int32_
     return n;
 }
 
+int graft_template_branching(int width, int depth, int beta_num, int beta_den, int cap, int32_t *parent,
+                             int32_t *rank, int32_t *tdepth) {
+    if (width < 1 || depth < 1 || beta_num < 0 || beta_den < 1 || cap < 0 || !parent || !rank || !tdepth)
+        return GRAFT_EINVAL;
+    // Best-first over rank paths with a binary heap keyed (cost, depth, ranks),
+    // cost = depth*den + num*sum(ranks): a popped node is the next in the order.
+    struct Cand {
+        long long cost;
+        std::vector<int> path;
+        int parent;
+    };
+    auto later = [](const Cand &a, const Cand &b) {  // heap order: a after b
+        if (a.cost != b.cost) return a.cost > b.cost;
+        if (a.path.size() != b.path.size()) return a.path.size() > b.path.size();
+        return a.path > b.path;
+    };
+    std::vector<Cand> heap;
+    for (int j = 0; j < width; ++j) heap.push_back({(long long)beta_den + (long long)beta_num * j, {j}, -1});
+    std::make_heap(heap.begin(), heap.end(), later);
+    int n = 0;
+    while (n < cap && !heap.empty()) {
+        std::pop_heap(heap.begin(), heap.end(), later);
+        Cand c = std::move(heap.back());
+        heap.pop_back();
+        parent[n] = c.parent;
+        rank[n] = c.path.back();
+        tdepth[n] = (int)c.path.size();
+        if ((int)c.path.size() < depth) {
+            for (int j = 0; j < width; ++j) {
+                Cand ch{c.cost + beta_den + (long long)beta_num * j, c.path, n};
+                ch.path.push_back(j);
+                heap.push_back(std::move(ch));
+                std::push_heap(heap.begin(), heap.end(), later);
+            }
+        }
+        ++n;
+    }
+    return n;
+}
+
 int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_t *table,
                           const int32_t *root_tok, const int32_t *n_keep, const int32_t *d_tok,
                           int Nd, const graft_template *tpl, const graft_prune_cfg *cfg,
@@ -122,7 +162,7 @@ int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_
         if (tpl->size > 0 && (!tpl->parent || !tpl->rank || !tpl->depth)) return GRAFT_EINVAL;
         if (r_out < tpl->size) return GRAFT_EINVAL;
         for (int s = 0; s < 3; ++s)
-            if (slots - cfg->keep[s] > tpl->size || slots - cfg->keep[s] < 0) return GRAFT_EINVAL;
+            if (slots - cfg->keep[s] < 0) return GRAFT_EINVAL;
         tsize = tpl->size;
         tp = tpl->parent;
         tr = tpl->rank;
@@ -189,9 +229,7 @@ int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slo
         if (tpl->size > 0 && (!tpl->parent || !tpl->rank || !tpl->depth)) return GRAFT_EINVAL;
         if (r_out < tpl->size) return GRAFT_EINVAL;
         for (int s = 0; s < 3; ++s)
-            if (cfg->keep[s] < 0 || cfg->keep[s] > Nd || slots - cfg->keep[s] > tpl->size ||
-                slots - cfg->keep[s] < 0)
-                return GRAFT_EINVAL;
+            if (cfg->keep[s] < 0 || cfg->keep[s] > Nd || slots - cfg->keep[s] < 0) return GRAFT_EINVAL;
         a.tpl_size = tpl->size;
         a.tpl_parent = tpl->parent;
         a.tpl_rank = tpl->rank;

@@ -33,8 +33,8 @@ from . import _lib as L
 class GraftPipeline:
     def __init__(self, *, V, B, k=8, slots=60, mode="tree", layout="compact", dtype="bf16",
                  n_draft=60, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), keep=(8, 24, 40),
-                 tail_thr=0.5, tpl_width=8, tpl_depth=8, want_prob=False, want_coverage=False,
-                 device="cuda", fused=True):
+                 tail_thr=0.5, tpl_width=8, tpl_depth=8, tpl_kind="chain", tpl_beta=(1, 1),
+                 want_prob=False, want_coverage=False, device="cuda", fused=True):
         L.load()
         self.fused = bool(fused)
         self.V, self.B, self.k = int(V), int(B), int(k)
@@ -71,7 +71,13 @@ class GraftPipeline:
         self.cum = torch.zeros(B, Nd, dtype=torch.float32, device=dev)
 
         if self.mode == L.MODE_TREE:
-            par, rk, dp = L.graft_template_master(tpl_width, tpl_depth, self.slots - min(keep))
+            cap = self.slots - min(keep)
+            if tpl_kind == "branching":
+                par, rk, dp = L.graft_template_branching(tpl_width, tpl_depth, tpl_beta[0], tpl_beta[1], cap)
+            elif tpl_kind == "chain":
+                par, rk, dp = L.graft_template_master(tpl_width, tpl_depth, cap)
+            else:
+                raise ValueError("unknown template kind %r" % (tpl_kind,))
             self.tpl_parent = torch.tensor(par, **i32)
             self.tpl_rank = torch.tensor(rk, **i32)
             self.tpl_depth = torch.tensor(dp, **i32)
@@ -108,7 +114,8 @@ class GraftPipeline:
                    slots=cfg.tail_block if cfg.mode == "tail" else cfg.slots,
                    mode=cfg.mode, layout=cfg.layout, dtype=cfg.dtype, n_draft=cfg.n_draft,
                    ckpt_layers=cfg.ckpt_layers, tau=cfg.tau, keep=cfg.keep, tail_thr=cfg.tail_thr,
-                   tpl_width=cfg.tpl_width, tpl_depth=cfg.tpl_depth, want_prob=want_prob,
+                   tpl_width=cfg.tpl_width, tpl_depth=cfg.tpl_depth, tpl_kind=cfg.tpl_kind,
+                   tpl_beta=cfg.tpl_beta, want_prob=want_prob,
                    want_coverage=want_coverage, device=device, fused=fused)
 
     # ------------------------------------------------------------------ state

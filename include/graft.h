@@ -78,8 +78,9 @@ typedef struct graft_prune_cfg {
 } graft_prune_cfg;
 
 /* Retrieval template (host struct holding DEVICE arrays of `size` entries), in
- * the master order of graft_template_master(); a budget of R retrieval slots
- * uses entries 0..R-1.  parent[t] < t is a template index, -1 for the root. */
+ * a master order such as graft_template_master()'s or
+ * graft_template_branching()'s; a budget of R retrieval slots uses entries
+ * 0..min(R, size)-1.  parent[t] < t is a template index, -1 for the root. */
 typedef struct graft_template {
     int32_t size;
     const int32_t *parent; /* device [size] */
@@ -117,12 +118,26 @@ int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const i
 int graft_template_master(int width, int depth, int cap, int32_t *parent, int32_t *rank,
                           int32_t *tdepth);
 
+/* graft_template_branching -- host only; a branching form of section 二's
+ * asymmetric template (better-ranked successors get more children and reach
+ * deeper, after Token Recycling).  Nodes are rank paths (r_1..r_d), 1 <= d <=
+ * depth, every r < width; cost = d*beta_den + beta_num*(r_1+..+r_d); the
+ * master order is ascending (cost, d, ranks lexicographically), so beta =
+ * beta_num/beta_den = 0 is breadth-first and a large beta approaches rank-0
+ * chains.  Writes the first min(cap, all paths) nodes into HOST arrays and
+ * returns their count, or GRAFT_EINVAL (width, depth >= 1, beta_num >= 0,
+ * beta_den >= 1, cap >= 0).  With a matrix of k successors, width <= k. */
+int graft_template_branching(int width, int depth, int beta_num, int beta_den, int cap, int32_t *parent,
+                             int32_t *rank, int32_t *tdepth);
+
 /* graft_retrieve_expand -- section 二, gear 2: one matrix row lookup per node,
  * GPU only.
- * TREE: R_b = slots - n_keep[b] retrieval nodes (0 <= R_b <= tpl->size); node
- *   t reads ret_tok[t] = table[src][rank[t]] with src = root_tok[b] for root
- *   children, else ret_tok[parent[t]].  cfg (host) is used to check
- *   slots - keep[s] <= tpl->size for every stage.  d_tok may be NULL.
+ * TREE: R_b = min(slots - n_keep[b], tpl->size) retrieval nodes (a template
+ *   smaller than the freed budget leaves the rest of it empty); node t reads
+ *   ret_tok[t] = table[src][rank[t]] with src = root_tok[b] for root
+ *   children, else ret_tok[parent[t]] (-1 below an out-of-range token or
+ *   rank).  cfg (host) is used to check 0 <= slots - keep[s].  d_tok may be
+ *   NULL.
  * TAIL: R_b = slots - n_keep[b]; a chain x <- table[x][0] of R_b steps from
  *   the last kept block token d_tok[b, n_keep-1] (root_tok[b] when n_keep is
  *   0); ret_parent[t] = t-1.  tpl and cfg may be NULL.
@@ -143,7 +158,9 @@ int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_
  * topological (parent row < child row).
  * Inputs: root_tok, base_pos int32 [B]; d_tok, d_parent int32 [B, Nd];
  * keep uint8 [B, Nd]; n_keep int32 [B]; ret_tok, ret_parent int32 [B, r_out];
- * n_ret int32 [B].  n_keep + n_ret must equal T1 - 1 per request.
+ * n_ret int32 [B].  n_keep + n_ret <= T1 - 1 per request: rows nothing is
+ * placed in are empty (token -1, parent -1, depth 0, mask = the row itself,
+ * GRAFT_ROW_EMPTY).
  * Outputs [B, T1]: tok, parent (-1 at the root), depth, pos_id = base_pos +
  * depth (int32), anc (uint64: bit g set iff row g is an ancestor of the row or
  * the row itself), row_src (uint8, nullable: GRAFT_ROW_* of every row, the

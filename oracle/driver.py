@@ -20,7 +20,11 @@ class OracleGraft:
         self.table = np.tile(np.arange(k, dtype=np.int32), (V, 1))
         self.table_prob = None
         if cfg.mode == "tree":
-            self.tpl = O.template(W=cfg.tpl_width, D=cfg.tpl_depth, Rmax=cfg.slots - min(cfg.keep))
+            Rmax = cfg.slots - min(cfg.keep)
+            if cfg.tpl_kind == "branching":
+                self.tpl = O.template_branching(W=cfg.tpl_width, D=cfg.tpl_depth, beta=cfg.tpl_beta, Rmax=Rmax)
+            else:
+                self.tpl = O.template(W=cfg.tpl_width, D=cfg.tpl_depth, Rmax=Rmax)
         self.roots = np.zeros(cfg.B, np.int32)
         self.base_pos = np.zeros(cfg.B, np.int32)
         self.last = {}

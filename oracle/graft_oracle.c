@@ -514,6 +514,7 @@ int oracle_update(int64_t n_rows, int V, int k, const int32_t *row_tok, const in
                   int32_t *table, const double *prob, float *table_prob) {
     for (int64_t P = 0; P < n_rows; ++P) {
         int x = row_tok[P];
+        if (x == -1) continue; /* an empty row (no candidate placed): nothing was verified */
         if (x < 0 || x >= V) return -2;
         for (int j = 0; j < k; ++j) {
             table[(size_t)x * k + j] = topk[P * k + j];

@@ -36,6 +36,8 @@ class GraftConfig:
     keep: tuple = (8, 24, 40)
     tpl_width: int = 8
     tpl_depth: int = 8
+    tpl_kind: str = "chain"          # "chain" (rank chains) or "branching"
+    tpl_beta: tuple = (1, 1)         # branching: rank charge num/den
     tail_block: int = 16
     tail_thr: float = 0.5
     warmup_steps: int = 5

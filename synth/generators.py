@@ -336,6 +336,9 @@ def tree_row_cols(intent, tok_flat, parent_flat, prev_root):
     """Intended next token for every flattened row of one request."""
     cols = []
     for f in range(len(tok_flat)):
+        if int(tok_flat[f]) < 0:      # an empty row (padding): its scores are never used
+            cols.append(0)
+            continue
         p = int(parent_flat[f])
         prev = prev_root if p < 0 else int(tok_flat[p])
         cols.append(intent.next(prev, int(tok_flat[f])))

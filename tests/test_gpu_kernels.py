@@ -220,16 +220,23 @@ def test_prune_tail_parity():
     np.testing.assert_array_equal(kp, o["keep"])
 
 
-def _tpl_dev(R):
-    par, rk, dp = L.graft_template_master(8, 8, R)
+def _tpl_dev(R, kind="chain", W=8, D=8, beta=(1, 1)):
+    if kind == "chain":
+        par, rk, dp = L.graft_template_master(W, D, R)
+    else:
+        par, rk, dp = L.graft_template_branching(W, D, beta[0], beta[1], R)
     tp, tr, td = (_t(np.array(x, np.int32)) for x in (par, rk, dp))
     return L.Template(len(par), tp.data_ptr(), tr.data_ptr(), td.data_ptr()), (tp, tr, td), len(par)
 
 
-def gpu_retrieve_tree(table, roots, n_keep, slots=60, R=52, V=None):
+def _tpl_host(R, kind="chain", W=8, D=8, beta=(1, 1)):
+    return O.template(W, D, R) if kind == "chain" else O.template_branching(W, D, beta, R)
+
+
+def gpu_retrieve_tree(table, roots, n_keep, slots=60, R=52, V=None, **tk):
     B = len(roots)
     V = table.shape[0] if V is None else V
-    tpl, keepalive, r_out = _tpl_dev(R)
+    tpl, keepalive, r_out = _tpl_dev(R, **tk)
     cfg = L.prune_cfg(CFG["ckpt"], [-1.0] * 3, CFG["keep"], 0.5)
     tb, rt, nk = _t(table, torch.int32), _t(roots, torch.int32), _t(n_keep, torch.int32)
     ret_tok = torch.zeros(B, r_out, dtype=torch.int32, device=DEV)
@@ -254,6 +261,28 @@ def test_retrieve_tree_parity():
     np.testing.assert_array_equal(nr, o["n_ret"])
     np.testing.assert_array_equal(rt, o["ret_tok"])
     np.testing.assert_array_equal(rp, o["ret_parent"])
+
+
+@pytest.mark.parametrize("kind,W,D,beta,R", [
+    ("branching", 8, 8, (1, 1), 52),     # branching: several ranks at every depth
+    ("branching", 8, 12, (0, 1), 64),    # breadth-first: depth 2 only within 64 nodes
+    ("branching", 2, 30, (100, 1), 52),  # a depth-30 rank-0 chain: the level-by-level path
+    ("chain", 8, 2, (1, 1), 52),         # 16 nodes: less than most budgets (empty slots)
+    ("branching", 4, 3, (1, 2), 20),
+])
+def test_retrieve_tree_parity_templates(kind, W, D, beta, R):
+    rng = np.random.default_rng(14)
+    V = 20011
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    B = 29
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    n_keep = rng.choice([8, 24, 40, 60], size=B).astype(np.int32)
+    tpl = _tpl_host(R, kind, W, D, beta)
+    o = O.retrieve_tree(table, roots, n_keep, 60, tpl)
+    rt, rp, nr = gpu_retrieve_tree(table, roots, n_keep, R=R, kind=kind, W=W, D=D, beta=beta)
+    np.testing.assert_array_equal(nr, o["n_ret"])
+    np.testing.assert_array_equal(rp, o["ret_parent"])
+    np.testing.assert_array_equal(rt, o["ret_tok"])
 
 
 def test_retrieve_tail_parity():
@@ -436,7 +465,10 @@ def test_update_parity_collisions(n, ntok):
 
 # ----------------------------------------------------------------------------- fused entry points
 
-def test_build_hybrid_tree_matches_oracle_tree():
+@pytest.mark.parametrize("kind,W,D,beta", [("chain", 8, 8, (1, 1)), ("branching", 8, 8, (1, 1)),
+                                           ("chain", 8, 2, (1, 1)), ("branching", 2, 30, (100, 1))],
+                         ids=["chain8x8", "branching8x8", "chain8x2_empty_rows", "deep_chain30"])
+def test_build_hybrid_tree_matches_oracle_tree(kind, W, D, beta):
     rng = np.random.default_rng(30)
     B, V = 37, 5000
     par, lay, _ = TOPO
@@ -446,7 +478,8 @@ def test_build_hybrid_tree_matches_oracle_tree():
     roots = rng.integers(0, V, size=B).astype(np.int32)
     base = rng.integers(0, 100000, size=B).astype(np.int32)
     d_tok = rng.integers(0, V, size=(B, 60)).astype(np.int32)
-    tpl, keepalive, r_out = _tpl_dev(52)
+    tpl, keepalive, r_out = _tpl_dev(52, kind, W, D, beta)
+    tpl_h = _tpl_host(52, kind, W, D, beta)
     cfg = L.prune_cfg(CFG["ckpt"], [float(np.float32(math.log(t))) for t in CFG["tau"]], CFG["keep"], 0.5)
     for layout in ("compact", "in_place"):
         ins = [_t(x, torch.int32) for x in (table, roots, base, P, Ly)]
@@ -467,7 +500,7 @@ def test_build_hybrid_tree_matches_oracle_tree():
                                   anc.data_ptr(), src.data_ptr(), _s())
         torch.cuda.synchronize()
         pr = O.prune_tree(P, Ly, lp, want_cum=True)
-        ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, O.template(8, 8, 52))
+        ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, tpl_h)
         fl = O.flatten(layout, 61, roots, base, d_tok, P, pr["keep"], pr["n_keep"], ret)
         np.testing.assert_array_equal(st.cpu().numpy(), pr["stage"])
         np.testing.assert_array_equal(nk.cpu().numpy(), pr["n_keep"])

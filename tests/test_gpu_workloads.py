@@ -98,6 +98,17 @@ def test_lockstep_with_probabilities():
     np.testing.assert_allclose(tp_h, ob.o.table_prob, rtol=1e-5, atol=0)
 
 
+@pytest.mark.parametrize("cfg_id,kw", [
+    (2, {"tpl_kind": "branching", "tpl_beta": (1, 1)}),
+    (3, {"V": 20000, "B": 8, "tpl_kind": "branching", "tpl_beta": (2, 1), "tpl_depth": 10}),
+    (2, {"tpl_depth": 3}),                                   # 24-node chains: empty slots every step
+], ids=["cfg2_branching", "cfg3_branching_deep", "cfg2_short_chains"])
+def test_lockstep_templates(cfg_id, kw):
+    cfg = _small(cfg_id, **kw)
+    st = _compare_runs(cfg, 15, warmup=cfg.warmup_steps)
+    assert st["accepted"] > 0
+
+
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "five_calls"])
 def test_lockstep_coverage_gain(fused):
     """The coverage-gain diagnostic through whole steps (row sources from the

@@ -88,10 +88,24 @@ def test_host_validation_rejects_without_launch():
     # null pointers
     assert lib.graft_prune_select(1, 60, 0, None, P, P, ctypes.byref(cfg), P, P, P, None, None) == L.GRAFT_EINVAL
     assert lib.graft_update_topk(10, 100, 8, 1, None, None, None, P, P, None, None, P, 1 << 20, None) == L.GRAFT_EINVAL
-    # template budget check: slots - keep must fit the template
-    tpl = L.Template(20, P, P, P)
+    # template checks: the output rows must hold the template; a stage may not keep more than the slots
+    tpl = L.Template(60, P, P, P)
     assert lib.graft_retrieve_expand(1, 100, 8, 0, 60, P, P, P, None, 60, ctypes.byref(tpl),
                                      ctypes.byref(cfg), P, P, P, 52, None) == L.GRAFT_EINVAL
+    tpl = L.Template(20, P, P, P)
+    over = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 61), 0.5)
+    assert lib.graft_retrieve_expand(1, 100, 8, 0, 60, P, P, P, None, 60, ctypes.byref(tpl),
+                                     ctypes.byref(over), P, P, P, 52, None) == L.GRAFT_EINVAL
+    assert lib.graft_template_branching(8, 8, -1, 1, 52, P, P, P) == L.GRAFT_EINVAL
+    assert lib.graft_template_branching(8, 8, 1, 0, 52, P, P, P) == L.GRAFT_EINVAL
     # empty batches enqueue nothing and succeed
     assert lib.graft_prune_select(0, 60, 0, None, None, None, ctypes.byref(cfg), None, None, None, None, None) == 0
     assert lib.graft_update_topk(0, 100, 8, 1, None, None, None, None, None, None, None, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("W,D,beta,cap", [(8, 8, (1, 1), 52), (8, 12, (3, 2), 64), (4, 6, (0, 1), 64),
+                                          (6, 10, (5, 1), 52), (2, 3, (1, 1), 64), (8, 2, (1, 1), 64)])
+def test_branching_template_matches_oracle(W, D, beta, cap):
+    par, rk, dp = L.graft_template_branching(W, D, beta[0], beta[1], cap)
+    o = O.template_branching(W, D, beta, cap)
+    assert par == o["parent"].tolist() and rk == o["rank"].tolist() and dp == o["depth"].tolist()

@@ -98,3 +98,14 @@ def test_accept_ignores_empty_rows():
     acc = O.accept(tok, par, g, 3)
     assert acc["accept_len"][0] == 2 and acc["bonus"][0] == 7
     np.testing.assert_array_equal(acc["accept_idx"][0], [1, 3, -1])
+
+
+def test_update_skips_empty_rows():
+    table = np.tile(np.arange(8, dtype=np.int32), (10, 1))
+    tk = (np.arange(24, dtype=np.int32) + 100).reshape(3, 8)
+    O.update(table, np.array([3, -1, 5], np.int32), tk)
+    np.testing.assert_array_equal(table[3], tk[0])
+    np.testing.assert_array_equal(table[5], tk[2])
+    assert (table[[0, 1, 2, 4, 6, 7, 8, 9]] == np.arange(8)).all()
+    with pytest.raises(RuntimeError):
+        O.update(table, np.array([10], np.int32), tk[:1])      # an id >= V is still an error
