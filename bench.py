@@ -20,6 +20,10 @@ acceptance walk and matrix update) is then timed on its own with HIP events
 around each launch, on the stream it is launched on.  The CPU oracle is timed on host copies of the same inputs.
 
     python bench.py [--steps K] [--warmup W] [--pool P] [--no-cpu-baseline]
+
+A second mode, ``--template-sweep``, measures the retrieval template instead of
+speed: mean accepted length per step on workloads 2 and 4 for rank-chain and
+branching templates over a grid of depths and widths (one JSON line per point).
 """
 from __future__ import annotations
 
@@ -55,6 +59,12 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--template-sweep", action="store_true",
+                    help="accept length vs retrieval template on workloads 2 and 4 (no timing)")
+    ap.add_argument("--sweep-steps", type=int, default=200)
+    ap.add_argument("--sweep-depths", default="2,4,6,8,10,12")
+    ap.add_argument("--sweep-widths", default="4,6,8")
+    ap.add_argument("--sweep-configs", default="2,4")
     return ap.parse_args()
 
 
@@ -89,6 +99,9 @@ class _Adapter:
     def verify_update(self, rows):
         return {k: v.cpu().numpy() for k, v in self.p.verify_update(rows).items()}
 
+    def ingest_chunk(self, row_tok, rows):
+        return self.p.ingest_chunk(row_tok, rows)
+
 
 def kernel_source_hash():
     h = hashlib.sha256()
@@ -111,8 +124,68 @@ def load_traffic(bytes_alg):
     return d.get("hbm_bytes_per_launch"), d.get("note", "")
 
 
+def template_sweep(args):
+    """Accepted tokens per step vs the retrieval template (no timing).  For every
+    workload, template family, depth and width: a fresh pipeline (matrix reset,
+    prompt re-ingested for workload 4), the workload's warm-up, then
+    --sweep-steps steps; reports the mean accepted length, the share of steps
+    whose accepted path reaches a retrieved row, and the mean coverage gain."""
+    import numpy as np
+    import torch
+
+    from hybrid_draft_tree_amd import _lib as L
+    from hybrid_draft_tree_amd.driver import GraftPipeline
+    from synth import CONFIGS
+    from synth import generators as G
+    from synth import runner as R
+
+    assert torch.cuda.is_available(), "the template sweep runs on the GPU"
+    dev = torch.device("cuda", 0)
+    families = [("chain", (1, 1)), ("branching", (1, 1)), ("branching", (2, 1))]
+    depths = [int(x) for x in args.sweep_depths.split(",")]
+    widths = [int(x) for x in args.sweep_widths.split(",")]
+    for cfg_id in [int(x) for x in args.sweep_configs.split(",")]:
+        base = CONFIGS[cfg_id]
+        for kind, beta in families:
+            for D in depths:
+                for W in widths:
+                    cfg = base.scaled(tpl_kind=kind, tpl_beta=beta, tpl_depth=D, tpl_width=W)
+                    t0 = time.time()
+                    pipe = GraftPipeline.from_config(cfg, want_coverage=True, device=dev)
+                    ad = _Adapter(pipe, torch)
+                    wl = R.Workload(cfg)
+                    R.start(ad, wl)
+                    for s in range(cfg.warmup_steps if cfg_id != 4 else 0):
+                        R.step(ad, wl, s, G.WARMUP_STREAM_OFFSET)
+                    acc, via_ret, gain, n, with_ret = 0, 0, 0.0, 0, 0
+                    for s in range(args.sweep_steps):
+                        flat, res = R.step(ad, wl, s)
+                        alen = np.asarray(res["accept_len"])
+                        aidx = np.asarray(res["accept_idx"])
+                        src = np.asarray(flat["row_src"])
+                        for b in range(cfg.B):
+                            path = aidx[b, :alen[b]]
+                            via_ret += int((src[b, path] == L.ROW_RETRIEVED).any())
+                        acc += int(alen.sum())
+                        with_ret += int((np.asarray(flat["n_ret"]) > 0).sum())
+                        gain += float(np.asarray(res["coverage"]).sum())
+                        n += cfg.B
+                    rec = {"sweep": "template", "workload": cfg.name, "template": kind,
+                           "beta": list(beta) if kind == "branching" else None, "depth": D, "width": W,
+                           "template_nodes": int(pipe.r_out), "steps": args.sweep_steps, "requests": cfg.B,
+                           "mean_accept_len": round(acc / n, 4), "tokens_per_step": round(acc / n + 1, 4),
+                           "steps_with_retrieval": round(with_ret / n, 4),
+                           "accepted_via_retrieval": round(via_ret / n, 4), "mean_coverage_gain": round(gain / n, 5),
+                           "seconds": round(time.time() - t0, 1)}
+                    print(json.dumps(rec), flush=True)
+                    del pipe, ad
+                    torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.template_sweep:
+        return template_sweep(args)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build measures the single-GPU Graft "
               "step (no collectives); run with --gpus 1", file=sys.stderr)
