@@ -23,6 +23,8 @@ class OracleGraft:
             Rmax = cfg.slots - min(cfg.keep)
             if cfg.tpl_kind == "branching":
                 self.tpl = O.template_branching(W=cfg.tpl_width, D=cfg.tpl_depth, beta=cfg.tpl_beta, Rmax=Rmax)
+            elif cfg.tpl_kind == "none":
+                self.tpl = {k: np.zeros(0, np.int32) for k in ("parent", "rank", "depth")}
             else:
                 self.tpl = O.template(W=cfg.tpl_width, D=cfg.tpl_depth, Rmax=Rmax)
         self.roots = np.zeros(cfg.B, np.int32)
@@ -47,7 +49,7 @@ class OracleGraft:
         T1 = cfg.rows_per_request
         if cfg.mode == "tree":
             pr = O.prune_tree(draft["parent"], draft["layer"], draft["logp"], cfg.ckpt_layers, cfg.tau,
-                              cfg.keep, want_cum=True)
+                              cfg.keep, want_cum=True, node_tau=cfg.node_tau)
             ret = O.retrieve_tree(self.table, self.roots, pr["n_keep"], cfg.slots, self.tpl)
         else:
             pr = O.prune_tail(draft["conf"], cfg.tail_thr)

@@ -60,9 +60,14 @@ void oracle_set_threads(int n) {
 /* of layers <= c_s with the highest cumulative confidence (ties -> lower    */
 /* node index); with no prune every draft node is kept.                      */
 /* ------------------------------------------------------------------------- */
+/* node_tau > 0 selects the per-node variant instead of the checkpoints      */
+/* (section 四's static slots, "low-confidence draft nodes are replaced"):   */
+/* keep every node whose cumulative log-confidence is >= (float)ln node_tau, */
+/* a set closed under ancestors since confidences only fall along a path;    */
+/* stage 4 when a node was cut, else 3.                                      */
 int oracle_prune_tree(int B, int Nd, const int32_t *parent, const int32_t *layer,
                       const float *logp, const int32_t *ckpt_layer, const double *tau,
-                      const int32_t *keep_n, int32_t *stage, int32_t *n_keep,
+                      const int32_t *keep_n, double node_tau, int32_t *stage, int32_t *n_keep,
                       uint8_t *keep, float *cum_out) {
     if (B < 0 || Nd <= 0) return -1;
     float *cum = (float *)malloc(sizeof(float) * (size_t)Nd);
@@ -78,6 +83,20 @@ int oracle_prune_tree(int B, int Nd, const int32_t *parent, const int32_t *layer
             }
             float base = (par[i] < 0) ? 0.0f : cum[par[i]];
             cum[i] = base + lp[i];
+        }
+        if (node_tau > 0.0) {
+            float nthr = (float)log(node_tau);
+            uint8_t *kp = keep + (size_t)b * Nd;
+            int N = 0;
+            for (int i = 0; i < Nd; ++i) {
+                kp[i] = cum[i] >= nthr;
+                N += kp[i];
+            }
+            stage[b] = N < Nd ? 4 : 3;
+            n_keep[b] = N;
+            if (cum_out)
+                for (int i = 0; i < Nd; ++i) cum_out[(size_t)b * Nd + i] = cum[i];
+            continue;
         }
         int st = 3;
         for (int s = 0; s < 3 && st == 3; ++s) {

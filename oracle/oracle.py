@@ -29,7 +29,7 @@ def lib():
             _b.build()
         L = C.CDLL(path)
         P = C.c_void_p
-        L.oracle_prune_tree.argtypes = [C.c_int, C.c_int, P, P, P, P, P, P, P, P, P, P]
+        L.oracle_prune_tree.argtypes = [C.c_int, C.c_int, P, P, P, P, P, P, C.c_double, P, P, P, P]
         L.oracle_prune_tail.argtypes = [C.c_int, C.c_int, P, C.c_float, P, P, P]
         L.oracle_template.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P]
         L.oracle_template_branching.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P]
@@ -71,7 +71,8 @@ def set_threads(n: int) -> None:
 
 
 def prune_tree(parent, layer, logp, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), keep=(8, 24, 40),
-               want_cum=False):
+               want_cum=False, node_tau=0.0):
+    """Checkpoint pruning; with node_tau > 0 the per-node variant instead (stage 4 when it cuts)."""
     parent, layer = _i32(parent), _i32(layer)
     logp = np.ascontiguousarray(logp, dtype=np.float32)
     B, Nd = parent.shape
@@ -83,7 +84,7 @@ def prune_tree(parent, layer, logp, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), 
     ta = np.ascontiguousarray(tau, dtype=np.float64)
     kn = _i32(keep)
     rc = lib().oracle_prune_tree(B, Nd, _p(parent), _p(layer), _p(logp), _p(ck), _p(ta), _p(kn),
-                                 _p(stage), _p(n_keep), _p(keepm), _p(cum))
+                                 float(node_tau), _p(stage), _p(n_keep), _p(keepm), _p(cum))
     _check(rc, "prune_tree")
     out = {"stage": stage, "n_keep": n_keep, "keep": keepm}
     if want_cum:

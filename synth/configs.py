@@ -36,8 +36,9 @@ class GraftConfig:
     keep: tuple = (8, 24, 40)
     tpl_width: int = 8
     tpl_depth: int = 8
-    tpl_kind: str = "chain"          # "chain" (rank chains) or "branching"
+    tpl_kind: str = "chain"          # "chain" (rank chains), "branching", or "none" (no retrieval)
     tpl_beta: tuple = (1, 1)         # branching: rank charge num/den
+    node_tau: float = 0.0            # > 0: per-node pruning threshold instead of the checkpoints
     tail_block: int = 16
     tail_thr: float = 0.5
     warmup_steps: int = 5
