@@ -44,7 +44,8 @@ class GraftError(RuntimeError):
 
 class PruneCfg(C.Structure):
     _fields_ = [("ckpt_layer", C.c_int32 * 3), ("log_thr", C.c_float * 3),
-                ("keep", C.c_int32 * 3), ("tail_thr", C.c_float)]
+                ("keep", C.c_int32 * 3), ("tail_thr", C.c_float), ("node_mode", C.c_int32),
+                ("node_log_thr", C.c_float)]
 
 
 class Template(C.Structure):
@@ -94,13 +95,16 @@ def _chk(fn, rc):
     return rc
 
 
-def prune_cfg(ckpt_layers, log_thr, keep, tail_thr) -> PruneCfg:
+def prune_cfg(ckpt_layers, log_thr, keep, tail_thr, node_log_thr=None) -> PruneCfg:
+    """node_log_thr (fp32 log-confidence) switches TREE pruning to the per-node variant."""
     c = PruneCfg()
     for i in range(3):
         c.ckpt_layer[i] = int(ckpt_layers[i])
         c.log_thr[i] = float(log_thr[i])
         c.keep[i] = int(keep[i])
     c.tail_thr = float(tail_thr)
+    c.node_mode = 0 if node_log_thr is None else 1
+    c.node_log_thr = 0.0 if node_log_thr is None else float(node_log_thr)
     return c
 
 

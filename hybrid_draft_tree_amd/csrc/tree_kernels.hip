@@ -55,6 +55,13 @@ __device__ __forceinline__ PruneOut prune_tree_wave(bool valid, int par, int lay
     }
     // order-preserving integer keys (-0 == +0): integer max and compares
     const int key = f32_key(__float_as_uint(cum));
+    if (cfg.node_mode) {
+        // per-node variant: every node at or above the threshold (closed under
+        // ancestors: confidences only fall along a path)
+        const bool kept = valid && key >= f32_key(__float_as_uint(cfg.node_log_thr));
+        const int N = __popcll(ballot(kept));
+        return {N < __popcll(ballot(valid)) ? 4 : 3, N, kept, cum};
+    }
     int st = 3;
     for (int s = 0; s < 3; ++s) {
         const int c = cfg.ckpt_layer[s];

@@ -33,7 +33,7 @@ from . import _lib as L
 class GraftPipeline:
     def __init__(self, *, V, B, k=8, slots=60, mode="tree", layout="compact", dtype="bf16",
                  n_draft=60, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), keep=(8, 24, 40),
-                 tail_thr=0.5, tpl_width=8, tpl_depth=8, tpl_kind="chain", tpl_beta=(1, 1),
+                 tail_thr=0.5, tpl_width=8, tpl_depth=8, tpl_kind="chain", tpl_beta=(1, 1), node_tau=0.0,
                  want_prob=False, want_coverage=False, device="cuda", fused=True):
         L.load()
         self.fused = bool(fused)
@@ -52,8 +52,10 @@ class GraftPipeline:
             self.device = torch.device("cuda", torch.cuda.current_device())
         dev = self.device
         i32 = dict(dtype=torch.int32, device=dev)
-        log_thr = [float(np.float32(math.log(t))) for t in tau]
-        self.cfg = L.prune_cfg(ckpt_layers, log_thr, keep, tail_thr)
+        # fp32 thresholds; tau 0 never fires (-inf), tau +inf always fires
+        log_thr = [-math.inf if t == 0 else float(np.float32(math.log(t))) for t in tau]
+        node_thr = float(np.float32(math.log(node_tau))) if node_tau > 0 else None
+        self.cfg = L.prune_cfg(ckpt_layers, log_thr, keep, tail_thr, node_thr)
 
         self.table = torch.arange(self.k, **i32).repeat(self.V, 1).contiguous()
         self.table_prob = torch.zeros(self.V, self.k, dtype=torch.float32, device=dev) if want_prob else None
@@ -76,6 +78,8 @@ class GraftPipeline:
                 par, rk, dp = L.graft_template_branching(tpl_width, tpl_depth, tpl_beta[0], tpl_beta[1], cap)
             elif tpl_kind == "chain":
                 par, rk, dp = L.graft_template_master(tpl_width, tpl_depth, cap)
+            elif tpl_kind == "none":      # no retrieval: freed slots stay empty
+                par, rk, dp = [], [], []
             else:
                 raise ValueError("unknown template kind %r" % (tpl_kind,))
             self.tpl_parent = torch.tensor(par, **i32)
@@ -115,7 +119,7 @@ class GraftPipeline:
                    mode=cfg.mode, layout=cfg.layout, dtype=cfg.dtype, n_draft=cfg.n_draft,
                    ckpt_layers=cfg.ckpt_layers, tau=cfg.tau, keep=cfg.keep, tail_thr=cfg.tail_thr,
                    tpl_width=cfg.tpl_width, tpl_depth=cfg.tpl_depth, tpl_kind=cfg.tpl_kind,
-                   tpl_beta=cfg.tpl_beta, want_prob=want_prob,
+                   tpl_beta=cfg.tpl_beta, node_tau=cfg.node_tau, want_prob=want_prob,
                    want_coverage=want_coverage, device=device, fused=fused)
 
     # ------------------------------------------------------------------ state

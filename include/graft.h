@@ -72,9 +72,14 @@ extern "C" {
  * confidence cut (0.5 in section 七). */
 typedef struct graft_prune_cfg {
     int32_t ckpt_layer[3]; /* draft layers of the checkpoints; layer 0 = the root's children */
-    float log_thr[3];      /* fire when best cumulative log-confidence < log_thr[s] */
+    float log_thr[3];      /* fire when best cumulative log-confidence < log_thr[s] (+inf: always,
+                              -inf: never -- a fixed draft/retrieval split, section 五's ablation) */
     int32_t keep[3];       /* draft nodes kept when checkpoint s fires */
     float tail_thr;        /* TAIL: keep the longest prefix with confidence >= tail_thr */
+    int32_t node_mode;     /* TREE: nonzero = per-node variant (section 四's static slots): keep
+                              every node with cumulative log-confidence >= node_log_thr instead of
+                              the checkpoints; stage 4 when a node is cut, else 3 */
+    float node_log_thr;
 } graft_prune_cfg;
 
 /* Retrieval template (host struct holding DEVICE arrays of `size` entries), in

@@ -152,10 +152,14 @@ def _random_logp(rng, B):
     return np.array(out, np.float32)
 
 
-def gpu_prune(parent, layer, score, mode, cfg_t):
+def _log_thr(t):
+    return -math.inf if t == 0 else float(np.float32(math.log(t)))
+
+
+def gpu_prune(parent, layer, score, mode, cfg_t, node_tau=0.0):
     B, Nd = score.shape
-    cfg = L.prune_cfg(cfg_t["ckpt"], [float(np.float32(math.log(t))) for t in cfg_t["tau"]],
-                      cfg_t["keep"], cfg_t["tail_thr"])
+    cfg = L.prune_cfg(cfg_t["ckpt"], [_log_thr(t) for t in cfg_t["tau"]], cfg_t["keep"], cfg_t["tail_thr"],
+                      _log_thr(node_tau) if node_tau > 0 else None)
     dp, dl, ds = _t(parent, torch.int32), _t(layer, torch.int32), _t(score, torch.float32)
     st = torch.zeros(B, dtype=torch.int32, device=DEV)
     nk = torch.zeros(B, dtype=torch.int32, device=DEV)
@@ -187,6 +191,37 @@ def test_prune_tree_parity():
     np.testing.assert_array_equal(kp, o["keep"])
     np.testing.assert_array_equal(cum.view(np.uint32), o["cum"].view(np.uint32))
     assert set(st.tolist()) == {0, 1, 2, 3}
+
+
+@pytest.mark.parametrize("node_tau", [0.05, 0.2, 0.3, 0.5])
+def test_prune_per_node_parity(node_tau):
+    rng = np.random.default_rng(11)
+    B = 53
+    par, lay, _ = TOPO
+    lp = _random_logp(rng, B)
+    lp[0, :] = np.float32(math.log(node_tau))        # the threshold hit exactly: kept (>=)
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    st, nk, kp, cum = gpu_prune(P, Ly, lp, L.MODE_TREE, CFG, node_tau=node_tau)
+    o = O.prune_tree(P, Ly, lp, want_cum=True, node_tau=node_tau)
+    np.testing.assert_array_equal(st, o["stage"])
+    np.testing.assert_array_equal(nk, o["n_keep"])
+    np.testing.assert_array_equal(kp, o["keep"])
+    np.testing.assert_array_equal(cum.view(np.uint32), o["cum"].view(np.uint32))
+
+
+@pytest.mark.parametrize("tau", [(math.inf, 0, 0), (0, math.inf, 0), (0, 0, math.inf), (0, 0, 0)])
+def test_prune_fixed_split_parity(tau):
+    rng = np.random.default_rng(12)
+    B = 31
+    par, lay, _ = TOPO
+    lp = _random_logp(rng, B)
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    cfg_t = dict(CFG, tau=tau)
+    st, nk, kp, _ = gpu_prune(P, Ly, lp, L.MODE_TREE, cfg_t)
+    o = O.prune_tree(P, Ly, lp, tau=tau)
+    np.testing.assert_array_equal(st, o["stage"])
+    np.testing.assert_array_equal(kp, o["keep"])
+    assert len(set(st.tolist())) == 1
 
 
 def test_prune_small_trees_and_unreached_checkpoints():

@@ -109,6 +109,18 @@ def test_lockstep_templates(cfg_id, kw):
     assert st["accepted"] > 0
 
 
+@pytest.mark.parametrize("kw", [
+    {"node_tau": 0.15},                         # per-node static-slot replacement
+    {"tpl_kind": "none"},                       # pruning without retrieval: empty slots
+    {"tau": (0.0, 0.0, float("inf"))},          # fixed 40/20 draft/retrieval split
+], ids=["per_node", "no_retrieval", "fixed_split"])
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "five_calls"])
+def test_lockstep_ablation_variants(kw, fused):
+    cfg = _small(3, V=20000, B=8, **kw)
+    st = _compare_runs(cfg, 10, warmup=cfg.warmup_steps, fused=fused)
+    assert st["accepted"] > 0
+
+
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "five_calls"])
 def test_lockstep_coverage_gain(fused):
     """The coverage-gain diagnostic through whole steps (row sources from the
