@@ -24,6 +24,9 @@ around each launch, on the stream it is launched on.  The CPU oracle is timed on
 A second mode, ``--template-sweep``, measures the retrieval template instead of
 speed: mean accepted length per step on workloads 2 and 4 for rank-chain and
 branching templates over a grid of depths and widths (one JSON line per point).
+A third, ``--ablation``, compares the pruning/retrieval variants of the
+write-up's ablations (no retrieval, fixed splits, a dense tree, per-node
+thresholds) with the adaptive default on workloads 2, 3 and 4.
 """
 from __future__ import annotations
 
@@ -65,6 +68,9 @@ def parse():
     ap.add_argument("--sweep-depths", default="2,4,6,8,10,12")
     ap.add_argument("--sweep-widths", default="4,6,8")
     ap.add_argument("--sweep-configs", default="2,4")
+    ap.add_argument("--ablation", action="store_true",
+                    help="accept length of the pruning/retrieval variants (no timing)")
+    ap.add_argument("--ablation-configs", default="2,3,4")
     return ap.parse_args()
 
 
@@ -124,20 +130,82 @@ def load_traffic(bytes_alg):
     return d.get("hbm_bytes_per_launch"), d.get("note", "")
 
 
+def _accept_run(cfg, steps, dev):
+    """One fresh pipeline through the workload's warm-up and `steps` steps:
+    accepted tokens per request-step, the share of request-steps that retrieved
+    anything, whose accepted path reaches a retrieved row, and the coverage gain."""
+    import numpy as np
+    import torch
+
+    from hybrid_draft_tree_amd import _lib as L
+    from hybrid_draft_tree_amd.driver import GraftPipeline
+    from synth import generators as G
+    from synth import runner as R
+
+    pipe = GraftPipeline.from_config(cfg, want_coverage=True, device=dev)
+    ad = _Adapter(pipe, torch)
+    wl = R.Workload(cfg)
+    R.start(ad, wl)
+    for s in range(cfg.warmup_steps if cfg.cfg_id != 4 else 0):
+        R.step(ad, wl, s, G.WARMUP_STREAM_OFFSET)
+    acc = via_ret = n = with_ret = kept = 0
+    gain = 0.0
+    for s in range(steps):
+        flat, res = R.step(ad, wl, s)
+        alen = np.asarray(res["accept_len"])
+        aidx = np.asarray(res["accept_idx"])
+        src = np.asarray(flat["row_src"])
+        for b in range(cfg.B):
+            via_ret += int((src[b, aidx[b, :alen[b]]] == L.ROW_RETRIEVED).any())
+        acc += int(alen.sum())
+        with_ret += int((np.asarray(flat["n_ret"]) > 0).sum())
+        kept += int(np.asarray(flat["n_keep"]).sum())
+        gain += float(np.asarray(res["coverage"]).sum())
+        n += cfg.B
+    out = {"template_nodes": int(pipe.tpl.size) if pipe.tpl is not None else 0, "steps": steps, "requests": cfg.B,
+           "mean_accept_len": round(acc / n, 4), "tokens_per_step": round(acc / n + 1, 4),
+           "mean_draft_kept": round(kept / n, 2), "steps_with_retrieval": round(with_ret / n, 4),
+           "accepted_via_retrieval": round(via_ret / n, 4), "mean_coverage_gain": round(gain / n, 5)}
+    del pipe, ad
+    torch.cuda.empty_cache()
+    return out
+
+
+def ablation(args):
+    """Accept length of the variants behind the write-up's ablations, all with
+    the same 60-slot budget: the adaptive default, no retrieval (freed slots
+    stay empty), fixed draft/retrieval splits, the dense draft tree (never
+    prune, no retrieval) and the per-node static-slot threshold."""
+    import torch
+
+    from synth import CONFIGS
+
+    assert torch.cuda.is_available(), "the ablation runs on the GPU"
+    dev = torch.device("cuda", 0)
+    inf = float("inf")
+    variants = [("graft (adaptive)", {}), ("no retrieval", {"tpl_kind": "none"}),
+                ("fixed 8/52", {"tau": (inf, 0.0, 0.0)}), ("fixed 24/36", {"tau": (0.0, inf, 0.0)}),
+                ("fixed 40/20", {"tau": (0.0, 0.0, inf)}), ("dense (no prune)", {"tau": (0.0, 0.0, 0.0)})]
+    variants += [("per-node tau=%g" % t, {"node_tau": t}) for t in (0.05, 0.1, 0.2, 0.3)]
+    for cfg_id in [int(x) for x in args.ablation_configs.split(",")]:
+        base = CONFIGS[cfg_id]
+        for name, kw in variants:
+            t0 = time.time()
+            rec = {"ablation": name, "workload": base.name}
+            rec.update(_accept_run(base.scaled(**kw), args.sweep_steps, dev))
+            rec["seconds"] = round(time.time() - t0, 1)
+            print(json.dumps(rec), flush=True)
+
+
 def template_sweep(args):
     """Accepted tokens per step vs the retrieval template (no timing).  For every
     workload, template family, depth and width: a fresh pipeline (matrix reset,
     prompt re-ingested for workload 4), the workload's warm-up, then
     --sweep-steps steps; reports the mean accepted length, the share of steps
     whose accepted path reaches a retrieved row, and the mean coverage gain."""
-    import numpy as np
     import torch
 
-    from hybrid_draft_tree_amd import _lib as L
-    from hybrid_draft_tree_amd.driver import GraftPipeline
     from synth import CONFIGS
-    from synth import generators as G
-    from synth import runner as R
 
     assert torch.cuda.is_available(), "the template sweep runs on the GPU"
     dev = torch.device("cuda", 0)
@@ -149,43 +217,21 @@ def template_sweep(args):
         for kind, beta in families:
             for D in depths:
                 for W in widths:
-                    cfg = base.scaled(tpl_kind=kind, tpl_beta=beta, tpl_depth=D, tpl_width=W)
                     t0 = time.time()
-                    pipe = GraftPipeline.from_config(cfg, want_coverage=True, device=dev)
-                    ad = _Adapter(pipe, torch)
-                    wl = R.Workload(cfg)
-                    R.start(ad, wl)
-                    for s in range(cfg.warmup_steps if cfg_id != 4 else 0):
-                        R.step(ad, wl, s, G.WARMUP_STREAM_OFFSET)
-                    acc, via_ret, gain, n, with_ret = 0, 0, 0.0, 0, 0
-                    for s in range(args.sweep_steps):
-                        flat, res = R.step(ad, wl, s)
-                        alen = np.asarray(res["accept_len"])
-                        aidx = np.asarray(res["accept_idx"])
-                        src = np.asarray(flat["row_src"])
-                        for b in range(cfg.B):
-                            path = aidx[b, :alen[b]]
-                            via_ret += int((src[b, path] == L.ROW_RETRIEVED).any())
-                        acc += int(alen.sum())
-                        with_ret += int((np.asarray(flat["n_ret"]) > 0).sum())
-                        gain += float(np.asarray(res["coverage"]).sum())
-                        n += cfg.B
+                    cfg = base.scaled(tpl_kind=kind, tpl_beta=beta, tpl_depth=D, tpl_width=W)
                     rec = {"sweep": "template", "workload": cfg.name, "template": kind,
-                           "beta": list(beta) if kind == "branching" else None, "depth": D, "width": W,
-                           "template_nodes": int(pipe.r_out), "steps": args.sweep_steps, "requests": cfg.B,
-                           "mean_accept_len": round(acc / n, 4), "tokens_per_step": round(acc / n + 1, 4),
-                           "steps_with_retrieval": round(with_ret / n, 4),
-                           "accepted_via_retrieval": round(via_ret / n, 4), "mean_coverage_gain": round(gain / n, 5),
-                           "seconds": round(time.time() - t0, 1)}
+                           "beta": list(beta) if kind == "branching" else None, "depth": D, "width": W}
+                    rec.update(_accept_run(cfg, args.sweep_steps, dev))
+                    rec["seconds"] = round(time.time() - t0, 1)
                     print(json.dumps(rec), flush=True)
-                    del pipe, ad
-                    torch.cuda.empty_cache()
 
 
 def main():
     args = parse()
     if args.template_sweep:
         return template_sweep(args)
+    if args.ablation:
+        return ablation(args)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build measures the single-GPU Graft "
               "step (no collectives); run with --gpus 1", file=sys.stderr)
