@@ -30,6 +30,20 @@ class OracleGraft:
         self.roots = np.zeros(cfg.B, np.int32)
         self.base_pos = np.zeros(cfg.B, np.int32)
         self.last = {}
+        self.log_thr = None        # calibrated fp32 log-thresholds, else (float) ln cfg.tau
+        self._calib = None
+
+    # -- threshold calibration over warm-up steps (section 二) ----------------
+    def begin_calibration(self):
+        self._calib = []
+
+    def end_calibration(self, q):
+        """Thresholds from the checkpoint statistics of the steps built since
+        begin_calibration(); used by every later step.  Returns them (fp32 ln)."""
+        samples = np.concatenate(self._calib) if self._calib else np.zeros((0, 3), np.float32)
+        self._calib = None
+        self.log_thr = O.calibrate(samples, q)
+        return self.log_thr.copy()
 
     # -- state -------------------------------------------------------------
     def set_roots(self, roots, base_pos):
@@ -48,8 +62,11 @@ class OracleGraft:
         B = cfg.B
         T1 = cfg.rows_per_request
         if cfg.mode == "tree":
+            if self._calib is not None:
+                self._calib.append(O.checkpoint_stats(draft["parent"], draft["layer"], draft["logp"],
+                                                      cfg.ckpt_layers, cfg.keep))
             pr = O.prune_tree(draft["parent"], draft["layer"], draft["logp"], cfg.ckpt_layers, cfg.tau,
-                              cfg.keep, want_cum=True, node_tau=cfg.node_tau)
+                              cfg.keep, want_cum=True, node_tau=cfg.node_tau, log_thr=self.log_thr)
             ret = O.retrieve_tree(self.table, self.roots, pr["n_keep"], cfg.slots, self.tpl)
         else:
             pr = O.prune_tail(draft["conf"], cfg.tail_thr)

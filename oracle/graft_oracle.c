@@ -53,7 +53,9 @@ void oracle_set_threads(int n) {
 /* cum[i] = cum[parent] + logp[i] in fp32 (root contributes 0): the log of   */
 /* the product of draft probabilities along the path.  Checkpoint s at draft */
 /* layer c_s (layer 0 = the root's children) fires when the best cumulative  */
-/* confidence on that layer is below ln(tau_s).  Checkpoints are taken in    */
+/* confidence on that layer is below log_thr[s] = (float) ln tau_s (taken   */
+/* by the caller: tau 0 gives -inf, never fires; +inf always fires).         */
+/* Checkpoints are taken in                                                  */
 /* drafting order; the first that fires decides the stage.  Readings: a      */
 /* checkpoint whose layer is empty, or whose layers 0..c_s hold fewer than   */
 /* keep_s nodes, is not reached; the kept draft nodes are the keep_s nodes   */
@@ -61,12 +63,13 @@ void oracle_set_threads(int n) {
 /* node index); with no prune every draft node is kept.                      */
 /* ------------------------------------------------------------------------- */
 /* node_tau > 0 selects the per-node variant instead of the checkpoints      */
-/* (section 四's static slots, "low-confidence draft nodes are replaced"):   */
+/* (section 四's static slots, where draft nodes of low confidence give up   */
+/* their slots):                                                             */
 /* keep every node whose cumulative log-confidence is >= (float)ln node_tau, */
 /* a set closed under ancestors since confidences only fall along a path;    */
 /* stage 4 when a node was cut, else 3.                                      */
 int oracle_prune_tree(int B, int Nd, const int32_t *parent, const int32_t *layer,
-                      const float *logp, const int32_t *ckpt_layer, const double *tau,
+                      const float *logp, const int32_t *ckpt_layer, const float *log_thr,
                       const int32_t *keep_n, double node_tau, int32_t *stage, int32_t *n_keep,
                       uint8_t *keep, float *cum_out) {
     if (B < 0 || Nd <= 0) return -1;
@@ -111,8 +114,7 @@ int oracle_prune_tree(int B, int Nd, const int32_t *parent, const int32_t *layer
                 if (lay[i] <= c) upto++;
             }
             if (on_layer == 0 || upto < keep_n[s]) continue;
-            float lthr = (float)log(tau[s]);
-            if (best < lthr) st = s;
+            if (best < log_thr[s]) st = s;
         }
         int N = (st < 3) ? keep_n[st] : Nd;
         int climit = (st < 3) ? ckpt_layer[st] : 0x7fffffff;
@@ -134,6 +136,88 @@ int oracle_prune_tree(int B, int Nd, const int32_t *parent, const int32_t *layer
             for (int i = 0; i < Nd; ++i) cum_out[(size_t)b * Nd + i] = cum[i];
     }
     free(cum);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Threshold calibration (section 二: a few warm-up rounds show the spread of */
+/* confidence at each checkpoint, and the thresholds are set from it; the    */
+/* pages give no rule for turning that spread into a threshold).             */
+/*                                                                           */
+/* Readings.  The statistic recorded is the one a checkpoint compares: the   */
+/* largest cumulative log-confidence on its layer, taken on the full warm-up */
+/* draft tree for all three checkpoints (an earlier checkpoint firing does   */
+/* not hide the later ones), NaN where the checkpoint is not reached (its    */
+/* layer empty, or layers <= its layer holding fewer than keep_n[s] nodes).  */
+/* The threshold of checkpoint s is the q_s-quantile of its recorded values: */
+/* the r-th smallest of the m recorded values, r = ceil(q_s * m) in double   */
+/* (at least 1), so that the checkpoint fires (value < threshold) on fewer   */
+/* than a share q_s of the warm-up trees; q_s == 0, or nothing recorded,     */
+/* gives -inf (never fires).                                                 */
+int oracle_checkpoint_stats(int B, int Nd, const int32_t *parent, const int32_t *layer,
+                            const float *logp, const int32_t *ckpt_layer, const int32_t *keep_n,
+                            float *out) {
+    if (B < 0 || Nd <= 0) return -1;
+    float *cum = (float *)malloc(sizeof(float) * (size_t)Nd);
+    if (!cum) return -1;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parent + (size_t)b * Nd;
+        const int32_t *lay = layer + (size_t)b * Nd;
+        const float *lp = logp + (size_t)b * Nd;
+        for (int i = 0; i < Nd; ++i) {
+            if (par[i] >= i) {
+                free(cum);
+                return -1;
+            }
+            cum[i] = ((par[i] < 0) ? 0.0f : cum[par[i]]) + lp[i];
+        }
+        for (int s = 0; s < 3; ++s) {
+            int on_layer = 0, upto = 0;
+            float best = -INFINITY;
+            for (int i = 0; i < Nd; ++i) {
+                if (lay[i] == ckpt_layer[s]) {
+                    on_layer++;
+                    if (cum[i] > best) best = cum[i];
+                }
+                if (lay[i] <= ckpt_layer[s]) upto++;
+            }
+            out[(size_t)b * 3 + s] = (on_layer == 0 || upto < keep_n[s]) ? NAN : best;
+        }
+    }
+    free(cum);
+    return 0;
+}
+
+static int cmp_float(const void *a, const void *b) {
+    float x = *(const float *)a, y = *(const float *)b;
+    return (x > y) - (x < y);
+}
+
+int oracle_calibrate(int64_t n, const float *samples, const float *q, float *log_thr) {
+    if (n < 0) return -1;
+    float *vals = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+    if (!vals) return -1;
+    for (int s = 0; s < 3; ++s) {
+        if (!(q[s] >= 0.0f && q[s] <= 1.0f)) {
+            free(vals);
+            return -1;
+        }
+        int64_t m = 0;
+        for (int64_t i = 0; i < n; ++i) {
+            float v = samples[(size_t)i * 3 + s];
+            if (!isnan(v)) vals[m++] = v;
+        }
+        if (m == 0 || q[s] == 0.0f) {
+            log_thr[s] = -INFINITY;
+            continue;
+        }
+        qsort(vals, (size_t)m, sizeof(float), cmp_float);
+        int64_t r = (int64_t)ceil((double)q[s] * (double)m);
+        if (r < 1) r = 1;
+        if (r > m) r = m;
+        log_thr[s] = vals[r - 1];
+    }
+    free(vals);
     return 0;
 }
 

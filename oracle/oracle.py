@@ -31,6 +31,8 @@ def lib():
         P = C.c_void_p
         L.oracle_prune_tree.argtypes = [C.c_int, C.c_int, P, P, P, P, P, P, C.c_double, P, P, P, P]
         L.oracle_prune_tail.argtypes = [C.c_int, C.c_int, P, C.c_float, P, P, P]
+        L.oracle_checkpoint_stats.argtypes = [C.c_int, C.c_int, P, P, P, P, P, P]
+        L.oracle_calibrate.argtypes = [C.c_int64, P, P, P]
         L.oracle_template.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P]
         L.oracle_template_branching.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P]
         L.oracle_retrieve_tree.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, C.c_int, C.c_int, P, P,
@@ -71,8 +73,9 @@ def set_threads(n: int) -> None:
 
 
 def prune_tree(parent, layer, logp, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), keep=(8, 24, 40),
-               want_cum=False, node_tau=0.0):
-    """Checkpoint pruning; with node_tau > 0 the per-node variant instead (stage 4 when it cuts)."""
+               want_cum=False, node_tau=0.0, log_thr=None):
+    """Checkpoint pruning; with node_tau > 0 the per-node variant instead (stage 4 when it cuts).
+    log_thr (fp32 [3]), when given, replaces (float) ln tau, e.g. calibrated thresholds."""
     parent, layer = _i32(parent), _i32(layer)
     logp = np.ascontiguousarray(logp, dtype=np.float32)
     B, Nd = parent.shape
@@ -81,15 +84,41 @@ def prune_tree(parent, layer, logp, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), 
     keepm = np.zeros((B, Nd), np.uint8)
     cum = np.zeros((B, Nd), np.float32) if want_cum else None
     ck = _i32(ckpt_layers)
-    ta = np.ascontiguousarray(tau, dtype=np.float64)
+    lt = log_thresholds(tau) if log_thr is None else np.ascontiguousarray(log_thr, dtype=np.float32)
     kn = _i32(keep)
-    rc = lib().oracle_prune_tree(B, Nd, _p(parent), _p(layer), _p(logp), _p(ck), _p(ta), _p(kn),
+    rc = lib().oracle_prune_tree(B, Nd, _p(parent), _p(layer), _p(logp), _p(ck), _p(lt), _p(kn),
                                  float(node_tau), _p(stage), _p(n_keep), _p(keepm), _p(cum))
     _check(rc, "prune_tree")
     out = {"stage": stage, "n_keep": n_keep, "keep": keepm}
     if want_cum:
         out["cum"] = cum
     return out
+
+
+def checkpoint_stats(parent, layer, logp, ckpt_layers=(0, 1, 5), keep=(8, 24, 40)):
+    """Per request, the statistic each checkpoint compares (fp32 [B, 3], NaN where not reached)."""
+    parent, layer = _i32(parent), _i32(layer)
+    logp = np.ascontiguousarray(logp, dtype=np.float32)
+    B, Nd = parent.shape
+    out = np.zeros((B, 3), np.float32)
+    _check(lib().oracle_checkpoint_stats(B, Nd, _p(parent), _p(layer), _p(logp), _p(_i32(ckpt_layers)),
+                                         _p(_i32(keep)), _p(out)), "checkpoint_stats")
+    return out
+
+
+def calibrate(samples, q):
+    """fp32 log-thresholds [3] from warm-up statistics [n, 3] at quantile levels q [3]."""
+    samples = np.ascontiguousarray(samples, dtype=np.float32).reshape(-1, 3)
+    qa = np.ascontiguousarray(q, dtype=np.float32)
+    out = np.zeros(3, np.float32)
+    _check(lib().oracle_calibrate(samples.shape[0], _p(samples), _p(qa), _p(out)), "calibrate")
+    return out
+
+
+def log_thresholds(tau):
+    """(float) ln tau per checkpoint: tau 0 -> -inf (never fires), +inf -> +inf (always)."""
+    with np.errstate(divide="ignore"):
+        return np.log(np.asarray(tau, np.float64)).astype(np.float32)
 
 
 def prune_tail(conf, thr=0.5):

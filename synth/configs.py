@@ -39,6 +39,7 @@ class GraftConfig:
     tpl_kind: str = "chain"          # "chain" (rank chains), "branching", or "none" (no retrieval)
     tpl_beta: tuple = (1, 1)         # branching: rank charge num/den
     node_tau: float = 0.0            # > 0: per-node pruning threshold instead of the checkpoints
+    calib_q: tuple = ()              # (q0, q1, q2): thresholds from warm-up quantiles instead of tau
     tail_block: int = 16
     tail_thr: float = 0.5
     warmup_steps: int = 5

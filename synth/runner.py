@@ -9,6 +9,8 @@ Backend protocol:
     verify_update(logits_rows) -> dict with host "accept_len", "accept_idx", "bonus"
     ingest_chunk(row_tok, logits_rows) -> top-k rows (host or device)
     materialize(pool, desc) -> logits rows in the backend's own memory
+    begin_calibration() / end_calibration(q) -> fp32 log-thresholds [3]
+        (only when the workload sets calib_q)
 """
 from __future__ import annotations
 
@@ -136,6 +138,19 @@ def step(backend, wl: Workload, step_idx: int, stream_off: int = 0, record=None)
     return flat, res
 
 
+def warm_up(backend, wl: Workload, n: int):
+    """n warm-up steps on their own seed streams; with cfg.calib_q set, the
+    backend calibrates its checkpoint thresholds over them."""
+    calib = bool(wl.cfg.calib_q) and wl.cfg.mode == "tree"
+    if calib:
+        backend.begin_calibration()
+    for s in range(n):
+        step(backend, wl, s, G.WARMUP_STREAM_OFFSET)
+    if calib:
+        return backend.end_calibration(wl.cfg.calib_q)
+    return None
+
+
 def run(backend, wl: Workload, n_steps: int, warmup: int | None = None, on_step=None):
     """start + warm-up (own seed streams) + n_steps measured steps."""
     cfg = wl.cfg
@@ -143,8 +158,7 @@ def run(backend, wl: Workload, n_steps: int, warmup: int | None = None, on_step=
     w = cfg.warmup_steps if warmup is None else warmup
     if cfg.cfg_id == 4:
         w = 0 if warmup is None else warmup
-    for s in range(w):
-        step(backend, wl, s, G.WARMUP_STREAM_OFFSET)
+    warm_up(backend, wl, w)
     for s in range(n_steps):
         flat, res = step(backend, wl, s)
         if on_step is not None:

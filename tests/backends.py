@@ -37,6 +37,12 @@ class OracleBackend:
     def ingest_chunk(self, row_tok, rows):
         return self.o.ingest_chunk(row_tok, rows)
 
+    def begin_calibration(self):
+        self.o.begin_calibration()
+
+    def end_calibration(self, q):
+        return self.o.end_calibration(q)
+
 
 class HipBackend:
     """HIP path through the C-ABI; host copies of the small outputs are made for
@@ -78,3 +84,9 @@ class HipBackend:
 
     def ingest_chunk(self, row_tok, rows):
         return self.p.ingest_chunk(row_tok, rows)
+
+    def begin_calibration(self):
+        self.p.begin_calibration()
+
+    def end_calibration(self, q):
+        return self.p.end_calibration(q)
