@@ -75,6 +75,31 @@ int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const i
     return launch_status();
 }
 
+int graft_checkpoint_stats(int B, int Nd, const int32_t *d_parent, const int32_t *d_layer,
+                           const float *d_score, const graft_prune_cfg *cfg, float *out,
+                           hipStream_t stream) {
+    if (B < 0 || Nd < 1 || Nd > GRAFT_MAX_ROWS || !cfg) return GRAFT_EINVAL;
+    if (B == 0) return GRAFT_OK;
+    if (!d_parent || !d_layer || !d_score || !out) return GRAFT_EINVAL;
+    CkptStatsArgs a{B, Nd, d_parent, d_layer, d_score, {}, {}, out};
+    for (int s = 0; s < 3; ++s) {
+        a.ckpt_layer[s] = cfg->ckpt_layer[s];
+        a.keep[s] = cfg->keep[s];
+    }
+    launch_ckpt_stats(a, stream);
+    return launch_status();
+}
+
+int graft_calibrate_thresholds(int64_t n, const float *samples, const float *q, float *log_thr,
+                               hipStream_t stream) {
+    if (n < 0 || n > GRAFT_MAX_CALIB_SAMPLES || !q || !log_thr || (n > 0 && !samples)) return GRAFT_EINVAL;
+    CalibArgs a{n, samples, {q[0], q[1], q[2]}, log_thr};
+    for (int s = 0; s < 3; ++s)
+        if (!(q[s] >= 0.0f && q[s] <= 1.0f)) return GRAFT_EINVAL;  // NaN fails too
+    launch_calibrate(a, stream);
+    return launch_status();
+}
+
 int graft_template_master(int width, int depth, int cap, int32_t *parent, int32_t *rank,
                           int32_t *tdepth) {
     if (width < 1 || depth < 1 || cap < 0 || !parent || !rank || !tdepth) return GRAFT_EINVAL;

@@ -21,6 +21,21 @@ struct PruneKernelArgs {
     float *cum_out;
 };
 
+struct CkptStatsArgs {
+    int B, Nd;
+    const int32_t *parent, *layer;
+    const float *score;
+    int32_t ckpt_layer[3], keep[3];
+    float *out;  // [B, 3]
+};
+
+struct CalibArgs {
+    int64_t n;
+    const float *samples;  // [n, 3], NaN = not recorded
+    float q[3];
+    float *log_thr;        // [3]
+};
+
 struct RetrieveKernelArgs {
     int B, V, k, mode, slots;
     const int32_t *table, *root_tok, *n_keep, *d_tok;
@@ -62,6 +77,8 @@ struct BuildKernelArgs {
 };
 
 void launch_prune(const PruneKernelArgs &a, hipStream_t s);
+void launch_ckpt_stats(const CkptStatsArgs &a, hipStream_t s);
+void launch_calibrate(const CalibArgs &a, hipStream_t s);
 void launch_retrieve(const RetrieveKernelArgs &a, hipStream_t s);
 void launch_flatten(const FlattenKernelArgs &a, hipStream_t s);
 void launch_build(const BuildKernelArgs &a, hipStream_t s);

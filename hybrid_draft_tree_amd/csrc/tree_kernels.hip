@@ -34,8 +34,7 @@ struct PruneOut {
 // parent's value is final when read (the association of the definition);
 // checkpoints in drafting order, the first that fires is the stage; keep the
 // N nodes of layers <= c_s with the largest cum (ties -> lower index).
-__device__ __forceinline__ PruneOut prune_tree_wave(bool valid, int par, int lay, float lp, int Nd,
-                                                   const graft_prune_cfg &cfg) {
+__device__ __forceinline__ float cum_levels(bool valid, int par, float lp) {
     const int lane = lane_id();
     // one level per pass: a node is done once its parent is (root children first)
     bool done = valid && par < 0;
@@ -53,6 +52,12 @@ __device__ __forceinline__ PruneOut prune_tree_wave(bool valid, int par, int lay
         if (left == todo) break;  // a parent link that never resolves (bad input)
         todo = left;
     }
+    return cum;
+}
+
+__device__ __forceinline__ PruneOut prune_tree_wave(bool valid, int par, int lay, float lp, int Nd,
+                                                   const graft_prune_cfg &cfg) {
+    const float cum = cum_levels(valid, par, lp);
     // order-preserving integer keys (-0 == +0): integer max and compares
     const int key = f32_key(__float_as_uint(cum));
     if (cfg.node_mode) {
@@ -318,6 +323,81 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_prune(PruneKernelArgs a
     }
 }
 
+// Warm-up statistic of every checkpoint (the value its test compares): the
+// largest cumulative log-confidence on its layer, NaN where the checkpoint is
+// not reached; all three are taken on the full tree.
+__global__ __launch_bounds__(kWave *kReqPerBlock) void k_ckpt_stats(CkptStatsArgs a) {
+    const int lane = lane_id();
+    const int b = blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
+    if (b >= a.B) return;
+    const bool valid = lane < a.Nd;
+    const size_t o = (size_t)b * a.Nd + lane;
+    const int par = valid ? a.parent[o] : -1;
+    const int lay = valid ? a.layer[o] : 0x7fffffff;
+    const float lp = valid ? a.score[o] : 0.0f;
+    const int key = f32_key(__float_as_uint(cum_levels(valid, par, lp)));
+    float mine = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        const int c = a.ckpt_layer[s];
+        const int on = __popcll(ballot(valid && lay == c));
+        const int upto = __popcll(ballot(valid && lay <= c));
+        const int best = wave_max_i32((valid && lay == c) ? key : INT_MIN);
+        if (lane == s) mine = (on > 0 && upto >= a.keep[s]) ? key_to_f32(best) : __int_as_float(0x7fc00000);
+    }
+    if (lane < 3) a.out[(size_t)b * 3 + lane] = mine;
+}
+
+constexpr int kCalibThreads = 256;
+
+// Number of recorded (non-NaN) samples of column s whose order-preserving
+// unsigned key u has (u & mask) == want; block-wide, every thread gets it.
+__device__ int calib_count(const float *__restrict__ x, int64_t n, int s, uint32_t mask, uint32_t want,
+                           int *s_cnt) {
+    int c = 0;
+    for (int64_t i = threadIdx.x; i < n; i += kCalibThreads) {
+        const float v = x[i * 3 + s];
+        if (v == v) {
+            const uint32_t u = (uint32_t)f32_key(__float_as_uint(v)) ^ 0x80000000u;
+            c += (u & mask) == want ? 1 : 0;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    __syncthreads();  // every thread has read the previous total
+    if (threadIdx.x == 0) *s_cnt = 0;
+    __syncthreads();
+    if (lane_id() == 0) atomicAdd(s_cnt, c);
+    __syncthreads();
+    return *s_cnt;
+}
+
+// Threshold of checkpoint s = blockIdx.x: the r-th smallest recorded sample,
+// r = ceil(q * m) (m recorded), found bit by bit on the unsigned key image
+// (32 block-wide counts); -inf when q == 0 or nothing was recorded.
+__global__ __launch_bounds__(kCalibThreads) void k_calibrate(CalibArgs a) {
+    __shared__ int s_cnt;
+    const int s = blockIdx.x;
+    const float q = a.q[s];
+    const int64_t m = calib_count(a.samples, a.n, s, 0u, 0u, &s_cnt);
+    if (q == 0.0f || m == 0) {
+        if (threadIdx.x == 0) a.log_thr[s] = -__builtin_huge_valf();
+        return;
+    }
+    int64_t r = (int64_t)ceil((double)q * (double)m);
+    r = r < 1 ? 1 : (r > m ? m : r);
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t mask = ~0u << bit;
+        const int64_t c0 = calib_count(a.samples, a.n, s, mask, T, &s_cnt);
+        if (r > c0) {
+            r -= c0;
+            T |= 1u << bit;
+        }
+    }
+    if (threadIdx.x == 0) a.log_thr[s] = key_to_f32((int32_t)(T ^ 0x80000000u));
+}
+
 __global__ __launch_bounds__(kWave *kReqPerBlock) void k_retrieve(RetrieveKernelArgs a) {
     const int lane = lane_id();
     const int b = blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
@@ -486,6 +566,15 @@ static inline int blocks_for(int B) { return (B + kReqPerBlock - 1) / kReqPerBlo
 void launch_prune(const PruneKernelArgs &a, hipStream_t s) {
     if (a.B <= 0) return;
     hipLaunchKernelGGL(k_prune, dim3(blocks_for(a.B)), dim3(kWave * kReqPerBlock), 0, s, a);
+}
+
+void launch_ckpt_stats(const CkptStatsArgs &a, hipStream_t s) {
+    if (a.B <= 0) return;
+    hipLaunchKernelGGL(k_ckpt_stats, dim3(blocks_for(a.B)), dim3(kWave * kReqPerBlock), 0, s, a);
+}
+
+void launch_calibrate(const CalibArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(k_calibrate, dim3(3), dim3(kCalibThreads), 0, s, a);
 }
 
 void launch_retrieve(const RetrieveKernelArgs &a, hipStream_t s) {

@@ -111,6 +111,8 @@ class GraftPipeline:
         self.ws_bytes = L.graft_workspace_bytes(B * T1, self.V, self.k, self.dtype)
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
         self._ingest_ws = None
+        self._calib = None          # warm-up checkpoint statistics [steps * B, 3] while calibrating
+        self._calib_rows = 0
 
     @classmethod
     def from_config(cls, cfg, want_prob=False, want_coverage=False, device="cuda", fused=True):
@@ -154,6 +156,8 @@ class GraftPipeline:
         if bufs is None:
             bufs = {"parent": self.d_parent, "layer": self.d_layer, "score": self.d_score, "tok": self.d_tok}
         d_parent, d_layer, d_score, d_tok = bufs["parent"], bufs["layer"], bufs["score"], bufs["tok"]
+        if self._calib is not None:
+            self._record_stats(d_parent, d_layer, d_score)
         if self.fused:
             L.graft_build_hybrid_tree(
                 B, Nd, T1, self.mode, self.layout, self.slots, self.cfg, self.tpl, self.V, self.k,
@@ -180,6 +184,35 @@ class GraftPipeline:
                                 self.ret_parent.data_ptr(), self.n_ret.data_ptr(), self.r_out,
                                 self.tok.data_ptr(), self.parent.data_ptr(), self.depth.data_ptr(),
                                 self.pos_id.data_ptr(), self.anc.data_ptr(), self._ptr(self.row_src), s)
+
+    # ------------------------------------------------------------------ threshold calibration
+    def begin_calibration(self, max_steps=64):
+        """Record the checkpoint statistics of every tree built from now on (up to
+        max_steps builds) for end_calibration()."""
+        if self.mode != L.MODE_TREE:
+            raise ValueError("threshold calibration applies to TREE pruning")
+        self._calib = torch.full((max_steps * self.B, 3), float("nan"), dtype=torch.float32,
+                                 device=self.device)
+        self._calib_rows = 0
+
+    def _record_stats(self, d_parent, d_layer, d_score):
+        if self._calib_rows + self.B > self._calib.shape[0]:
+            raise RuntimeError("more calibration steps than begin_calibration(max_steps) allows")
+        out = self._calib[self._calib_rows:self._calib_rows + self.B]
+        L.graft_checkpoint_stats(self.B, self.Nd, d_parent.data_ptr(), d_layer.data_ptr(), d_score.data_ptr(),
+                                 self.cfg, out.data_ptr(), self.stream())
+        self._calib_rows += self.B
+
+    def end_calibration(self, q):
+        """Set the checkpoint thresholds to the q-quantiles of the recorded
+        statistics (graft_calibrate_thresholds); returns them (fp32 ln tau)."""
+        thr = torch.empty(3, dtype=torch.float32, device=self.device)
+        L.graft_calibrate_thresholds(self._calib_rows, self._calib.data_ptr(), q, thr.data_ptr(), self.stream())
+        host = thr.cpu().numpy()
+        for s in range(3):
+            self.cfg.log_thr[s] = float(host[s])
+        self._calib = None
+        return host
 
     def build(self, draft):
         self.load_draft(draft)

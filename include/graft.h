@@ -112,6 +112,35 @@ int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const i
                        const float *d_score, const graft_prune_cfg *cfg, int32_t *stage,
                        int32_t *n_keep, uint8_t *keep, float *cum_out, hipStream_t stream);
 
+/* Threshold calibration -- section 二, gear 1: the checkpoint thresholds are
+ * set from the confidence the drafter shows at each checkpoint over a few
+ * warm-up rounds.  The pages give no rule; the one here is a quantile.
+ *
+ * graft_checkpoint_stats: per request b and checkpoint s, out[b, s] = the
+ *   largest cumulative log-confidence (cum as in graft_prune_select) on layer
+ *   cfg->ckpt_layer[s], or NaN when that checkpoint is not reached (its layer
+ *   is empty, or layers <= it hold fewer than cfg->keep[s] nodes).  All three
+ *   are taken on the full tree, whether or not an earlier checkpoint would
+ *   fire.  d_parent, d_layer int32 [B, Nd], d_score fp32 [B, Nd], out fp32
+ *   [B, 3], all device; cfg host (only ckpt_layer and keep are read).
+ *   Requires 1 <= Nd <= 64, B >= 0 (B == 0 enqueues nothing).
+ *
+ * graft_calibrate_thresholds: for each checkpoint s, log_thr[s] = the r-th
+ *   smallest of the m non-NaN values in column s of samples, r = ceil(q[s] * m)
+ *   computed in double (clamped to [1, m]), so the checkpoint fires
+ *   (statistic < log_thr[s]) on fewer than a share q[s] of the samples;
+ *   -inf (never fires) when q[s] == 0 or m == 0.  -0 and +0 count as one
+ *   value (returned as +0).  samples fp32 [n, 3] device (rows of
+ *   graft_checkpoint_stats outputs, NaN = not recorded); q host fp32 [3], each
+ *   in [0, 1]; log_thr fp32 [3] device, ready for graft_prune_cfg.log_thr.
+ *   0 <= n <= GRAFT_MAX_CALIB_SAMPLES.  One launch of 3 workgroups. */
+#define GRAFT_MAX_CALIB_SAMPLES (1 << 26)
+int graft_checkpoint_stats(int B, int Nd, const int32_t *d_parent, const int32_t *d_layer,
+                           const float *d_score, const graft_prune_cfg *cfg, float *out,
+                           hipStream_t stream);
+int graft_calibrate_thresholds(int64_t n, const float *samples, const float *q, float *log_thr,
+                               hipStream_t stream);
+
 /* graft_template_master -- host only; section 二's stage-adaptive asymmetric
  * template and section 五's depth/width optimum (8, 8).  Writes the master
  * order into HOST arrays of capacity `cap`: the `width` children of the root

@@ -239,6 +239,74 @@ def test_prune_small_trees_and_unreached_checkpoints():
     np.testing.assert_array_equal(nk, o["n_keep"])
 
 
+def gpu_ckpt_stats(parent, layer, score, ckpt=(0, 1, 5), keep=(8, 24, 40)):
+    B, Nd = score.shape
+    cfg = L.prune_cfg(ckpt, [0.0, 0.0, 0.0], keep, 0.5)
+    dp, dl, ds = _t(parent, torch.int32), _t(layer, torch.int32), _t(score, torch.float32)
+    out = torch.full((B, 3), -7.0, dtype=torch.float32, device=DEV)
+    L.graft_checkpoint_stats(B, Nd, dp.data_ptr(), dl.data_ptr(), ds.data_ptr(), cfg, out.data_ptr(), _s())
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_checkpoint_stats_parity():
+    rng = np.random.default_rng(21)
+    B = 67
+    par, lay, _ = TOPO
+    lp = _random_logp(rng, B)
+    lp[3, :] = np.float32(math.log(0.7))              # ties across a whole layer
+    lp[4, lay == 1] = -np.inf                          # probability 0 below layer 0
+    lp[5, :] = 0.0                                     # probability 1 everywhere
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    got = gpu_ckpt_stats(P, Ly, lp)
+    want = O.checkpoint_stats(P, Ly, lp)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert not np.isnan(got).any()
+    # unreached checkpoints: layer 5 absent; too few nodes up to layer 1 for keep 9
+    par_s = np.array([-1, -1, 0, 0, 1, 2, 2, 3], np.int32)
+    lay_s = np.array([0, 0, 1, 1, 1, 2, 2, 2], np.int32)
+    Bs = 20
+    lps = np.log(rng.uniform(0.01, 1.0, size=(Bs, 8))).astype(np.float32)
+    for keep in [(2, 5, 6), (2, 9, 6), (3, 5, 6)]:
+        Ps, Ls = np.tile(par_s, (Bs, 1)), np.tile(lay_s, (Bs, 1))
+        got = gpu_ckpt_stats(Ps, Ls, lps, keep=keep)
+        want = O.checkpoint_stats(Ps, Ls, lps, keep=keep)
+        np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+        assert np.isnan(got[:, 2]).all()
+
+
+def gpu_calibrate(samples, q):
+    n = samples.shape[0]
+    x = _t(samples if n else np.zeros((1, 3), np.float32), torch.float32)
+    out = torch.full((3,), 7.0, dtype=torch.float32, device=DEV)
+    L.graft_calibrate_thresholds(n, x.data_ptr(), q, out.data_ptr(), _s())
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [0, 1, 5, 80, 1000, 300_000])
+def test_calibrate_parity(n):
+    rng = np.random.default_rng(100 + n)
+    x = (rng.standard_normal((n, 3)) * 3).astype(np.float32)
+    x[:, 1] = np.round(x[:, 1] * 4) / 4                 # many ties
+    if n >= 5:
+        x[: n // 5, 2] = -np.inf
+        x[n // 5: n // 5 + 2, 2] = np.inf
+        x[-1, 0] = 0.0
+    x[rng.random((n, 3)) < 0.2] = np.nan
+    for q in [(0.0, 0.2, 1.0), (1e-6, 0.5, 0.3), (0.25, 0.25, 0.25), (1.0, 1.0, 1.0), (0.1, 0.9, 0.05)]:
+        got = gpu_calibrate(x, q)
+        want = O.calibrate(x, q)
+        np.testing.assert_array_equal(got, want, err_msg="n=%d q=%s" % (n, q))
+
+
+def test_calibrate_all_nan_and_constant_columns():
+    x = np.full((50, 3), np.nan, np.float32)
+    x[:, 1] = -2.5
+    got = gpu_calibrate(x, (0.5, 0.5, 0.0))
+    np.testing.assert_array_equal(got, [-np.inf, -2.5, -np.inf])
+
+
 def test_prune_tail_parity():
     rng = np.random.default_rng(12)
     B = 40

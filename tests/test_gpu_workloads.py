@@ -33,7 +33,15 @@ def _compare_runs(cfg, n_steps, warmup, table_every=1, fused=True, want_prob=Fal
     np.testing.assert_array_equal(hb.get_table(), ob.get_table())
     np.testing.assert_array_equal(hb.get_roots(), ob.get_roots())
     stats = {"accepted": 0, "stages": set()}
+    calib = bool(cfg.calib_q) and cfg.mode == "tree"
+    if calib:
+        ob.begin_calibration()
+        hb.begin_calibration()
     for s in range(warmup + n_steps):
+        if calib and s == warmup:
+            to, th = ob.end_calibration(cfg.calib_q), hb.end_calibration(cfg.calib_q)
+            np.testing.assert_array_equal(th, to, err_msg="calibrated thresholds")
+            stats["log_thr"] = to
         off = G.WARMUP_STREAM_OFFSET if s < warmup else 0
         idx = s if s < warmup else s - warmup
         fo, ro = R.step(ob, wl_o, idx, off)
@@ -119,6 +127,17 @@ def test_lockstep_ablation_variants(kw, fused):
     cfg = _small(3, V=20000, B=8, **kw)
     st = _compare_runs(cfg, 10, warmup=cfg.warmup_steps, fused=fused)
     assert st["accepted"] > 0
+
+
+@pytest.mark.parametrize("q", [(0.2, 0.2, 0.2), (0.5, 0.3, 0.1)])
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "five_calls"])
+def test_lockstep_calibrated_thresholds(q, fused):
+    """Thresholds calibrated on the warm-up steps (each side its own statistics
+    and quantiles) agree bit for bit, and the later steps prune with them."""
+    cfg = _small(3, V=20000, B=16, calib_q=q)
+    st = _compare_runs(cfg, 10, warmup=cfg.warmup_steps, fused=fused)
+    assert st["accepted"] > 0 and np.isfinite(st["log_thr"]).all()
+    assert len(st["stages"]) >= 2
 
 
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "five_calls"])

@@ -60,6 +60,25 @@ def test_template_matches_oracle(W, D, R):
     assert dp == o["depth"].tolist()
 
 
+def test_calibration_validation_rejects_without_launch():
+    cfg = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 40), 0.5)
+    lib = L.load()
+    P = 0x1000  # never dereferenced
+    q = (ctypes.c_float * 3)
+    ok = q(0.2, 0.2, 0.2)
+    assert lib.graft_checkpoint_stats(1, 65, P, P, P, ctypes.byref(cfg), P, None) == L.GRAFT_EINVAL
+    assert lib.graft_checkpoint_stats(1, 0, P, P, P, ctypes.byref(cfg), P, None) == L.GRAFT_EINVAL
+    assert lib.graft_checkpoint_stats(1, 60, P, P, P, None, P, None) == L.GRAFT_EINVAL
+    assert lib.graft_checkpoint_stats(1, 60, P, None, P, ctypes.byref(cfg), P, None) == L.GRAFT_EINVAL
+    assert lib.graft_checkpoint_stats(0, 60, None, None, None, ctypes.byref(cfg), None, None) == L.GRAFT_OK
+    for bad in [q(1.5, 0.2, 0.2), q(0.2, -0.1, 0.2), q(0.2, 0.2, float("nan"))]:
+        assert lib.graft_calibrate_thresholds(10, P, ctypes.byref(bad), P, None) == L.GRAFT_EINVAL
+    assert lib.graft_calibrate_thresholds(-1, P, ctypes.byref(ok), P, None) == L.GRAFT_EINVAL
+    assert lib.graft_calibrate_thresholds((1 << 26) + 1, P, ctypes.byref(ok), P, None) == L.GRAFT_EINVAL
+    assert lib.graft_calibrate_thresholds(10, None, ctypes.byref(ok), P, None) == L.GRAFT_EINVAL
+    assert lib.graft_calibrate_thresholds(10, P, ctypes.byref(ok), None, None) == L.GRAFT_EINVAL
+
+
 def test_host_validation_rejects_without_launch():
     cfg = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 40), 0.5)
     lib = L.load()
