@@ -26,7 +26,9 @@ speed: mean accepted length per step on workloads 2 and 4 for rank-chain and
 branching templates over a grid of depths and widths (one JSON line per point).
 A third, ``--ablation``, compares the pruning/retrieval variants of the
 write-up's ablations (no retrieval, fixed splits, a dense tree, per-node
-thresholds) with the adaptive default on workloads 2, 3 and 4.
+thresholds) with the adaptive default on workloads 2, 3 and 4.  A fourth,
+``--calibration``, sets the thresholds from warm-up quantiles and moves them
+between workloads.
 """
 from __future__ import annotations
 
@@ -71,6 +73,8 @@ def parse():
     ap.add_argument("--ablation", action="store_true",
                     help="accept length of the pruning/retrieval variants (no timing)")
     ap.add_argument("--ablation-configs", default="2,3,4")
+    ap.add_argument("--calibration", action="store_true",
+                    help="calibrated thresholds vs quantile level, and their transfer across workloads")
     return ap.parse_args()
 
 
@@ -108,6 +112,13 @@ class _Adapter:
     def ingest_chunk(self, row_tok, rows):
         return self.p.ingest_chunk(row_tok, rows)
 
+    def begin_calibration(self):
+        self.p.begin_calibration()
+
+    def end_calibration(self, q):
+        self.samples = self.p.calibration_samples().cpu().numpy()
+        return self.p.end_calibration(q)
+
 
 def kernel_source_hash():
     h = hashlib.sha256()
@@ -130,10 +141,12 @@ def load_traffic(bytes_alg):
     return d.get("hbm_bytes_per_launch"), d.get("note", "")
 
 
-def _accept_run(cfg, steps, dev):
+def _accept_run(cfg, steps, dev, warmup=None, log_thr=None):
     """One fresh pipeline through the workload's warm-up and `steps` steps:
     accepted tokens per request-step, the share of request-steps that retrieved
-    anything, whose accepted path reaches a retrieved row, and the coverage gain."""
+    anything, whose accepted path reaches a retrieved row, and the coverage gain.
+    With cfg.calib_q the thresholds are calibrated over the warm-up; log_thr
+    (fp32 ln tau) replaces them after the warm-up instead."""
     import numpy as np
     import torch
 
@@ -146,9 +159,14 @@ def _accept_run(cfg, steps, dev):
     ad = _Adapter(pipe, torch)
     wl = R.Workload(cfg)
     R.start(ad, wl)
-    for s in range(cfg.warmup_steps if cfg.cfg_id != 4 else 0):
-        R.step(ad, wl, s, G.WARMUP_STREAM_OFFSET)
+    if warmup is None:
+        warmup = cfg.warmup_steps if cfg.cfg_id != 4 else 0
+    thr = R.warm_up(ad, wl, warmup)
+    if log_thr is not None:
+        for i in range(3):
+            pipe.cfg.log_thr[i] = float(log_thr[i])
     acc = via_ret = n = with_ret = kept = 0
+    stages = np.zeros(5, np.int64)
     gain = 0.0
     for s in range(steps):
         flat, res = R.step(ad, wl, s)
@@ -160,12 +178,22 @@ def _accept_run(cfg, steps, dev):
         acc += int(alen.sum())
         with_ret += int((np.asarray(flat["n_ret"]) > 0).sum())
         kept += int(np.asarray(flat["n_keep"]).sum())
+        stages += np.bincount(np.asarray(flat["stage"]), minlength=5)[:5]
         gain += float(np.asarray(res["coverage"]).sum())
         n += cfg.B
     out = {"template_nodes": int(pipe.tpl.size) if pipe.tpl is not None else 0, "steps": steps, "requests": cfg.B,
            "mean_accept_len": round(acc / n, 4), "tokens_per_step": round(acc / n + 1, 4),
            "mean_draft_kept": round(kept / n, 2), "steps_with_retrieval": round(with_ret / n, 4),
-           "accepted_via_retrieval": round(via_ret / n, 4), "mean_coverage_gain": round(gain / n, 5)}
+           "accepted_via_retrieval": round(via_ret / n, 4), "mean_coverage_gain": round(gain / n, 5),
+           "stage_share": [round(float(x) / n, 4) for x in stages[:4]],
+           "log_thr": [float(pipe.cfg.log_thr[i]) for i in range(3)]}
+    if thr is not None:
+        out["calibrated_tau"] = [round(float(np.exp(np.float64(t))), 5) for t in thr]
+        # where the workload's fixed thresholds sit in the warm-up statistics
+        smp = ad.samples
+        lt = np.log(np.asarray(cfg.tau, np.float64)).astype(np.float32)
+        out["fixed_tau_quantile"] = [round(float((smp[:, i][~np.isnan(smp[:, i])] < lt[i]).mean()), 4)
+                                     for i in range(3)]
     del pipe, ad
     torch.cuda.empty_cache()
     return out
@@ -195,6 +223,50 @@ def ablation(args):
             rec.update(_accept_run(base.scaled(**kw), args.sweep_steps, dev))
             rec["seconds"] = round(time.time() - t0, 1)
             print(json.dumps(rec), flush=True)
+
+
+def calibration(args):
+    """Thresholds calibrated over 5 warm-up steps at quantile levels q, the
+    accept length they give, where the fixed thresholds (0.3, 0.2, 0.1) sit in
+    the same warm-up statistics, and transfer: the thresholds of one workload
+    applied to another (the write-up's cross-task table).  No timing."""
+    import math
+
+    import numpy as np
+    import torch
+
+    from synth import CONFIGS
+
+    assert torch.cuda.is_available(), "the calibration study runs on the GPU"
+    dev = torch.device("cuda", 0)
+    ids = [int(x) for x in args.ablation_configs.split(",")]
+    levels = [(0.1, 0.1, 0.1), (0.25, 0.25, 0.25), (0.5, 0.5, 0.5), (0.75, 0.75, 0.75),
+              (0.1, 0.4, 0.9), (0.1, 0.5, 0.97)]
+    own = {}
+    for cfg_id in ids:
+        base = CONFIGS[cfg_id]
+        fixed = [float(np.float32(math.log(t))) for t in base.tau]
+        rec = {"calibration": "fixed tau %s" % (base.tau,), "workload": base.name}
+        # calibrate only to record the statistics; the fixed thresholds are kept
+        rec.update(_accept_run(base.scaled(calib_q=(0.5, 0.5, 0.5)), args.sweep_steps, dev,
+                               warmup=base.warmup_steps, log_thr=fixed))
+        rec.pop("calibrated_tau", None)
+        print(json.dumps(rec), flush=True)
+        for q in levels:
+            rec = {"calibration": "q=%s" % (q,), "workload": base.name}
+            rec.update(_accept_run(base.scaled(calib_q=q), args.sweep_steps, dev, warmup=base.warmup_steps))
+            own[(cfg_id, q)] = rec["log_thr"]
+            print(json.dumps(rec), flush=True)
+    for q in [levels[2], levels[5]]:
+        for src in ids:
+            for dst in ids:
+                if src == dst:
+                    continue
+                rec = {"calibration": "q=%s transferred" % (q,), "from": CONFIGS[src].name,
+                       "workload": CONFIGS[dst].name}
+                rec.update(_accept_run(CONFIGS[dst], args.sweep_steps, dev, warmup=CONFIGS[dst].warmup_steps,
+                                       log_thr=own[(src, q)]))
+                print(json.dumps(rec), flush=True)
 
 
 def template_sweep(args):
@@ -232,6 +304,8 @@ def main():
         return template_sweep(args)
     if args.ablation:
         return ablation(args)
+    if args.calibration:
+        return calibration(args)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build measures the single-GPU Graft "
               "step (no collectives); run with --gpus 1", file=sys.stderr)

@@ -203,6 +203,10 @@ class GraftPipeline:
                                  self.cfg, out.data_ptr(), self.stream())
         self._calib_rows += self.B
 
+    def calibration_samples(self):
+        """The checkpoint statistics recorded so far (device fp32 [n, 3], NaN = not reached)."""
+        return self._calib[:self._calib_rows]
+
     def end_calibration(self, q):
         """Set the checkpoint thresholds to the q-quantiles of the recorded
         statistics (graft_calibrate_thresholds); returns them (fp32 ln tau)."""
