@@ -30,7 +30,7 @@ MAX_K = 8
 EXPORTS = (
     "graft_prune_select", "graft_checkpoint_stats", "graft_calibrate_thresholds", "graft_template_master", "graft_template_branching", "graft_retrieve_expand",
     "graft_build_tree_mask", "graft_verify_accept", "graft_update_topk",
-    "graft_build_hybrid_tree", "graft_verify_update", "graft_coverage_gain",
+    "graft_build_hybrid_tree", "graft_build_after_retrieval", "graft_verify_update", "graft_coverage_gain",
     "graft_workspace_bytes", "graft_status_string",
 )
 
@@ -78,6 +78,8 @@ def load():
     L.graft_update_topk.argtypes = [I64, I, I, I, P, P, P, P, P, P, P, P, S, P]
     L.graft_build_hybrid_tree.argtypes = [I, I, I, I, I, I, C.POINTER(PruneCfg), C.POINTER(Template), I, I,
                                           P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P]
+    L.graft_build_after_retrieval.argtypes = [I, I, I, I, I, C.POINTER(PruneCfg), P, P, P, P, P, P, P, P, P, P,
+                                              P, P, P, I, P, P, P, P, P, P, P]
     L.graft_verify_update.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
     L.graft_coverage_gain.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
     L.graft_workspace_bytes.argtypes = [I64, I, I, I]
@@ -182,6 +184,15 @@ def graft_build_hybrid_tree(B, Nd, T1, mode, layout, slots, cfg, tpl, V, k, tabl
         B, Nd, T1, mode, layout, slots, C.byref(cfg), C.byref(tpl) if tpl is not None else None, V, k,
         table, root_tok, base_pos, d_parent, d_layer, d_score, d_tok, stage, n_keep, keep, cum_out,
         ret_tok, ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, row_src, stream))
+
+
+def graft_build_after_retrieval(B, Nd, T1, layout, slots, cfg, root_tok, base_pos, d_parent, d_layer, d_score,
+                                d_tok, stage, n_keep, keep, cum_out, ret_tok, ret_parent, n_ret, r_out, tok, parent,
+                                depth, pos_id, anc, row_src, stream):
+    return _chk("graft_build_after_retrieval", load().graft_build_after_retrieval(
+        B, Nd, T1, layout, slots, C.byref(cfg), root_tok, base_pos, d_parent, d_layer, d_score, d_tok, stage,
+        n_keep, keep, cum_out, ret_tok, ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, row_src,
+        stream))
 
 
 def graft_verify_update(B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob,

@@ -179,7 +179,8 @@ int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_
         r_out > GRAFT_MAX_ROWS)
         return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
-    if (!table || !root_tok || !n_keep || !ret_tok || !ret_parent || !n_ret) return GRAFT_EINVAL;
+    if (!table || !root_tok || !ret_tok || !ret_parent || !n_ret) return GRAFT_EINVAL;
+    if (!n_keep && mode != GRAFT_MODE_TREE) return GRAFT_EINVAL;
     int tsize = 0;
     const int32_t *tp = nullptr, *tr = nullptr, *td = nullptr;
     if (mode == GRAFT_MODE_TREE) {
@@ -226,14 +227,14 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
     return launch_status();
 }
 
-int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slots,
-                            const graft_prune_cfg *cfg, const graft_template *tpl, int V, int k,
-                            const int32_t *table, const int32_t *root_tok, const int32_t *base_pos,
-                            const int32_t *d_parent, const int32_t *d_layer, const float *d_score,
-                            const int32_t *d_tok, int32_t *stage, int32_t *n_keep, uint8_t *keep,
-                            float *cum_out, int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret,
-                            int r_out, int32_t *tok, int32_t *parent, int32_t *depth, int32_t *pos_id,
-                            uint64_t *anc, uint8_t *row_src, hipStream_t stream) {
+namespace {
+
+int build_tree(int B, int Nd, int T1, int mode, int layout, int slots, const graft_prune_cfg *cfg,
+               const graft_template *tpl, int V, int k, const int32_t *table, const int32_t *root_tok,
+               const int32_t *base_pos, const int32_t *d_parent, const int32_t *d_layer, const float *d_score,
+               const int32_t *d_tok, int32_t *stage, int32_t *n_keep, uint8_t *keep, float *cum_out,
+               int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret, int r_out, int32_t *tok, int32_t *parent,
+               int32_t *depth, int32_t *pos_id, uint64_t *anc, uint8_t *row_src, bool pre, hipStream_t stream) {
     if (mode != GRAFT_MODE_TREE && mode != GRAFT_MODE_TAIL) return GRAFT_EUNSUPPORTED;
     if (layout != GRAFT_LAYOUT_COMPACT && layout != GRAFT_LAYOUT_IN_PLACE && layout != GRAFT_LAYOUT_CHAIN)
         return GRAFT_EUNSUPPORTED;
@@ -244,12 +245,17 @@ int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slo
     if (T1 != slots + 1) return GRAFT_EINVAL;
     if (layout == GRAFT_LAYOUT_IN_PLACE && T1 != Nd + 1) return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
-    if (!table || !root_tok || !base_pos || !d_score || !d_tok || !stage || !n_keep || !keep ||
+    if ((!pre && !table) || !root_tok || !base_pos || !d_score || !d_tok || !stage || !n_keep || !keep ||
         !ret_tok || !ret_parent || !n_ret || !tok || !parent || !depth || !pos_id || !anc)
         return GRAFT_EINVAL;
     if (!aligned(anc, 8)) return GRAFT_EINVAL;
     BuildKernelArgs a{};
-    if (mode == GRAFT_MODE_TREE) {
+    if (pre) {
+        if (!d_parent || !d_layer) return GRAFT_EINVAL;
+        for (int s = 0; s < 3; ++s)
+            if (cfg->keep[s] < 0 || cfg->keep[s] > Nd || slots - cfg->keep[s] < 0) return GRAFT_EINVAL;
+        a.pre = 1;
+    } else if (mode == GRAFT_MODE_TREE) {
         if (!d_parent || !d_layer || !tpl || tpl->size < 0 || tpl->size > GRAFT_MAX_ROWS) return GRAFT_EINVAL;
         if (tpl->size > 0 && (!tpl->parent || !tpl->rank || !tpl->depth)) return GRAFT_EINVAL;
         if (r_out < tpl->size) return GRAFT_EINVAL;
@@ -294,6 +300,35 @@ int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slo
     a.row_src = row_src;
     launch_build(a, stream);
     return launch_status();
+}
+
+}  // namespace
+
+int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slots,
+                            const graft_prune_cfg *cfg, const graft_template *tpl, int V, int k,
+                            const int32_t *table, const int32_t *root_tok, const int32_t *base_pos,
+                            const int32_t *d_parent, const int32_t *d_layer, const float *d_score,
+                            const int32_t *d_tok, int32_t *stage, int32_t *n_keep, uint8_t *keep,
+                            float *cum_out, int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret,
+                            int r_out, int32_t *tok, int32_t *parent, int32_t *depth, int32_t *pos_id,
+                            uint64_t *anc, uint8_t *row_src, hipStream_t stream) {
+    return build_tree(B, Nd, T1, mode, layout, slots, cfg, tpl, V, k, table, root_tok, base_pos, d_parent,
+                      d_layer, d_score, d_tok, stage, n_keep, keep, cum_out, ret_tok, ret_parent, n_ret, r_out,
+                      tok, parent, depth, pos_id, anc, row_src, false, stream);
+}
+
+int graft_build_after_retrieval(int B, int Nd, int T1, int layout, int slots, const graft_prune_cfg *cfg,
+                                const int32_t *root_tok, const int32_t *base_pos, const int32_t *d_parent,
+                                const int32_t *d_layer, const float *d_score, const int32_t *d_tok,
+                                int32_t *stage, int32_t *n_keep, uint8_t *keep, float *cum_out,
+                                int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret, int r_out, int32_t *tok,
+                                int32_t *parent, int32_t *depth, int32_t *pos_id, uint64_t *anc,
+                                uint8_t *row_src, hipStream_t stream) {
+    if (layout == GRAFT_LAYOUT_CHAIN) return GRAFT_EUNSUPPORTED;  // TAIL retrieval follows the prune
+    // the table and vocabulary are not read: the retrieval is done
+    return build_tree(B, Nd, T1, GRAFT_MODE_TREE, layout, slots, cfg, nullptr, 1, 1, nullptr, root_tok,
+                      base_pos, d_parent, d_layer, d_score, d_tok, stage, n_keep, keep, cum_out, ret_tok,
+                      ret_parent, n_ret, r_out, tok, parent, depth, pos_id, anc, row_src, true, stream);
 }
 
 int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logits, const int32_t *tok,

@@ -74,6 +74,7 @@ struct BuildKernelArgs {
     int32_t *tok, *parent, *depth, *pos_id;
     uint64_t *anc;
     uint8_t *row_src;  // nullable
+    int pre;           // TREE: ret_tok / ret_parent / n_ret already hold the whole template
 };
 
 void launch_prune(const PruneKernelArgs &a, hipStream_t s);

@@ -404,7 +404,8 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_retrieve(RetrieveKernel
     if (b >= a.B) return;
     int R, val, rp;
     if (a.mode == GRAFT_MODE_TREE) {
-        R = min(max(a.slots - a.n_keep[b], 0), a.tpl_size);
+        // no n_keep: the whole template, ahead of pruning
+        R = min(max(a.slots - (a.n_keep ? a.n_keep[b] : 0), 0), a.tpl_size);
         const bool act = lane < R;
         const int tp = act ? a.tpl_parent[lane] : -1;
         const int tr = act ? a.tpl_rank[lane] : 0;
@@ -466,14 +467,24 @@ __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
     const int root = a.root_tok[b];
 
     if (a.mode == GRAFT_MODE_TREE) {
-        const bool act = lane < a.tpl_size;
-        const int tp = act ? a.tpl_parent[lane] : -1;
+        // pre: the retrieval was done ahead (whole template, n_ret[b] nodes in
+        // ret_tok / ret_parent); read before anything is written
+        const int tsz = a.pre ? min(max(a.n_ret[b], 0), a.r_out) : a.tpl_size;
+        const bool act = lane < tsz;
+        const size_t orr = (size_t)b * a.r_out + lane;
+        const int tp = act ? (a.pre ? a.ret_parent[orr] : a.tpl_parent[lane]) : -1;
         int val = -1;
+        if (a.pre) {
+            if (wv == 0 && act) val = a.ret_tok[orr];
+            __syncthreads();
+        }
         if (wv == 0) {
-            // wave 0: the whole template from the root (the budget R is not known yet)
-            const int tr = act ? a.tpl_rank[lane] : 0;
-            const int td = act ? a.tpl_depth[lane] : 0;
-            val = retrieve_tree_wave(a.tpl_size, tp, tr, td, root, a.table, a.V, a.k);
+            if (!a.pre) {
+                // wave 0: the whole template from the root (the budget R is not known yet)
+                const int tr = act ? a.tpl_rank[lane] : 0;
+                const int td = act ? a.tpl_depth[lane] : 0;
+                val = retrieve_tree_wave(a.tpl_size, tp, tr, td, root, a.table, a.V, a.k);
+            }
         } else {
             // wave 1: prune, then the whole tree structure, which does not depend on
             // the retrieved tokens (rows, parents, depths, positions, masks, draft
@@ -489,7 +500,7 @@ __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
                 if (a.cum_out) a.cum_out[od] = r.cum;
             }
             const int nk = r.N;
-            const int R = min(max(a.slots - nk, 0), a.tpl_size);
+            const int R = min(max(a.slots - nk, 0), tsz);
             const bool isr = lane < R;
             FlatIn in;
             in.isd = isd;

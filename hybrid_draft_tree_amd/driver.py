@@ -19,6 +19,10 @@ device, so consecutive steps need no host round trip.
 With ``want_coverage`` the build also records each row's source (root, draft,
 retrieved), verification exports every row's softmax statistics, and
 ``verify_update`` adds the coverage gain per request (graft_coverage_gain).
+
+With ``overlap`` (TREE) the retrieval runs ahead on a side stream: it needs only
+the roots and the matrix, so ``build`` launches it before the draft is loaded
+and the prune + flatten launch (graft_build_after_retrieval) waits for it.
 """
 from __future__ import annotations
 
@@ -34,9 +38,10 @@ class GraftPipeline:
     def __init__(self, *, V, B, k=8, slots=60, mode="tree", layout="compact", dtype="bf16",
                  n_draft=60, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), keep=(8, 24, 40),
                  tail_thr=0.5, tpl_width=8, tpl_depth=8, tpl_kind="chain", tpl_beta=(1, 1), node_tau=0.0,
-                 want_prob=False, want_coverage=False, device="cuda", fused=True):
+                 want_prob=False, want_coverage=False, device="cuda", fused=True, overlap=False):
         L.load()
         self.fused = bool(fused)
+        self.overlap = bool(overlap)
         self.V, self.B, self.k = int(V), int(B), int(k)
         self.mode = L.MODE_TREE if mode == "tree" else L.MODE_TAIL
         self.layout = L.LAYOUT[layout]
@@ -113,16 +118,22 @@ class GraftPipeline:
         self._ingest_ws = None
         self._calib = None          # warm-up checkpoint statistics [steps * B, 3] while calibrating
         self._calib_rows = 0
+        if self.overlap:
+            if self.mode != L.MODE_TREE:
+                raise ValueError("retrieval ahead of the draft applies to TREE mode only")
+            self.side = torch.cuda.Stream(device=dev)   # default priority
+            self._ev_inputs = torch.cuda.Event()
+            self._ev_ret = torch.cuda.Event()
 
     @classmethod
-    def from_config(cls, cfg, want_prob=False, want_coverage=False, device="cuda", fused=True):
+    def from_config(cls, cfg, want_prob=False, want_coverage=False, device="cuda", fused=True, overlap=False):
         return cls(V=cfg.V, B=cfg.B, k=cfg.k,
                    slots=cfg.tail_block if cfg.mode == "tail" else cfg.slots,
                    mode=cfg.mode, layout=cfg.layout, dtype=cfg.dtype, n_draft=cfg.n_draft,
                    ckpt_layers=cfg.ckpt_layers, tau=cfg.tau, keep=cfg.keep, tail_thr=cfg.tail_thr,
                    tpl_width=cfg.tpl_width, tpl_depth=cfg.tpl_depth, tpl_kind=cfg.tpl_kind,
                    tpl_beta=cfg.tpl_beta, node_tau=cfg.node_tau, want_prob=want_prob,
-                   want_coverage=want_coverage, device=device, fused=fused)
+                   want_coverage=want_coverage, device=device, fused=fused, overlap=overlap)
 
     # ------------------------------------------------------------------ state
     def stream(self):
@@ -218,9 +229,45 @@ class GraftPipeline:
         self._calib = None
         return host
 
+    def retrieve_ahead(self):
+        """Section 二: the retrieval tree from each root (the whole template)
+        on the side stream, once the roots and the matrix of the last step are
+        final; it needs no draft, so it runs while the draft is produced."""
+        main = torch.cuda.current_stream(self.device)
+        self._ev_inputs.record(main)
+        self.side.wait_event(self._ev_inputs)
+        L.graft_retrieve_expand(self.B, self.V, self.k, self.mode, self.slots, self.table.data_ptr(),
+                                self.roots.data_ptr(), None, None, self.Nd, self.tpl, self.cfg,
+                                self.ret_tok.data_ptr(), self.ret_parent.data_ptr(), self.n_ret.data_ptr(),
+                                self.r_out, self.side.cuda_stream)
+        self._ev_ret.record(self.side)
+
+    def build_after_retrieval(self, bufs=None):
+        """prune -> keep the first R retrieved nodes -> flatten, once the draft is
+        on the device and retrieve_ahead() has finished (the stream waits)."""
+        B, Nd, T1 = self.B, self.Nd, self.T1
+        if bufs is None:
+            bufs = {"parent": self.d_parent, "layer": self.d_layer, "score": self.d_score, "tok": self.d_tok}
+        if self._calib is not None:
+            self._record_stats(bufs["parent"], bufs["layer"], bufs["score"])
+        main = torch.cuda.current_stream(self.device)
+        main.wait_event(self._ev_ret)
+        L.graft_build_after_retrieval(
+            B, Nd, T1, self.layout, self.slots, self.cfg, self.roots.data_ptr(), self.base_pos.data_ptr(),
+            bufs["parent"].data_ptr(), bufs["layer"].data_ptr(), bufs["score"].data_ptr(), bufs["tok"].data_ptr(),
+            self.stage.data_ptr(), self.n_keep.data_ptr(), self.keep.data_ptr(), self.cum.data_ptr(),
+            self.ret_tok.data_ptr(), self.ret_parent.data_ptr(), self.n_ret.data_ptr(), self.r_out,
+            self.tok.data_ptr(), self.parent.data_ptr(), self.depth.data_ptr(), self.pos_id.data_ptr(),
+            self.anc.data_ptr(), self._ptr(self.row_src), main.cuda_stream)
+
     def build(self, draft):
-        self.load_draft(draft)
-        self.build_device()
+        if self.overlap:
+            self.retrieve_ahead()          # overlaps the draft's upload below
+            self.load_draft(draft)
+            self.build_after_retrieval()
+        else:
+            self.load_draft(draft)
+            self.build_device()
         out = {"stage": self.stage, "n_keep": self.n_keep, "keep": self.keep, "ret_tok": self.ret_tok,
                "ret_parent": self.ret_parent, "n_ret": self.n_ret, "tok": self.tok, "parent": self.parent,
                "depth": self.depth, "pos_id": self.pos_id, "anc": self.anc}

@@ -177,7 +177,9 @@ int graft_template_branching(int width, int depth, int beta_num, int beta_den, i
  *   0); ret_parent[t] = t-1.  tpl and cfg may be NULL.
  * table int32 [V, k] (1 <= k <= 8); root_tok, n_keep int32 [B]; d_tok int32
  * [B, Nd].  Outputs: ret_tok, ret_parent int32 [B, r_out] (-1 beyond R_b),
- * n_ret int32 [B].  Requires r_out <= 64 and r_out >= the largest R_b. */
+ * n_ret int32 [B].  Requires r_out <= 64 and r_out >= the largest R_b.
+ * TREE with n_keep == NULL: R_b = min(slots, tpl->size), the whole template
+ * ahead of pruning (for graft_build_after_retrieval). */
 int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_t *table,
                           const int32_t *root_tok, const int32_t *n_keep, const int32_t *d_tok,
                           int Nd, const graft_template *tpl, const graft_prune_cfg *cfg,
@@ -268,6 +270,28 @@ int graft_build_hybrid_tree(int B, int Nd, int T1, int mode, int layout, int slo
                             float *cum_out, int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret,
                             int r_out, int32_t *tok, int32_t *parent, int32_t *depth, int32_t *pos_id,
                             uint64_t *anc, uint8_t *row_src, hipStream_t stream);
+
+/* graft_build_after_retrieval -- graft_build_hybrid_tree with the retrieval
+ * already done.  Section 二: retrieval depends only on the request's root
+ * token and the matrix, so it can run while the drafter is still building the
+ * tree, off the critical path.  ret_tok, ret_parent, n_ret (in/out) are as
+ * graft_retrieve_expand writes them with n_keep == NULL: the whole template
+ * from each root, computed before the draft exists, usually on another
+ * stream that this call's stream waits for (an event).  This call prunes,
+ * keeps the first R_b = min(slots - n_keep[b], n_ret[b]) retrieved nodes (the
+ * template's master order makes every prefix a tree) and flattens, in one
+ * launch; on return ret_tok / ret_parent hold -1 beyond R_b and n_ret[b] =
+ * R_b, so every output equals graft_build_hybrid_tree's on the same inputs.
+ * TREE only: layout COMPACT or IN_PLACE (a TAIL chain starts from the last
+ * kept block token, known only after the prune -> GRAFT_EUNSUPPORTED).  Other
+ * arguments and preconditions as graft_build_hybrid_tree. */
+int graft_build_after_retrieval(int B, int Nd, int T1, int layout, int slots, const graft_prune_cfg *cfg,
+                                const int32_t *root_tok, const int32_t *base_pos, const int32_t *d_parent,
+                                const int32_t *d_layer, const float *d_score, const int32_t *d_tok,
+                                int32_t *stage, int32_t *n_keep, uint8_t *keep, float *cum_out,
+                                int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret, int r_out, int32_t *tok,
+                                int32_t *parent, int32_t *depth, int32_t *pos_id, uint64_t *anc,
+                                uint8_t *row_src, hipStream_t stream);
 
 /* graft_verify_update -- graft_verify_accept followed by
  * graft_update_topk(row_tok = tok, topk_in = the top-k just computed) in one

@@ -48,14 +48,14 @@ class HipBackend:
     """HIP path through the C-ABI; host copies of the small outputs are made for
     the synthetic generator and for comparison."""
 
-    def __init__(self, cfg, want_prob=False, device="cuda", fused=True, want_coverage=False):
+    def __init__(self, cfg, want_prob=False, device="cuda", fused=True, want_coverage=False, overlap=False):
         import torch
         from hybrid_draft_tree_amd.driver import GraftPipeline
         from synth.device import DeviceRows
         self.torch = torch
         self.cfg = cfg
         self.p = GraftPipeline.from_config(cfg, want_prob=want_prob, want_coverage=want_coverage,
-                                           device=device, fused=fused)
+                                           device=device, fused=fused, overlap=overlap)
         self.rows = None
         self._DeviceRows = DeviceRows
         self.want_prob = want_prob

@@ -571,7 +571,11 @@ def test_update_parity_collisions(n, ntok):
 @pytest.mark.parametrize("kind,W,D,beta", [("chain", 8, 8, (1, 1)), ("branching", 8, 8, (1, 1)),
                                            ("chain", 8, 2, (1, 1)), ("branching", 2, 30, (100, 1))],
                          ids=["chain8x8", "branching8x8", "chain8x2_empty_rows", "deep_chain30"])
-def test_build_hybrid_tree_matches_oracle_tree(kind, W, D, beta):
+@pytest.mark.parametrize("ahead", [False, True], ids=["one_launch", "retrieval_ahead"])
+def test_build_hybrid_tree_matches_oracle_tree(kind, W, D, beta, ahead):
+    """graft_build_hybrid_tree, or graft_retrieve_expand without n_keep (the
+    whole template before the draft exists) followed by
+    graft_build_after_retrieval: the same outputs as the oracle's step."""
     rng = np.random.default_rng(30)
     B, V = 37, 5000
     par, lay, _ = TOPO
@@ -595,12 +599,26 @@ def test_build_hybrid_tree_matches_oracle_tree(kind, W, D, beta):
         tok, par_o, dep, pos = (torch.zeros(B, 61, **i32) for _ in range(4))
         anc = torch.zeros(B, 61, dtype=torch.int64, device=DEV)
         src = torch.full((B, 61), 99, dtype=torch.uint8, device=DEV)
-        L.graft_build_hybrid_tree(B, 60, 61, L.MODE_TREE, L.LAYOUT[layout], 60, cfg, tpl, V, 8,
-                                  ins[0].data_ptr(), ins[1].data_ptr(), ins[2].data_ptr(), ins[3].data_ptr(),
-                                  ins[4].data_ptr(), sc.data_ptr(), dt.data_ptr(), st.data_ptr(), nk.data_ptr(),
-                                  kp.data_ptr(), cum.data_ptr(), rt.data_ptr(), rp.data_ptr(), nr.data_ptr(),
-                                  r_out, tok.data_ptr(), par_o.data_ptr(), dep.data_ptr(), pos.data_ptr(),
-                                  anc.data_ptr(), src.data_ptr(), _s())
+        if not ahead:
+            L.graft_build_hybrid_tree(B, 60, 61, L.MODE_TREE, L.LAYOUT[layout], 60, cfg, tpl, V, 8,
+                                      ins[0].data_ptr(), ins[1].data_ptr(), ins[2].data_ptr(), ins[3].data_ptr(),
+                                      ins[4].data_ptr(), sc.data_ptr(), dt.data_ptr(), st.data_ptr(),
+                                      nk.data_ptr(), kp.data_ptr(), cum.data_ptr(), rt.data_ptr(), rp.data_ptr(),
+                                      nr.data_ptr(), r_out, tok.data_ptr(), par_o.data_ptr(), dep.data_ptr(),
+                                      pos.data_ptr(), anc.data_ptr(), src.data_ptr(), _s())
+        else:
+            L.graft_retrieve_expand(B, V, 8, L.MODE_TREE, 60, ins[0].data_ptr(), ins[1].data_ptr(), None, None,
+                                    60, tpl, cfg, rt.data_ptr(), rp.data_ptr(), nr.data_ptr(), r_out, _s())
+            torch.cuda.synchronize()
+            full = O.retrieve_tree(table, roots, np.zeros(B, np.int32), 60, tpl_h)
+            np.testing.assert_array_equal(nr.cpu().numpy(), full["n_ret"])
+            np.testing.assert_array_equal(rt.cpu().numpy()[:, :full["ret_tok"].shape[1]], full["ret_tok"])
+            L.graft_build_after_retrieval(B, 60, 61, L.LAYOUT[layout], 60, cfg, ins[1].data_ptr(),
+                                          ins[2].data_ptr(), ins[3].data_ptr(), ins[4].data_ptr(), sc.data_ptr(),
+                                          dt.data_ptr(), st.data_ptr(), nk.data_ptr(), kp.data_ptr(),
+                                          cum.data_ptr(), rt.data_ptr(), rp.data_ptr(), nr.data_ptr(), r_out,
+                                          tok.data_ptr(), par_o.data_ptr(), dep.data_ptr(), pos.data_ptr(),
+                                          anc.data_ptr(), src.data_ptr(), _s())
         torch.cuda.synchronize()
         pr = O.prune_tree(P, Ly, lp, want_cum=True)
         ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, tpl_h)

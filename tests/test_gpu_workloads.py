@@ -25,8 +25,9 @@ KEYS_BUILD = ("stage", "n_keep", "keep", "n_ret", "ret_tok", "tok", "parent", "d
 KEYS_VERIFY = ("topk", "accept_len", "accept_idx", "bonus")
 
 
-def _compare_runs(cfg, n_steps, warmup, table_every=1, fused=True, want_prob=False):
-    ob, hb = OracleBackend(cfg, want_prob=want_prob), HipBackend(cfg, want_prob=want_prob, fused=fused)
+def _compare_runs(cfg, n_steps, warmup, table_every=1, fused=True, want_prob=False, overlap=False):
+    ob = OracleBackend(cfg, want_prob=want_prob)
+    hb = HipBackend(cfg, want_prob=want_prob, fused=fused, overlap=overlap)
     wl_o, wl_h = R.Workload(cfg), R.Workload(cfg, pool=None)
     R.start(ob, wl_o)
     R.start(hb, wl_h)
@@ -127,6 +128,16 @@ def test_lockstep_ablation_variants(kw, fused):
     cfg = _small(3, V=20000, B=8, **kw)
     st = _compare_runs(cfg, 10, warmup=cfg.warmup_steps, fused=fused)
     assert st["accepted"] > 0
+
+
+@pytest.mark.parametrize("cfg_id,kw", [(3, {"V": 20000, "B": 16}), (1, {}), (3, {"V": 20000, "B": 8,
+                                                                                 "calib_q": (0.1, 0.4, 0.9)})])
+def test_lockstep_retrieval_ahead_of_the_draft(cfg_id, kw):
+    """Retrieval on a side stream before the draft is loaded, then prune +
+    flatten (graft_build_after_retrieval): every output as the oracle's."""
+    cfg = _small(cfg_id, **kw)
+    st = _compare_runs(cfg, 12, warmup=cfg.warmup_steps, overlap=True)
+    assert st["accepted"] > 0 and len(st["stages"]) >= 2
 
 
 @pytest.mark.parametrize("q", [(0.2, 0.2, 0.2), (0.5, 0.3, 0.1)])

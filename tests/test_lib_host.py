@@ -79,6 +79,24 @@ def test_calibration_validation_rejects_without_launch():
     assert lib.graft_calibrate_thresholds(10, P, ctypes.byref(ok), None, None) == L.GRAFT_EINVAL
 
 
+def test_retrieval_ahead_validation_rejects_without_launch():
+    cfg = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 40), 0.5)
+    lib = L.load()
+    P = 0x1000  # never dereferenced
+    cb = ctypes.byref(cfg)
+    # TAIL retrieval needs the kept prefix: no n_keep is invalid there
+    assert lib.graft_retrieve_expand(1, 100, 8, 1, 16, P, P, None, P, 16, None, None, P, P, P, 16, None) == L.GRAFT_EINVAL
+    # the chain layout (TAIL) cannot take a retrieval done ahead
+    args = [P] * 14
+    assert lib.graft_build_after_retrieval(1, 60, 61, 2, 60, cb, *args[:13], 52, *args[:6], None) == \
+        L.GRAFT_EUNSUPPORTED
+    assert lib.graft_build_after_retrieval(1, 60, 62, 0, 60, cb, *args[:13], 52, *args[:6], None) == L.GRAFT_EINVAL
+    assert lib.graft_build_after_retrieval(1, 60, 61, 0, 60, None, *args[:13], 52, *args[:6], None) == L.GRAFT_EINVAL
+    assert lib.graft_build_after_retrieval(1, 60, 61, 0, 60, cb, None, *args[:12], 52, *args[:6], None) == \
+        L.GRAFT_EINVAL
+    assert lib.graft_build_after_retrieval(1, 60, 61, 0, 60, cb, *args[:13], 65, *args[:6], None) == L.GRAFT_EINVAL
+
+
 def test_host_validation_rejects_without_launch():
     cfg = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 40), 0.5)
     lib = L.load()
