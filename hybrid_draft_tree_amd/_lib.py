@@ -28,7 +28,7 @@ MAX_ROWS = 64
 MAX_K = 8
 
 EXPORTS = (
-    "graft_prune_select", "graft_checkpoint_stats", "graft_calibrate_thresholds", "graft_template_master", "graft_template_branching", "graft_retrieve_expand",
+    "graft_prune_select", "graft_check_draft", "graft_check_tree", "graft_checkpoint_stats", "graft_calibrate_thresholds", "graft_template_master", "graft_template_branching", "graft_retrieve_expand",
     "graft_build_tree_mask", "graft_verify_accept", "graft_update_topk",
     "graft_build_hybrid_tree", "graft_build_after_retrieval", "graft_verify_update", "graft_coverage_gain",
     "graft_workspace_bytes", "graft_status_string",
@@ -67,6 +67,8 @@ def load():
     L = C.CDLL(LIB_PATH)
     P, I, I64, S = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
     L.graft_prune_select.argtypes = [I, I, I, P, P, P, C.POINTER(PruneCfg), P, P, P, P, P]
+    L.graft_check_draft.argtypes = [I, I, I, I, P, P, P, P, P, P]
+    L.graft_check_tree.argtypes = [I, I, I, P, P, P, P, P]
     L.graft_checkpoint_stats.argtypes = [I, I, P, P, P, C.POINTER(PruneCfg), P, P]
     L.graft_calibrate_thresholds.argtypes = [I64, P, C.POINTER(C.c_float * 3), P, P]
     L.graft_template_master.argtypes = [I, I, I, P, P, P]
@@ -115,6 +117,18 @@ def prune_cfg(ckpt_layers, log_thr, keep, tail_thr, node_log_thr=None) -> PruneC
 def graft_prune_select(B, Nd, mode, d_parent, d_layer, d_score, cfg, stage, n_keep, keep, cum_out, stream):
     return _chk("graft_prune_select", load().graft_prune_select(
         B, Nd, mode, d_parent, d_layer, d_score, C.byref(cfg), stage, n_keep, keep, cum_out, stream))
+
+
+BAD_PARENT, BAD_LAYER, BAD_SCORE, BAD_TOKEN, BAD_DEPTH = 1, 2, 4, 8, 16
+
+
+def graft_check_draft(B, Nd, mode, V, d_parent, d_layer, d_score, d_tok, status, stream):
+    return _chk("graft_check_draft", load().graft_check_draft(
+        B, Nd, mode, V, d_parent, d_layer, d_score, d_tok, status, stream))
+
+
+def graft_check_tree(B, T1, V, tok, parent, depth, status, stream):
+    return _chk("graft_check_tree", load().graft_check_tree(B, T1, V, tok, parent, depth, status, stream))
 
 
 def graft_checkpoint_stats(B, Nd, d_parent, d_layer, d_score, cfg, out, stream):

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INC = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgraft.so")
-SOURCES = ["tree_kernels.hip", "topk_kernels.hip", "verify_kernels.hip", "graft_api.hip"]
+SOURCES = ["tree_kernels.hip", "topk_kernels.hip", "verify_kernels.hip", "check_kernels.hip", "graft_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

@@ -27,6 +27,7 @@ and the prune + flatten launch (graft_build_after_retrieval) waits for it.
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 import torch
@@ -38,10 +39,16 @@ class GraftPipeline:
     def __init__(self, *, V, B, k=8, slots=60, mode="tree", layout="compact", dtype="bf16",
                  n_draft=60, ckpt_layers=(0, 1, 5), tau=(0.3, 0.2, 0.1), keep=(8, 24, 40),
                  tail_thr=0.5, tpl_width=8, tpl_depth=8, tpl_kind="chain", tpl_beta=(1, 1), node_tau=0.0,
-                 want_prob=False, want_coverage=False, device="cuda", fused=True, overlap=False):
+                 want_prob=False, want_coverage=False, device="cuda", fused=True, overlap=False,
+                 debug_checks=None):
         L.load()
         self.fused = bool(fused)
         self.overlap = bool(overlap)
+        # check every loaded draft on the device (graft_check_draft) and raise on a
+        # failed precondition; default from GRAFT_DEBUG_CHECKS=1 in the environment
+        if debug_checks is None:
+            debug_checks = os.environ.get("GRAFT_DEBUG_CHECKS", "0") not in ("", "0")
+        self.debug_checks = bool(debug_checks)
         self.V, self.B, self.k = int(V), int(B), int(k)
         self.mode = L.MODE_TREE if mode == "tree" else L.MODE_TAIL
         self.layout = L.LAYOUT[layout]
@@ -154,6 +161,33 @@ class GraftPipeline:
             self.d_score.copy_(torch.as_tensor(np.asarray(draft["conf"], np.float32)))
         self.d_tok.copy_(torch.as_tensor(np.asarray(draft["tok"], np.int32)))
 
+    def check_draft(self, bufs=None):
+        """graft_check_draft on a draft already on the device: per-request flag
+        words (host int32 [B], 0 = every precondition holds).  Synchronises."""
+        if bufs is None:
+            bufs = {"parent": self.d_parent, "layer": self.d_layer, "score": self.d_score, "tok": self.d_tok}
+        st = torch.empty(self.B, dtype=torch.int32, device=self.device)
+        tree = self.mode == L.MODE_TREE
+        L.graft_check_draft(self.B, self.Nd, self.mode, self.V, bufs["parent"].data_ptr() if tree else None,
+                            bufs["layer"].data_ptr() if tree else None, bufs["score"].data_ptr(),
+                            bufs["tok"].data_ptr(), st.data_ptr(), self.stream())
+        return st.cpu().numpy()
+
+    def check_tree(self):
+        """graft_check_tree on the flattened tree of the last build (host int32 [B])."""
+        st = torch.empty(self.B, dtype=torch.int32, device=self.device)
+        L.graft_check_tree(self.B, self.T1, self.V, self.tok.data_ptr(), self.parent.data_ptr(),
+                           self.depth.data_ptr(), st.data_ptr(), self.stream())
+        return st.cpu().numpy()
+
+    def _raise_if_bad(self, flags, what):
+        bad = np.nonzero(flags)[0]
+        if bad.size:
+            names = [n for n, f in (("parent", L.BAD_PARENT), ("layer", L.BAD_LAYER), ("score", L.BAD_SCORE),
+                                    ("token", L.BAD_TOKEN), ("depth", L.BAD_DEPTH)) if int(flags[bad[0]]) & f]
+            raise ValueError("%s fails its preconditions for request(s) %s (first: %s)"
+                             % (what, bad.tolist(), ", ".join(names)))
+
     def draft_buffers(self):
         """A fresh set of device draft buffers shaped like the pipeline's own."""
         return {"parent": torch.empty_like(self.d_parent), "layer": torch.empty_like(self.d_layer),
@@ -261,6 +295,9 @@ class GraftPipeline:
             self.anc.data_ptr(), self._ptr(self.row_src), main.cuda_stream)
 
     def build(self, draft):
+        if self.debug_checks:
+            self.load_draft(draft)
+            self._raise_if_bad(self.check_draft(), "draft tree")
         if self.overlap:
             self.retrieve_ahead()          # overlaps the draft's upload below
             self.load_draft(draft)

@@ -25,6 +25,7 @@
  *    enqueued.  GRAFT_EDEVICE reports a launch failure (hipGetLastError).
  *  - Device-side data preconditions (token ids in [0, V), parents before
  *    children, log-probs finite) are the caller's; no NaN is handled.
+ *    graft_check_draft / graft_check_tree test them on the device.
  *  - Row-major layouts throughout; "[B, T1]" means B*T1 contiguous elements.
  *  - The continuation matrix is int32 [V, k]; only graft_update_topk and
  *    graft_verify_update write it.
@@ -111,6 +112,34 @@ typedef struct graft_template {
 int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const int32_t *d_layer,
                        const float *d_score, const graft_prune_cfg *cfg, int32_t *stage,
                        int32_t *n_keep, uint8_t *keep, float *cum_out, hipStream_t stream);
+
+/* Optional input checks.  The other calls assume the data preconditions
+ * below and never read out of bounds when they fail, but then compute
+ * nothing meaningful.  These write, per request b, status[b] = the OR of the
+ * flags of the conditions that fail (0 = all hold); status int32 [B], device.
+ *
+ * graft_check_draft (inputs of graft_prune_select / graft_build_hybrid_tree):
+ *   GRAFT_BAD_TOKEN d_tok outside [0, V); GRAFT_BAD_SCORE a TREE log-
+ *   probability that is NaN or > 0, or a TAIL confidence NaN or outside
+ *   [0, 1]; TREE only: GRAFT_BAD_PARENT d_parent[i] outside [-1, i);
+ *   GRAFT_BAD_LAYER d_layer[i] != d_layer[parent] + 1 (0 for root
+ *   children).  TAIL ignores d_parent / d_layer (may be NULL).
+ * graft_check_tree (the flattened tree given to graft_verify_accept /
+ *   graft_verify_update): row 0 is the root (token in [0, V), parent -1,
+ *   depth 0); a row f >= 1 is either empty (token -1, parent -1, depth 0) or
+ *   has a token in [0, V), a parent row in [0, f) that is not empty, and
+ *   depth = parent's depth + 1 (GRAFT_BAD_TOKEN / GRAFT_BAD_PARENT /
+ *   GRAFT_BAD_DEPTH).
+ * Requires 1 <= Nd, T1 <= 64, V >= 1. */
+#define GRAFT_BAD_PARENT 1
+#define GRAFT_BAD_LAYER 2
+#define GRAFT_BAD_SCORE 4
+#define GRAFT_BAD_TOKEN 8
+#define GRAFT_BAD_DEPTH 16
+int graft_check_draft(int B, int Nd, int mode, int V, const int32_t *d_parent, const int32_t *d_layer,
+                      const float *d_score, const int32_t *d_tok, int32_t *status, hipStream_t stream);
+int graft_check_tree(int B, int T1, int V, const int32_t *tok, const int32_t *parent, const int32_t *depth,
+                     int32_t *status, hipStream_t stream);
 
 /* Threshold calibration -- section 二, gear 1: the checkpoint thresholds are
  * set from the confidence the drafter shows at each checkpoint over a few

@@ -759,3 +759,141 @@ def test_coverage_gain_hand_tree_closed_form():
     torch.cuda.synchronize()
     assert abs(float(gain.item()) - 2.0 / V) <= 1e-6 * (2.0 / V)
     assert float(O.coverage_gain(rows, tok, par, src, "bf16")[0]) == pytest.approx(2.0 / V, rel=1e-14)
+
+
+# ----------------------------------------------------------------------------- input checks
+
+def _draft_flags(par, lay, score, tok, V, mode):
+    """The header's conditions, per request."""
+    B, Nd = score.shape
+    out = np.zeros(B, np.int32)
+    for b in range(B):
+        f = 0
+        for i in range(Nd):
+            if not (0 <= tok[b, i] < V):
+                f |= L.BAD_TOKEN
+            s = score[b, i]
+            if mode == L.MODE_TREE and not (s <= 0):
+                f |= L.BAD_SCORE
+            if mode == L.MODE_TAIL and not (0 <= s <= 1):
+                f |= L.BAD_SCORE
+            if mode == L.MODE_TREE:
+                p = par[b, i]
+                if not (-1 <= p < i):
+                    f |= L.BAD_PARENT
+                elif lay[b, i] != (0 if p < 0 else lay[b, p] + 1):
+                    f |= L.BAD_LAYER
+        out[b] = f
+    return out
+
+
+def _gpu_check_draft(par, lay, score, tok, V, mode):
+    B, Nd = score.shape
+    st = torch.full((B,), -5, dtype=torch.int32, device=DEV)
+    # keep every input tensor alive until the launch has run
+    dp = _t(par, torch.int32) if par is not None else None
+    dl = _t(lay, torch.int32) if lay is not None else None
+    ds, dt = _t(score, torch.float32), _t(tok, torch.int32)
+    L.graft_check_draft(B, Nd, mode, V, dp.data_ptr() if dp is not None else None,
+                        dl.data_ptr() if dl is not None else None, ds.data_ptr(), dt.data_ptr(), st.data_ptr(), _s())
+    torch.cuda.synchronize()
+    return st.cpu().numpy()
+
+
+def test_check_draft_flags():
+    rng = np.random.default_rng(40)
+    par, lay, _ = TOPO
+    B, V = 24, 1000
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    lp = _random_logp(rng, B)
+    tok = rng.integers(0, V, size=(B, 60)).astype(np.int32)
+    np.testing.assert_array_equal(_gpu_check_draft(P, Ly, lp, tok, V, L.MODE_TREE), 0)
+    tok[1, 5] = V
+    tok[2, 0] = -1
+    lp[3, 7] = np.nan
+    lp[4, 59] = 0.25                     # a probability above 1
+    P[5, 30] = 30                         # own index
+    P[6, 10] = -2
+    Ly[7, 12] += 1                        # layer not parent's + 1
+    P[8, 40], Ly[8, 3] = 41, 4            # two faults in one request
+    lp[9, :] = 0.0                        # probability 1 everywhere is fine
+    got = _gpu_check_draft(P, Ly, lp, tok, V, L.MODE_TREE)
+    np.testing.assert_array_equal(got, _draft_flags(P, Ly, lp, tok, V, L.MODE_TREE))
+    assert (got[1:9] != 0).all() and got[9] == 0 and got[8] == L.BAD_PARENT | L.BAD_LAYER
+    # TAIL: confidences in [0, 1], tokens in range; parents and layers not read
+    conf = rng.uniform(0, 1, size=(B, 16)).astype(np.float32)
+    tt = rng.integers(0, V, size=(B, 16)).astype(np.int32)
+    conf[0, 3], conf[1, 0], tt[2, 15] = 1.5, -0.1, V + 3
+    got = _gpu_check_draft(None, None, conf, tt, V, L.MODE_TAIL)
+    np.testing.assert_array_equal(got, _draft_flags(None, None, conf, tt, V, L.MODE_TAIL))
+    assert list(got[:4]) == [L.BAD_SCORE, L.BAD_SCORE, L.BAD_TOKEN, 0]
+
+
+def _gpu_check_tree(tok, par, dep, V):
+    B, T1 = tok.shape
+    st = torch.full((B,), -5, dtype=torch.int32, device=DEV)
+    dt, dp, dd = _t(tok, torch.int32), _t(par, torch.int32), _t(dep, torch.int32)
+    L.graft_check_tree(B, T1, V, dt.data_ptr(), dp.data_ptr(), dd.data_ptr(), st.data_ptr(), _s())
+    torch.cuda.synchronize()
+    return st.cpu().numpy()
+
+
+@pytest.mark.parametrize("layout", ["compact", "in_place"])
+def test_check_tree_accepts_built_trees_and_flags_faults(layout):
+    rng = np.random.default_rng(41)
+    par, lay, _ = TOPO
+    B, V = 16, 3000
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    lp = _random_logp(rng, B)
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    d_tok = rng.integers(0, V, size=(B, 60)).astype(np.int32)
+    pr = O.prune_tree(P, Ly, lp)
+    tpl = O.template_branching(8, 2, (1, 1), 20)          # small template: empty rows too
+    ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, tpl)
+    fl = O.flatten(layout, 61, roots, np.zeros(B, np.int32), d_tok, P, pr["keep"], pr["n_keep"], ret)
+    tok, pa, de = fl["tok"].copy(), fl["parent"].copy(), fl["depth"].copy()
+    assert (tok == -1).any()
+    np.testing.assert_array_equal(_gpu_check_tree(tok, pa, de, V), 0)
+    with_empty = [b for b in range(B) if (tok[b] == -1).any()]
+    assert len(with_empty) >= 2
+    e0, e1 = with_empty[0], with_empty[1]
+    rest = [b for b in range(B) if b not in (e0, e1)]
+    r0, r1, r2 = rest[:3]
+    tok[r0, 0] = V                                   # root token out of range
+    pa[r1, 0] = 0                                    # root with a parent
+    f = int(np.nonzero(tok[r2] >= 0)[0][3])
+    de[r2, f] += 1                                   # depth not parent's + 1
+    e = int(np.nonzero(tok[e0] == -1)[0][0])
+    pa[e0, e] = 0                                    # an empty slot with a parent
+    ce = int(np.nonzero(tok[e1] == -1)[0][0])
+    c = int(np.nonzero((tok[e1] >= 0) & (np.arange(61) > ce))[0][0]) if (tok[e1, ce + 1:] >= 0).any() else None
+    if c is not None:
+        pa[e1, c] = ce                               # a child of an empty slot
+        de[e1, c] = 1
+    got = _gpu_check_tree(tok, pa, de, V)
+    assert got[r0] & L.BAD_TOKEN and got[r1] & L.BAD_PARENT and got[r2] & L.BAD_DEPTH
+    assert got[e0] & L.BAD_PARENT
+    if c is not None:
+        assert got[e1] & L.BAD_PARENT
+    clean = [b for b in range(B) if b not in (r0, r1, r2, e0, e1)]
+    assert (got[clean] == 0).all()
+
+
+def test_pipeline_debug_checks_raise_on_a_bad_draft():
+    from hybrid_draft_tree_amd.driver import GraftPipeline
+    from synth import CONFIGS
+    from synth import runner as R
+    from tests.backends import HipBackend
+
+    cfg = CONFIGS[3].scaled(V=8000, B=4, noise_pool_rows=8)
+    hb = HipBackend(cfg)
+    hb.p.debug_checks = True
+    wl = R.Workload(cfg)
+    R.start(hb, wl)
+    R.step(hb, wl, 0)                      # a valid draft passes
+    d = wl.draft(1, hb.get_roots())
+    d["logp"][2, 5] = np.nan
+    with pytest.raises(ValueError, match=r"request\(s\) \[2\].*score"):
+        hb.build(d)
+    assert isinstance(hb.p, GraftPipeline)

@@ -146,3 +146,17 @@ def test_branching_template_matches_oracle(W, D, beta, cap):
     par, rk, dp = L.graft_template_branching(W, D, beta[0], beta[1], cap)
     o = O.template_branching(W, D, beta, cap)
     assert par == o["parent"].tolist() and rk == o["rank"].tolist() and dp == o["depth"].tolist()
+
+
+def test_input_check_validation_rejects_without_launch():
+    lib = L.load()
+    P = 0x1000  # never dereferenced
+    assert lib.graft_check_draft(1, 60, 9, 100, P, P, P, P, P, None) == L.GRAFT_EUNSUPPORTED
+    assert lib.graft_check_draft(1, 65, 0, 100, P, P, P, P, P, None) == L.GRAFT_EINVAL
+    assert lib.graft_check_draft(1, 60, 0, 0, P, P, P, P, P, None) == L.GRAFT_EINVAL
+    assert lib.graft_check_draft(1, 60, 0, 100, None, P, P, P, P, None) == L.GRAFT_EINVAL
+    assert lib.graft_check_draft(1, 16, 1, 100, None, None, P, P, None, None) == L.GRAFT_EINVAL
+    assert lib.graft_check_draft(0, 60, 0, 100, None, None, None, None, None, None) == L.GRAFT_OK
+    assert lib.graft_check_tree(1, 65, 100, P, P, P, P, None) == L.GRAFT_EINVAL
+    assert lib.graft_check_tree(1, 61, 100, P, None, P, P, None) == L.GRAFT_EINVAL
+    assert lib.graft_check_tree(0, 61, 100, None, None, None, None, None) == L.GRAFT_OK
