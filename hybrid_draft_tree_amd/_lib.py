@@ -18,6 +18,9 @@ GRAFT_OK = 0
 GRAFT_EINVAL = -1
 GRAFT_EUNSUPPORTED = -2
 GRAFT_EDEVICE = -3
+GRAFT_MAX_ROWS = 64
+GRAFT_MAX_K = 8
+GRAFT_MAX_VOCAB = 1000000   # logits per row accepted by the top-k calls
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 MODE_TREE = 0

@@ -53,7 +53,8 @@ const char *graft_status_string(int status) {
 }
 
 size_t graft_workspace_bytes(int64_t n_rows, int V, int k, int dtype) {
-    if (n_rows < 0 || V <= 0 || k < 1 || k > GRAFT_MAX_K || k > V || !dtype_ok(dtype)) return 0;
+    if (n_rows < 0 || V <= 0 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K || k > V || !dtype_ok(dtype))
+        return 0;
     return ws_layout(n_rows, V, k, dtype).total;
 }
 
@@ -337,8 +338,8 @@ int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logi
                         int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws,
                         size_t ws_bytes, hipStream_t stream) {
     if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || k < 1 || k > GRAFT_MAX_K || k > V ||
-        dmax < 0)
+    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K ||
+        k > V || dmax < 0)
         return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
     if (!logits || !tok || !parent || !depth || !table || !topk || !accept_len || !bonus ||
@@ -370,8 +371,8 @@ int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logi
                         int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws,
                         size_t ws_bytes, hipStream_t stream) {
     if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || k < 1 || k > GRAFT_MAX_K || k > V ||
-        dmax < 0)
+    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K ||
+        k > V || dmax < 0)
         return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
     if (!logits || !tok || !parent || !depth || !topk || !accept_len || !bonus ||
@@ -400,7 +401,7 @@ int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logit
                       int32_t *table, float *table_prob, int32_t *topk_out, void *ws,
                       size_t ws_bytes, hipStream_t stream) {
     if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
-    if (n_rows < 0 || V < 1 || k < 1 || k > GRAFT_MAX_K || k > V) return GRAFT_EINVAL;
+    if (n_rows < 0 || V < 1 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K || k > V) return GRAFT_EINVAL;
     if (n_rows == 0) return GRAFT_OK;
     if (!row_tok || !table || (!logits && !topk_in)) return GRAFT_EINVAL;
     const int32_t *tk = topk_in;
@@ -425,7 +426,7 @@ int graft_coverage_gain(int B, int T1, int V, int dtype, const void *logits, con
                         const int32_t *parent, const uint8_t *row_src, const float *row_stats,
                         float *gain, hipStream_t stream) {
     if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1) return GRAFT_EINVAL;
+    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB) return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
     if (!logits || !tok || !parent || !row_src || !row_stats || !gain) return GRAFT_EINVAL;
     if (!aligned(row_stats, 8)) return GRAFT_EINVAL;

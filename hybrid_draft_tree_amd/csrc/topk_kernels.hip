@@ -763,13 +763,16 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     p.V = V;
     // S waves per row: about 4096 waves in flight over the chip (~16 per CU),
     // at most 16 per row, and few enough blocks per wave that local offsets
-    // fit 16 bits (bf16: 127 blocks of 512 elements per wave).
+    // fit: bf16 ranks hold 16-bit offsets (127 blocks of 512 elements per
+    // wave), fp32 ranks 32-bit ones, where the 16-bit pending-group index
+    // allows 1023 blocks of 256.
     const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
     const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
     const int64_t target_waves = 4096;
     int64_t S = (target_waves + (n_rows > 0 ? n_rows : 1) - 1) / (n_rows > 0 ? n_rows : 1);
     S = S < 1 ? 1 : (S > kMaxWavesPerRow ? kMaxWavesPerRow : S);
-    const int64_t smin = (nblk + 126) / 127;
+    const int64_t per_wave = dtype == GRAFT_DTYPE_BF16 ? 127 : 1023;
+    const int64_t smin = (nblk + per_wave - 1) / per_wave;
     if (S < smin) S = smin;
     if (S > nblk && nblk > 0) S = nblk;
     if (S < 1) S = 1;

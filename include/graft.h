@@ -65,6 +65,7 @@ extern "C" {
 
 #define GRAFT_MAX_ROWS 64 /* rows per request (root + candidate slots); one wavefront */
 #define GRAFT_MAX_K 8     /* successors per matrix row */
+#define GRAFT_MAX_VOCAB 1000000 /* logits per row for the top-k calls (at most 16 wavefronts per row) */
 
 /* Prune configuration (host POD).  Section 二, gear 1: checkpoints at draft
  * depths 0, 1 and 5 compare the best cumulative path confidence with a
@@ -259,7 +260,8 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
  * acceptance walk as soon as all its rows are in.  accept_len[b] == -1 reports
  * a coordinator that gave up waiting (about a second; never in normal
  * operation): the outputs are then invalid and the workspace must be
- * zero-filled again.  Requires 1 <= T1 <= 64, 1 <= k <= 8, k <= V, dmax >= 0. */
+ * zero-filled again.  Requires 1 <= T1 <= 64, 1 <= k <= 8, k <= V <= GRAFT_MAX_VOCAB,
+ * dmax >= 0. */
 int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logits,
                         const int32_t *tok, const int32_t *parent, const int32_t *depth,
                         int32_t *topk, float *topk_prob, float *row_stats, int32_t *accept_len,
@@ -279,7 +281,7 @@ int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logi
  * row_tok int32 [n_rows].  topk_out int32 [n_rows, k] (nullable) receives the
  * top-k computed from `logits` (e.g. the last prompt row's greedy token is the
  * first decode root); ignored with topk_in.  ws as for graft_verify_accept
- * with n_rows rows.  Requires n_rows >= 0, 1 <= k <= 8. */
+ * with n_rows rows.  Requires n_rows >= 0, 1 <= k <= 8, k <= V <= GRAFT_MAX_VOCAB. */
 int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logits,
                       const int32_t *topk_in, const float *prob_in, const int32_t *row_tok,
                       int32_t *table, float *table_prob, int32_t *topk_out, void *ws,
@@ -347,7 +349,7 @@ int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logi
  * logits [B, T1, V] as verified; tok, parent, row_src [B, T1] from the build;
  * row_stats [B, T1, 2] from graft_verify_accept / graft_verify_update on the
  * same logits (so only the retrieved entries are read here).  One wavefront
- * per request, one launch.  Requires 1 <= T1 <= 64. */
+ * per request, one launch.  Requires 1 <= T1 <= 64, V <= GRAFT_MAX_VOCAB. */
 int graft_coverage_gain(int B, int T1, int V, int dtype, const void *logits, const int32_t *tok,
                         const int32_t *parent, const uint8_t *row_src, const float *row_stats,
                         float *gain, hipStream_t stream);

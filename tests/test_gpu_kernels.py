@@ -78,7 +78,7 @@ def _rows_suite(rng, n, V):
     return suite
 
 
-@pytest.mark.parametrize("V", [151936, 32000, 1001, 4097, 9, 8, 15])
+@pytest.mark.parametrize("V", [151936, 32000, 1001, 4097, 9, 8, 15, L.GRAFT_MAX_VOCAB, 999_999])
 def test_topk_bf16_parity(V):
     rng = np.random.default_rng(V)
     n = 24 if V > 10000 else 40
@@ -88,7 +88,7 @@ def test_topk_bf16_parity(V):
         assert (got == want).all(), (name, V, np.nonzero((got != want).any(1))[0][:5])
 
 
-@pytest.mark.parametrize("V,k", [(32000, 8), (1003, 8), (5, 5), (64, 3), (128256, 1)])
+@pytest.mark.parametrize("V,k", [(32000, 8), (1003, 8), (5, 5), (64, 3), (128256, 1), (L.GRAFT_MAX_VOCAB, 8)])
 def test_topk_f32_parity(V, k):
     rng = np.random.default_rng(V + k)
     z = rng.standard_normal((20, V)).astype(np.float32)

@@ -160,3 +160,19 @@ def test_input_check_validation_rejects_without_launch():
     assert lib.graft_check_tree(1, 65, 100, P, P, P, P, None) == L.GRAFT_EINVAL
     assert lib.graft_check_tree(1, 61, 100, P, None, P, P, None) == L.GRAFT_EINVAL
     assert lib.graft_check_tree(0, 61, 100, None, None, None, None, None) == L.GRAFT_OK
+
+
+def test_vocabulary_limit_rejects_without_launch():
+    """Top-k calls take at most GRAFT_MAX_VOCAB logits per row (16 wavefronts
+    per row, 16-bit local offsets); the header's value is the binding's."""
+    src = open(os.path.join(ROOT, "include", "graft.h")).read()
+    assert re.search(r"#define GRAFT_MAX_VOCAB (\d+)", src).group(1) == str(L.GRAFT_MAX_VOCAB)
+    lib = L.load()
+    P = 0x1000  # never dereferenced
+    big = L.GRAFT_MAX_VOCAB + 1
+    assert L.graft_workspace_bytes(976, big, 8, L.DTYPE_BF16) == 0
+    assert L.graft_workspace_bytes(976, L.GRAFT_MAX_VOCAB, 8, L.DTYPE_BF16) > 0
+    assert lib.graft_verify_accept(1, 61, big, 8, 1, *([P] * 9), 60, P, None, P, 1 << 30, None) == L.GRAFT_EINVAL
+    assert lib.graft_verify_update(1, 61, big, 8, 1, *([P] * 11), 60, P, None, P, 1 << 30, None) == L.GRAFT_EINVAL
+    assert lib.graft_update_topk(4, big, 8, 1, P, None, None, P, P, None, P, P, 1 << 30, None) == L.GRAFT_EINVAL
+    assert lib.graft_coverage_gain(1, 61, big, 1, P, P, P, P, P, P, None) == L.GRAFT_EINVAL
