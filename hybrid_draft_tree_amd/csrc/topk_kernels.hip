@@ -761,14 +761,15 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     TopkPlan p;
     p.n_rows = n_rows;
     p.V = V;
-    // S waves per row: about 4096 waves in flight over the chip (~16 per CU),
+    // S waves per row: about 3840 waves over the chip (15 per CU; measured:
+    // at 976 rows 4 per row beat 3 and 5, and 6 was far slower),
     // at most 16 per row, and few enough blocks per wave that local offsets
     // fit: bf16 ranks hold 16-bit offsets (127 blocks of 512 elements per
     // wave), fp32 ranks 32-bit ones, where the 16-bit pending-group index
     // allows 1023 blocks of 256.
     const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
     const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
-    const int64_t target_waves = 4096;
+    const int64_t target_waves = 3840;
     int64_t S = (target_waves + (n_rows > 0 ? n_rows : 1) - 1) / (n_rows > 0 ? n_rows : 1);
     S = S < 1 ? 1 : (S > kMaxWavesPerRow ? kMaxWavesPerRow : S);
     const int64_t per_wave = dtype == GRAFT_DTYPE_BF16 ? 127 : 1023;
