@@ -88,8 +88,8 @@ void launch_build(const BuildKernelArgs &a, hipStream_t s);
 struct TopkPlan {
     int64_t n_rows = 0;
     int V = 0;
-    int splits = 1;           // wavefronts per row (one workgroup per row)
-    int chunk = 0;            // unused
+    int splits = 1;           // wavefronts per row (one workgroup per row), plain launches
+    int dtype = 0;            // GRAFT_DTYPE_*
     size_t off_counters = 0;  // completion words [n_rows]
     size_t off_occ = 0;       // last holder per token [V], one spare word, hand-offs [n_rows]
     size_t ws_bytes = 0;      // workspace bytes the kernel uses (all zero between calls)

@@ -757,19 +757,13 @@ void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
 
 }  // namespace
 
-TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
-    TopkPlan p;
-    p.n_rows = n_rows;
-    p.V = V;
-    // S waves per row: about 3840 waves over the chip (15 per CU; measured:
-    // at 976 rows 4 per row beat 3 and 5, and 6 was far slower),
-    // at most 16 per row, and few enough blocks per wave that local offsets
-    // fit: bf16 ranks hold 16-bit offsets (127 blocks of 512 elements per
-    // wave), fp32 ranks 32-bit ones, where the 16-bit pending-group index
-    // allows 1023 blocks of 256.
+// S waves per row: about target_waves over the chip, at most 16 per row, and
+// few enough blocks per wave that local offsets fit: bf16 ranks hold 16-bit
+// offsets (127 blocks of 512 elements per wave), fp32 ranks 32-bit ones,
+// where the 16-bit pending-group index allows 1023 blocks of 256.
+static int waves_per_row(int64_t n_rows, int V, int dtype, int64_t target_waves) {
     const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
     const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
-    const int64_t target_waves = 3840;
     int64_t S = (target_waves + (n_rows > 0 ? n_rows : 1) - 1) / (n_rows > 0 ? n_rows : 1);
     S = S < 1 ? 1 : (S > kMaxWavesPerRow ? kMaxWavesPerRow : S);
     const int64_t per_wave = dtype == GRAFT_DTYPE_BF16 ? 127 : 1023;
@@ -777,8 +771,20 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     if (S < smin) S = smin;
     if (S > nblk && nblk > 0) S = nblk;
     if (S < 1) S = 1;
-    p.splits = (int)S;
-    p.chunk = 0;
+    return (int)S;
+}
+
+// The plain stream: 3840 waves (15 per CU; at 976 rows 4 per row beat 3
+// and 5, 6 was far slower).  With softmax statistics the rows are bound by
+// the exponentials instead, and more waves pay: 4880.
+constexpr int64_t kTargetWaves = 3840, kTargetWavesProb = 4880;
+
+TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
+    TopkPlan p;
+    p.n_rows = n_rows;
+    p.V = V;
+    p.dtype = dtype;
+    p.splits = waves_per_row(n_rows, V, dtype, kTargetWaves);
     // workspace: [completion words [n_rows] | last holder per token [V], spare,
     //             hand-offs [n_rows]]
     p.off_counters = 0;
@@ -794,7 +800,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     a.logits = logits;
     a.n_rows = p.n_rows;
     a.V = p.V;
-    a.S = p.splits;
+    a.S = (prob || stats) ? waves_per_row(p.n_rows, p.V, p.dtype, kTargetWavesProb) : p.splits;
     a.k = k;
     a.topk = topk;
     a.prob = prob;
@@ -806,7 +812,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
         v.last_occ = (int32_t *)((char *)ws + p.off_occ);
         v.handoff = (uint32_t *)(v.last_occ + p.V + 1);
         v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
-        v.ncoord = (v.B + p.splits - 1) / p.splits;  // one wavefront per request
+        v.ncoord = (v.B + a.S - 1) / a.S;  // one wavefront per request
     }
     if (dtype == GRAFT_DTYPE_BF16)
         launch_rows<Bf16Traits>(a, verify ? &v : nullptr, s);
