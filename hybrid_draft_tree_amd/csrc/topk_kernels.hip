@@ -648,7 +648,20 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     __syncthreads();
     if (wv != 0) return;
     uint64_t rtop = 0;  // lanes 0..7: the row's top-8 (row ranks), descending
-    {
+    if (S * kTop <= kWave) {
+        // one entry per lane: its rank is the number of entries above it (row
+        // ranks are distinct, zeros mark empty slots), read as LDS broadcasts
+        const int nent = S * kTop;
+        const uint64_t x = lane < nent ? s_cand[lane] : 0ull;
+        int above = 0;
+        for (int j = 0; j < nent; ++j) above += s_cand[j] > x ? 1 : 0;
+        if (lane < kTop) s_top[lane] = 0ull;
+        if (x != 0ull && above < kTop) s_top[above] = x;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        rtop = lane < kTop ? s_top[lane] : 0ull;
+    } else {
         int T = INT_MIN;
         for (int w = 0; w < S; ++w) T = max(T, s_kth[w]);
         uint64_t c[2];
