@@ -509,6 +509,62 @@ def main():
     log("retrieval ahead: one-launch build %.2f us; retrieval alone %.2f us; prune + flatten after it %.2f us"
         % (build_ms * 1e3, ret_ms * 1e3, after_ms * 1e3))
 
+    # ---------------- the same kernel on the other shapes (outside the step) ----------------
+    # TAIL (16 requests x 17 rows: a 16-token block plus its anchor, 82.65 MB of
+    # logits) and one prompt-ingest chunk (2048 rows, 622.3 MB): each a single
+    # k_topk_rows launch, timed like the dominant kernel.
+    tcfg = CONFIGS[5]
+    tp = GraftPipeline.from_config(tcfg, device=dev)
+    tad = _Adapter(tp, torch)
+    twl = R.Workload(tcfg)
+    R.start(tad, twl)
+    for s_ in range(2):
+        R.step(tad, twl, s_, G.WARMUP_STREAM_OFFSET)
+    tflat = tad.build(twl.draft(0, tad.get_roots()))
+    tbuf = torch.empty(tcfg.B * tcfg.rows_per_request, V, dtype=torch.bfloat16, device=dev)
+    tad.rows = tad.DeviceRows(twl.pool, dev)
+    tad.rows.materialize(twl.logit_desc(0, tflat), out=tbuf)
+    t_scratch = torch.zeros(tcfg.B, dtype=torch.int32, device=dev)
+
+    def tail_call(i):
+        L.graft_verify_update(tcfg.B, tp.T1, V, k, tp.dtype, tbuf.data_ptr(), tp.tok.data_ptr(), tp.parent.data_ptr(),
+                              tp.depth.data_ptr(), tp.table.data_ptr(), None, tp.topk.data_ptr(), None, None,
+                              tp.accept_len.data_ptr(), tp.accept_idx.data_ptr(), tp.dmax, t_scratch.data_ptr(), None,
+                              tp.ws.data_ptr(), tp.ws_bytes, stream.cuda_stream)
+
+    tail_bytes = tbuf.numel() * 2 + tbuf.shape[0] * k * 4
+    tail_ms = time_calls(tail_call, 50)
+    chunk = 2048
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20240)
+    ibuf = torch.randn(chunk, V, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    irow = torch.randint(0, V, (chunk,), generator=gen, device=dev, dtype=torch.int32)
+    itab = torch.zeros(V, k, dtype=torch.int32, device=dev)
+    iout = torch.empty(chunk, k, dtype=torch.int32, device=dev)
+    iws_n = L.graft_workspace_bytes(chunk, V, k, pipe.dtype)
+    iws = torch.zeros(iws_n, dtype=torch.uint8, device=dev)
+
+    def ingest_call(i):
+        L.graft_update_topk(chunk, V, k, pipe.dtype, ibuf.data_ptr(), None, None, irow.data_ptr(), itab.data_ptr(),
+                            None, iout.data_ptr(), iws.data_ptr(), iws_n, stream.cuda_stream)
+
+    ingest_bytes = ibuf.numel() * 2 + chunk * k * 4
+    ingest_ms = time_calls(ingest_call, 20)
+    # one request's tree (61 rows of the same vocabulary): top-k + matrix update
+    b1 = T1
+
+    def b1_call(i):
+        L.graft_update_topk(b1, V, k, pipe.dtype, ibuf.data_ptr(), None, None, irow.data_ptr(), itab.data_ptr(),
+                            None, iout.data_ptr(), iws.data_ptr(), iws_n, stream.cuda_stream)
+
+    b1_bytes = b1 * V * 2 + b1 * k * 4
+    b1_ms = time_calls(b1_call, 50)
+    log("other shapes: TAIL verify %.2f us (%.0f GB/s); ingest chunk of %d rows %.2f us (%.0f GB/s); "
+        "one request's %d rows %.2f us (%.0f GB/s)"
+        % (tail_ms * 1e3, tail_bytes / (tail_ms * 1e-3) / 1e9, chunk, ingest_ms * 1e3,
+           ingest_bytes / (ingest_ms * 1e-3) / 1e9, b1, b1_ms * 1e3, b1_bytes / (b1_ms * 1e-3) / 1e9))
+    del ibuf, iws, tbuf
+
     copy_gbps = None
     if args.copy_calib:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -580,6 +636,16 @@ def main():
                                        "note": "event-timed single launches (dispatch included) outside the timed "
                                                "step; with retrieval run ahead on a side stream during drafting, "
                                                "the post-draft build is build_after_retrieval_us"},
+        "other_shapes_diagnostic": {
+            "tail_verify_us": round(tail_ms * 1e3, 3),
+            "tail_GBps": round(tail_bytes / (tail_ms * 1e-3) / 1e9, 1),
+            "ingest_chunk_us": round(ingest_ms * 1e3, 3),
+            "ingest_GBps": round(ingest_bytes / (ingest_ms * 1e-3) / 1e9, 1),
+            "one_request_61_rows_us": round(b1_ms * 1e3, 3),
+            "one_request_61_rows_GBps": round(b1_bytes / (b1_ms * 1e-3) / 1e9, 1),
+            "note": "k_topk_rows on the TAIL shape (16 x 17 rows, graft_verify_update) and on one 2048-row "
+                    "prompt-ingest chunk and on one request's 61 rows (graft_update_topk with logits), "
+                    "event-timed single launches outside the timed step"},
         "roofline": {"kernel": "k_topk_rows (graft_verify_update: row-wise top-k + acceptance walk + matrix update)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,

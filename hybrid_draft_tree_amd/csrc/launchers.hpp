@@ -92,6 +92,10 @@ struct TopkPlan {
     int dtype = 0;            // GRAFT_DTYPE_*
     size_t off_counters = 0;  // completion words [n_rows]
     size_t off_occ = 0;       // last holder per token [V], one spare word, hand-offs [n_rows]
+    int groups = 1;           // workgroups per row (rows split when there are few of them)
+    size_t off_cnt = 0;       // groups > 1: arrival counters [n_rows], slice results [n_rows, groups]
+    size_t off_part = 0;
+    size_t off_pstat = 0;
     size_t ws_bytes = 0;      // workspace bytes the kernel uses (all zero between calls)
 };
 
@@ -105,6 +109,12 @@ struct TopkArgs {
     int32_t *topk;
     float *prob;   // nullable: softmax probability of each top-k id
     float *stats;  // nullable: per row (largest value, sum of exp(value - largest))
+    // rows split over `groups` workgroups (groups > 1): per-row arrival counters,
+    // each slice's top-8 (row ranks) and softmax statistics, all in the workspace
+    int groups;
+    uint32_t *cnt;
+    uint64_t *part;
+    float *pstat;
 };
 
 struct VerifyArgs {

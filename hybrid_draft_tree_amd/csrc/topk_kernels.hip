@@ -417,7 +417,7 @@ struct RowSmem {
     }
 };
 
-template <typename TR, bool PROB, bool ACCEPT, bool NT>
+template <typename TR, bool PROB, bool ACCEPT, bool NT, bool SPLIT>
 __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a, VerifyArgs v) {
     using Rank = typename TR::Rank;
     using SM = RowSmem<Rank>;
@@ -430,14 +430,18 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int S = blockDim.x >> 6;
-    int64_t row = blockIdx.x;
+    int64_t unit = blockIdx.x;
     if constexpr (ACCEPT) {
-        if (row < v.ncoord) {
-            coordinate(a, v, (int)row);
+        if (unit < v.ncoord) {
+            coordinate(a, v, (int)unit);
             return;
         }
-        row -= v.ncoord;
+        unit -= v.ncoord;
     }
+    // SPLIT: the row is cut into G slices of whole blocks, one per workgroup
+    const int G = SPLIT ? a.groups : 1;
+    const int64_t row = SPLIT ? unit / G : unit;
+    const int g = SPLIT ? (int)(unit - row * G) : 0;
     if (row >= a.n_rows) return;
 
     uint4 *sd = (uint4 *)(smem + (size_t)wv * SM::kData);
@@ -453,11 +457,15 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     // head (until 16-byte alignment), body of 16-byte groups in 1 KB blocks, tail
     int head = (int)(((16u - (uint32_t)((uintptr_t)rowp & 15u)) & 15u) / ESZ);
     head = min(head, V);
-    const int ng = (V - head) / EPG;
-    const int ntail = V - head - ng * EPG;
-    const int nblk = (ng + kWave - 1) / kWave;
+    const int ng_row = (V - head) / EPG;
+    const int ntail = V - head - ng_row * EPG;
+    const int nblk_row = (ng_row + kWave - 1) / kWave;
+    const int blk0 = SPLIT ? (int)((int64_t)g * nblk_row / G) : 0;  // this slice's blocks [blk0, blk1)
+    const int blk1 = SPLIT ? (int)((int64_t)(g + 1) * nblk_row / G) : nblk_row;
+    const int ng = SPLIT ? min(ng_row, blk1 * kWave) - blk0 * kWave : ng_row;  // groups of the slice
+    const int nblk = blk1 - blk0;
     const int kcount = nblk > wv ? (nblk - wv + S - 1) / S : 0;  // blocks of this wave
-    const uint4 *vp = (const uint4 *)(rowp + (size_t)head * ESZ);
+    const uint4 *vp = (const uint4 *)(rowp + (size_t)head * ESZ) + (size_t)blk0 * kWave;
 
     // Local offsets (monotone in the element id for this wave): head elements
     // 0..head-1 (wave 0), body kHeadPad + k*BLK + lane*EPG + e for the wave's
@@ -465,8 +473,8 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     auto global_id = [&](uint32_t off) __attribute__((always_inline)) -> uint32_t {
         if (off < (uint32_t)kHeadPad) return off;
         const uint32_t q = off - kHeadPad;
-        if (q < (uint32_t)kcount * BLK) return head + (wv + (q / BLK) * S) * BLK + q % BLK;
-        return head + ng * EPG + (q - (uint32_t)kcount * BLK);
+        if (q < (uint32_t)kcount * BLK) return head + (blk0 + wv + (q / BLK) * S) * BLK + q % BLK;
+        return head + ng_row * EPG + (q - (uint32_t)kcount * BLK);
     };
 
     Rank top = 0;   // lanes 0..7: the wave's top-8, descending
@@ -474,7 +482,7 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     int thr = INT_MIN;
     SoftStats st;
 
-    if (wv == 0) {  // head and tail elements: at most EPG-1 each
+    if (wv == 0 && g == 0) {  // head and tail elements: at most EPG-1 each
         Rank c[1] = {0};
         bool have = false;
         int off = 0, idx = 0;
@@ -484,7 +492,7 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
             have = true;
         } else if (lane >= 16 && lane - 16 < ntail) {
             off = kHeadPad + kcount * BLK + (lane - 16);
-            idx = head + ng * EPG + (lane - 16);
+            idx = head + ng_row * EPG + (lane - 16);
             have = true;
         }
         if (have) {
@@ -702,16 +710,66 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
             merge_top8<uint64_t, 2>(c, rtop);
         }
     }
+    // the workgroup's softmax statistics (largest value, sum of exp(x - largest))
+    float rowM = -INFINITY, rowS = 0.0f;
+    if constexpr (PROB) {
+        const float2 sv = lane < S ? s_stat[lane] : make_float2(-INFINITY, 0.0f);
+        rowM = wave_max_f32(sv.x);
+        const float s = (sv.x == -INFINITY) ? 0.0f : sv.y * __expf(sv.x - rowM);
+        rowS = wave_sum_f32(s);
+    }
+    if constexpr (SPLIT) {
+        // Publish this slice's top-8 and statistics; the row's last slice to
+        // arrive (per-row counter, no waiting) merges the G results and goes on
+        // as the row's finisher, clearing what it read.
+        const size_t pb = (size_t)row * G * kTop;
+        if (lane < kTop) st_agent(&a.part[pb + (size_t)g * kTop + lane], rtop);
+        if (PROB && lane == 0) {
+            st_agent((int32_t *)&a.pstat[2 * ((size_t)row * G + g)], __float_as_int(rowM));
+            st_agent((int32_t *)&a.pstat[2 * ((size_t)row * G + g) + 1], __float_as_int(rowS));
+        }
+        publish();
+        uint32_t old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(&a.cnt[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int)readlane_i32((int)old, 0) != G - 1) return;
+        after_count();
+        const int n = G * kTop;  // <= 64: one entry per lane
+        const uint64_t x = lane < n ? ld_agent(&a.part[pb + lane]) : 0ull;
+        int above = 0;
+        for (int j = 0; j < n; ++j) {
+            const uint32_t lo = (uint32_t)readlane_i32((int)(uint32_t)x, j);
+            const uint32_t hi = (uint32_t)readlane_i32((int)(uint32_t)(x >> 32), j);
+            above += (((uint64_t)hi << 32) | lo) > x ? 1 : 0;
+        }
+        if (lane < kTop) s_top[lane] = 0ull;
+        if (x != 0ull && above < kTop) s_top[above] = x;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        rtop = lane < kTop ? s_top[lane] : 0ull;
+        if (lane < n) st_agent(&a.part[pb + lane], 0ull);
+        if constexpr (PROB) {
+            float m = -INFINITY, ss = 0.0f;
+            if (lane < G) {
+                const size_t q = 2 * ((size_t)row * G + lane);
+                m = __int_as_float(ld_agent((const int32_t *)&a.pstat[q]));
+                ss = __int_as_float(ld_agent((const int32_t *)&a.pstat[q + 1]));
+                st_agent((int32_t *)&a.pstat[q], 0);
+                st_agent((int32_t *)&a.pstat[q + 1], 0);
+            }
+            rowM = wave_max_f32(m);
+            rowS = wave_sum_f32((m == -INFINITY) ? 0.0f : ss * __expf(m - rowM));
+        }
+        if (lane == 0) st_agent(&a.cnt[row], 0u);
+    }
     int32_t my_id = -1;  // lanes j < k: the row's j-th id and probability
     float my_p = 0.0f;
     {
         my_id = rtop ? (int32_t)rank64_id(rtop) : -1;
         if (lane < a.k) st_agent(&a.topk[row * a.k + lane], my_id);
         if (PROB) {
-            const float2 sv = lane < S ? s_stat[lane] : make_float2(-INFINITY, 0.0f);
-            const float M = wave_max_f32(sv.x);
-            const float s = (sv.x == -INFINITY) ? 0.0f : sv.y * __expf(sv.x - M);
-            const float Ssum = wave_sum_f32(s);
+            const float M = rowM;
+            const float Ssum = rowS;
             if (a.stats && lane == 0) *(float2 *)&a.stats[row * 2] = make_float2(M, Ssum);
             if (a.prob && lane < a.k) {
                 const float x = key_to_f32(rank64_key(rtop));
@@ -746,25 +804,33 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     }
 }
 
+template <typename TR, bool PROB, bool ACCEPT>
+void launch_rows_as(const TopkArgs &a, const VerifyArgs &vv, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    if (a.groups > 1)
+        hipLaunchKernelGGL((k_topk_rows<TR, PROB, ACCEPT, true, true>), grid, block, lds, s, a, vv);
+    else
+        hipLaunchKernelGGL((k_topk_rows<TR, PROB, ACCEPT, true, false>), grid, block, lds, s, a, vv);
+}
+
 template <typename TR>
 void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
     using Rank = typename TR::Rank;
     const int extra = v ? v->ncoord : 0;  // the coordinator workgroups
-    const dim3 grid((unsigned)(a.n_rows + extra));
+    const dim3 grid((unsigned)(a.n_rows * a.groups + extra));
     const dim3 block(kWave * a.S);
     const size_t lds = RowSmem<Rank>::bytes(a.S);
     const VerifyArgs vv = v ? *v : VerifyArgs{};
     const bool prob = a.prob != nullptr || a.stats != nullptr;  // softmax statistics wanted
     if (v) {
         if (prob)
-            hipLaunchKernelGGL((k_topk_rows<TR, true, true, true>), grid, block, lds, s, a, vv);
+            launch_rows_as<TR, true, true>(a, vv, grid, block, lds, s);
         else
-            hipLaunchKernelGGL((k_topk_rows<TR, false, true, true>), grid, block, lds, s, a, vv);
+            launch_rows_as<TR, false, true>(a, vv, grid, block, lds, s);
     } else {
         if (prob)
-            hipLaunchKernelGGL((k_topk_rows<TR, true, false, true>), grid, block, lds, s, a, vv);
+            launch_rows_as<TR, true, false>(a, vv, grid, block, lds, s);
         else
-            hipLaunchKernelGGL((k_topk_rows<TR, false, false, true>), grid, block, lds, s, a, vv);
+            launch_rows_as<TR, false, false>(a, vv, grid, block, lds, s);
     }
 }
 
@@ -774,10 +840,11 @@ void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
 // few enough blocks per wave that local offsets fit: bf16 ranks hold 16-bit
 // offsets (127 blocks of 512 elements per wave), fp32 ranks 32-bit ones,
 // where the 16-bit pending-group index allows 1023 blocks of 256.
-static int waves_per_row(int64_t n_rows, int V, int dtype, int64_t target_waves) {
+static int waves_per_row(int64_t n_rows, int V, int dtype, int64_t target_waves, int groups) {
     const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
-    const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
-    int64_t S = (target_waves + (n_rows > 0 ? n_rows : 1) - 1) / (n_rows > 0 ? n_rows : 1);
+    const int64_t nblk = (((int64_t)V / epg + kWave - 1) / kWave + groups - 1) / groups;  // blocks per slice
+    const int64_t units = (n_rows > 0 ? n_rows : 1) * groups;
+    int64_t S = (target_waves + units - 1) / units;
     S = S < 1 ? 1 : (S > kMaxWavesPerRow ? kMaxWavesPerRow : S);
     const int64_t per_wave = dtype == GRAFT_DTYPE_BF16 ? 127 : 1023;
     const int64_t smin = (nblk + per_wave - 1) / per_wave;
@@ -792,17 +859,41 @@ static int waves_per_row(int64_t n_rows, int V, int dtype, int64_t target_waves)
 // the exponentials instead, and more waves pay: 4880.
 constexpr int64_t kTargetWaves = 3840, kTargetWavesProb = 4880;
 
+// Rows are split over several workgroups when there are too few of them to
+// spread over the chip (fewer than 512): about 1024 workgroups in all, at most
+// 8 per row (one merge entry per lane), each slice at least 8 blocks.
+constexpr int64_t kSplitBelowRows = 512, kSplitTargetUnits = 1024;
+constexpr int kMaxGroups = 8;
+
+static int groups_per_row(int64_t n_rows, int V, int dtype) {
+    if (n_rows <= 0 || n_rows >= kSplitBelowRows) return 1;
+    const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
+    const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
+    int64_t G = (kSplitTargetUnits + n_rows - 1) / n_rows;
+    G = G > kMaxGroups ? kMaxGroups : G;
+    G = G > nblk / 8 ? nblk / 8 : G;
+    return G < 1 ? 1 : (int)G;
+}
+
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     TopkPlan p;
     p.n_rows = n_rows;
     p.V = V;
     p.dtype = dtype;
-    p.splits = waves_per_row(n_rows, V, dtype, kTargetWaves);
+    p.groups = groups_per_row(n_rows, V, dtype);
+    p.splits = waves_per_row(n_rows, V, dtype, kTargetWaves, p.groups);
     // workspace: [completion words [n_rows] | last holder per token [V], spare,
     //             hand-offs [n_rows]]
     p.off_counters = 0;
     p.off_occ = ((size_t)n_rows * sizeof(int32_t) + 255) / 256 * 256;
     p.ws_bytes = p.off_occ + ((size_t)(V + 1 + n_rows) * sizeof(uint32_t) + 255) / 256 * 256;
+    if (p.groups > 1) {  // [arrival counters [n_rows] | slice top-8s [n_rows, G, 8] | slice statistics]
+        const size_t nr = (size_t)n_rows, G = (size_t)p.groups;
+        p.off_cnt = p.ws_bytes;
+        p.off_part = p.off_cnt + (nr * sizeof(uint32_t) + 255) / 256 * 256;
+        p.off_pstat = p.off_part + (nr * G * kTop * sizeof(uint64_t) + 255) / 256 * 256;
+        p.ws_bytes = p.off_pstat + (nr * G * 2 * sizeof(float) + 255) / 256 * 256;
+    }
     return p;
 }
 
@@ -813,7 +904,11 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     a.logits = logits;
     a.n_rows = p.n_rows;
     a.V = p.V;
-    a.S = (prob || stats) ? waves_per_row(p.n_rows, p.V, p.dtype, kTargetWavesProb) : p.splits;
+    a.S = (prob || stats) ? waves_per_row(p.n_rows, p.V, p.dtype, kTargetWavesProb, p.groups) : p.splits;
+    a.groups = p.groups;
+    a.cnt = p.groups > 1 ? (uint32_t *)((char *)ws + p.off_cnt) : nullptr;
+    a.part = p.groups > 1 ? (uint64_t *)((char *)ws + p.off_part) : nullptr;
+    a.pstat = p.groups > 1 ? (float *)((char *)ws + p.off_pstat) : nullptr;
     a.k = k;
     a.topk = topk;
     a.prob = prob;
