@@ -412,9 +412,15 @@ int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logit
         if (ws_bytes < L.total) return GRAFT_EINVAL;
         int32_t *tk_ws = topk_out ? topk_out : (int32_t *)((char *)ws + L.off_topk);
         float *pr_ws = table_prob ? (float *)((char *)ws + L.off_prob) : nullptr;
-        launch_topk(L.plan, dtype, logits, k, tk_ws, pr_ws, nullptr, ws, nullptr, stream);
-        tk = tk_ws;
-        pr = pr_ws;
+        // top-k and the matrix update in one launch: the registration workgroup
+        // and the per-row hand-off of graft_verify_update, without requests
+        VerifyArgs v{};
+        v.tok = row_tok;
+        v.table = table;
+        v.table_prob = table_prob;
+        v.update_only = 1;
+        launch_topk(L.plan, dtype, logits, k, tk_ws, pr_ws, nullptr, ws, &v, stream);
+        return launch_status();
     } else if (table_prob && !prob_in) {
         return GRAFT_EINVAL;
     }

@@ -135,6 +135,7 @@ struct VerifyArgs {
     uint32_t *handoff = nullptr;   // [n_rows] row-done / registration-done hand-off
     int B = 0;
     int ncoord = 0;                // coordinator workgroups (one wavefront per request)
+    int update_only = 0;           // no requests: the matrix update alone (one registration workgroup)
 };
 
 // Row-wise top-k of logits [n_rows, V] into topk [n_rows, k] (+ probabilities);

@@ -780,7 +780,7 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     }
     if constexpr (ACCEPT) {
         // Completion word for the coordinator: greedy token + 1 (lane 0 holds it).
-        if (lane == 0) st_agent(&v.done[row], my_id + 1);
+        if (v.B > 0 && lane == 0) st_agent(&v.done[row], my_id + 1);
         // Fused update: hand the row to the update.  Fast path: the registration
         // already arrived (it finishes long before the rows do); otherwise the
         // second arrival at the row's hand-off word updates the row.
@@ -919,8 +919,13 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
         v.done = (int32_t *)((char *)ws + p.off_counters);
         v.last_occ = (int32_t *)((char *)ws + p.off_occ);
         v.handoff = (uint32_t *)(v.last_occ + p.V + 1);
-        v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
-        v.ncoord = (v.B + a.S - 1) / a.S;  // one wavefront per request
+        if (v.update_only) {
+            v.B = 0;
+            v.ncoord = 1;  // the registration
+        } else {
+            v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
+            v.ncoord = (v.B + a.S - 1) / a.S;  // one wavefront per request
+        }
     }
     if (dtype == GRAFT_DTYPE_BF16)
         launch_rows<Bf16Traits>(a, verify ? &v : nullptr, s);

@@ -281,7 +281,10 @@ int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logi
  * row_tok int32 [n_rows].  topk_out int32 [n_rows, k] (nullable) receives the
  * top-k computed from `logits` (e.g. the last prompt row's greedy token is the
  * first decode root); ignored with topk_in.  ws as for graft_verify_accept
- * with n_rows rows.  Requires n_rows >= 0, 1 <= k <= 8, k <= V <= GRAFT_MAX_VOCAB. */
+ * with n_rows rows.  With logits the update runs in the same launch as the
+ * top-k (each row hands its result to the update as in graft_verify_update);
+ * with topk_in it is a launch of its own.  Requires n_rows >= 0,
+ * 1 <= k <= 8, k <= V <= GRAFT_MAX_VOCAB. */
 int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logits,
                       const int32_t *topk_in, const float *prob_in, const int32_t *row_tok,
                       int32_t *table, float *table_prob, int32_t *topk_out, void *ws,
