@@ -897,3 +897,56 @@ def test_pipeline_debug_checks_raise_on_a_bad_draft():
     with pytest.raises(ValueError, match=r"request\(s\) \[2\].*score"):
         hb.build(d)
     assert isinstance(hb.p, GraftPipeline)
+
+
+@pytest.mark.parametrize("layout", ["compact", "in_place"])
+def test_build_at_the_largest_tree(layout):
+    """63 draft nodes, 63 slots, 64 verified rows: the ancestor mask's top bit
+    is used and the retrieval fills up to 55 slots."""
+    rng = np.random.default_rng(50)
+    par, lay, _ = G.static_tree((8, 16, 16, 12, 8, 3))
+    Nd, slots, T1 = 63, 63, 64
+    B, V = 24, 7000
+    P, Ly = np.tile(par, (B, 1)), np.tile(lay, (B, 1))
+    lp = np.log(rng.dirichlet(np.ones(8), size=(B, Nd)).max(2)).astype(np.float32)
+    lp[0::4, lay == 0] -= 1.5          # stage 0
+    lp[1::4, lay == 1] -= 1.2          # stage 1
+    lp[2::4, lay == 5] -= 3.0          # stage 2
+    lp[3::4] = 0.0                     # no prune
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    base = rng.integers(0, 100000, size=B).astype(np.int32)
+    d_tok = rng.integers(0, V, size=(B, Nd)).astype(np.int32)
+    R = slots - 8
+    tpl, keepalive, r_out = _tpl_dev(R)
+    tpl_h = _tpl_host(R)
+    cfg = L.prune_cfg(CFG["ckpt"], [float(np.float32(math.log(t))) for t in CFG["tau"]], CFG["keep"], 0.5)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    ins = [_t(x, torch.int32) for x in (table, roots, base, P, Ly)]
+    sc, dt = _t(lp, torch.float32), _t(d_tok, torch.int32)
+    st, nk, nr = (torch.zeros(B, **i32) for _ in range(3))
+    kp = torch.zeros(B, Nd, dtype=torch.uint8, device=DEV)
+    cum = torch.zeros(B, Nd, dtype=torch.float32, device=DEV)
+    rt, rp = torch.zeros(B, r_out, **i32), torch.zeros(B, r_out, **i32)
+    tok, par_o, dep, pos = (torch.zeros(B, T1, **i32) for _ in range(4))
+    anc = torch.zeros(B, T1, dtype=torch.int64, device=DEV)
+    src = torch.full((B, T1), 99, dtype=torch.uint8, device=DEV)
+    L.graft_build_hybrid_tree(B, Nd, T1, L.MODE_TREE, L.LAYOUT[layout], slots, cfg, tpl, V, 8, ins[0].data_ptr(),
+                              ins[1].data_ptr(), ins[2].data_ptr(), ins[3].data_ptr(), ins[4].data_ptr(),
+                              sc.data_ptr(), dt.data_ptr(), st.data_ptr(), nk.data_ptr(), kp.data_ptr(),
+                              cum.data_ptr(), rt.data_ptr(), rp.data_ptr(), nr.data_ptr(), r_out, tok.data_ptr(),
+                              par_o.data_ptr(), dep.data_ptr(), pos.data_ptr(), anc.data_ptr(), src.data_ptr(), _s())
+    torch.cuda.synchronize()
+    pr = O.prune_tree(P, Ly, lp, want_cum=True)
+    ret = O.retrieve_tree(table, roots, pr["n_keep"], slots, tpl_h)
+    fl = O.flatten(layout, T1, roots, base, d_tok, P, pr["keep"], pr["n_keep"], ret)
+    assert set(pr["stage"].tolist()) == {0, 1, 2, 3}
+    np.testing.assert_array_equal(st.cpu().numpy(), pr["stage"])
+    np.testing.assert_array_equal(kp.cpu().numpy(), pr["keep"])
+    np.testing.assert_array_equal(nr.cpu().numpy(), ret["n_ret"])
+    for name, got in (("tok", tok), ("parent", par_o), ("depth", dep), ("pos_id", pos)):
+        np.testing.assert_array_equal(got.cpu().numpy(), fl[name], err_msg=(layout, name))
+    a = anc.cpu().numpy().view(np.uint64)
+    np.testing.assert_array_equal(a, fl["anc"])
+    np.testing.assert_array_equal(src.cpu().numpy(), fl["row_src"])
+    assert ((a >> np.uint64(63)) & np.uint64(1)).any()     # row 63 exists and is its own ancestor

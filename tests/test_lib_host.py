@@ -176,3 +176,19 @@ def test_vocabulary_limit_rejects_without_launch():
     assert lib.graft_verify_update(1, 61, big, 8, 1, *([P] * 11), 60, P, None, P, 1 << 30, None) == L.GRAFT_EINVAL
     assert lib.graft_update_topk(4, big, 8, 1, P, None, None, P, P, None, P, P, 1 << 30, None) == L.GRAFT_EINVAL
     assert lib.graft_coverage_gain(1, 61, big, 1, P, P, P, P, P, P, None) == L.GRAFT_EINVAL
+
+
+def test_empty_batches_enqueue_nothing():
+    """B == 0 (or n_rows == 0) returns GRAFT_OK before any pointer is looked at."""
+    cfg = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 40), 0.5)
+    lib = L.load()
+    cb = ctypes.byref(cfg)
+    assert lib.graft_prune_select(0, 60, 0, None, None, None, cb, None, None, None, None, None) == L.GRAFT_OK
+    assert lib.graft_build_tree_mask(0, 60, 61, 0, *([None] * 9), 52, *([None] * 6), None) == L.GRAFT_OK
+    assert lib.graft_build_hybrid_tree(0, 60, 61, 0, 1, 60, cb, None, 100, 8, *([None] * 14), 52,
+                                       *([None] * 6), None) == L.GRAFT_OK
+    assert lib.graft_verify_accept(0, 61, 100, 8, 1, *([None] * 9), 60, None, None, None, 0, None) == L.GRAFT_OK
+    assert lib.graft_verify_update(0, 61, 100, 8, 1, *([None] * 11), 60, None, None, None, 0, None) == L.GRAFT_OK
+    assert lib.graft_update_topk(0, 100, 8, 1, *([None] * 7), None, 0, None) == L.GRAFT_OK
+    assert lib.graft_coverage_gain(0, 61, 100, 1, *([None] * 6), None) == L.GRAFT_OK
+    assert lib.graft_checkpoint_stats(0, 60, None, None, None, cb, None, None) == L.GRAFT_OK
