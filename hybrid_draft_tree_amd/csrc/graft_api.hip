@@ -21,7 +21,9 @@ inline int launch_status() {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// workspace: [top-k partials | softmax stats | counters | top-k rows | top-k probs]
+// workspace: [the top-k launch's words (completion words, last holder per
+// token, hand-offs; with split rows: arrival counters and slice results) |
+// top-k rows | top-k probabilities] -- the last two for graft_update_topk
 struct WsLayout {
     TopkPlan plan;
     size_t off_topk = 0, off_prob = 0, total = 0;

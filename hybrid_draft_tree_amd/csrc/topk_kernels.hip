@@ -5,20 +5,23 @@
 // Order: value descending, ties -> lower id, -0 == +0.  The kernel is an HBM
 // stream: no MFMA (nothing is a contraction).
 //
-// One workgroup per row, S wavefronts.  The row is cut into 1 KB blocks (64
+// One workgroup per row, S wavefronts (with few rows, G workgroups per row,
+//   each on a slice of whole blocks).  The row is cut into 1 KB blocks (64
 //   lanes x 16 bytes = 8 bf16 or 4 fp32 per lane); wavefront j reads blocks
 //   j, j+S, j+2S, ... so that the S waves of a row sweep it together (a
 //   contiguous front per row keeps HBM pages open), two blocks per batch with
-//   the next batch in flight.  A wave-uniform threshold -- the key of the
-//   wave's current 8th-best value -- filters each 16-byte group with a few
-//   packed integer ops; the rare groups that pass are compacted into LDS with a
-//   ballot and merged into the wave's exact top-8 (DPP wave maxima) when 64
-//   are pending.
-// Epilogue: the S waves meet at one barrier; wave 0 merges their candidates
-//   (and softmax statistics) from LDS into the row's top-k.  With the
-//   acceptance walk fused, the last row of a request to finish (device-scope
-//   counter) runs the walk for that request, then its share of the matrix
-//   update.  One launch per call.
+//   the next batch issued before the current one is filtered.  A wave-uniform
+//   threshold -- the key of the wave's current 8th-best value -- filters each
+//   16-byte group with a few packed integer ops; the rare groups that pass
+//   are compacted into LDS with a ballot and merged into the wave's exact
+//   top-8 (DPP wave maxima) when 64 are pending.
+// Epilogue: the S waves meet at one barrier; wave 0 ranks their candidates
+//   (and combines their softmax statistics) into the row's top-k; with G > 1
+//   the row's last slice to arrive merges the slices' results.  The row then
+//   publishes its greedy token in a completion word, which coordinator
+//   wavefronts (one per request, in front of the rows) watch to run the
+//   acceptance walk, and hands its top-k to the matrix update, which a
+//   registration workgroup has prepared.  One launch per call.
 #include "device_utils.hpp"
 #include "launchers.hpp"
 
