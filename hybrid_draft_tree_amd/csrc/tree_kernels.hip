@@ -36,21 +36,20 @@ struct PruneOut {
 // N nodes of layers <= c_s with the largest cum (ties -> lower index).
 __device__ __forceinline__ float cum_levels(bool valid, int par, float lp) {
     const int lane = lane_id();
-    // one level per pass: a node is done once its parent is (root children first)
-    bool done = valid && par < 0;
-    float cum = done ? 0.0f + lp : 0.0f;
-    uint64_t todo = ballot(valid && !done);
-    while (todo) {
-        const int src = par >= 0 ? par : lane;
+    // one level per pass: a node is done once its parent is (root children
+    // first).  The done set is a wave-uniform lane mask, so a node tests its
+    // parent's bit without a shuffle; lane masks are combined as scalars.
+    const uint64_t vmask = ballot(valid);
+    const uint64_t cmask = ballot(par >= 0) & vmask;  // nodes below another node
+    uint64_t done = vmask & ~cmask;
+    float cum = (valid && par < 0) ? 0.0f + lp : 0.0f;
+    const int src = (par >= 0 ? par : lane) & (kWave - 1);
+    while (done != vmask) {
         const float pc = __shfl(cum, src);
-        const int pd = __shfl((int)done, src);
-        if (valid && !done && par >= 0 && pd) {
-            cum = pc + lp;
-            done = true;
-        }
-        const uint64_t left = ballot(valid && !done);
-        if (left == todo) break;  // a parent link that never resolves (bad input)
-        todo = left;
+        const uint64_t newly = ballot(((done >> src) & 1ull) != 0ull) & cmask & ~done;
+        if (!newly) break;  // a parent link that never resolves (bad input)
+        if ((newly >> lane) & 1ull) cum = pc + lp;
+        done |= newly;
     }
     return cum;
 }
@@ -67,31 +66,37 @@ __device__ __forceinline__ PruneOut prune_tree_wave(bool valid, int par, int lay
         const int N = __popcll(ballot(kept));
         return {N < __popcll(ballot(valid)) ? 4 : 3, N, kept, cum};
     }
-    int st = 3;
+    // the three checkpoints are evaluated independently (their wave reductions
+    // overlap); the first in drafting order that fires is the stage
+    const uint64_t vmask = ballot(valid);
+    int on[3], upto[3], best[3];
+#pragma unroll
     for (int s = 0; s < 3; ++s) {
         const int c = cfg.ckpt_layer[s];
-        const int on = __popcll(ballot(valid && lay == c));
-        const int upto = __popcll(ballot(valid && lay <= c));
-        const int best = wave_max_i32((valid && lay == c) ? key : INT_MIN);
-        if (on > 0 && upto >= cfg.keep[s] && best < f32_key(__float_as_uint(cfg.log_thr[s]))) {
-            st = s;
-            break;
-        }
+        on[s] = __popcll(ballot(lay == c) & vmask);
+        upto[s] = __popcll(ballot(lay <= c) & vmask);
+        best[s] = wave_max_i32((valid && lay == c) ? key : INT_MIN);
     }
+    int st = 3;
+#pragma unroll
+    for (int s = 2; s >= 0; --s)
+        if (on[s] > 0 && upto[s] >= cfg.keep[s] && best[s] < f32_key(__float_as_uint(cfg.log_thr[s]))) st = s;
     const int N = st < 3 ? cfg.keep[st] : Nd;
     const int climit = st < 3 ? cfg.ckpt_layer[st] : 0x7fffffff;
-    const bool elig = valid && lay <= climit;
+    const uint64_t emask = ballot(lay <= climit) & vmask;  // eligible nodes
+    const bool elig = (emask >> lane_id()) & 1ull;
     // T = the N-th largest key among the eligible nodes (bitwise search on the
-    // unsigned image of the key); keep every node above T and, of the nodes at
-    // T, the lowest-indexed ones up to N
+    // unsigned image of the key; each step is one compare and a scalar count);
+    // keep every node above T and, of the nodes at T, the lowest-indexed ones
+    // up to N
     const uint32_t u = (uint32_t)key ^ 0x80000000u;
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = T | (1u << bit);
-        if (__popcll(ballot(elig && u >= cand)) >= N) T = cand;
+        if (__popcll(ballot(u >= cand) & emask) >= N) T = cand;
     }
-    const uint64_t gt = ballot(elig && u > T);
-    const uint64_t eq = ballot(elig && u == T);
+    const uint64_t gt = ballot(u > T) & emask;
+    const uint64_t eq = ballot(u == T) & emask;
     const int need = N - __popcll(gt);
     const bool kept = elig && (u > T || (u == T && lanes_below(eq) < need));
     return {st, N, kept, cum};
@@ -140,21 +145,21 @@ __device__ __forceinline__ int retrieve_tree_wave(int R, int tp, int tr, int td,
     const int maxd = wave_max_i32(act ? td : 0);
     if (maxd > kPathLevels) return retrieve_tree_levels(R, tp, tr, td, root, table, V, k);
     const bool own_ok = tr >= 0 && tr < k && td >= 1;
-    uint64_t P = (act && own_ok) ? ((uint64_t)tr << (3 * (td - 1))) : 0ull;
-    int bad = (act && !own_ok) ? 1 : 0;  // some rank on the path is out of range
+    // bit 63 (above the 21 levels of 3-bit ranks) flags a path with a rank out of range
+    constexpr uint64_t kBad = 1ull << 63;
+    uint64_t P = act ? (own_ok ? ((uint64_t)tr << (3 * (td - 1))) : kBad) : 0ull;
     int a = act ? tp : -1;
-#pragma unroll
     for (int r = 0; r < 6; ++r) {
+        if (!ballot(a >= 0)) break;  // every path complete (depth <= 2^r)
         const int src = a >= 0 ? a : lane;
         const uint64_t Pa = shfl_u64(P, src);
-        const int ba = __shfl(bad, src);
         const int aa = __shfl(a, src);
         if (a >= 0) {
             P |= Pa;
-            bad |= ba;
             a = aa;
         }
     }
+    const bool bad = (P & kBad) != 0ull;
     int x = root;
     for (int d = 1; d <= maxd; ++d) {
         if (act && d <= td) {
@@ -275,8 +280,8 @@ __device__ __forceinline__ void flatten_wave(int layout, int T1, const FlatIn &i
     const int p = (link & 0xff) - 1;
     int a = (row_ok && lane > 0) ? p : -1;
     uint64_t A = row_ok ? ((1ull << lane) | (a >= 0 ? (1ull << a) : 0ull)) : 0ull;
-#pragma unroll
     for (int r = 0; r < 6; ++r) {
+        if (!ballot(a >= 0)) break;  // every row's chain has reached the root
         const int src = a >= 0 ? a : lane;
         const uint64_t Aa = shfl_u64(A, src);
         const int aa = __shfl(a, src);
