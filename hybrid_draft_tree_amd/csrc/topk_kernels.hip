@@ -247,40 +247,47 @@ __device__ __forceinline__ void add_groups(SoftStats &st, const uint4 (&d)[U]) {
     st.add_batch<U * EPG>(x);
 }
 
-// Strict greedy acceptance walk of request b (section 二, gear 3), one wavefront;
-// lane f is flattened row f with its greedy token g, token t, parent row p and
-// depth d.  A row is accepted iff every row on its path from the root carries
-// the greedy token of its parent row; the deepest accepted row wins, ties ->
-// lowest row.
-__device__ __forceinline__ void accept_walk(const VerifyArgs &v, int b, int g, int t, int p, int d) {
+// Ancestor-or-self mask of flattened row `lane` (p = parent row, -1 for the
+// root and for lanes that are not rows), by pointer doubling over the parent
+// links.  Depends on the tree alone, so coordinators compute it while they wait
+// for the rows.
+__device__ __forceinline__ uint64_t ancestor_mask(bool row, int p) {
     const int lane = lane_id();
-    const int T1 = v.T1;
-    const bool row = lane < T1;
-    if (!row || lane == 0) p = -1;
-    const int gp = __shfl(g, p >= 0 ? p : lane);
-    bool ok = row && (lane == 0 || (p >= 0 && t == gp));
-    // AND of the edge checks along the path and the ancestor-or-self mask, by
-    // pointer doubling over parent links
     int a = p;
     uint64_t A = row ? ((1ull << lane) | (a >= 0 ? (1ull << a) : 0ull)) : 0ull;
-#pragma unroll
     for (int r = 0; r < 6; ++r) {
+        if (!ballot(a >= 0)) break;  // every chain has reached the root
         const int src = a >= 0 ? a : lane;
-        const int oka = __shfl((int)ok, src);
         const uint64_t Aa = shfl_u64(A, src);
         const int aa = __shfl(a, src);
         if (a >= 0) {
-            ok = ok && oka;
             A |= Aa;
             a = aa;
         }
     }
+    return A;
+}
+
+// Strict greedy acceptance walk of request b (section 二, gear 3), one wavefront;
+// lane f is flattened row f with its greedy token g, token t, parent row p (-1
+// for the root and non-rows), depth d and ancestor-or-self mask A.  A row is
+// accepted iff every row on its path from the root carries the greedy token of
+// its parent row, i.e. iff its mask holds no row whose edge check fails; the
+// deepest accepted row wins, ties -> lowest row.
+__device__ __forceinline__ void accept_walk(const VerifyArgs &v, int b, int g, int t, int p, int d, uint64_t A) {
+    const int lane = lane_id();
+    const int T1 = v.T1;
+    const bool row = lane < T1;
+    const int gp = __shfl(g, p >= 0 ? p : lane);
+    const uint64_t E = ballot(row && (lane == 0 || (p >= 0 && t == gp)));  // edges that hold
+    const bool ok = row && (A & ~E) == 0ull;
     const int key = ok ? (d << 8) | (255 - lane) : -1;
     const int best = wave_max_i32(key);
-    const int fstar = 255 - (best & 255);
+    const int fstar = 255 - (best & 255);  // uniform (the root is always accepted)
     const int len = best >> 8;
-    const uint64_t path = shfl_u64(A, fstar);
-    const int gstar = __shfl(g, fstar);
+    const uint64_t path = ((uint64_t)(uint32_t)readlane_i32((int)(uint32_t)(A >> 32), fstar) << 32) |
+                          (uint32_t)readlane_i32((int)(uint32_t)A, fstar);
+    const int gstar = readlane_i32(g, fstar);
     // the path's rows have depths 1..len: row at depth d goes to slot d-1
     if (row && lane > 0 && ((path >> lane) & 1ull) && d >= 1 && d <= v.dmax)
         v.accept_idx[(size_t)b * v.dmax + d - 1] = lane;
@@ -385,6 +392,8 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
             d = v.depth[o];
             g = 0;
         }
+        if (!row || lane == 0) p = -1;
+        const uint64_t A = ancestor_mask(row, p);
         const uint64_t t0 = wall_clock64();
         bool ok = true;
         while (true) {
@@ -399,7 +408,7 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
             if (lane == 0) v.accept_len[b] = -1;
             continue;
         }
-        accept_walk(v, b, g - 1, t, p, d);
+        accept_walk(v, b, g - 1, t, p, d, A);
         if (row) st_agent(&v.done[o], 0);
     }
 }
