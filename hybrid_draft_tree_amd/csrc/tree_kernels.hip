@@ -144,6 +144,9 @@ __device__ __forceinline__ int retrieve_tree_wave(int R, int tp, int tr, int td,
     const bool act = lane < R;
     const int maxd = wave_max_i32(act ? td : 0);
     if (maxd > kPathLevels) return retrieve_tree_levels(R, tp, tr, td, root, table, V, k);
+    // depth 1 reads the root's row: load all of it now, so the first gather
+    // overlaps the path-code doubling below
+    const int rrow = (root >= 0 && root < V && lane < k) ? table[(size_t)root * k + lane] : -1;
     const bool own_ok = tr >= 0 && tr < k && td >= 1;
     // bit 63 (above the 21 levels of 3-bit ranks) flags a path with a rank out of range
     constexpr uint64_t kBad = 1ull << 63;
@@ -160,8 +163,10 @@ __device__ __forceinline__ int retrieve_tree_wave(int R, int tp, int tr, int td,
         }
     }
     const bool bad = (P & kBad) != 0ull;
-    int x = root;
-    for (int d = 1; d <= maxd; ++d) {
+    // the path's rank at depth 1 is a valid rank or 0 (a path with a rank out of
+    // range carries only the bad flag), so it indexes the loaded root row
+    int x = __shfl(rrow, (int)(P & 7ull));
+    for (int d = 2; d <= maxd; ++d) {
         if (act && d <= td) {
             const int r = (int)((P >> (3 * (d - 1))) & 7ull);
             x = (x >= 0 && x < V) ? table[(size_t)x * k + r] : -1;
