@@ -270,11 +270,13 @@ __device__ __forceinline__ uint64_t ancestor_mask(bool row, int p) {
 
 // Strict greedy acceptance walk of request b (section 二, gear 3), one wavefront;
 // lane f is flattened row f with its greedy token g, token t, parent row p (-1
-// for the root and non-rows), depth d and ancestor-or-self mask A.  A row is
+// for the root and non-rows), depth d and ancestor-or-self mask A; base is the
+// request's position base (read before the rows were waited for).  A row is
 // accepted iff every row on its path from the root carries the greedy token of
 // its parent row, i.e. iff its mask holds no row whose edge check fails; the
 // deepest accepted row wins, ties -> lowest row.
-__device__ __forceinline__ void accept_walk(const VerifyArgs &v, int b, int g, int t, int p, int d, uint64_t A) {
+__device__ __forceinline__ void accept_walk(const VerifyArgs &v, int b, int g, int t, int p, int d, uint64_t A,
+                                            int base) {
     const int lane = lane_id();
     const int T1 = v.T1;
     const bool row = lane < T1;
@@ -296,7 +298,7 @@ __device__ __forceinline__ void accept_walk(const VerifyArgs &v, int b, int g, i
     if (lane == 0) {
         v.accept_len[b] = len;
         v.bonus[b] = gstar;
-        if (v.base_pos_io) v.base_pos_io[b] += len + 1;
+        if (v.base_pos_io) v.base_pos_io[b] = base + len + 1;
     }
 }
 
@@ -394,6 +396,7 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
         }
         if (!row || lane == 0) p = -1;
         const uint64_t A = ancestor_mask(row, p);
+        const int base = v.base_pos_io ? v.base_pos_io[b] : 0;  // only this wave writes it
         const uint64_t t0 = wall_clock64();
         bool ok = true;
         while (true) {
@@ -408,7 +411,7 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
             if (lane == 0) v.accept_len[b] = -1;
             continue;
         }
-        accept_walk(v, b, g - 1, t, p, d, A);
+        accept_walk(v, b, g - 1, t, p, d, A, base);
         if (row) st_agent(&v.done[o], 0);
     }
 }
@@ -489,6 +492,11 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         return head + ng_row * EPG + (q - (uint32_t)kcount * BLK);
     };
 
+    // the row's token for the matrix update, loaded now and used at the row's end
+    int row_tok = -1;
+    if constexpr (ACCEPT) {
+        if (wv == 0 && v.table) row_tok = v.tok[row];
+    }
     Rank top = 0;   // lanes 0..7: the wave's top-8, descending
     Rank kth = 0;   // the 8th best (uniform); 0 while fewer than 8 candidates
     int thr = INT_MIN;
@@ -639,6 +647,12 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
             append(d[u], inb && (thr == INT_MIN || TR::group_pass(d[u], thr)), kk + u);
         }
         maybe_process();
+    }
+    // the row's hand-off word, read before the final merges: once it shows the
+    // registration (1) it keeps that value until this row clears it
+    int handoff_seen = 0;
+    if constexpr (ACCEPT) {
+        if (wv == 0 && lane == 0 && v.table) handoff_seen = ld_agent((const int32_t *)&v.handoff[row]);
     }
     if (count) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -796,11 +810,9 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         // Fused update: hand the row to the update.  Fast path: the registration
         // already arrived (it finishes long before the rows do); otherwise the
         // second arrival at the row's hand-off word updates the row.
-        const int t = v.table ? __builtin_amdgcn_readfirstlane(v.tok[row]) : -1;
+        const int t = v.table ? __builtin_amdgcn_readfirstlane(row_tok) : -1;
         if (t >= 0 && t < a.V) {
-            int h = 0;
-            if (lane == 0) h = ld_agent((const int32_t *)&v.handoff[row]);
-            bool mine = readlane_i32(h, 0) == 1;
+            bool mine = readlane_i32(handoff_seen, 0) == 1;
             if (!mine) {
                 publish();
                 uint32_t o = 0;

@@ -1,0 +1,139 @@
+"""Summaries of rocprofv3 CSV output for the committed profile files.
+
+    python -m hybrid_draft_tree_amd.rocprof_summary trace KERNEL_TRACE_CSV > profiles/<name>.md
+    python -m hybrid_draft_tree_amd.rocprof_summary pmc FETCH_CSV WRITE_CSV > profiles/<name>.json
+
+``trace`` groups a ``--kernel-trace`` CSV by kernel and launch shape
+(workgroups x threads) and reports calls and begin-to-end durations.  ``pmc``
+averages ``FETCH_SIZE`` / ``WRITE_SIZE`` (KiB per dispatch) over the verify
+launches at the B=16, V=151936 shape (976 rows + 4 coordinator workgroups of
+256 threads) and scales each counter by what it reads for the run's plain 1 GiB
+device copy (``__amd_rocclr_copyBuffer``, 1 GiB read and 1 GiB written), giving
+HBM bytes per launch.  Reads CSV text only.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+# sources the verify kernel is compiled from; the hash marks which build the counters describe
+KERNEL_SRCS = ["hybrid_draft_tree_amd/csrc/topk_kernels.hip", "hybrid_draft_tree_amd/csrc/device_utils.hpp",
+               "hybrid_draft_tree_amd/csrc/launchers.hpp"]
+
+B, T1, V, K = 16, 61, 151936, 8
+VERIFY_GRID = (B * T1 + 4) * 256      # threads of the metric-shape verify launch
+ALG_BYTES = B * T1 * V * 2 + B * T1 * K * 4
+COPY_KIB = 1 << 20                      # 1 GiB
+
+# launch shapes of bench.py's legs (workgroups, threads) -> label
+SHAPES = {
+    ("k_topk_rows", 980, 256): "verify, 976 rows (the timed step's launch)",
+    ("k_topk_rows", 980, 320): "verify with row statistics (coverage leg)",
+    ("k_topk_rows", 1092, 256): "TAIL verify, 272 rows in 4 slices",
+    ("k_topk_rows", 2049, 192): "ingest chunk, 2048 rows, update fused",
+    ("k_topk_rows", 489, 512): "one request, 61 rows in 8 slices",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SRCS:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    m = re.search(r"graft::\(anonymous namespace\)::(\w+)", name)
+    if m:
+        return m.group(1)
+    return name[:60]
+
+
+def trace(path: str) -> str:
+    groups = defaultdict(list)
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            groups[(short_name(r["Kernel_Name"]), grid // max(wg, 1), wg)].append(dur)
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    out = ["| kernel | workgroups x threads | shape | calls | avg us | min us | max us |",
+           "|---|---|---|---:|---:|---:|---:|"]
+    for (name, nwg, wg), d in rows:
+        out.append("| `%s` | %d x %d | %s | %d | %.2f | %.2f | %.2f |"
+                   % (name, nwg, wg, SHAPES.get((name, nwg, wg), ""), len(d), sum(d) / len(d), min(d), max(d)))
+    return "\n".join(out) + "\n"
+
+
+def _counter(path: str):
+    verify, copies = [], []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            val = float(r["Counter_Value"])
+            if "k_topk_rows" in r["Kernel_Name"] and int(r["Grid_Size"]) == VERIFY_GRID \
+                    and int(r["Workgroup_Size"]) == 256:
+                verify.append(val)
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copies.append(val)
+    if not verify or not copies:
+        raise SystemExit("%s: no verify launches at the metric shape or no device copy" % path)
+    return sum(verify) / len(verify), max(copies), len(verify)
+
+
+def pmc(fetch_csv: str, write_csv: str, commands) -> dict:
+    f_avg, f_copy, n = _counter(fetch_csv)
+    w_avg, w_copy, _ = _counter(write_csv)
+    fs, ws = COPY_KIB / f_copy, COPY_KIB / w_copy
+    rd, wr = int(round(f_avg * fs * 1024)), int(round(w_avg * ws * 1024))
+    return {
+        "kernel": "k_topk_rows (graft_verify_update / graft_verify_accept), bf16, 976 rows x 151936",
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_sources": KERNEL_SRCS,
+        "dispatches": n,
+        "fetch_kib_per_dispatch_raw": round(f_avg, 1),
+        "write_kib_per_dispatch_raw": round(w_avg, 1),
+        "copy_1GiB_fetch_kib_raw": round(f_copy, 1),
+        "copy_1GiB_write_kib_raw": round(w_copy, 1),
+        "fetch_scale": round(fs, 5),
+        "write_scale": round(ws, 5),
+        "hbm_read_bytes_per_launch": rd,
+        "hbm_write_bytes_per_launch": wr,
+        "hbm_bytes_per_launch": rd + wr,
+        "alg_bytes_per_launch": ALG_BYTES,
+        "traffic_over_alg": round((rd + wr) / ALG_BYTES, 4),
+        "commands": list(commands),
+        "note": "FETCH_SIZE/WRITE_SIZE averaged over the run's plain verify launches at the metric shape "
+                "(k_topk_rows dispatches of 980 workgroups x 256 threads: 976 rows and 4 coordinators; the "
+                "other shapes the run times are left out), scaled by what the same counter reads for the run's "
+                "plain 1 GiB device copy (__amd_rocclr_copyBuffer, 1048576 KiB read and written)",
+    }
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "trace":
+        sys.stdout.write(trace(argv[1]))
+    elif len(argv) >= 3 and argv[0] == "pmc":
+        cmds = [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- python3 bench.py "
+            "--steps 40 --warmup 8 --kernel-iters 20 --no-cpu-baseline --copy-calib",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- python3 bench.py "
+            "--steps 40 --warmup 8 --kernel-iters 20 --no-cpu-baseline --copy-calib",
+            "python -m hybrid_draft_tree_amd.rocprof_summary pmc gpurun_out/pmc_fetch/fetch_counter_collection.csv "
+            "gpurun_out/pmc_write/write_counter_collection.csv",
+        ]
+        print(json.dumps(pmc(argv[1], argv[2], cmds), indent=1))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

@@ -48,3 +48,38 @@ def test_profile_summaries_are_committed_and_small(name):
     assert os.path.exists(p) and os.path.getsize(p) < 16384
     text = open(p).read()
     assert "rocprofv3" in text
+
+
+def test_summary_tool_hash_matches_bench():
+    from hybrid_draft_tree_amd import rocprof_summary as rs
+    assert rs.kernel_source_hash() == bench.kernel_source_hash()
+    assert [os.path.join(ROOT, p) for p in rs.KERNEL_SRCS] == bench.KERNEL_SRCS
+
+
+def test_summary_tool_scales_counters_by_the_copy(tmp_path):
+    """Two verify dispatches at the metric shape, one at another shape (left
+    out) and the 1 GiB copy: bytes per launch = mean counter x (1 GiB / copy's
+    counter)."""
+    from hybrid_draft_tree_amd import rocprof_summary as rs
+    hdr = "Correlation_Id,Dispatch_Id,Grid_Size,Kernel_Name,Workgroup_Size,Counter_Name,Counter_Value\n"
+
+    def write(name, counter, verify_vals, copy_val):
+        p = tmp_path / name
+        lines = [hdr]
+        for i, v in enumerate(verify_vals):
+            lines.append('%d,%d,%d,"void graft::(anonymous namespace)::k_topk_rows<x>(y)",256,%s,%f\n'
+                         % (i, i, rs.VERIFY_GRID, counter, v))
+        lines.append('9,9,%d,"void graft::(anonymous namespace)::k_topk_rows<x>(y)",256,%s,1.0\n'
+                     % (1092 * 256, counter))
+        lines.append('10,10,131072,"__amd_rocclr_copyBuffer",512,%s,%f\n' % (counter, copy_val))
+        p.write_text("".join(lines))
+        return str(p)
+
+    f = write("f.csv", "FETCH_SIZE", [100.0, 300.0], float(1 << 19))   # reads half the copied bytes
+    w = write("w.csv", "WRITE_SIZE", [10.0, 10.0], float(1 << 20))
+    d = rs.pmc(f, w, ["cmd"])
+    assert d["dispatches"] == 2
+    assert d["fetch_scale"] == 2.0 and d["write_scale"] == 1.0
+    assert d["hbm_read_bytes_per_launch"] == 200 * 2 * 1024
+    assert d["hbm_write_bytes_per_launch"] == 10 * 1024
+    assert d["alg_bytes_per_launch"] == 976 * 151936 * 2 + 976 * 8 * 4
