@@ -28,7 +28,8 @@ A third, ``--ablation``, compares the pruning/retrieval variants of the
 write-up's ablations (no retrieval, fixed splits, a dense tree, per-node
 thresholds) with the adaptive default on workloads 2, 3 and 4.  A fourth,
 ``--calibration``, sets the thresholds from warm-up quantiles and moves them
-between workloads.
+between workloads.  A fifth, ``--all-configs``, times the full step on each
+of the five workloads at its own shape (one JSON line each).
 """
 from __future__ import annotations
 
@@ -73,6 +74,9 @@ def parse():
     ap.add_argument("--ablation", action="store_true",
                     help="accept length of the pruning/retrieval variants (no timing)")
     ap.add_argument("--ablation-configs", default="2,3,4")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time the full step (build + verify/update, HIP graph) on each workload's own shape")
+    ap.add_argument("--config-list", default="1,2,3,4,5")
     ap.add_argument("--calibration", action="store_true",
                     help="calibrated thresholds vs quantile level, and their transfer across workloads")
     return ap.parse_args()
@@ -298,8 +302,101 @@ def template_sweep(args):
                     print(json.dumps(rec), flush=True)
 
 
+def all_configs(args):
+    """The full Graft step on each of the five workloads at its own shape: one
+    build launch + one verify/update launch per step, replayed from a HIP graph
+    over a pool of `--pool` steps of a real seeded trajectory (after the
+    workload's warm-up; workload 4 ingests its prompt first).  One JSON line per
+    workload: time per step and the step's logits bytes against 8 TB/s."""
+    import numpy as np
+    import torch
+
+    from hybrid_draft_tree_amd.driver import GraftPipeline
+    from synth import CONFIGS
+    from synth import generators as G
+    from synth import runner as R
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    P = max(1, args.pool)
+    for cid in [int(x) for x in args.config_list.split(",") if x.strip()]:
+        cfg = CONFIGS[cid]
+        t0 = time.time()
+        pipe = GraftPipeline.from_config(cfg, device=dev)
+        ad = _Adapter(pipe, torch)
+        wl = R.Workload(cfg)
+        R.start(ad, wl)
+        for s_ in range(cfg.warmup_steps):
+            R.step(ad, wl, s_, G.WARMUP_STREAM_OFFSET)
+        T1 = cfg.rows_per_request
+        n_rows = cfg.B * T1
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        pool_logits, pool_drafts = [], []
+        for p in range(P):
+            roots = ad.get_roots()
+            draft = wl.draft(p, roots)
+            flat = ad.build(draft)
+            desc = wl.logit_desc(p, flat)
+            buf = torch.empty(n_rows, cfg.V, dtype=tdt, device=dev)
+            if ad.rows is None:
+                ad.rows = ad.DeviceRows(wl.pool, dev)
+            ad.rows.materialize(desc, out=buf)
+            res = ad.verify_update(buf)
+            wl.commit(roots, flat, res)
+            bufs = pipe.draft_buffers()
+            if cfg.mode == "tree":
+                bufs["parent"].copy_(torch.as_tensor(draft["parent"]))
+                bufs["layer"].copy_(torch.as_tensor(draft["layer"]))
+                bufs["score"].copy_(torch.as_tensor(draft["logp"]))
+            else:
+                bufs["score"].copy_(torch.as_tensor(draft["conf"]))
+            bufs["tok"].copy_(torch.as_tensor(draft["tok"]))
+            pool_logits.append(buf)
+            pool_drafts.append(bufs)
+        torch.cuda.synchronize()
+
+        def one_pass():
+            for p in range(P):
+                pipe.build_device(pool_drafts[p])
+                pipe.verify_update_device(pool_logits[p])
+
+        one_pass()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_pass()
+        n_rep = max(1, math.ceil(args.steps / P))
+        for _ in range(max(1, math.ceil(args.warmup / P))):
+            g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_rep):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (n_rep * P)
+        lb = n_rows * cfg.V * (2 if cfg.dtype == "bf16" else 4)
+        step_bytes = lb + n_rows * cfg.k * 4
+        log("workload %d (%s): %.2f us/step, %.0f GB/s (setup %.1fs)"
+            % (cid, cfg.name, us, step_bytes / (us * 1e-6) / 1e9, time.time() - t0))
+        print(json.dumps({"mode": "all_configs", "workload": cfg.name, "config": cid, "batch": cfg.B,
+                          "vocab": cfg.V, "rows_per_request": T1, "verified_rows": n_rows, "dtype": cfg.dtype,
+                          "layout": cfg.layout, "steps": n_rep * P, "us_per_step": round(us, 3),
+                          "steps_per_s": round(1e6 / us, 1), "logits_bytes_per_step": lb,
+                          "step_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
+                          "step_frac_of_peak": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                          "hip_graph": True, "data": "synthetic"}), flush=True)
+        del g, pool_logits, pool_drafts, pipe, ad
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.all_configs:
+        return all_configs(args)
     if args.template_sweep:
         return template_sweep(args)
     if args.ablation:

@@ -23,7 +23,7 @@ def test_help_lists_the_modes():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        timeout=120, cwd=ROOT)
     assert r.returncode == 0
-    for flag in ("--steps", "--warmup", "--gpus", "--template-sweep", "--ablation", "--calibration"):
+    for flag in ("--steps", "--warmup", "--gpus", "--template-sweep", "--ablation", "--calibration", "--all-configs"):
         assert flag in r.stdout
 
 
