@@ -372,6 +372,8 @@ def test_retrieve_tree_parity():
     ("branching", 2, 30, (100, 1), 52),  # a depth-30 rank-0 chain: the level-by-level path
     ("chain", 8, 2, (1, 1), 52),         # 16 nodes: less than most budgets (empty slots)
     ("branching", 4, 3, (1, 2), 20),
+    ("chain", 4, 16, (1, 1), 52),        # rank chains to depth 16: a 16-level path walk
+    ("chain", 8, 1, (1, 1), 52),         # root children only: every node reads the root's row
 ])
 def test_retrieve_tree_parity_templates(kind, W, D, beta, R):
     rng = np.random.default_rng(14)
@@ -379,6 +381,7 @@ def test_retrieve_tree_parity_templates(kind, W, D, beta, R):
     table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
     B = 29
     roots = rng.integers(0, V, size=B).astype(np.int32)
+    roots[:2] = [0, V - 1]                # the first and the last matrix row
     n_keep = rng.choice([8, 24, 40, 60], size=B).astype(np.int32)
     tpl = _tpl_host(R, kind, W, D, beta)
     o = O.retrieve_tree(table, roots, n_keep, 60, tpl)
