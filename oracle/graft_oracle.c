@@ -14,6 +14,17 @@
  * variant; section 四 (long context) for prompt ingest.
  *
  * Where the pages leave a step open, the reading taken is stated at that step.
+ * Parity unpinned by the pages: the following readings are fixed by no worked
+ * example, formula or table on the pages, so the tests pin them only through
+ * invariants (budget split, superset and monotonicity of acceptance,
+ * losslessness, closures) and through agreement with the GPU path -- which
+ * draft nodes a prune keeps (top N by cumulative confidence among layers up
+ * to the checkpoint, ties to the lower index); a checkpoint whose layer is
+ * empty or too small is not reached; the static draft tree's layer sizes; the
+ * rank-chain template and its master order; the flatten order of each layout;
+ * static-slot replacement as the same stage logic; equally long accepted
+ * paths resolved to the lowest row; the update overwriting whole rows for
+ * every verified position, highest batch-wide position winning.
  * Every decision that floating point makes (stage, keep set, TAIL prefix) is
  * taken in fp32, the precision of the GPU kernels; top-k compares values as
  * reals (bf16/fp32 widened exactly to double); softmax probabilities are fp64.
