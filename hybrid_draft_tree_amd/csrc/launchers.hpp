@@ -93,6 +93,7 @@ struct TopkPlan {
     size_t off_counters = 0;  // completion words [n_rows]
     size_t off_occ = 0;       // last holder per token [V], one spare word, hand-offs [n_rows]
     int groups = 1;           // workgroups per row (rows split when there are few of them)
+    int loads = 2;            // 1 KB blocks per wave per batch (2 or 4)
     size_t off_cnt = 0;       // groups > 1: arrival counters [n_rows], slice results [n_rows, groups]
     size_t off_part = 0;
     size_t off_pstat = 0;
@@ -112,6 +113,7 @@ struct TopkArgs {
     // rows split over `groups` workgroups (groups > 1): per-row arrival counters,
     // each slice's top-8 (row ranks) and softmax statistics, all in the workspace
     int groups;
+    int loads;  // 1 KB blocks per wave per batch: selects the kernel instantiation
     uint32_t *cnt;
     uint64_t *part;
     float *pstat;

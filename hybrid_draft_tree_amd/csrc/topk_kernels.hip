@@ -28,8 +28,9 @@
 namespace graft {
 namespace {
 
-constexpr int kLoadsInFlight = 2;  // U: 1 KB blocks per wave per batch
-constexpr int kCap = kWave * (kLoadsInFlight + 1);  // pending groups per wave
+// U = 1 KB blocks per wave per batch (a template parameter: 2 or 4, chosen per
+// launch); each wave keeps up to kWave * (U + 1) pending groups
+constexpr int kMaxLdsPerGroup = 65536;  // dynamic LDS a workgroup may take
 constexpr int kTop = 8;
 constexpr int kMaxWavesPerRow = 16;
 constexpr int kHeadPad = 8;  // local offsets below this are the row's unaligned head
@@ -416,9 +417,10 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
     }
 }
 
-// Dynamic LDS layout of a row's workgroup (S waves).
-template <typename Rank>
+// Dynamic LDS layout of a row's workgroup (S waves, U blocks per batch).
+template <typename Rank, int U>
 struct RowSmem {
+    static constexpr int kCap = kWave * (U + 1);                // pending groups per wave
     static constexpr size_t kData = sizeof(uint4) * kCap;      // pending groups
     static constexpr size_t kMerge = sizeof(Rank) * kWave;     // compaction scratch
     static constexpr size_t kGidx = sizeof(uint16_t) * kCap;   // pending group indices
@@ -432,11 +434,11 @@ struct RowSmem {
     }
 };
 
-template <typename TR, bool PROB, bool ACCEPT, bool NT, bool SPLIT>
+template <typename TR, bool PROB, bool ACCEPT, bool NT, bool SPLIT, int U>
 __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a, VerifyArgs v) {
     using Rank = typename TR::Rank;
-    using SM = RowSmem<Rank>;
-    constexpr int U = kLoadsInFlight;
+    using SM = RowSmem<Rank, U>;
+    constexpr int kCap = SM::kCap;
     constexpr int EPG = TR::kPerGroup;
     constexpr int ESZ = 16 / EPG;
     constexpr int BLK = kWave * EPG;  // elements per 1 KB block
@@ -828,33 +830,41 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     }
 }
 
-template <typename TR, bool PROB, bool ACCEPT>
-void launch_rows_as(const TopkArgs &a, const VerifyArgs &vv, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+template <typename TR, bool PROB, bool ACCEPT, int U>
+void launch_rows_u(const TopkArgs &a, const VerifyArgs &vv, dim3 grid, dim3 block, hipStream_t s) {
+    const size_t lds = RowSmem<typename TR::Rank, U>::bytes(a.S);
     if (a.groups > 1)
-        hipLaunchKernelGGL((k_topk_rows<TR, PROB, ACCEPT, true, true>), grid, block, lds, s, a, vv);
+        hipLaunchKernelGGL((k_topk_rows<TR, PROB, ACCEPT, true, true, U>), grid, block, lds, s, a, vv);
     else
-        hipLaunchKernelGGL((k_topk_rows<TR, PROB, ACCEPT, true, false>), grid, block, lds, s, a, vv);
+        hipLaunchKernelGGL((k_topk_rows<TR, PROB, ACCEPT, true, false, U>), grid, block, lds, s, a, vv);
+}
+
+template <typename TR, bool PROB, bool ACCEPT>
+void launch_rows_as(const TopkArgs &a, const VerifyArgs &vv, dim3 grid, dim3 block, hipStream_t s) {
+    // four blocks per batch where the plan asks for them and the LDS allows
+    if (a.loads == 4 && RowSmem<typename TR::Rank, 4>::bytes(a.S) <= (size_t)kMaxLdsPerGroup)
+        launch_rows_u<TR, PROB, ACCEPT, 4>(a, vv, grid, block, s);
+    else
+        launch_rows_u<TR, PROB, ACCEPT, 2>(a, vv, grid, block, s);
 }
 
 template <typename TR>
 void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
-    using Rank = typename TR::Rank;
     const int extra = v ? v->ncoord : 0;  // the coordinator workgroups
     const dim3 grid((unsigned)(a.n_rows * a.groups + extra));
     const dim3 block(kWave * a.S);
-    const size_t lds = RowSmem<Rank>::bytes(a.S);
     const VerifyArgs vv = v ? *v : VerifyArgs{};
     const bool prob = a.prob != nullptr || a.stats != nullptr;  // softmax statistics wanted
     if (v) {
         if (prob)
-            launch_rows_as<TR, true, true>(a, vv, grid, block, lds, s);
+            launch_rows_as<TR, true, true>(a, vv, grid, block, s);
         else
-            launch_rows_as<TR, false, true>(a, vv, grid, block, lds, s);
+            launch_rows_as<TR, false, true>(a, vv, grid, block, s);
     } else {
         if (prob)
-            launch_rows_as<TR, true, false>(a, vv, grid, block, lds, s);
+            launch_rows_as<TR, true, false>(a, vv, grid, block, s);
         else
-            launch_rows_as<TR, false, false>(a, vv, grid, block, lds, s);
+            launch_rows_as<TR, false, false>(a, vv, grid, block, s);
     }
 }
 
@@ -889,6 +899,22 @@ constexpr int64_t kTargetWaves = 3840, kTargetWavesProb = 4880;
 constexpr int64_t kSplitBelowRows = 512, kSplitTargetUnits = 1024;
 constexpr int kMaxGroups = 8;
 
+// Blocks per batch (measured): four for prompt-sized launches (a 2048-row ingest
+// chunk: 109 -> 101 us) and for split rows whose waves stream at least 8 blocks
+// each (TAIL 272 rows: 26.1 -> 23.9 us; 244 rows: 1.8 us off the step); two for
+// one workgroup per row in between (976 rows: 55.4 vs 56.6 us per step with
+// four) and for split rows with only a few blocks per wave (61 rows: 3.4 us
+// slower with four at V=32000 fp32).
+constexpr int64_t kDeepBatchRows = 1536;
+constexpr int64_t kDeepBatchMinBlocks = 8;
+static int loads_for(int64_t n_rows, int V, int dtype, int groups, int S) {
+    if (n_rows >= kDeepBatchRows) return 4;
+    if (n_rows >= kSplitBelowRows) return 2;
+    const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
+    const int64_t nblk = (((int64_t)V / epg + kWave - 1) / kWave + groups - 1) / groups;  // blocks per slice
+    return nblk / (S > 0 ? S : 1) >= kDeepBatchMinBlocks ? 4 : 2;
+}
+
 static int groups_per_row(int64_t n_rows, int V, int dtype) {
     if (n_rows <= 0 || n_rows >= kSplitBelowRows) return 1;
     const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
@@ -906,6 +932,7 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     p.dtype = dtype;
     p.groups = groups_per_row(n_rows, V, dtype);
     p.splits = waves_per_row(n_rows, V, dtype, kTargetWaves, p.groups);
+    p.loads = loads_for(n_rows, V, dtype, p.groups, p.splits);
     // workspace: [completion words [n_rows] | last holder per token [V], spare,
     //             hand-offs [n_rows]]
     p.off_counters = 0;
@@ -930,6 +957,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     a.V = p.V;
     a.S = (prob || stats) ? waves_per_row(p.n_rows, p.V, p.dtype, kTargetWavesProb, p.groups) : p.splits;
     a.groups = p.groups;
+    a.loads = p.loads;
     a.cnt = p.groups > 1 ? (uint32_t *)((char *)ws + p.off_cnt) : nullptr;
     a.part = p.groups > 1 ? (uint64_t *)((char *)ws + p.off_part) : nullptr;
     a.pstat = p.groups > 1 ? (float *)((char *)ws + p.off_pstat) : nullptr;
