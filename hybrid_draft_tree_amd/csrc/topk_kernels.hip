@@ -9,8 +9,9 @@
 //   each on a slice of whole blocks).  The row is cut into 1 KB blocks (64
 //   lanes x 16 bytes = 8 bf16 or 4 fp32 per lane); wavefront j reads blocks
 //   j, j+S, j+2S, ... so that the S waves of a row sweep it together (a
-//   contiguous front per row keeps HBM pages open), two blocks per batch with
-//   the next batch issued before the current one is filtered.  A wave-uniform
+//   contiguous front per row keeps HBM pages open), U blocks per batch (2 or
+//   4, chosen per launch) with the next batch issued before the current one is
+//   filtered.  A wave-uniform
 //   threshold -- the key of the wave's current 8th-best value -- filters each
 //   16-byte group with a few packed integer ops; the rare groups that pass
 //   are compacted into LDS with a ballot and merged into the wave's exact
