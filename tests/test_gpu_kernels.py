@@ -120,6 +120,21 @@ def test_topk_prob_parity():
     np.testing.assert_allclose(tprob[:12], want_p, rtol=1e-5, atol=0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_prompt_sized_launch(dtype):
+    """1600 rows: one workgroup per row with four blocks per batch (the plan for
+    prompt-sized launches), every row compared, tie-heavy and ragged rows included."""
+    rng = np.random.default_rng(31)
+    n, V = 1600, 4097
+    z = rng.standard_normal((n, V)).astype(np.float32)
+    z[::7] = np.round(z[::7] * 2) / 2
+    z[3::11] = -np.abs(z[3::11]) - 0.5
+    rows = _bf16(z) if dtype == "bf16" else z
+    got = gpu_topk(rows, 8, dtype)
+    want = O.topk(rows, 8, dtype)
+    assert (got == want).all(), np.nonzero((got != want).any(1))[0][:5]
+
+
 def test_topk_many_rows_and_ragged_split():
     # many rows, V chosen so the last range of a row is ragged
     rng = np.random.default_rng(4)

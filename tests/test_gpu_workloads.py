@@ -183,10 +183,10 @@ def test_lockstep_ingest_reduced():
     assert st["accepted"] > 0
 
 
-@pytest.mark.parametrize("cfg_id,steps", [(3, 3), (5, 3)])
+@pytest.mark.parametrize("cfg_id,steps", [(3, 3), (5, 3), (2, 20)])
 def test_lockstep_full_size(cfg_id, steps):
-    """Real shapes (B=16, V=151936, 61 or 17 rows per request): every output and
-    the full matrix, for a few steps after warm-up."""
+    """Real shapes (B=16, V=151936, 61 or 17 rows per request; B=1, V=128256):
+    every output and the full matrix, for a few steps after warm-up."""
     cfg = CONFIGS[cfg_id]
     st = _compare_runs(cfg, steps, warmup=2, table_every=steps + 2)
     assert st["accepted"] > 0
