@@ -896,9 +896,13 @@ constexpr int64_t kTargetWaves = 3840, kTargetWavesProb = 4880;
 
 // Rows are split over several workgroups when there are too few of them to
 // spread over the chip (fewer than 512): about 1024 workgroups in all, at most
-// 8 per row (one merge entry per lane), each slice at least 8 blocks.
+// 4 per row, each slice at least 8 blocks, and about 1920 waves in all (fewer,
+// longer waves than the unsplit launch: measured over 61-, 244- and 272-row
+// launches, 4 slices x 1920 waves beat 8 slices x 3840 by 2-3 us at 61 rows and
+// 1 us at 244 rows, and 2 or 3 slices, 960 or 2880 waves did worse overall).
 constexpr int64_t kSplitBelowRows = 512, kSplitTargetUnits = 1024;
-constexpr int kMaxGroups = 8;
+constexpr int kMaxGroups = 4;
+constexpr int64_t kSplitTargetWaves = 1920;
 
 // Blocks per batch (measured): four for prompt-sized launches (a 2048-row ingest
 // chunk: 109 -> 101 us) and for split rows whose waves stream at least 8 blocks
@@ -932,7 +936,7 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     p.V = V;
     p.dtype = dtype;
     p.groups = groups_per_row(n_rows, V, dtype);
-    p.splits = waves_per_row(n_rows, V, dtype, kTargetWaves, p.groups);
+    p.splits = waves_per_row(n_rows, V, dtype, p.groups > 1 ? kSplitTargetWaves : kTargetWaves, p.groups);
     p.loads = loads_for(n_rows, V, dtype, p.groups, p.splits);
     // workspace: [completion words [n_rows] | last holder per token [V], spare,
     //             hand-offs [n_rows]]

@@ -36,9 +36,9 @@ COPY_KIB = 1 << 20                      # 1 GiB
 SHAPES = {
     ("k_topk_rows", 980, 256): "verify, 976 rows (the timed step's launch)",
     ("k_topk_rows", 980, 320): "verify with row statistics (coverage leg)",
-    ("k_topk_rows", 1092, 256): "TAIL verify, 272 rows in 4 slices",
+    ("k_topk_rows", 1096, 128): "TAIL verify, 272 rows in 4 slices",
     ("k_topk_rows", 2049, 192): "ingest chunk, 2048 rows, update fused",
-    ("k_topk_rows", 489, 512): "one request, 61 rows in 8 slices",
+    ("k_topk_rows", 245, 512): "one request, 61 rows in 4 slices",
 }
 
 
