@@ -11,11 +11,10 @@
 //   j, j+S, j+2S, ... so that the S waves of a row sweep it together (a
 //   contiguous front per row keeps HBM pages open), U blocks per batch (2 or
 //   4, chosen per launch) with the next batch issued before the current one is
-//   filtered.  A wave-uniform
-//   threshold -- the key of the wave's current 8th-best value -- filters each
-//   16-byte group with a few packed integer ops; the rare groups that pass
-//   are compacted into LDS with a ballot and merged into the wave's exact
-//   top-8 (DPP wave maxima) when 64 are pending.
+//   filtered.  A wave-uniform threshold -- the key of the wave's current
+//   8th-best value -- filters each 16-byte group with a few packed integer
+//   ops; the rare groups that pass are compacted into LDS with a ballot and
+//   merged into the wave's exact top-8 (DPP wave maxima) when 64 are pending.
 // Epilogue: the S waves meet at one barrier; wave 0 ranks their candidates
 //   (and combines their softmax statistics) into the row's top-k; with G > 1
 //   the row's last slice to arrive merges the slices' results.  The row then
