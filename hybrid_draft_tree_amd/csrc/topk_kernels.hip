@@ -888,10 +888,11 @@ static int waves_per_row(int64_t n_rows, int V, int dtype, int64_t target_waves,
     return (int)S;
 }
 
-// The plain stream: 3840 waves (15 per CU; at 976 rows 4 per row beat 3
-// and 5, 6 was far slower).  With softmax statistics the rows are bound by
-// the exponentials instead, and more waves pay: 4880.
-constexpr int64_t kTargetWaves = 3840, kTargetWavesProb = 4880;
+// The plain stream: about 2928 waves (11-12 per CU: at 976 rows 3 per row with
+// four blocks per batch beat 4 per row with two by 0.3 us per step; 3 per row
+// with two blocks, and 5 or 6 per row, were slower).  With softmax statistics
+// the rows are bound by the exponentials instead, and more waves pay: 4880.
+constexpr int64_t kTargetWaves = 2928, kTargetWavesProb = 4880;
 
 // Rows are split over several workgroups when there are too few of them to
 // spread over the chip (fewer than 512): about 1024 workgroups in all, at most
@@ -903,17 +904,14 @@ constexpr int64_t kSplitBelowRows = 512, kSplitTargetUnits = 1024;
 constexpr int kMaxGroups = 4;
 constexpr int64_t kSplitTargetWaves = 1920;
 
-// Blocks per batch (measured): four for prompt-sized launches (a 2048-row ingest
-// chunk: 109 -> 101 us) and for split rows whose waves stream at least 8 blocks
-// each (TAIL 272 rows: 26.1 -> 23.9 us; 244 rows: 1.8 us off the step); two for
-// one workgroup per row in between (976 rows: 55.4 vs 56.6 us per step with
-// four) and for split rows with only a few blocks per wave (61 rows: 3.4 us
-// slower with four at V=32000 fp32).
-constexpr int64_t kDeepBatchRows = 1536;
+// Blocks per batch (measured): four for one workgroup per row (a 2048-row
+// ingest chunk: 109 -> 101 us; 976 rows at 3 waves per row: see kTargetWaves)
+// and for split rows whose waves stream at least 8 blocks each (TAIL 272 rows:
+// 26.1 -> 23.9 us; 244 rows: 1.8 us off the step); two for split rows with only
+// a few blocks per wave (61 rows: 3.4 us slower with four at V=32000 fp32).
 constexpr int64_t kDeepBatchMinBlocks = 8;
 static int loads_for(int64_t n_rows, int V, int dtype, int groups, int S) {
-    if (n_rows >= kDeepBatchRows) return 4;
-    if (n_rows >= kSplitBelowRows) return 2;
+    if (n_rows >= kSplitBelowRows) return 4;
     const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
     const int64_t nblk = (((int64_t)V / epg + kWave - 1) / kWave + groups - 1) / groups;  // blocks per slice
     return nblk / (S > 0 ? S : 1) >= kDeepBatchMinBlocks ? 4 : 2;

@@ -6,8 +6,8 @@
 ``trace`` groups a ``--kernel-trace`` CSV by kernel and launch shape
 (workgroups x threads) and reports calls and begin-to-end durations.  ``pmc``
 averages ``FETCH_SIZE`` / ``WRITE_SIZE`` (KiB per dispatch) over the verify
-launches at the B=16, V=151936 shape (976 rows + 4 coordinator workgroups of
-256 threads) and scales each counter by what it reads for the run's plain 1 GiB
+launches at the B=16, V=151936 shape (976 rows + 6 coordinator workgroups of
+192 threads: 3 wavefronts per row) and scales each counter by what it reads for the run's plain 1 GiB
 device copy (``__amd_rocclr_copyBuffer``, 1 GiB read and 1 GiB written), giving
 HBM bytes per launch.  Reads CSV text only.
 """
@@ -28,13 +28,14 @@ KERNEL_SRCS = ["hybrid_draft_tree_amd/csrc/topk_kernels.hip", "hybrid_draft_tree
                "hybrid_draft_tree_amd/csrc/launchers.hpp"]
 
 B, T1, V, K = 16, 61, 151936, 8
-VERIFY_GRID = (B * T1 + 4) * 256      # threads of the metric-shape verify launch
+VERIFY_WG = 192                        # 3 wavefronts per row at the metric shape
+VERIFY_GRID = (B * T1 + 6) * VERIFY_WG  # threads of the metric-shape verify launch (6 coordinator workgroups)
 ALG_BYTES = B * T1 * V * 2 + B * T1 * K * 4
 COPY_KIB = 1 << 20                      # 1 GiB
 
 # launch shapes of bench.py's legs (workgroups, threads) -> label
 SHAPES = {
-    ("k_topk_rows", 980, 256): "verify, 976 rows (the timed step's launch)",
+    ("k_topk_rows", 982, 192): "verify, 976 rows (the timed step's launch)",
     ("k_topk_rows", 980, 320): "verify with row statistics (coverage leg)",
     ("k_topk_rows", 1096, 128): "TAIL verify, 272 rows in 4 slices",
     ("k_topk_rows", 2049, 192): "ingest chunk, 2048 rows, update fused",
@@ -80,7 +81,7 @@ def _counter(path: str):
         for r in csv.DictReader(f):
             val = float(r["Counter_Value"])
             if "k_topk_rows" in r["Kernel_Name"] and int(r["Grid_Size"]) == VERIFY_GRID \
-                    and int(r["Workgroup_Size"]) == 256:
+                    and int(r["Workgroup_Size"]) == VERIFY_WG:
                 verify.append(val)
             elif "copyBuffer" in r["Kernel_Name"]:
                 copies.append(val)
@@ -112,7 +113,7 @@ def pmc(fetch_csv: str, write_csv: str, commands) -> dict:
         "traffic_over_alg": round((rd + wr) / ALG_BYTES, 4),
         "commands": list(commands),
         "note": "FETCH_SIZE/WRITE_SIZE averaged over the run's plain verify launches at the metric shape "
-                "(k_topk_rows dispatches of 980 workgroups x 256 threads: 976 rows and 4 coordinators; the "
+                "(k_topk_rows dispatches of 982 workgroups x 192 threads: 976 rows and 6 coordinators; the "
                 "other shapes the run times are left out), scaled by what the same counter reads for the run's "
                 "plain 1 GiB device copy (__amd_rocclr_copyBuffer, 1048576 KiB read and written)",
     }
