@@ -888,11 +888,12 @@ static int waves_per_row(int64_t n_rows, int V, int dtype, int64_t target_waves,
     return (int)S;
 }
 
-// The plain stream: about 2928 waves (11-12 per CU: at 976 rows 3 per row with
-// four blocks per batch beat 4 per row with two by 0.3 us per step; 3 per row
-// with two blocks, and 5 or 6 per row, were slower).  With softmax statistics
-// the rows are bound by the exponentials instead, and more waves pay: 4880.
-constexpr int64_t kTargetWaves = 2928, kTargetWavesProb = 4880;
+// About 2928 waves (11-12 per CU: at 976 rows 3 per row with four blocks per
+// batch beat 4 per row with two by 0.4 us per step; 3 per row with two blocks,
+// and 5 or 6 per row, were slower).  Launches with softmax statistics take the
+// same plan (58.1 us at 976 rows, against 58.5-58.8 us for 5 per row with two
+// blocks, the best plan with two).
+constexpr int64_t kTargetWaves = 2928;
 
 // Rows are split over several workgroups when there are too few of them to
 // spread over the chip (fewer than 512): about 1024 workgroups in all, at most
@@ -957,7 +958,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     a.logits = logits;
     a.n_rows = p.n_rows;
     a.V = p.V;
-    a.S = (prob || stats) ? waves_per_row(p.n_rows, p.V, p.dtype, kTargetWavesProb, p.groups) : p.splits;
+    a.S = p.splits;
     a.groups = p.groups;
     a.loads = p.loads;
     a.cnt = p.groups > 1 ? (uint32_t *)((char *)ws + p.off_cnt) : nullptr;

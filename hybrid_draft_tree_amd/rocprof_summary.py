@@ -33,13 +33,15 @@ VERIFY_GRID = (B * T1 + 6) * VERIFY_WG  # threads of the metric-shape verify lau
 ALG_BYTES = B * T1 * V * 2 + B * T1 * K * 4
 COPY_KIB = 1 << 20                      # 1 GiB
 
-# launch shapes of bench.py's legs (workgroups, threads) -> label
+# bench.py's top-k launches: (kernel with its template flags, workgroups, threads) -> label;
+# the flags are <element traits, softmax statistics, acceptance, non-temporal, split rows, blocks per batch>
+VERIFY = "k_topk_rows<Bf16, false, true, true, false, 4>"
 SHAPES = {
-    ("k_topk_rows", 982, 192): "verify, 976 rows (the timed step's launch)",
-    ("k_topk_rows", 980, 320): "verify with row statistics (coverage leg)",
-    ("k_topk_rows", 1096, 128): "TAIL verify, 272 rows in 4 slices",
-    ("k_topk_rows", 2049, 192): "ingest chunk, 2048 rows, update fused",
-    ("k_topk_rows", 245, 512): "one request, 61 rows in 4 slices",
+    (VERIFY, 982, 192): "verify, 976 rows (the timed step's launch)",
+    ("k_topk_rows<Bf16, true, true, true, false, 4>", 982, 192): "verify with row statistics (coverage leg)",
+    ("k_topk_rows<Bf16, false, true, true, true, 4>", 1096, 128): "TAIL verify, 272 rows in 4 slices",
+    ("k_topk_rows<Bf16, false, true, true, false, 4>", 2049, 192): "ingest chunk, 2048 rows, update fused",
+    ("k_topk_rows<Bf16, false, true, true, true, 4>", 245, 512): "one request, 61 rows in 4 slices",
 }
 
 
@@ -52,10 +54,14 @@ def kernel_source_hash() -> str:
 
 
 def short_name(name: str) -> str:
+    """Kernel name without namespaces; the top-k kernel keeps its template
+    arguments (its instantiations differ in what they compute)."""
+    t = re.search(r"k_topk_rows<(.*)>\(", name)
+    if t:
+        args = [a.strip().split("::")[-1].replace("Traits", "") for a in t.group(1).split(",")]
+        return "k_topk_rows<%s>" % ", ".join(args)
     m = re.search(r"graft::\(anonymous namespace\)::(\w+)", name)
-    if m:
-        return m.group(1)
-    return name[:60]
+    return m.group(1) if m else name[:60]
 
 
 def trace(path: str) -> str:
@@ -80,7 +86,7 @@ def _counter(path: str):
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
             val = float(r["Counter_Value"])
-            if "k_topk_rows" in r["Kernel_Name"] and int(r["Grid_Size"]) == VERIFY_GRID \
+            if short_name(r["Kernel_Name"]) == VERIFY and int(r["Grid_Size"]) == VERIFY_GRID \
                     and int(r["Workgroup_Size"]) == VERIFY_WG:
                 verify.append(val)
             elif "copyBuffer" in r["Kernel_Name"]:

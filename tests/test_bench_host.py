@@ -67,9 +67,9 @@ def test_summary_tool_scales_counters_by_the_copy(tmp_path):
         p = tmp_path / name
         lines = [hdr]
         for i, v in enumerate(verify_vals):
-            lines.append('%d,%d,%d,"void graft::(anonymous namespace)::k_topk_rows<x>(y)",%d,%s,%f\n'
+            lines.append('%d,%d,%d,"void graft::(anonymous namespace)::k_topk_rows<graft::(anonymous namespace)::Bf16Traits, false, true, true, false, 4>(graft::TopkArgs, graft::VerifyArgs)",%d,%s,%f\n'
                          % (i, i, rs.VERIFY_GRID, rs.VERIFY_WG, counter, v))
-        lines.append('9,9,%d,"void graft::(anonymous namespace)::k_topk_rows<x>(y)",256,%s,1.0\n'
+        lines.append('9,9,%d,"void graft::(anonymous namespace)::k_topk_rows<graft::(anonymous namespace)::Bf16Traits, false, true, true, false, 4>(graft::TopkArgs, graft::VerifyArgs)",256,%s,1.0\n'
                      % (1092 * 256, counter))
         lines.append('10,10,131072,"__amd_rocclr_copyBuffer",512,%s,%f\n' % (counter, copy_val))
         p.write_text("".join(lines))
