@@ -135,6 +135,30 @@ def test_topk_prompt_sized_launch(dtype):
     assert (got == want).all(), np.nonzero((got != want).any(1))[0][:5]
 
 
+def test_topk_max_vocab_unsplit_sampled():
+    """512 rows at the largest vocabulary (one workgroup per row, 16 waves per
+    row, where four-block batches would need more LDS than a workgroup may
+    take, so the launch runs two): logits generated on the device, 16 rows
+    compared with the oracle."""
+    n, V, k = 512, L.GRAFT_MAX_VOCAB, 8
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    lg = torch.randn(n, V, generator=g, device=DEV).to(torch.bfloat16)
+    out = torch.full((n, k), -7, dtype=torch.int32, device=DEV)
+    table = torch.zeros(V, k, dtype=torch.int32, device=DEV)
+    row_tok = torch.arange(n, dtype=torch.int32, device=DEV)
+    wsb = L.graft_workspace_bytes(n, V, k, L.DTYPE_BF16)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    L.graft_update_topk(n, V, k, L.DTYPE_BF16, lg.data_ptr(), None, None, row_tok.data_ptr(), table.data_ptr(),
+                        None, out.data_ptr(), ws.data_ptr(), wsb, _s())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rows = np.random.default_rng(5).choice(n, size=16, replace=False)
+    host = lg[torch.as_tensor(rows, device=DEV)].view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got[rows], O.topk(host, k, "bf16"))
+    np.testing.assert_array_equal(table.cpu().numpy()[rows], got[rows])
+
+
 def test_topk_many_rows_and_ragged_split():
     # many rows, V chosen so the last range of a row is ragged
     rng = np.random.default_rng(4)
