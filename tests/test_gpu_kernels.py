@@ -135,6 +135,41 @@ def test_topk_prompt_sized_launch(dtype):
     assert (got == want).all(), np.nonzero((got != want).any(1))[0][:5]
 
 
+# launch plans on both sides of their thresholds: split below 512 rows (at most
+# 4 slices), four blocks per batch for unsplit launches and for split rows whose
+# waves stream 8 or more blocks, two otherwise or when four exceed the LDS
+@pytest.mark.parametrize("n,V,dtype,prob", [
+    (511, 40000, "bf16", False),    # split into 3 slices, 13 blocks per wave: four
+    (512, 40000, "bf16", True),     # one workgroup per row, 6 waves: four, with probabilities
+    (300, 20000, "bf16", False),    # split, 5 blocks per wave: two
+    (100, 151936, "f32", True),     # split fp32, 30 blocks per wave: four, with probabilities
+    (2000, 3000, "f32", False),     # unsplit, short rows
+    (700, 9, "bf16", False),        # a row shorter than one block
+    (5, 151936, "bf16", False),     # split, 16 waves per slice: two
+    (1, 999_999, "bf16", False),    # split, four would exceed the LDS: two
+])
+def test_topk_launch_plans(n, V, dtype, prob):
+    rng = np.random.default_rng(n * 7 + V)
+    z = rng.standard_normal((n, V)).astype(np.float32)
+    z[::5] = np.round(z[::5] * 2) / 2
+    rows = _bf16(z) if dtype == "bf16" else z
+    if prob:
+        tk, tprob, table = gpu_topk(rows, 8, dtype, want_prob=True)
+        want_tk, want_p = O.topk(rows, 8, dtype, want_prob=True)
+        assert (tk == want_tk).all(), np.nonzero((tk != want_tk).any(1))[0][:5]
+        # table row x holds the top-k of the highest row with token x (row_tok = row % V)
+        last = {}
+        for r in range(n):
+            last[r % V] = r
+        xs = np.array(sorted(last)[:64])
+        rs = np.array([last[x] for x in xs])
+        np.testing.assert_allclose(tprob[xs], want_p[rs], rtol=1e-5, atol=0)
+    else:
+        got = gpu_topk(rows, 8 if V >= 8 else V, dtype)
+        want = O.topk(rows, 8 if V >= 8 else V, dtype)
+        assert (got == want).all(), np.nonzero((got != want).any(1))[0][:5]
+
+
 def test_topk_max_vocab_unsplit_sampled():
     """512 rows at the largest vocabulary (one workgroup per row, 16 waves per
     row, where four-block batches would need more LDS than a workgroup may
