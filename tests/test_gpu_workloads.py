@@ -183,6 +183,16 @@ def test_lockstep_ingest_reduced():
     assert st["accepted"] > 0
 
 
+def test_lockstep_longctx_full_vocab():
+    """Workload 4 at its real vocabulary and batch (V=151936, B=4: 244 split rows
+    per step) after an 8192-token prompt ingested in four 2048-row chunks (tokens
+    repeated across chunks: the last position wins): every output and the full
+    matrix."""
+    cfg = _small(4, prompt_len=8192)
+    st = _compare_runs(cfg, 12, warmup=0, table_every=4)
+    assert st["accepted"] > 0
+
+
 @pytest.mark.parametrize("cfg_id,steps", [(3, 3), (5, 3), (2, 20)])
 def test_lockstep_full_size(cfg_id, steps):
     """Real shapes (B=16, V=151936, 61 or 17 rows per request; B=1, V=128256):
