@@ -111,12 +111,13 @@ struct TopkArgs {
     float *prob;   // nullable: softmax probability of each top-k id
     float *stats;  // nullable: per row (largest value, sum of exp(value - largest))
     // rows split over `groups` workgroups (groups > 1): per-row arrival counters,
-    // each slice's top-8 (row ranks) and softmax statistics, all in the workspace
+    // each slice's top-8 (row ranks) and softmax statistics (largest value and
+    // sum packed in one word), all in the workspace, zero between calls
     int groups;
     int loads;  // 1 KB blocks per wave per batch: selects the kernel instantiation
     uint32_t *cnt;
     uint64_t *part;
-    float *pstat;
+    uint64_t *pstat;
 };
 
 struct VerifyArgs {

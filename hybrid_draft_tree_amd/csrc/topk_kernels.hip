@@ -35,6 +35,7 @@ constexpr int kTop = 8;
 constexpr int kMaxWavesPerRow = 16;
 constexpr int kHeadPad = 8;  // local offsets below this are the row's unaligned head
 constexpr uint64_t kSpinTicks = 100000000ull;  // coordinator gives up after ~1 s (100 MHz clock)
+constexpr uint64_t kEmptyRank = 1ull;  // a slice's empty top-8 entry (no real row rank has a zero high word)
 
 typedef short short2v __attribute__((ext_vector_type(2)));
 typedef int int4v __attribute__((ext_vector_type(4)));
@@ -236,6 +237,13 @@ struct SoftStats {
         add_batch<1>(x);
     }
 };
+
+// A slice's softmax statistics (largest value, sum of exp(value - largest)) in
+// one word: never zero (a finite largest value contributes at least 1 to the
+// sum, and -inf has nonzero bits).
+__device__ __forceinline__ uint64_t pack_stats(float m, float s) {
+    return ((uint64_t)__float_as_uint(m) << 32) | __float_as_uint(s);
+}
 
 template <typename TR, int U>
 __device__ __forceinline__ void add_groups(SoftStats &st, const uint4 (&d)[U]) {
@@ -747,22 +755,41 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         rowS = wave_sum_f32(s);
     }
     if constexpr (SPLIT) {
-        // Publish this slice's top-8 and statistics; the row's last slice to
-        // arrive (per-row counter, no waiting) merges the G results and goes on
-        // as the row's finisher, clearing what it read.
+        // Store this slice's top-8 and statistics and arrive at the row's counter
+        // at once, without waiting for the stores: the row's last slice to arrive
+        // merges the G results and goes on as the row's finisher, clearing what it
+        // read.  Every stored word is nonzero (an empty entry is stored as
+        // kEmptyRank; the packed statistics never read zero), so the finisher
+        // reads another slice's words again until none is zero (a store still on
+        // its way); its own come from registers.  A wait beyond kSpinTicks gives
+        // up: the row then reports no ids.
         const size_t pb = (size_t)row * G * kTop;
-        if (lane < kTop) st_agent(&a.part[pb + (size_t)g * kTop + lane], rtop);
-        if (PROB && lane == 0) {
-            st_agent((int32_t *)&a.pstat[2 * ((size_t)row * G + g)], __float_as_int(rowM));
-            st_agent((int32_t *)&a.pstat[2 * ((size_t)row * G + g) + 1], __float_as_int(rowS));
-        }
-        publish();
+        const size_t ps = (size_t)row * G;
+        if (lane < kTop) st_agent(&a.part[pb + (size_t)g * kTop + lane], rtop ? rtop : kEmptyRank);
+        if (PROB && lane == 0) st_agent(&a.pstat[ps + g], pack_stats(rowM, rowS));
         uint32_t old = 0;
         if (lane == 0) old = __hip_atomic_fetch_add(&a.cnt[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((int)readlane_i32((int)old, 0) != G - 1) return;
         after_count();
         const int n = G * kTop;  // <= 64: one entry per lane
-        const uint64_t x = lane < n ? ld_agent(&a.part[pb + lane]) : 0ull;
+        const bool own = lane >= g * kTop && lane < (g + 1) * kTop;
+        const bool other = lane < n && !own;
+        const bool other_st = PROB && lane < G && lane != g;
+        const uint64_t mine = shfl_u64(rtop, own ? lane - g * kTop : 0);
+        uint64_t x = own ? (mine ? mine : kEmptyRank) : 0ull;
+        uint64_t sv = 0ull;
+        const uint64_t t0 = wall_clock64();
+        bool ok = true;
+        while (true) {
+            if (other && x == 0ull) x = ld_agent(&a.part[pb + lane]);
+            if (other_st && sv == 0ull) sv = ld_agent(&a.pstat[ps + lane]);
+            if (!ballot((other && x == 0ull) || (other_st && sv == 0ull))) break;
+            if (wall_clock64() - t0 > kSpinTicks) {
+                ok = false;
+                break;
+            }
+        }
+        if (x == kEmptyRank) x = 0ull;
         int above = 0;
         for (int j = 0; j < n; ++j) {
             const uint32_t lo = (uint32_t)readlane_i32((int)(uint32_t)x, j);
@@ -774,16 +801,21 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        rtop = lane < kTop ? s_top[lane] : 0ull;
-        if (lane < n) st_agent(&a.part[pb + lane], 0ull);
+        rtop = (lane < kTop && ballot(!ok) == 0ull) ? s_top[lane] : 0ull;
+        // clear what was read: the other slices' words by the lanes that read
+        // them, this slice's own by the lanes that stored them
+        if (other) st_agent(&a.part[pb + lane], 0ull);
+        if (lane < kTop) st_agent(&a.part[pb + (size_t)g * kTop + lane], 0ull);
         if constexpr (PROB) {
+            if (lane == 0) st_agent(&a.pstat[ps + g], 0ull);
             float m = -INFINITY, ss = 0.0f;
-            if (lane < G) {
-                const size_t q = 2 * ((size_t)row * G + lane);
-                m = __int_as_float(ld_agent((const int32_t *)&a.pstat[q]));
-                ss = __int_as_float(ld_agent((const int32_t *)&a.pstat[q + 1]));
-                st_agent((int32_t *)&a.pstat[q], 0);
-                st_agent((int32_t *)&a.pstat[q + 1], 0);
+            if (lane == g) {
+                m = rowM;
+                ss = rowS;
+            } else if (other_st) {
+                m = __uint_as_float((uint32_t)(sv >> 32));
+                ss = __uint_as_float((uint32_t)sv);
+                st_agent(&a.pstat[ps + lane], 0ull);
             }
             rowM = wave_max_f32(m);
             rowS = wave_sum_f32((m == -INFINITY) ? 0.0f : ss * __expf(m - rowM));
@@ -946,7 +978,7 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
         p.off_cnt = p.ws_bytes;
         p.off_part = p.off_cnt + (nr * sizeof(uint32_t) + 255) / 256 * 256;
         p.off_pstat = p.off_part + (nr * G * kTop * sizeof(uint64_t) + 255) / 256 * 256;
-        p.ws_bytes = p.off_pstat + (nr * G * 2 * sizeof(float) + 255) / 256 * 256;
+        p.ws_bytes = p.off_pstat + (nr * G * sizeof(uint64_t) + 255) / 256 * 256;
     }
     return p;
 }
@@ -963,7 +995,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     a.loads = p.loads;
     a.cnt = p.groups > 1 ? (uint32_t *)((char *)ws + p.off_cnt) : nullptr;
     a.part = p.groups > 1 ? (uint64_t *)((char *)ws + p.off_part) : nullptr;
-    a.pstat = p.groups > 1 ? (float *)((char *)ws + p.off_pstat) : nullptr;
+    a.pstat = p.groups > 1 ? (uint64_t *)((char *)ws + p.off_pstat) : nullptr;
     a.k = k;
     a.topk = topk;
     a.prob = prob;
