@@ -465,7 +465,8 @@ __global__ __launch_bounds__(kWave *kReqPerBlock) void k_flatten(FlattenKernelAr
 // Fused build: one workgroup (2 wavefronts) per request.  TREE: wave 0 expands
 // the whole template from the root while wave 1 prunes; after one barrier wave
 // 0 keeps the first R = slots - n_keep template nodes and flattens.  TAIL:
-// wave 0 does all three (the chain starts from the last kept block token).
+// both waves take the prefix; wave 0 walks the chain (from the last kept block
+// token) while wave 1 flattens, then wave 0 stores the chain's tokens.
 __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
     __shared__ int s_misc[1];
     __shared__ int s_tok[kWave], s_par[kWave], s_rowret[kWave], s_rowtpl[kWave];
@@ -544,39 +545,49 @@ __global__ __launch_bounds__(2 * kWave) void k_build_tree(BuildKernelArgs a) {
         const int tv = __shfl(val, tn >= 0 ? tn : lane);
         if (tn >= 0) a.tok[(size_t)b * a.T1 + lane] = tv;
     } else {
-        if (wv != 0) return;
+        // TAIL: both waves take the prefix (one ballot); wave 0 follows the
+        // retrieval chain (dependent gathers) while wave 1 flattens the rows,
+        // whose structure does not depend on the retrieved tokens
         const float c = isd ? a.d_score[od] : 1.0f;
         const PruneOut r = prune_tail_wave(isd, c, a.Nd, a.cfg.tail_thr);
         const int p = r.N;
         const int dt = isd ? a.d_tok[od] : -1;
-        const int x0 = p <= 0 ? root : readlane_i32(dt, p - 1);
         const int R = min(max(a.slots - p, 0), a.r_out);
-        const int val = retrieve_tail_wave(R, x0, a.table, a.V, a.k);
-        if (isd) a.keep[od] = r.kept ? 1 : 0;
-        FlatIn in;
-        in.isd = isd;
-        in.kp = r.kept ? 1 : 0;
-        in.dt = dt;
-        in.dp = -1;
-        in.isr = lane < R;
-        in.rt = lane < R ? val : -1;
-        in.rp = lane < R ? lane - 1 : -1;
-        in.nk = p;
-        in.R = R;
-        in.root = root;
-        in.base = a.base_pos[b];
-        if (lane < a.r_out) {
-            a.ret_tok[(size_t)b * a.r_out + lane] = in.rt;
-            a.ret_parent[(size_t)b * a.r_out + lane] = in.rp;
+        int val = -1;
+        if (wv == 0) {
+            const int x0 = p <= 0 ? root : readlane_i32(dt, p - 1);
+            val = retrieve_tail_wave(R, x0, a.table, a.V, a.k);
+            if (lane < a.r_out) a.ret_tok[(size_t)b * a.r_out + lane] = lane < R ? val : -1;
+        } else {
+            if (isd) a.keep[od] = r.kept ? 1 : 0;
+            FlatIn in;
+            in.isd = isd;
+            in.kp = r.kept ? 1 : 0;
+            in.dt = dt;
+            in.dp = -1;
+            in.isr = lane < R;
+            in.rt = -1;
+            in.rp = lane < R ? lane - 1 : -1;
+            in.nk = p;
+            in.R = R;
+            in.root = root;
+            in.base = a.base_pos[b];
+            if (lane < a.r_out) a.ret_parent[(size_t)b * a.r_out + lane] = in.rp;
+            if (lane == 0) {
+                a.stage[b] = r.stage;
+                a.n_keep[b] = p;
+                a.n_ret[b] = R;
+            }
+            const size_t o = (size_t)b * a.T1;
+            flatten_wave(GRAFT_LAYOUT_CHAIN, a.T1, in, s_tok, s_par, s_rowret, s_rowtpl, a.tok + o, a.parent + o,
+                         a.depth + o, a.pos_id + o, a.anc + o, a.row_src ? a.row_src + o : nullptr);
         }
-        if (lane == 0) {
-            a.stage[b] = r.stage;
-            a.n_keep[b] = p;
-            a.n_ret[b] = R;
-        }
-        const size_t o = (size_t)b * a.T1;
-        flatten_wave(GRAFT_LAYOUT_CHAIN, a.T1, in, s_tok, s_par, s_rowret, nullptr, a.tok + o, a.parent + o,
-                     a.depth + o, a.pos_id + o, a.anc + o, a.row_src ? a.row_src + o : nullptr);
+        __syncthreads();
+        if (wv != 0) return;
+        // wave 0: the retrieved tokens into the rows that hold them
+        const int tn = lane < a.T1 ? s_rowtpl[lane] : -1;
+        const int tv = __shfl(val, tn >= 0 ? tn : lane);
+        if (tn >= 0) a.tok[(size_t)b * a.T1 + lane] = tv;
     }
 }
 
