@@ -27,14 +27,20 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 struct WsLayout {
     TopkPlan plan;
     size_t off_topk = 0, off_prob = 0, total = 0;
+    bool fits = false;  // the launch's size is within what one launch can hold
 };
 
 WsLayout ws_layout(int64_t n_rows, int V, int k, int dtype) {
     WsLayout L;
+    if (n_rows < 0 || n_rows >= INT32_MAX) return L;  // row positions are kept as P + 1 in 32 bits
     L.plan = plan_topk(n_rows, V, dtype);
     L.off_topk = align256(L.plan.ws_bytes);
     L.off_prob = L.off_topk + align256((size_t)n_rows * k * sizeof(int32_t));
     L.total = L.off_prob + align256((size_t)n_rows * k * sizeof(float));
+    // the launch's thread count is 32-bit: (row slices + coordinators, which never
+    // outnumber the rows) x wavefronts per slice x 64 lanes
+    const int64_t units = n_rows * L.plan.groups + n_rows;
+    L.fits = units * L.plan.splits * 64 <= (int64_t)UINT32_MAX;
     return L;
 }
 
@@ -57,7 +63,8 @@ const char *graft_status_string(int status) {
 size_t graft_workspace_bytes(int64_t n_rows, int V, int k, int dtype) {
     if (n_rows < 0 || V <= 0 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K || k > V || !dtype_ok(dtype))
         return 0;
-    return ws_layout(n_rows, V, k, dtype).total;
+    const WsLayout L = ws_layout(n_rows, V, k, dtype);
+    return L.fits ? L.total : 0;
 }
 
 int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const int32_t *d_layer,
@@ -350,7 +357,7 @@ int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logi
     if (!aligned(logits, 16) || !aligned(ws, 256) || !aligned(row_stats, 8)) return GRAFT_EINVAL;
     const int64_t n_rows = (int64_t)B * T1;
     const WsLayout L = ws_layout(n_rows, V, k, dtype);
-    if (ws_bytes < L.total) return GRAFT_EINVAL;
+    if (!L.fits || ws_bytes < L.total) return GRAFT_EINVAL;
     VerifyArgs v;
     v.T1 = T1;
     v.tok = tok;
@@ -383,7 +390,7 @@ int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logi
     if (!aligned(logits, 16) || !aligned(ws, 256) || !aligned(row_stats, 8)) return GRAFT_EINVAL;
     const int64_t n_rows = (int64_t)B * T1;
     const WsLayout L = ws_layout(n_rows, V, k, dtype);
-    if (ws_bytes < L.total) return GRAFT_EINVAL;
+    if (!L.fits || ws_bytes < L.total) return GRAFT_EINVAL;
     VerifyArgs v;
     v.T1 = T1;
     v.tok = tok;
@@ -411,7 +418,7 @@ int graft_update_topk(int64_t n_rows, int V, int k, int dtype, const void *logit
     if (logits) {
         if (!ws || !aligned(logits, 16) || !aligned(ws, 256)) return GRAFT_EINVAL;
         const WsLayout L = ws_layout(n_rows, V, k, dtype);
-        if (ws_bytes < L.total) return GRAFT_EINVAL;
+        if (!L.fits || ws_bytes < L.total) return GRAFT_EINVAL;
         int32_t *tk_ws = topk_out ? topk_out : (int32_t *)((char *)ws + L.off_topk);
         float *pr_ws = table_prob ? (float *)((char *)ws + L.off_prob) : nullptr;
         // top-k and the matrix update in one launch: the registration workgroup

@@ -359,7 +359,11 @@ int graft_coverage_gain(int B, int T1, int V, int dtype, const void *logits, con
 
 /* Workspace bytes needed by graft_verify_accept / graft_verify_update /
  * graft_update_topk for n_rows rows of V logits (0 on invalid sizes).  Zero-fill it once after
- * allocating it; calls leave it zero-filled. */
+ * allocating it; calls leave it zero-filled.  Also 0 when n_rows rows do not fit one launch:
+ * n_rows must be below 2^31 - 1, and (2 n_rows) x wavefronts per row x 64 threads below 2^32
+ * (one wavefront per row from ~3000 rows on at V <= 127 x 512 bf16, so up to ~33 million rows
+ * there; rows of larger V take more wavefronts, up to 16 at V = 10^6).  Those three calls
+ * return GRAFT_EINVAL for such sizes: split the rows over several calls. */
 size_t graft_workspace_bytes(int64_t n_rows, int V, int k, int dtype);
 
 /* Static description of a status code. */

@@ -51,6 +51,30 @@ def test_workspace_bytes():
     assert L.graft_workspace_bytes(0, 100, 8, L.DTYPE_F32) >= 0
 
 
+def test_launch_size_limits():
+    """Row counts that do not fit one top-k launch (32-bit thread count, 32-bit
+    row positions) get no workspace size and are rejected before any launch."""
+    bf = L.DTYPE_BF16
+    # small vocabulary: one wavefront per row, rows + coordinators <= 2 n_rows
+    assert L.graft_workspace_bytes(30_000_000, 100, 8, bf) > 0
+    assert L.graft_workspace_bytes(40_000_000, 100, 8, bf) == 0
+    assert L.graft_workspace_bytes((1 << 31) - 1, 100, 8, bf) == 0
+    # V = 10^6 bf16 needs 16 wavefronts per row (127 blocks of 512 elements per wavefront at most)
+    assert L.graft_workspace_bytes(2_000_000, 10 ** 6, 8, bf) > 0
+    assert L.graft_workspace_bytes(3_000_000, 10 ** 6, 8, bf) == 0
+    lib = L.load()
+    P = 0x1000  # never dereferenced
+    huge = 1 << 62
+    assert lib.graft_update_topk(40_000_000, 100, 8, bf, P, None, None, P, P, None, None, P, huge, None) == \
+        L.GRAFT_EINVAL
+    assert lib.graft_update_topk(1 << 40, 100, 8, bf, P, None, None, P, P, None, None, P, huge, None) == \
+        L.GRAFT_EINVAL
+    assert lib.graft_verify_accept(700_000, 61, 100, 8, bf, *([P] * 9), 60, P, None, P, huge, None) == \
+        L.GRAFT_EINVAL
+    assert lib.graft_verify_update(700_000, 61, 100, 8, bf, *([P] * 11), 60, P, None, P, huge, None) == \
+        L.GRAFT_EINVAL
+
+
 @pytest.mark.parametrize("W,D,R", [(8, 8, 52), (8, 8, 64), (8, 8, 20), (4, 6, 24), (1, 3, 3), (5, 1, 5)])
 def test_template_matches_oracle(W, D, R):
     par, rk, dp = L.graft_template_master(W, D, R)
