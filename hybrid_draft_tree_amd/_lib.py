@@ -21,6 +21,7 @@ GRAFT_EDEVICE = -3
 GRAFT_MAX_ROWS = 64
 GRAFT_MAX_K = 8
 GRAFT_MAX_VOCAB = 1000000   # logits per row accepted by the top-k calls
+GRAFT_MAX_BATCH = 1 << 24   # requests per call
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 MODE_TREE = 0

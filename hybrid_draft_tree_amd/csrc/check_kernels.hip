@@ -96,7 +96,7 @@ extern "C" {
 int graft_check_draft(int B, int Nd, int mode, int V, const int32_t *d_parent, const int32_t *d_layer,
                       const float *d_score, const int32_t *d_tok, int32_t *status, hipStream_t stream) {
     if (mode != GRAFT_MODE_TREE && mode != GRAFT_MODE_TAIL) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || Nd < 1 || Nd > GRAFT_MAX_ROWS || V < 1) return GRAFT_EINVAL;
+    if (B < 0 || B > GRAFT_MAX_BATCH || Nd < 1 || Nd > GRAFT_MAX_ROWS || V < 1) return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
     if (!d_score || !d_tok || !status || (mode == GRAFT_MODE_TREE && (!d_parent || !d_layer))) return GRAFT_EINVAL;
     hipLaunchKernelGGL(k_check_draft, dim3((B + kReq - 1) / kReq), dim3(graft::kWave * kReq), 0, stream, B, Nd,
@@ -106,7 +106,7 @@ int graft_check_draft(int B, int Nd, int mode, int V, const int32_t *d_parent, c
 
 int graft_check_tree(int B, int T1, int V, const int32_t *tok, const int32_t *parent, const int32_t *depth,
                      int32_t *status, hipStream_t stream) {
-    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1) return GRAFT_EINVAL;
+    if (B < 0 || B > GRAFT_MAX_BATCH || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1) return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
     if (!tok || !parent || !depth || !status) return GRAFT_EINVAL;
     hipLaunchKernelGGL(k_check_tree, dim3((B + kReq - 1) / kReq), dim3(graft::kWave * kReq), 0, stream, B, T1, V,

@@ -71,7 +71,7 @@ int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const i
                        const float *d_score, const graft_prune_cfg *cfg, int32_t *stage,
                        int32_t *n_keep, uint8_t *keep, float *cum_out, hipStream_t stream) {
     if (mode != GRAFT_MODE_TREE && mode != GRAFT_MODE_TAIL) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || Nd < 1 || Nd > GRAFT_MAX_ROWS || !cfg) return GRAFT_EINVAL;
+    if (B < 0 || B > GRAFT_MAX_BATCH || Nd < 1 || Nd > GRAFT_MAX_ROWS || !cfg) return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
     if (!d_score || !stage || !n_keep || !keep) return GRAFT_EINVAL;
     if (mode == GRAFT_MODE_TREE) {
@@ -88,7 +88,7 @@ int graft_prune_select(int B, int Nd, int mode, const int32_t *d_parent, const i
 int graft_checkpoint_stats(int B, int Nd, const int32_t *d_parent, const int32_t *d_layer,
                            const float *d_score, const graft_prune_cfg *cfg, float *out,
                            hipStream_t stream) {
-    if (B < 0 || Nd < 1 || Nd > GRAFT_MAX_ROWS || !cfg) return GRAFT_EINVAL;
+    if (B < 0 || B > GRAFT_MAX_BATCH || Nd < 1 || Nd > GRAFT_MAX_ROWS || !cfg) return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
     if (!d_parent || !d_layer || !d_score || !out) return GRAFT_EINVAL;
     CkptStatsArgs a{B, Nd, d_parent, d_layer, d_score, {}, {}, out};
@@ -185,7 +185,7 @@ int graft_retrieve_expand(int B, int V, int k, int mode, int slots, const int32_
                           int32_t *ret_tok, int32_t *ret_parent, int32_t *n_ret, int r_out,
                           hipStream_t stream) {
     if (mode != GRAFT_MODE_TREE && mode != GRAFT_MODE_TAIL) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || V < 1 || k < 1 || k > GRAFT_MAX_K || slots < 0 || r_out < 1 ||
+    if (B < 0 || B > GRAFT_MAX_BATCH || V < 1 || k < 1 || k > GRAFT_MAX_K || slots < 0 || r_out < 1 ||
         r_out > GRAFT_MAX_ROWS)
         return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
@@ -221,7 +221,7 @@ int graft_build_tree_mask(int B, int Nd, int T1, int layout, const int32_t *root
     if (layout != GRAFT_LAYOUT_COMPACT && layout != GRAFT_LAYOUT_IN_PLACE &&
         layout != GRAFT_LAYOUT_CHAIN)
         return GRAFT_EUNSUPPORTED;
-    if (B < 0 || Nd < 1 || Nd > GRAFT_MAX_ROWS || T1 < 2 || T1 > GRAFT_MAX_ROWS || r_out < 1 ||
+    if (B < 0 || B > GRAFT_MAX_BATCH || Nd < 1 || Nd > GRAFT_MAX_ROWS || T1 < 2 || T1 > GRAFT_MAX_ROWS || r_out < 1 ||
         r_out > GRAFT_MAX_ROWS)
         return GRAFT_EINVAL;
     if (layout == GRAFT_LAYOUT_IN_PLACE && T1 != Nd + 1) return GRAFT_EINVAL;
@@ -249,7 +249,7 @@ int build_tree(int B, int Nd, int T1, int mode, int layout, int slots, const gra
     if (layout != GRAFT_LAYOUT_COMPACT && layout != GRAFT_LAYOUT_IN_PLACE && layout != GRAFT_LAYOUT_CHAIN)
         return GRAFT_EUNSUPPORTED;
     if ((mode == GRAFT_MODE_TAIL) != (layout == GRAFT_LAYOUT_CHAIN)) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || Nd < 1 || Nd > GRAFT_MAX_ROWS || T1 < 2 || T1 > GRAFT_MAX_ROWS || r_out < 1 ||
+    if (B < 0 || B > GRAFT_MAX_BATCH || Nd < 1 || Nd > GRAFT_MAX_ROWS || T1 < 2 || T1 > GRAFT_MAX_ROWS || r_out < 1 ||
         r_out > GRAFT_MAX_ROWS || V < 1 || k < 1 || k > GRAFT_MAX_K || slots < 0 || !cfg)
         return GRAFT_EINVAL;
     if (T1 != slots + 1) return GRAFT_EINVAL;
@@ -347,7 +347,7 @@ int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logi
                         int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws,
                         size_t ws_bytes, hipStream_t stream) {
     if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K ||
+    if (B < 0 || B > GRAFT_MAX_BATCH || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K ||
         k > V || dmax < 0)
         return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
@@ -380,7 +380,7 @@ int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logi
                         int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws,
                         size_t ws_bytes, hipStream_t stream) {
     if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K ||
+    if (B < 0 || B > GRAFT_MAX_BATCH || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K ||
         k > V || dmax < 0)
         return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
@@ -441,7 +441,7 @@ int graft_coverage_gain(int B, int T1, int V, int dtype, const void *logits, con
                         const int32_t *parent, const uint8_t *row_src, const float *row_stats,
                         float *gain, hipStream_t stream) {
     if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB) return GRAFT_EINVAL;
+    if (B < 0 || B > GRAFT_MAX_BATCH || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB) return GRAFT_EINVAL;
     if (B == 0) return GRAFT_OK;
     if (!logits || !tok || !parent || !row_src || !row_stats || !gain) return GRAFT_EINVAL;
     if (!aligned(row_stats, 8)) return GRAFT_EINVAL;

@@ -66,6 +66,7 @@ extern "C" {
 #define GRAFT_MAX_ROWS 64 /* rows per request (root + candidate slots); one wavefront */
 #define GRAFT_MAX_K 8     /* successors per matrix row */
 #define GRAFT_MAX_VOCAB 1000000 /* logits per row for the top-k calls (at most 16 wavefronts per row) */
+#define GRAFT_MAX_BATCH (1 << 24) /* requests per call (a launch's thread count is 32-bit); larger B: EINVAL */
 
 /* Prune configuration (host POD).  Section 二, gear 1: checkpoints at draft
  * depths 0, 1 and 5 compare the best cumulative path confidence with a

@@ -73,6 +73,14 @@ def test_launch_size_limits():
         L.GRAFT_EINVAL
     assert lib.graft_verify_update(700_000, 61, 100, 8, bf, *([P] * 11), 60, P, None, P, huge, None) == \
         L.GRAFT_EINVAL
+    # per-request calls: at most 2^24 requests
+    cfg = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 40), 0.5)
+    assert lib.graft_prune_select(L.GRAFT_MAX_BATCH + 1, 60, 0, P, P, P, ctypes.byref(cfg), P, P, P, None, None) == \
+        L.GRAFT_EINVAL
+    assert lib.graft_build_tree_mask(L.GRAFT_MAX_BATCH + 1, 60, 61, 0, *([P] * 9), 52, *([P] * 5), None, None) == \
+        L.GRAFT_EINVAL
+    assert lib.graft_coverage_gain(L.GRAFT_MAX_BATCH + 1, 61, 100, 1, *([P] * 6), None) == L.GRAFT_EINVAL
+    assert lib.graft_check_tree(L.GRAFT_MAX_BATCH + 1, 61, 100, P, P, P, P, None) == L.GRAFT_EINVAL
 
 
 @pytest.mark.parametrize("W,D,R", [(8, 8, 52), (8, 8, 64), (8, 8, 20), (4, 6, 24), (1, 3, 3), (5, 1, 5)])
