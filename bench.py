@@ -212,7 +212,7 @@ def ablation(args):
     prune, no retrieval) and the per-node static-slot threshold."""
     import torch
 
-    from synth import CONFIGS
+    from synth import WORKLOADS
 
     assert torch.cuda.is_available(), "the ablation runs on the GPU"
     dev = torch.device("cuda", 0)
@@ -222,7 +222,7 @@ def ablation(args):
                 ("fixed 40/20", {"tau": (0.0, 0.0, inf)}), ("dense (no prune)", {"tau": (0.0, 0.0, 0.0)})]
     variants += [("per-node tau=%g" % t, {"node_tau": t}) for t in (0.05, 0.1, 0.2, 0.3)]
     for cfg_id in [int(x) for x in args.ablation_configs.split(",")]:
-        base = CONFIGS[cfg_id]
+        base = WORKLOADS[cfg_id]
         for name, kw in variants:
             t0 = time.time()
             rec = {"ablation": name, "workload": base.name}
@@ -241,7 +241,7 @@ def calibration(args):
     import numpy as np
     import torch
 
-    from synth import CONFIGS
+    from synth import WORKLOADS
 
     assert torch.cuda.is_available(), "the calibration study runs on the GPU"
     dev = torch.device("cuda", 0)
@@ -250,7 +250,7 @@ def calibration(args):
               (0.1, 0.4, 0.9), (0.1, 0.5, 0.97)]
     own = {}
     for cfg_id in ids:
-        base = CONFIGS[cfg_id]
+        base = WORKLOADS[cfg_id]
         fixed = [float(np.float32(math.log(t))) for t in base.tau]
         rec = {"calibration": "fixed tau %s" % (base.tau,), "workload": base.name}
         # calibrate only to record the statistics; the fixed thresholds are kept
@@ -268,9 +268,9 @@ def calibration(args):
             for dst in ids:
                 if src == dst:
                     continue
-                rec = {"calibration": "q=%s transferred" % (q,), "from": CONFIGS[src].name,
-                       "workload": CONFIGS[dst].name}
-                rec.update(_accept_run(CONFIGS[dst], args.sweep_steps, dev, warmup=CONFIGS[dst].warmup_steps,
+                rec = {"calibration": "q=%s transferred" % (q,), "from": WORKLOADS[src].name,
+                       "workload": WORKLOADS[dst].name}
+                rec.update(_accept_run(WORKLOADS[dst], args.sweep_steps, dev, warmup=WORKLOADS[dst].warmup_steps,
                                        log_thr=own[(src, q)]))
                 print(json.dumps(rec), flush=True)
 
@@ -283,7 +283,7 @@ def template_sweep(args):
     whose accepted path reaches a retrieved row, and the mean coverage gain."""
     import torch
 
-    from synth import CONFIGS
+    from synth import WORKLOADS
 
     assert torch.cuda.is_available(), "the template sweep runs on the GPU"
     dev = torch.device("cuda", 0)
@@ -291,7 +291,7 @@ def template_sweep(args):
     depths = [int(x) for x in args.sweep_depths.split(",")]
     widths = [int(x) for x in args.sweep_widths.split(",")]
     for cfg_id in [int(x) for x in args.sweep_configs.split(",")]:
-        base = CONFIGS[cfg_id]
+        base = WORKLOADS[cfg_id]
         for kind, beta in families:
             for D in depths:
                 for W in widths:
@@ -314,7 +314,7 @@ def all_configs(args):
     import torch
 
     from hybrid_draft_tree_amd.driver import GraftPipeline
-    from synth import CONFIGS
+    from synth import WORKLOADS
     from synth import generators as G
     from synth import runner as R
 
@@ -323,7 +323,7 @@ def all_configs(args):
     torch.cuda.set_device(dev)
     P = max(1, args.pool)
     for cid in [int(x) for x in args.config_list.split(",") if x.strip()]:
-        cfg = CONFIGS[cid]
+        cfg = WORKLOADS[cid]
         t0 = time.time()
         pipe = GraftPipeline.from_config(cfg, device=dev)
         ad = _Adapter(pipe, torch)
@@ -406,22 +406,22 @@ def main():
     if args.calibration:
         return calibration(args)
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build measures the single-GPU Graft "
-              "step (no collectives); run with --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: it measures the single-GPU Graft step "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
 
     from hybrid_draft_tree_amd import _lib as L
     from hybrid_draft_tree_amd.driver import GraftPipeline
-    from synth import CONFIGS
+    from synth import WORKLOADS
     from synth import generators as G
     from synth import runner as R
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    cfg = CONFIGS[3]
+    cfg = WORKLOADS[3]
     B, T1, V, k = cfg.B, cfg.rows_per_request, cfg.V, cfg.k
     n_rows = B * T1
     P = max(1, args.pool)
@@ -622,7 +622,7 @@ def main():
     # TAIL (16 requests x 17 rows: a 16-token block plus its anchor, 82.65 MB of
     # logits) and one prompt-ingest chunk (2048 rows, 622.3 MB): each a single
     # k_topk_rows launch, timed like the dominant kernel.
-    tcfg = CONFIGS[5]
+    tcfg = WORKLOADS[5]
     tp = GraftPipeline.from_config(tcfg, device=dev)
     tad = _Adapter(tp, torch)
     twl = R.Workload(tcfg)

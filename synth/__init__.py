@@ -5,4 +5,4 @@ and benchmark.  It draws random numbers and lays out inputs; it computes none
 of the method's own arithmetic (no pruning, retrieval, flattening, top-k,
 acceptance or matrix update).
 """
-from .configs import CONFIGS, GraftConfig, get  # noqa: F401
+from .configs import WORKLOADS, GraftConfig, get  # noqa: F401

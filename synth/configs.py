@@ -81,7 +81,7 @@ class GraftConfig:
         return GraftConfig(**d)
 
 
-CONFIGS = {
+WORKLOADS = {
     1: GraftConfig(name="toy_v32000_f32", cfg_id=1, V=32000, B=1, steps=500, dtype="f32",
                    layout="compact"),
     2: GraftConfig(name="llama8b_v128256_b1", cfg_id=2, V=128256, B=1, steps=2000,
@@ -96,4 +96,4 @@ CONFIGS = {
 
 
 def get(cfg_id: int) -> GraftConfig:
-    return CONFIGS[cfg_id]
+    return WORKLOADS[cfg_id]

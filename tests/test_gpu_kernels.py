@@ -959,11 +959,11 @@ def test_check_tree_accepts_built_trees_and_flags_faults(layout):
 
 def test_pipeline_debug_checks_raise_on_a_bad_draft():
     from hybrid_draft_tree_amd.driver import GraftPipeline
-    from synth import CONFIGS
+    from synth import WORKLOADS
     from synth import runner as R
     from tests.backends import HipBackend
 
-    cfg = CONFIGS[3].scaled(V=8000, B=4, noise_pool_rows=8)
+    cfg = WORKLOADS[3].scaled(V=8000, B=4, noise_pool_rows=8)
     hb = HipBackend(cfg)
     hb.p.debug_checks = True
     wl = R.Workload(cfg)

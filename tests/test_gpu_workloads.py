@@ -14,7 +14,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from oracle import oracle as O  # noqa: E402
-from synth import CONFIGS  # noqa: E402
+from synth import WORKLOADS  # noqa: E402
 from synth import generators as G  # noqa: E402
 from synth import runner as R  # noqa: E402
 from tests.backends import HipBackend, OracleBackend  # noqa: E402
@@ -68,7 +68,7 @@ def _compare_runs(cfg, n_steps, warmup, table_every=1, fused=True, want_prob=Fal
 
 
 def _small(cfg_id, **kw):
-    cfg = CONFIGS[cfg_id]
+    cfg = WORKLOADS[cfg_id]
     d = dict(noise_pool_rows=16)
     d.update(kw)
     return cfg.scaled(**d)
@@ -197,14 +197,14 @@ def test_lockstep_longctx_full_vocab():
 def test_lockstep_full_size(cfg_id, steps):
     """Real shapes (B=16, V=151936, 61 or 17 rows per request; B=1, V=128256):
     every output and the full matrix, for a few steps after warm-up."""
-    cfg = CONFIGS[cfg_id]
+    cfg = WORKLOADS[cfg_id]
     st = _compare_runs(cfg, steps, warmup=2, table_every=steps + 2)
     assert st["accepted"] > 0
 
 
 def test_full_config1_500_steps():
     """Workload 1 end to end at its full length (500 steps after 5 warm-up steps)."""
-    cfg = CONFIGS[1]
+    cfg = WORKLOADS[1]
     if os.environ.get("GRAFT_QUICK"):
         pytest.skip("quick mode")
     st = _compare_runs(cfg, cfg.steps, warmup=cfg.warmup_steps, table_every=50)
@@ -216,7 +216,7 @@ def test_ingest_full_size_sampled():
     GPU; matrix rows and the first root checked against the oracle on a sample
     of prompt tokens (each row's expected value is the top-k of the last prompt
     row holding that token)."""
-    cfg = CONFIGS[4]
+    cfg = WORKLOADS[4]
     hb = HipBackend(cfg)
     wl = R.Workload(cfg)
     R.start(hb, wl)

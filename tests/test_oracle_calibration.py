@@ -111,11 +111,11 @@ def test_quantile_special_cases():
 def test_calibrated_run_uses_the_quantile_thresholds():
     """OracleGraft: the thresholds after warm-up are the quantiles of what the
     warm-up drafts showed, and later steps prune with them."""
-    from synth import CONFIGS
+    from synth import WORKLOADS
     from synth import runner as R
     from tests.backends import OracleBackend
 
-    cfg = CONFIGS[1].scaled(calib_q=(0.5, 0.5, 0.5))
+    cfg = WORKLOADS[1].scaled(calib_q=(0.5, 0.5, 0.5))
     be = OracleBackend(cfg)
     drafts = []
     orig = be.o.build

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from oracle import oracle as O
-from synth import CONFIGS
+from synth import WORKLOADS
 from synth import generators as G
 from synth import runner as R
 from synth.device import DeviceRows
@@ -13,7 +13,7 @@ from tests.backends import OracleBackend
 
 
 def _small(cfg_id):
-    cfg = CONFIGS[cfg_id]
+    cfg = WORKLOADS[cfg_id]
     kw = dict(V=997 if cfg.dtype == "f32" else 1000, noise_pool_rows=8)
     if cfg_id == 4:
         kw.update(prompt_len=600, ingest_chunk=256, ident_vocab=64, span_len=16)
