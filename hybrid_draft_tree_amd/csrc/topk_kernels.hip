@@ -320,11 +320,13 @@ __device__ __forceinline__ void accept_walk(const VerifyArgs &v, int b, int g, i
 
 // One row from registers (wave 0 of the row's workgroup): lanes j < k hold the
 // row's j-th id and probability.  t is the row's token (valid, uniform).
+// occ_read: the token's holder word if the row already read it (nonzero, lane
+// 0), else 0 and it is read here.
 __device__ __forceinline__ void update_row_regs(const VerifyArgs &v, int k, int64_t P, int t, int32_t id,
-                                                float pj, bool with_prob) {
+                                                float pj, bool with_prob, int occ_read) {
     const int lane = lane_id();
-    int occ = 0;
-    if (lane == 0) occ = ld_agent(&v.last_occ[t]);
+    int occ = occ_read;
+    if (occ == 0 && lane == 0) occ = ld_agent(&v.last_occ[t]);
     occ = readlane_i32(occ, 0);
     if (occ != (int32_t)(P + 1)) return;
     if (lane < k) {
@@ -691,6 +693,16 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     }
     __syncthreads();
     if (wv != 0) return;
+    // Unsplit rows: once the hand-off word has shown the registration, the row's
+    // holder word is final (the registration published its maxima before it
+    // arrived), so it is read now, under the row selection, instead of after it.
+    int occ_read = 0;
+    if constexpr (ACCEPT && !SPLIT) {
+        if (v.table && lane == 0 && handoff_seen == 1 && row_tok >= 0 && row_tok < a.V) {
+            after_count();
+            occ_read = ld_agent(&v.last_occ[row_tok]);
+        }
+    }
     uint64_t rtop = 0;  // lanes 0..7: the row's top-8 (row ranks), descending
     if (S * kTop <= kWave) {
         // one entry per lane: its rank is the number of entries above it (row
@@ -855,7 +867,7 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
             }
             if (mine) {
                 after_count();
-                update_row_regs(v, a.k, row, t, my_id, my_p, a.prob != nullptr);
+                update_row_regs(v, a.k, row, t, my_id, my_p, a.prob != nullptr, readlane_i32(occ_read, 0));
                 if (lane == 0) st_agent(&v.handoff[row], 0u);
             }
         }
