@@ -713,6 +713,68 @@ def test_build_hybrid_tree_matches_oracle_tree(kind, W, D, beta, ahead):
         np.testing.assert_array_equal(src.cpu().numpy(), fl["row_src"])
 
 
+@pytest.mark.parametrize("B", [1, 33])
+def test_build_hybrid_tree_tail_matches_oracle(B):
+    """graft_build_hybrid_tree in TAIL mode (one launch: prefix, chain of
+    rank-0 successors, chain rows) against the oracle's three TAIL steps, with
+    prefixes of every length including none (the chain starts at the root) and
+    the whole block (nothing retrieved), and a table with self-loops."""
+    rng = np.random.default_rng(41 + B)
+    V = 3001
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    loops = rng.choice(V, size=300, replace=False)
+    table[loops, 0] = loops                                  # x -> x: the chain repeats a token
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    base = rng.integers(0, 100000, size=B).astype(np.int32)
+    d_tok = rng.integers(0, V, size=(B, 16)).astype(np.int32)
+    d_tok[:, 3] = loops[0]
+    conf = rng.random((B, 16)).astype(np.float32)
+    for b in range(B):                                        # prefix length b % 17 (then one below 0.5)
+        p = (b * 7) % 17 if B > 1 else 15
+        conf[b, :p] = 0.5 + 0.5 * rng.random(p).astype(np.float32)
+        if p < 16:
+            conf[b, p] = 0.49
+    if B > 1:
+        conf[0] = 0.1                                         # p = 0: chain from the root
+        conf[1] = 1.0                                         # p = 16: nothing retrieved
+        conf[2, 0], conf[2, 1] = 0.5, np.float32(0.49999997)  # exactly at the threshold, then just below
+    dpar = np.tile(np.arange(-1, 15, dtype=np.int32), (B, 1))
+    lay = np.tile(np.arange(16, dtype=np.int32), (B, 1))
+    cfg = L.prune_cfg(CFG["ckpt"], [float(np.float32(math.log(t))) for t in CFG["tau"]], CFG["keep"], 0.5)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    ins = [_t(x, torch.int32) for x in (table, roots, base, dpar, lay, d_tok)]
+    sc = _t(conf, torch.float32)
+    st, nk, nr = (torch.full((B,), 77, **i32) for _ in range(3))
+    kp = torch.full((B, 16), 9, dtype=torch.uint8, device=DEV)
+    rt, rp = torch.full((B, 16), 77, **i32), torch.full((B, 16), 77, **i32)
+    tok, par_o, dep, pos = (torch.full((B, 17), 77, **i32) for _ in range(4))
+    anc = torch.zeros(B, 17, dtype=torch.int64, device=DEV)
+    src = torch.full((B, 17), 99, dtype=torch.uint8, device=DEV)
+    L.graft_build_hybrid_tree(B, 16, 17, L.MODE_TAIL, L.LAYOUT["chain"], 16, cfg, None, V, 8,
+                              ins[0].data_ptr(), ins[1].data_ptr(), ins[2].data_ptr(), ins[3].data_ptr(),
+                              ins[4].data_ptr(), sc.data_ptr(), ins[5].data_ptr(), st.data_ptr(), nk.data_ptr(),
+                              kp.data_ptr(), None, rt.data_ptr(), rp.data_ptr(), nr.data_ptr(), 16,
+                              tok.data_ptr(), par_o.data_ptr(), dep.data_ptr(), pos.data_ptr(), anc.data_ptr(),
+                              src.data_ptr(), _s())
+    torch.cuda.synchronize()
+    pr = O.prune_tail(conf, 0.5)
+    ret = O.retrieve_tail(table, roots, d_tok, pr["n_keep"])
+    fl = O.flatten("chain", 17, roots, base, d_tok, dpar, pr["keep"], pr["n_keep"], ret)
+    if B > 1:
+        assert pr["n_keep"][0] == 0 and pr["n_keep"][1] == 16 and pr["n_keep"][2] == 1
+        assert len(set(pr["n_keep"].tolist())) == 17            # every prefix length occurs
+    np.testing.assert_array_equal(st.cpu().numpy(), pr["stage"])
+    np.testing.assert_array_equal(nk.cpu().numpy(), pr["n_keep"])
+    np.testing.assert_array_equal(kp.cpu().numpy(), pr["keep"])
+    np.testing.assert_array_equal(nr.cpu().numpy(), ret["n_ret"])
+    np.testing.assert_array_equal(rt.cpu().numpy(), ret["ret_tok"])
+    np.testing.assert_array_equal(rp.cpu().numpy(), ret["ret_parent"])
+    for name, got in (("tok", tok), ("parent", par_o), ("depth", dep), ("pos_id", pos)):
+        np.testing.assert_array_equal(got.cpu().numpy(), fl[name], err_msg=name)
+    np.testing.assert_array_equal(anc.cpu().numpy().view(np.uint64), fl["anc"])
+    np.testing.assert_array_equal(src.cpu().numpy(), fl["row_src"])
+
+
 def test_verify_update_matches_oracle_with_collisions():
     rng = np.random.default_rng(31)
     B, T1, V = 16, 61, 20000
