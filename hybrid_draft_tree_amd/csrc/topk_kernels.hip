@@ -609,6 +609,30 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         maybe_process();
     };
 
+    // the wave's last blocks (fewer than U complete ones and the row's partial
+    // last block if this wave owns it), with bounds checks: loaded by load_rem,
+    // filtered by filter_rem
+    auto load_rem = [&](uint4 (&d)[U], int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int gi = min((wv + (k0 + u) * S) * kWave + lane, ng - 1);
+            d[u] = load16<NT>(vp + gi);
+        }
+    };
+    auto filter_rem = [&](const uint4 (&d)[U], int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool inb = (k0 + u < kcount) && ((wv + (k0 + u) * S) * kWave + lane < ng);
+            if constexpr (PROB) {
+                if (inb) {
+                    const uint4 one[1] = {d[u]};
+                    add_groups<TR, 1>(st, one);
+                }
+            }
+            append(d[u], inb && (thr == INT_MIN || TR::group_pass(d[u], thr)), k0 + u);
+        }
+        maybe_process();
+    };
     int kk = 0;
     if (kfull >= U) {
         uint4 cur[U], nxt[U];
@@ -635,30 +659,22 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
 #pragma unroll
             for (int u = 0; u < U; ++u) cur[u] = nxt[u];
         }
+        // unsplit rows: the last blocks are loaded while the last full batch is
+        // filtered (measured: -0.15 us per launch at 976 rows; split rows, whose
+        // waves stream few blocks, were 0.1 us slower with it)
+        const bool rem = !SPLIT && kk + U < kcount;
+        if (rem) load_rem(nxt, kk + U);
         filter_full(cur, kk);
         kk += U;
+        if (rem) {
+            filter_rem(nxt, kk);
+            kk += U;
+        }
     }
-    // Remaining blocks of this wave (fewer than U complete ones, and the row's
-    // partial last block if this wave owns it), with bounds checks.
     for (; kk < kcount; kk += U) {
         uint4 d[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int gi = min((wv + (kk + u) * S) * kWave + lane, ng - 1);
-            d[u] = load16<NT>(vp + gi);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool inb = (kk + u < kcount) && ((wv + (kk + u) * S) * kWave + lane < ng);
-            if constexpr (PROB) {
-                if (inb) {
-                    const uint4 one[1] = {d[u]};
-                    add_groups<TR, 1>(st, one);
-                }
-            }
-            append(d[u], inb && (thr == INT_MIN || TR::group_pass(d[u], thr)), kk + u);
-        }
-        maybe_process();
+        load_rem(d, kk);
+        filter_rem(d, kk);
     }
     // the row's hand-off word, read before the final merges: once it shows the
     // registration (1) it keeps that value until this row clears it
