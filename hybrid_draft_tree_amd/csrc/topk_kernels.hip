@@ -978,8 +978,15 @@ static int loads_for(int64_t n_rows, int V, int dtype, int groups, int S) {
     return nblk / (S > 0 ? S : 1) >= kDeepBatchMinBlocks ? 4 : 2;
 }
 
+// Rows stay whole below kSplitBelowRows too when one workgroup per row puts at
+// most one workgroup on each of the chip's 256 CUs and the per-row wave cap
+// still reaches kTargetWaves (183-256 rows).  Measured: 244 rows whole take 0.45
+// us off the step; 272 rows whole (16 CUs with two rows, finishing last) cost
+// 2.8 us, so they stay split.
+constexpr int64_t kCUs = 256;
 static int groups_per_row(int64_t n_rows, int V, int dtype) {
     if (n_rows <= 0 || n_rows >= kSplitBelowRows) return 1;
+    if (n_rows <= kCUs && (kTargetWaves + n_rows - 1) / n_rows <= kMaxWavesPerRow) return 1;
     const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
     const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
     int64_t G = (kSplitTargetUnits + n_rows - 1) / n_rows;
