@@ -480,3 +480,117 @@ def test_update_last_writer_wins():
             np.testing.assert_array_equal(table[x], tk[last[x]])
         else:
             np.testing.assert_array_equal(table[x], before[x])
+
+
+# ----------------------------------------------------------------------------- grafted subtree
+
+def _placement(layout, keep, n_ret):
+    """Rows of the kept draft nodes and of the template nodes under each layout's
+    placement rule, derived here from the rule alone: compact puts the kept draft
+    nodes first (ascending), then the template nodes in order; in place, draft slot
+    i is row i+1 and the vacated slots, ascending, take the template nodes."""
+    keep = keep.astype(bool)
+    kept = np.nonzero(keep)[0]
+    if layout == "compact":
+        drow = {int(i): 1 + n for n, i in enumerate(kept)}
+        trow = [1 + len(kept) + t for t in range(n_ret)]
+    else:
+        drow = {int(i): int(i) + 1 for i in kept}
+        trow = (np.nonzero(~keep)[0] + 1).tolist()[:n_ret]
+    return drow, trow
+
+
+def _random_logps(rng, n):
+    """Draft log-probabilities: log-softmax over each node's 8 siblings of N(0, 1.5)
+    logits (the toy workload's recipe), so the stage varies between requests."""
+    par, lay, _ = TOPO
+    out = []
+    for _ in range(n):
+        z = rng.normal(0.0, 1.5, size=60)
+        lp = np.zeros(60)
+        for p in np.unique(par):
+            sib = np.nonzero(par == p)[0]
+            zs = z[sib]
+            lp[sib] = zs - (zs.max() + np.log(np.exp(zs - zs.max()).sum()))
+        out.append(lp)
+    return out
+
+
+@pytest.mark.parametrize("layout", ["compact", "in_place"])
+@pytest.mark.parametrize("tpl_kind", ["chain", "branching"])
+def test_grafted_subtree_follows_template(layout, tpl_kind):
+    """Gear 2 of the write-up expands the retrieval tree from the current token: each
+    node is the rank-r successor, in the continuation matrix, of its parent node's
+    token.  So every row holding template node t must sit at depth tpl_depth[t],
+    hang under the row holding tpl_parent[t] (the root at depth 1), and carry
+    M[token of that row][tpl_rank[t]].  Kept draft nodes keep their own shape:
+    depth = layer + 1 under the row of their draft parent."""
+    rng = np.random.default_rng(21 if tpl_kind == "chain" else 22)
+    V = 500
+    table = rng.integers(0, V, size=(V, 8)).astype(np.int32)
+    tpl = O.template(8, 8, 52) if tpl_kind == "chain" else O.template_branching(4, 6, (1, 1), 52)
+    logps = _stage_logps() + _random_logps(rng, 12)
+    par_b, lay_b, lp = _tree_batch(logps)
+    par, lay, _ = TOPO
+    B = len(logps)
+    d_tok = rng.integers(0, V, size=(B, 60)).astype(np.int32)
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    base = rng.integers(0, 1000, size=B).astype(np.int32)
+    pr = O.prune_tree(par_b, lay_b, lp)
+    assert set(pr["stage"].tolist()) == {0, 1, 2, 3}
+    ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, tpl)
+    fl = O.flatten(layout, 61, roots, base, d_tok, par_b, pr["keep"], pr["n_keep"], ret)
+    for b in range(B):
+        R = int(ret["n_ret"][b])
+        assert R == min(60 - int(pr["n_keep"][b]), len(tpl["parent"]))
+        drow, trow = _placement(layout, pr["keep"][b], R)
+        tk, pa, dp, src = fl["tok"][b], fl["parent"][b], fl["depth"][b], fl["row_src"][b]
+        assert (src == O.ROW_RETRIEVED).sum() == R
+        for t, f in enumerate(trow):
+            pt = int(tpl["parent"][t])
+            assert src[f] == O.ROW_RETRIEVED
+            assert dp[f] == tpl["depth"][t]
+            assert pa[f] == (0 if pt < 0 else trow[pt])
+            assert tk[f] == table[tk[pa[f]], tpl["rank"][t]]
+        for i, f in drow.items():
+            assert src[f] == O.ROW_DRAFT and tk[f] == d_tok[b, i]
+            assert dp[f] == lay[i] + 1
+            assert pa[f] == (0 if par[i] < 0 else drow[int(par[i])])
+
+
+@pytest.mark.parametrize("layout", ["compact", "in_place"])
+@pytest.mark.parametrize("V,W", [(4, 4), (8, 8)])
+def test_superset_through_oracle_pipeline(layout, V, W):
+    """Section 三 of the write-up: the hybrid tree contains the pruned draft tree, so
+    strict greedy verification accepts at least as much on it.  Through the oracle's
+    own prune -> retrieve -> flatten -> accept chain, on the same drafts and matrix,
+    the rank-chain template against the empty one (no retrieval), for every greedy
+    target g: V -> V at V = 4 (k = 4, width 4) and 600 seeded ones at V = 8."""
+    rng = np.random.default_rng(100 * V + (layout == "compact"))
+    k = W
+    table = rng.integers(0, V, size=(V, k)).astype(np.int32)
+    tpl = O.template(W, 8, 52)
+    empty = {key: np.zeros(0, np.int32) for key in ("parent", "rank", "depth")}
+    logps = _stage_logps() + _random_logps(rng, 4)
+    par_b, lay_b, lp = _tree_batch(logps)
+    B = len(logps)
+    d_tok = rng.integers(0, V, size=(B, 60)).astype(np.int32)
+    roots = rng.integers(0, V, size=B).astype(np.int32)
+    base = np.zeros(B, np.int32)
+    pr = O.prune_tree(par_b, lay_b, lp)
+    trees = {}
+    for name, tp in (("hybrid", tpl), ("pruned", empty)):
+        ret = O.retrieve_tree(table, roots, pr["n_keep"], 60, tp, Rmax_out=52)
+        trees[name] = O.flatten(layout, 61, roots, base, d_tok, par_b, pr["keep"], pr["n_keep"], ret)
+    ph, pp = trees["hybrid"], trees["pruned"]
+    assert (pp["row_src"] != O.ROW_RETRIEVED).all()
+    maps = (itertools.product(range(V), repeat=V) if V <= 4
+            else (tuple(rng.integers(0, V, size=V)) for _ in range(600)))
+    gains = 0
+    for gmap in maps:
+        gm = np.array(gmap + (0,), np.int32)   # index -1 (an empty row) reads the pad
+        lh = O.accept(ph["tok"], ph["parent"], gm[ph["tok"]], 60)["accept_len"]
+        lq = O.accept(pp["tok"], pp["parent"], gm[pp["tok"]], 60)["accept_len"]
+        assert (lh >= lq).all()
+        gains += int((lh > lq).sum())
+    assert gains > 0   # retrieval does add accepted tokens on some targets
