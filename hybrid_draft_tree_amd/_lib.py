@@ -22,6 +22,7 @@ GRAFT_MAX_ROWS = 64
 GRAFT_MAX_K = 8
 GRAFT_MAX_VOCAB = 1000000   # logits per row accepted by the top-k calls
 GRAFT_MAX_BATCH = 1 << 24   # requests per call
+GRAFT_MAX_COORD_GROUPS = 128  # coordinator workgroups of a verify launch at most
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 MODE_TREE = 0
@@ -35,7 +36,7 @@ EXPORTS = (
     "graft_prune_select", "graft_check_draft", "graft_check_tree", "graft_checkpoint_stats", "graft_calibrate_thresholds", "graft_template_master", "graft_template_branching", "graft_retrieve_expand",
     "graft_build_tree_mask", "graft_verify_accept", "graft_update_topk",
     "graft_build_hybrid_tree", "graft_build_after_retrieval", "graft_verify_update", "graft_coverage_gain",
-    "graft_workspace_bytes", "graft_status_string",
+    "graft_launch_plan", "graft_workspace_bytes", "graft_status_string",
 )
 
 
@@ -55,6 +56,11 @@ class PruneCfg(C.Structure):
 class Template(C.Structure):
     _fields_ = [("size", C.c_int32), ("parent", C.c_void_p), ("rank", C.c_void_p),
                 ("depth", C.c_void_p)]
+
+
+class Plan(C.Structure):
+    _fields_ = [("waves_per_group", C.c_int32), ("groups_per_row", C.c_int32),
+                ("blocks_per_batch", C.c_int32), ("coord_groups", C.c_int32), ("workgroups", C.c_int64)]
 
 
 _LIB = None
@@ -88,6 +94,7 @@ def load():
                                               P, P, P, I, P, P, P, P, P, P, P]
     L.graft_verify_update.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
     L.graft_coverage_gain.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
+    L.graft_launch_plan.argtypes = [I64, I, I, I, C.POINTER(Plan)]
     L.graft_workspace_bytes.argtypes = [I64, I, I, I]
     L.graft_workspace_bytes.restype = S
     L.graft_status_string.argtypes = [I]
@@ -223,6 +230,13 @@ def graft_verify_update(B, T1, V, k, dtype, logits, tok, parent, depth, table, t
 def graft_coverage_gain(B, T1, V, dtype, logits, tok, parent, row_src, row_stats, gain, stream):
     return _chk("graft_coverage_gain", load().graft_coverage_gain(
         B, T1, V, dtype, logits, tok, parent, row_src, row_stats, gain, stream))
+
+
+def graft_launch_plan(n_rows, V, dtype, T1):
+    """The top-k launch's plan as a dict (host only; nothing is enqueued)."""
+    p = Plan()
+    _chk("graft_launch_plan", load().graft_launch_plan(n_rows, V, dtype, T1, C.byref(p)))
+    return {f: int(getattr(p, f)) for f, _ in Plan._fields_}
 
 
 def graft_workspace_bytes(n_rows, V, k, dtype):

@@ -37,9 +37,9 @@ WsLayout ws_layout(int64_t n_rows, int V, int k, int dtype) {
     L.off_topk = align256(L.plan.ws_bytes);
     L.off_prob = L.off_topk + align256((size_t)n_rows * k * sizeof(int32_t));
     L.total = L.off_prob + align256((size_t)n_rows * k * sizeof(float));
-    // the launch's thread count is 32-bit: (row slices + coordinators, which never
-    // outnumber the rows) x wavefronts per slice x 64 lanes
-    const int64_t units = n_rows * L.plan.groups + n_rows;
+    // the launch's thread count is 32-bit: (row slices + coordinators, at most
+    // GRAFT_MAX_COORD_GROUPS and never more than the rows) x wavefronts per slice x 64 lanes
+    const int64_t units = n_rows * L.plan.groups + std::min<int64_t>(n_rows, GRAFT_MAX_COORD_GROUPS);
     L.fits = units * L.plan.splits * 64 <= (int64_t)UINT32_MAX;
     return L;
 }
@@ -58,6 +58,21 @@ const char *graft_status_string(int status) {
         case GRAFT_EDEVICE: return "HIP launch error";
         default: return "unknown status";
     }
+}
+
+int graft_launch_plan(int64_t n_rows, int V, int dtype, int T1, graft_plan *out) {
+    if (!out || n_rows < 0 || V <= 0 || V > GRAFT_MAX_VOCAB || !dtype_ok(dtype) || T1 < 0 || T1 > GRAFT_MAX_ROWS)
+        return GRAFT_EINVAL;
+    if (T1 > 0 && n_rows % T1 != 0) return GRAFT_EINVAL;
+    const WsLayout L = ws_layout(n_rows, V, 1, dtype);
+    if (!L.fits) return GRAFT_EINVAL;
+    const int B = T1 > 0 ? (int)std::min<int64_t>(n_rows / T1, INT32_MAX) : 0;
+    out->waves_per_group = L.plan.splits;
+    out->groups_per_row = L.plan.groups;
+    out->blocks_per_batch = L.plan.loads;
+    out->coord_groups = n_rows == 0 ? 0 : (T1 > 0 ? coord_groups(L.plan, B) : 1);
+    out->workgroups = n_rows == 0 ? 0 : n_rows * L.plan.groups + out->coord_groups;
+    return GRAFT_OK;
 }
 
 size_t graft_workspace_bytes(int64_t n_rows, int V, int k, int dtype) {

@@ -101,6 +101,7 @@ struct TopkPlan {
 };
 
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype);
+int coord_groups(const TopkPlan &plan, int B);  // coordinator workgroups of a verify launch of B requests
 
 struct TopkArgs {
     const void *logits;

@@ -384,12 +384,14 @@ __device__ __forceinline__ void register_rows(const TopkArgs &a, const VerifyArg
 }
 
 // Coordinators (the first v.ncoord workgroups of a verify launch, one wavefront
-// per request; nothing waits on them, so they cannot hold up the rows).  The
-// first one registers the rows' tokens for the fused update.  Row P publishes
-// (greedy token + 1) into done[P], zero meaning "not yet"; wavefront w watches
-// request w (one load per unfinished row per poll, no atomics) and runs its
-// acceptance walk as soon as all its rows are in, then clears the words.  A
-// watch that exceeds kSpinTicks reports accept_len = -1 and stops.
+// per request up to a fixed number of workgroups; nothing waits on them, so
+// they cannot hold up the rows).  The first one registers the rows' tokens for
+// the fused update.  Row P publishes (greedy token + 1) into done[P], zero
+// meaning "not yet"; wavefront w watches requests w, w + N, w + 2N, ... (N =
+// coordinator wavefronts) in turn, in the order their rows are dispatched (one
+// load per unfinished row per poll, no atomics), runs each acceptance walk as
+// soon as all the request's rows are in, then clears the words.  A watch that
+// exceeds kSpinTicks reports accept_len = -1 for that request and moves on.
 __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &v, int cw) {
     if (cw == 0 && v.table) register_rows(a, v);
     const int lane = lane_id();
@@ -995,6 +997,17 @@ static int groups_per_row(int64_t n_rows, int V, int dtype) {
     return G < 1 ? 1 : (int)G;
 }
 
+// Coordinator workgroups of a verify launch: one wavefront per request, at
+// most GRAFT_MAX_COORD_GROUPS workgroups (each wavefront then watches every
+// (groups x S)-th request in turn).  The coordinators are dispatched ahead of
+// the rows and wait for them, so they must never fill the chip: 128
+// workgroups of at most 16 wavefronts and 64 KB of LDS take at most a quarter
+// of its wavefront slots and half the LDS of 128 CUs, whatever the batch.
+int coord_groups(const TopkPlan &p, int B) {
+    const int64_t want = ((int64_t)B + p.splits - 1) / p.splits;
+    return (int)(want < GRAFT_MAX_COORD_GROUPS ? want : GRAFT_MAX_COORD_GROUPS);
+}
+
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     TopkPlan p;
     p.n_rows = n_rows;
@@ -1046,7 +1059,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
             v.ncoord = 1;  // the registration
         } else {
             v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
-            v.ncoord = (v.B + a.S - 1) / a.S;  // one wavefront per request
+            v.ncoord = coord_groups(p, v.B);
         }
     }
     if (dtype == GRAFT_DTYPE_BF16)

@@ -352,9 +352,26 @@ class GraftPipeline:
                               self.parent.data_ptr(), self.row_src.data_ptr(), self.row_stats.data_ptr(),
                               self.gain.data_ptr(), s)
 
-    def verify_update(self, logits):
+    def raise_if_gave_up(self):
+        """accept_len == -1 marks a request whose coordinator gave up waiting for
+        its rows (about a second; never in normal operation).  The step's outputs
+        are then invalid and rows that finished late may have left words in the
+        workspace, so once the launch has drained the workspace is zero-filled
+        again and an error is raised.  Synchronises."""
+        al = self.accept_len.cpu().numpy()
+        bad = np.nonzero(al < 0)[0]
+        if bad.size:
+            torch.cuda.synchronize(self.device)
+            self.ws.zero_()
+            torch.cuda.synchronize(self.device)
+            raise RuntimeError("verification gave up waiting for the rows of request(s) %s; "
+                               "the workspace was reset" % bad.tolist())
+
+    def verify_update(self, logits, check=True):
         self._check_logits(logits, self.B * self.T1)
         self.verify_update_device(logits)
+        if check:
+            self.raise_if_gave_up()
         out = {"accept_len": self.accept_len, "accept_idx": self.accept_idx, "bonus": self.roots.clone(),
                "topk": self.topk, "base_pos": self.base_pos}
         if self.want_prob:

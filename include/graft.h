@@ -358,13 +358,35 @@ int graft_coverage_gain(int B, int T1, int V, int dtype, const void *logits, con
                         const int32_t *parent, const uint8_t *row_src, const float *row_stats,
                         float *gain, hipStream_t stream);
 
+/* Launch plan of the top-k launch of graft_verify_accept / graft_verify_update
+ * (T1 = rows per request, n_rows = B * T1) or of graft_update_topk with logits
+ * (T1 = 0: no requests, one registration workgroup); host only, nothing is
+ * enqueued.  A verify launch puts its coordinator workgroups (one wavefront
+ * per request, at most GRAFT_MAX_COORD_GROUPS workgroups; each wavefront then
+ * watches several requests in turn) ahead of the rows.  They wait for rows
+ * that are dispatched after them, so their number is bounded whatever the
+ * batch: GRAFT_MAX_COORD_GROUPS workgroups of at most 16 wavefronts take a
+ * quarter of the chip's wavefront slots at most.  Returns GRAFT_OK, or
+ * GRAFT_EINVAL for sizes the calls reject (out must be non-NULL; T1 in
+ * [0, 64] dividing n_rows). */
+#define GRAFT_MAX_COORD_GROUPS 128
+typedef struct graft_plan {
+    int32_t waves_per_group;  /* wavefronts per workgroup */
+    int32_t groups_per_row;   /* workgroups per row (rows are cut into slices when few) */
+    int32_t blocks_per_batch; /* 1 KB blocks each wavefront loads per batch */
+    int32_t coord_groups;     /* coordinator (or registration) workgroups ahead of the rows */
+    int64_t workgroups;       /* all workgroups of the launch */
+} graft_plan;
+int graft_launch_plan(int64_t n_rows, int V, int dtype, int T1, graft_plan *out);
+
 /* Workspace bytes needed by graft_verify_accept / graft_verify_update /
  * graft_update_topk for n_rows rows of V logits (0 on invalid sizes).  Zero-fill it once after
  * allocating it; calls leave it zero-filled.  Also 0 when n_rows rows do not fit one launch:
- * n_rows must be below 2^31 - 1, and (2 n_rows) x wavefronts per row x 64 threads below 2^32
- * (one wavefront per row from ~3000 rows on at V <= 127 x 512 bf16, so up to ~33 million rows
- * there; rows of larger V take more wavefronts, up to 16 at V = 10^6).  Those three calls
- * return GRAFT_EINVAL for such sizes: split the rows over several calls. */
+ * n_rows must be below 2^31 - 1, and (n_rows x workgroups per row + coordinator workgroups) x
+ * wavefronts per workgroup x 64 threads below 2^32 (one wavefront per row from ~3000 rows on
+ * at V <= 127 x 512 bf16, so up to ~67 million rows there; rows of larger V take more
+ * wavefronts, up to 16 at V = 10^6).  Those three calls return GRAFT_EINVAL for such sizes:
+ * split the rows over several calls. */
 size_t graft_workspace_bytes(int64_t n_rows, int V, int k, int dtype);
 
 /* Static description of a status code. */

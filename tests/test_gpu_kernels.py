@@ -811,6 +811,65 @@ def test_verify_update_matches_oracle_with_collisions():
         lg = _t(rows.view(np.int16)).view(torch.bfloat16)
 
 
+def _chain_batch(rng, B, T1, V):
+    """Chain trees whose first p_b candidates carry the target's bumped greedy
+    token: logits N(0, 1) with +6 at a random column per row."""
+    z = rng.standard_normal((B, T1, V)).astype(np.float32)
+    col = rng.integers(0, V, size=(B, T1))
+    np.put_along_axis(z, col[:, :, None], 6.0, axis=2)
+    rows = _bf16(z)
+    p = rng.integers(0, T1, size=B)
+    tok = rng.integers(0, V, size=(B, T1)).astype(np.int32)
+    for b in range(B):
+        tok[b, 1:p[b] + 1] = col[b, :p[b]]
+    par = np.tile(np.arange(-1, T1 - 1, dtype=np.int32), (B, 1))
+    dep = np.tile(np.arange(T1, dtype=np.int32), (B, 1))
+    return rows, tok, par, dep
+
+
+def test_verify_update_batch_above_resident_coordinators():
+    """8192 requests of 17 rows at V = 1024: one coordinator wavefront per request
+    would need 8192 workgroups ahead of the rows, more than the chip holds at once;
+    the launch caps them (each wavefront watches many requests).  Every output and
+    the matrix match the oracle on two calls in a row, the second with fewer
+    requests on the same workspace."""
+    rng = np.random.default_rng(8192)
+    V, T1, k = 1024, 17, 8
+    plan = L.graft_launch_plan(8192 * T1, V, L.DTYPE_BF16, T1)
+    assert plan["coord_groups"] == L.GRAFT_MAX_COORD_GROUPS and plan["waves_per_group"] == 1
+    i32 = dict(dtype=torch.int32, device=DEV)
+    table0 = rng.integers(0, V, size=(V, k)).astype(np.int32)
+    tb = _t(table0, torch.int32)
+    want_tab = table0.copy()
+    wsb = L.graft_workspace_bytes(8192 * T1, V, k, L.DTYPE_BF16)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    for B in (8192, 3000):
+        rows, tok, par, dep = _chain_batch(rng, B, T1, V)
+        base = rng.integers(0, 10000, size=B).astype(np.int32)
+        lg = _t(rows.view(np.int16)).view(torch.bfloat16)
+        tk = torch.zeros(B, T1, k, **i32)
+        al, bo = torch.zeros(B, **i32), torch.zeros(B, **i32)
+        bp = _t(base, torch.int32)
+        ai = torch.zeros(B, T1 - 1, **i32)
+        t_, p_, d_ = (_t(x, torch.int32) for x in (tok, par, dep))
+        print("verify_update B=%d T1=%d V=%d" % (B, T1, V), flush=True)
+        L.graft_verify_update(B, T1, V, k, L.DTYPE_BF16, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
+                              tb.data_ptr(), None, tk.data_ptr(), None, None, al.data_ptr(), ai.data_ptr(), T1 - 1,
+                              bo.data_ptr(), bp.data_ptr(), ws.data_ptr(), wsb, _s())
+        torch.cuda.synchronize()
+        want_tk = O.topk(rows.reshape(-1, V), k, "bf16").reshape(B, T1, k)
+        acc = O.accept(tok, par, want_tk[:, :, 0], T1 - 1)
+        O.update(want_tab, tok.reshape(-1), want_tk.reshape(-1, k))
+        np.testing.assert_array_equal(tk.cpu().numpy(), want_tk)
+        np.testing.assert_array_equal(al.cpu().numpy(), acc["accept_len"])
+        np.testing.assert_array_equal(ai.cpu().numpy(), acc["accept_idx"])
+        np.testing.assert_array_equal(bo.cpu().numpy(), acc["bonus"])
+        np.testing.assert_array_equal(bp.cpu().numpy(), base + acc["accept_len"] + 1)
+        np.testing.assert_array_equal(tb.cpu().numpy(), want_tab)
+        assert acc["accept_len"].max() >= T1 - 2
+    assert not ws.any().item()      # left zero-filled
+
+
 # ----------------------------------------------------------------------------- coverage gain
 
 def _coverage_case(rng, B, T1, V, layout, dtype):

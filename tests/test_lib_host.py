@@ -55,23 +55,23 @@ def test_launch_size_limits():
     """Row counts that do not fit one top-k launch (32-bit thread count, 32-bit
     row positions) get no workspace size and are rejected before any launch."""
     bf = L.DTYPE_BF16
-    # small vocabulary: one wavefront per row, rows + coordinators <= 2 n_rows
-    assert L.graft_workspace_bytes(30_000_000, 100, 8, bf) > 0
-    assert L.graft_workspace_bytes(40_000_000, 100, 8, bf) == 0
+    # small vocabulary: one wavefront per row, (rows + 128 coordinators) x 64 < 2^32
+    assert L.graft_workspace_bytes(67_108_735, 100, 8, bf) > 0
+    assert L.graft_workspace_bytes(67_108_736, 100, 8, bf) == 0
     assert L.graft_workspace_bytes((1 << 31) - 1, 100, 8, bf) == 0
     # V = 10^6 bf16 needs 16 wavefronts per row (127 blocks of 512 elements per wavefront at most)
-    assert L.graft_workspace_bytes(2_000_000, 10 ** 6, 8, bf) > 0
-    assert L.graft_workspace_bytes(3_000_000, 10 ** 6, 8, bf) == 0
+    assert L.graft_workspace_bytes(4_194_175, 10 ** 6, 8, bf) > 0
+    assert L.graft_workspace_bytes(4_194_176, 10 ** 6, 8, bf) == 0
     lib = L.load()
     P = 0x1000  # never dereferenced
     huge = 1 << 62
-    assert lib.graft_update_topk(40_000_000, 100, 8, bf, P, None, None, P, P, None, None, P, huge, None) == \
+    assert lib.graft_update_topk(67_108_736, 100, 8, bf, P, None, None, P, P, None, None, P, huge, None) == \
         L.GRAFT_EINVAL
     assert lib.graft_update_topk(1 << 40, 100, 8, bf, P, None, None, P, P, None, None, P, huge, None) == \
         L.GRAFT_EINVAL
-    assert lib.graft_verify_accept(700_000, 61, 100, 8, bf, *([P] * 9), 60, P, None, P, huge, None) == \
+    assert lib.graft_verify_accept(1_100_200, 61, 100, 8, bf, *([P] * 9), 60, P, None, P, huge, None) == \
         L.GRAFT_EINVAL
-    assert lib.graft_verify_update(700_000, 61, 100, 8, bf, *([P] * 11), 60, P, None, P, huge, None) == \
+    assert lib.graft_verify_update(1_100_200, 61, 100, 8, bf, *([P] * 11), 60, P, None, P, huge, None) == \
         L.GRAFT_EINVAL
     # per-request calls: at most 2^24 requests
     cfg = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 40), 0.5)
@@ -224,3 +224,41 @@ def test_empty_batches_enqueue_nothing():
     assert lib.graft_update_topk(0, 100, 8, 1, *([None] * 7), None, 0, None) == L.GRAFT_OK
     assert lib.graft_coverage_gain(0, 61, 100, 1, *([None] * 6), None) == L.GRAFT_OK
     assert lib.graft_checkpoint_stats(0, 60, None, None, None, cb, None, None) == L.GRAFT_OK
+
+
+def test_coordinators_are_bounded_whatever_the_batch():
+    """A verify launch's coordinator workgroups wait for rows dispatched after them,
+    so their number must stay far below what the chip holds at once (256 CUs,
+    32 wavefronts and 160 KB of LDS each): at most GRAFT_MAX_COORD_GROUPS
+    workgroups, one wavefront per request below that, for every batch the calls
+    accept."""
+    bf, f32 = L.DTYPE_BF16, L.DTYPE_F32
+    seen_cap = False
+    for T1 in (1, 2, 17, 61, 64):
+        for V in (8, 100, 1024, 16000, 32000, 151936, L.GRAFT_MAX_VOCAB):
+            for B in (1, 3, 4, 16, 33, 64, 127, 384, 1000, 8192, 20000, 100_000, 1_000_000, L.GRAFT_MAX_BATCH):
+                for dt in (bf, f32):
+                    n = B * T1
+                    if L.graft_workspace_bytes(n, V, min(8, V), dt) == 0:
+                        continue
+                    p = L.graft_launch_plan(n, V, dt, T1)
+                    S = p["waves_per_group"]
+                    assert 1 <= S <= 16
+                    assert p["coord_groups"] == min(-(-B // S), L.GRAFT_MAX_COORD_GROUPS)
+                    # a quarter of the chip's 8192 wavefront slots at most
+                    assert p["coord_groups"] * S <= 2048
+                    assert p["workgroups"] == n * p["groups_per_row"] + p["coord_groups"]
+                    assert p["workgroups"] * S * 64 < 2 ** 32
+                    seen_cap |= p["coord_groups"] == L.GRAFT_MAX_COORD_GROUPS
+    assert seen_cap
+    # the case found by reading the old code: 8192 one-wavefront coordinators
+    p = L.graft_launch_plan(8192 * 17, 16000, bf, 17)
+    assert p["waves_per_group"] == 1 and p["coord_groups"] == L.GRAFT_MAX_COORD_GROUPS
+    # the prompt ingest has no requests: one registration workgroup
+    assert L.graft_launch_plan(2048, 151936, bf, 0)["coord_groups"] == 1
+    assert L.graft_launch_plan(0, 151936, bf, 0)["workgroups"] == 0
+    # the metric shape keeps one coordinator wavefront per request
+    p = L.graft_launch_plan(16 * 61, 151936, bf, 61)
+    assert (p["waves_per_group"], p["groups_per_row"], p["blocks_per_batch"], p["coord_groups"]) == (3, 1, 4, 6)
+    with pytest.raises(L.GraftError):
+        L.graft_launch_plan(100, 1000, bf, 61)   # T1 does not divide the rows
