@@ -13,15 +13,19 @@ The pool is filled from a real seeded trajectory (warm-up first, table warmed
 up); during timing the matrix and roots keep evolving, so accepted lengths
 differ from the pool's own trajectory but every byte is still read.
 
-Timed region: `--steps` steps as HIP-graph replays (one graph = one pass over
-the pool), bracketed by synchronisation and HIP events on the replay stream.
+Timed region: exactly `--warmup` untimed steps, then `--repeats` windows of
+exactly `--steps` steps each, as HIP-graph replays (a whole pass over the pool
+per replay where the rotation allows, single-step graphs otherwise), each window
+bracketed by HIP events on the replay stream; the first event is recorded
+behind the queued warm-up, the host synchronises before the warm-up and after
+the last window.  The value is the median window.
 The dominant kernel (graft_verify_update's single launch: row-wise top-k,
 acceptance walk and matrix update) is then timed on its own with HIP events on
 the stream it is launched on: one pair around back-to-back launches (the
 roofline figure) and one pair around each launch (reported beside it).  The CPU
 oracle is timed on host copies of the same inputs.
 
-    python bench.py [--steps K] [--warmup W] [--pool P] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--repeats R] [--pool P] [--no-cpu-baseline] [--no-shapes]
 
 A second mode, ``--template-sweep``, measures the retrieval template instead of
 speed: mean accepted length per step on workloads 2 and 4 for rank-chain and
@@ -60,6 +64,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--repeats", type=int, default=5, help="timed windows of --steps steps (median reported)")
+    ap.add_argument("--shape-steps", type=int, default=400,
+                    help="steps per window of the full-step diagnostic at the other workloads")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the full-step diagnostic at other workloads")
     ap.add_argument("--pool", type=int, default=4)
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -304,95 +312,233 @@ def template_sweep(args):
                     print(json.dumps(rec), flush=True)
 
 
+def setup_pool(cfg, P, dev, torch):
+    """A fresh pipeline through the workload's start (prompt ingest for workload
+    4) and warm-up, then P steps of its seeded trajectory; each step's draft is
+    kept on the device and its logits in a pool buffer, so a replayed step does
+    the whole build + verify/update work on real inputs.  Returns the pipeline,
+    the pool (drafts, logits) and the accepted tokens of each pool step."""
+    from hybrid_draft_tree_amd.driver import GraftPipeline
+    from synth import generators as G
+    from synth import runner as R
+
+    pipe = GraftPipeline.from_config(cfg, device=dev)
+    ad = _Adapter(pipe, torch)
+    wl = R.Workload(cfg)
+    R.start(ad, wl)
+    for s_ in range(cfg.warmup_steps if cfg.cfg_id != 4 else 0):
+        R.step(ad, wl, s_, G.WARMUP_STREAM_OFFSET)
+    n_rows = cfg.B * cfg.rows_per_request
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    pool_logits, pool_drafts, acc = [], [], []
+    for p in range(P):
+        roots = ad.get_roots()
+        draft = wl.draft(p, roots)
+        flat = ad.build(draft)
+        desc = wl.logit_desc(p, flat)
+        buf = torch.empty(n_rows, cfg.V, dtype=tdt, device=dev)
+        if ad.rows is None:
+            ad.rows = ad.DeviceRows(wl.pool, dev)
+        ad.rows.materialize(desc, out=buf)
+        res = ad.verify_update(buf)
+        wl.commit(roots, flat, res)
+        acc.append(int(res["accept_len"].sum()))
+        bufs = pipe.draft_buffers()
+        if cfg.mode == "tree":
+            bufs["parent"].copy_(torch.as_tensor(draft["parent"]))
+            bufs["layer"].copy_(torch.as_tensor(draft["layer"]))
+            bufs["score"].copy_(torch.as_tensor(draft["logp"]))
+        else:
+            bufs["score"].copy_(torch.as_tensor(draft["conf"]))
+        bufs["tok"].copy_(torch.as_tensor(draft["tok"]))
+        pool_logits.append(buf)
+        pool_drafts.append(bufs)
+    torch.cuda.synchronize()
+    return pipe, pool_drafts, pool_logits, acc
+
+
+class StepReplayer:
+    """Enqueues steps i = s .. s+n-1 of a rotating pool (step i uses pool entry
+    i mod P): a whole pass over the pool as one HIP-graph replay when the
+    rotation allows, every other step as its own one-step graph, so any step
+    count is run exactly and the rotation never repeats a buffer back to back."""
+
+    def __init__(self, pipe, pool_drafts, pool_logits, torch, use_graph=True):
+        self.P = len(pool_logits)
+        self.pipe, self.drafts, self.logits = pipe, pool_drafts, pool_logits
+        self.use_graph = use_graph
+        if use_graph:
+            self._pass()            # warm the launch path before capture
+            torch.cuda.synchronize()
+            self.g_pool = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.g_pool):
+                self._pass()
+            self.g_one = []
+            for p in range(self.P):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    self._step(p)
+                self.g_one.append(g)
+            torch.cuda.synchronize()
+
+    def _step(self, p):
+        self.pipe.build_device(self.drafts[p])
+        self.pipe.verify_update_device(self.logits[p])
+
+    def _pass(self):
+        for p in range(self.P):
+            self._step(p)
+
+    def run(self, s, n):
+        while n > 0:
+            p = s % self.P
+            if p == 0 and n >= self.P:
+                if self.use_graph:
+                    self.g_pool.replay()
+                else:
+                    self._pass()
+                s, n = s + self.P, n - self.P
+            else:
+                if self.use_graph:
+                    self.g_one[p].replay()
+                else:
+                    self._step(p)
+                s, n = s + 1, n - 1
+        return s
+
+
+def timed_steps(rep, K, W, repeats, torch):
+    """Synchronise, enqueue exactly W untimed warm-up steps, then `repeats`
+    windows of exactly K steps, each bracketed by HIP events on the replay
+    stream; the first event is recorded behind the queued warm-up, so no window
+    starts on an idle device, and the host synchronises once all are done.
+    Returns the per-window milliseconds and the wall-clock seconds."""
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    s = rep.run(0, W)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(repeats + 1)]
+    evs[0].record(stream)
+    for r in range(repeats):
+        s = rep.run(s, K)
+        evs[r + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return [evs[r].elapsed_time(evs[r + 1]) for r in range(repeats)], wall
+
+
+def _median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def time_workload(cid, steps, warmup, P, dev, torch, repeats=3):
+    """Full step (build + verify/update) of workload `cid` at its own shape:
+    a pool of P steps of its trajectory, replayed exactly `steps` steps per
+    window, median over `repeats` windows."""
+    from synth import WORKLOADS
+
+    cfg = WORKLOADS[cid]
+    t0 = time.time()
+    pipe, drafts, logits, _ = setup_pool(cfg, P, dev, torch)
+    rep = StepReplayer(pipe, drafts, logits, torch)
+    ms, _ = timed_steps(rep, steps, warmup, repeats, torch)
+    us = _median(ms) * 1e3 / steps
+    n_rows = cfg.B * cfg.rows_per_request
+    lb = n_rows * cfg.V * cfg.elem_bytes
+    step_bytes = lb + n_rows * cfg.k * 4
+    rec = {"workload": cfg.name, "config": cid, "batch": cfg.B, "vocab": cfg.V,
+           "rows_per_request": cfg.rows_per_request, "verified_rows": n_rows, "dtype": cfg.dtype,
+           "layout": cfg.layout, "steps": steps, "repeats": repeats, "us_per_step": round(us, 3),
+           "us_per_step_min": round(min(ms) * 1e3 / steps, 3), "us_per_step_max": round(max(ms) * 1e3 / steps, 3),
+           "steps_per_s": round(1e6 / us, 1), "logits_bytes_per_step": lb,
+           "step_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
+           "step_frac_of_peak": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+           "setup_s": round(time.time() - t0, 1)}
+    del rep, pipe, drafts, logits
+    torch.cuda.empty_cache()
+    return rec
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, pipe, pool_drafts, pool_logits, step_bytes, seconds, torch):
+    """The CPU oracle as it stands, on host copies of the pool's inputs (drafts,
+    logits, the matrix and roots as the GPU left them): full steps (prune,
+    retrieve, flatten, top-k, accept, update) for about seconds/2 on one thread,
+    then on all the threads OpenMP is given.  The headline value is the all-thread
+    rate; cores = the threads it used."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from oracle.driver import OracleGraft
+
+    P = len(pool_logits)
+    host_logits = [b.view(torch.int16).cpu().numpy().view(np.uint16) for b in pool_logits]
+    host_drafts = [{"parent": d["parent"].cpu().numpy(), "layer": d["layer"].cpu().numpy(),
+                    "logp": d["score"].cpu().numpy(), "tok": d["tok"].cpu().numpy()} for d in pool_drafts]
+    table = pipe.table.cpu().numpy()
+    roots, base = pipe.roots.cpu().numpy(), pipe.base_pos.cpu().numpy()
+    all_threads = O.num_threads()
+    runs = {}
+    for threads in (1, all_threads):
+        O.set_threads(threads)
+        og = OracleGraft(cfg)
+        og.table = table.copy()
+        og.set_roots(roots, base)
+        n = 0
+        c0 = time.perf_counter()
+        while True:
+            p = n % P
+            og.build(host_drafts[p])
+            og.verify_update(host_logits[p])
+            n += 1
+            el = time.perf_counter() - c0
+            if el >= seconds / 2 or n >= 1000:
+                break
+        runs[threads] = (n, el)
+        log("cpu oracle: %d steps in %.1f s with %d thread(s)" % (n, el, threads))
+    O.set_threads(all_threads)
+    n, el = runs[all_threads]
+    n1, el1 = runs[1]
+    return {"value": round(n / el, 3), "unit": "steps/s", "cores": all_threads, "kind": "oracle",
+            "sample": "%d full oracle steps (B=16, V=151936, 61 rows/request) on host copies of the same pool "
+                      "inputs in %.1f s on %d threads; %d steps in %.1f s on 1 thread" % (n, el, all_threads, n1, el1),
+            "ms_per_step": round(el / n * 1e3, 2), "GBps": round(step_bytes * n / el / 1e9, 2),
+            "one_thread": {"steps_per_s": round(n1 / el1, 3), "ms_per_step": round(el1 / n1 * 1e3, 2),
+                           "GBps": round(step_bytes * n1 / el1 / 1e9, 3)},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "host_cpus_usable": len(os.sched_getaffinity(0))}
+
+
 def all_configs(args):
     """The full Graft step on each of the five workloads at its own shape: one
-    build launch + one verify/update launch per step, replayed from a HIP graph
+    build launch + one verify/update launch per step, replayed from HIP graphs
     over a pool of `--pool` steps of a real seeded trajectory (after the
     workload's warm-up; workload 4 ingests its prompt first).  One JSON line per
     workload: time per step and the step's logits bytes against 8 TB/s."""
-    import numpy as np
     import torch
-
-    from hybrid_draft_tree_amd.driver import GraftPipeline
-    from synth import WORKLOADS
-    from synth import generators as G
-    from synth import runner as R
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     P = max(1, args.pool)
     for cid in [int(x) for x in args.config_list.split(",") if x.strip()]:
-        cfg = WORKLOADS[cid]
-        t0 = time.time()
-        pipe = GraftPipeline.from_config(cfg, device=dev)
-        ad = _Adapter(pipe, torch)
-        wl = R.Workload(cfg)
-        R.start(ad, wl)
-        for s_ in range(cfg.warmup_steps):
-            R.step(ad, wl, s_, G.WARMUP_STREAM_OFFSET)
-        T1 = cfg.rows_per_request
-        n_rows = cfg.B * T1
-        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-        pool_logits, pool_drafts = [], []
-        for p in range(P):
-            roots = ad.get_roots()
-            draft = wl.draft(p, roots)
-            flat = ad.build(draft)
-            desc = wl.logit_desc(p, flat)
-            buf = torch.empty(n_rows, cfg.V, dtype=tdt, device=dev)
-            if ad.rows is None:
-                ad.rows = ad.DeviceRows(wl.pool, dev)
-            ad.rows.materialize(desc, out=buf)
-            res = ad.verify_update(buf)
-            wl.commit(roots, flat, res)
-            bufs = pipe.draft_buffers()
-            if cfg.mode == "tree":
-                bufs["parent"].copy_(torch.as_tensor(draft["parent"]))
-                bufs["layer"].copy_(torch.as_tensor(draft["layer"]))
-                bufs["score"].copy_(torch.as_tensor(draft["logp"]))
-            else:
-                bufs["score"].copy_(torch.as_tensor(draft["conf"]))
-            bufs["tok"].copy_(torch.as_tensor(draft["tok"]))
-            pool_logits.append(buf)
-            pool_drafts.append(bufs)
-        torch.cuda.synchronize()
-
-        def one_pass():
-            for p in range(P):
-                pipe.build_device(pool_drafts[p])
-                pipe.verify_update_device(pool_logits[p])
-
-        one_pass()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            one_pass()
-        n_rep = max(1, math.ceil(args.steps / P))
-        for _ in range(max(1, math.ceil(args.warmup / P))):
-            g.replay()
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n_rep):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (n_rep * P)
-        lb = n_rows * cfg.V * (2 if cfg.dtype == "bf16" else 4)
-        step_bytes = lb + n_rows * cfg.k * 4
+        rec = time_workload(cid, args.steps, args.warmup, P, dev, torch, repeats=args.repeats)
         log("workload %d (%s): %.2f us/step, %.0f GB/s (setup %.1fs)"
-            % (cid, cfg.name, us, step_bytes / (us * 1e-6) / 1e9, time.time() - t0))
-        print(json.dumps({"mode": "all_configs", "workload": cfg.name, "config": cid, "batch": cfg.B,
-                          "vocab": cfg.V, "rows_per_request": T1, "verified_rows": n_rows, "dtype": cfg.dtype,
-                          "layout": cfg.layout, "steps": n_rep * P, "us_per_step": round(us, 3),
-                          "steps_per_s": round(1e6 / us, 1), "logits_bytes_per_step": lb,
-                          "step_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
-                          "step_frac_of_peak": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                          "hip_graph": True, "data": "synthetic"}), flush=True)
-        del g, pool_logits, pool_drafts, pipe, ad
-        torch.cuda.empty_cache()
+            % (cid, rec["workload"], rec["us_per_step"], rec["step_GBps"], rec["setup_s"]))
+        rec.update({"mode": "all_configs", "hip_graph": True, "data": "synthetic"})
+        print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -409,7 +555,6 @@ def main():
         print("bench.py runs on one GPU only: it measures the single-GPU Graft step "
               "(no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     from hybrid_draft_tree_amd import _lib as L
@@ -428,72 +573,23 @@ def main():
     bytes_logits = n_rows * V * 2
 
     t0 = time.time()
-    pipe = GraftPipeline.from_config(cfg, device=dev)
-    ad = _Adapter(pipe, torch)
-    wl = R.Workload(cfg)
-    R.start(ad, wl)
-    for s in range(cfg.warmup_steps):
-        R.step(ad, wl, s, G.WARMUP_STREAM_OFFSET)
-    # pool: P steps of a real trajectory; keep each step's draft (on device) and logits
-    pool_logits, pool_drafts, acc_pool = [], [], []
-    for p in range(P):
-        roots = ad.get_roots()
-        draft = wl.draft(p, roots)
-        flat = ad.build(draft)
-        desc = wl.logit_desc(p, flat)
-        buf = torch.empty(n_rows, V, dtype=torch.bfloat16, device=dev)
-        if ad.rows is None:
-            ad.rows = ad.DeviceRows(wl.pool, dev)
-        ad.rows.materialize(desc, out=buf)
-        res = ad.verify_update(buf)
-        wl.commit(roots, flat, res)
-        acc_pool.append(int(res["accept_len"].sum()))
-        bufs = pipe.draft_buffers()
-        bufs["parent"].copy_(torch.as_tensor(draft["parent"]))
-        bufs["layer"].copy_(torch.as_tensor(draft["layer"]))
-        bufs["score"].copy_(torch.as_tensor(draft["logp"]))
-        bufs["tok"].copy_(torch.as_tensor(draft["tok"]))
-        pool_logits.append(buf)
-        pool_drafts.append(bufs)
-    torch.cuda.synchronize()
+    pipe, pool_drafts, pool_logits, acc_pool = setup_pool(cfg, P, dev, torch)
     log("setup %.1fs: pool of %d steps (%.1f MB each), accepted per step in pool: %s"
         % (time.time() - t0, P, bytes_logits / 1e6, acc_pool))
 
-    def one_pass():
-        for p in range(P):
-            pipe.build_device(pool_drafts[p])
-            pipe.verify_update_device(pool_logits[p])
-
     # ---------------- timed region: whole steps ----------------
-    n_rep = max(1, math.ceil(args.steps / P))
-    K = n_rep * P
-    W = max(0, math.ceil(args.warmup / P)) * P
-    if args.no_graph:
-        run = one_pass
-    else:
-        one_pass()  # warm the launch path before capture
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            one_pass()
-        run = g.replay
-    for _ in range(W // P):
-        run()
-    torch.cuda.synchronize()
+    # exactly --warmup untimed steps, then --repeats windows of exactly --steps
+    # steps each (HIP events on the replay stream, the first recorded behind the
+    # queued warm-up); the reported step time is the median window
+    K, W = max(1, args.steps), max(0, args.warmup)
+    rep = StepReplayer(pipe, pool_drafts, pool_logits, torch, use_graph=not args.no_graph)
+    win_ms, wall = timed_steps(rep, K, W, args.repeats, torch)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(n_rep):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / K
+    ms_step = _median(win_ms) / K
     steps_per_s = 1000.0 / ms_step
     step_bytes = bytes_logits + n_rows * k * 4
-    log("timed %d steps: %.3f ms event time, %.3f s wall, %.2f us/step" % (K, ms_total, wall, ms_step * 1e3))
+    log("timed %d x %d steps after %d warm-up steps: windows %s ms (median %.2f us/step), %.3f s wall"
+        % (args.repeats, K, W, ["%.3f" % x for x in win_ms], ms_step * 1e3, wall))
 
     # ---------------- dominant kernel alone ----------------
     # graft_verify_update: one launch of k_topk_rows (row-wise top-k + acceptance
@@ -689,31 +785,21 @@ def main():
         copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
         log("plain 1 GiB copy: %.0f GB/s (read + write)" % copy_gbps)
 
+    # ---------------- small shapes: the full step at other workloads ----------------
+    shapes = []
+    if not args.no_shapes:
+        for cid in (1, 2, 4, 5):
+            rec = time_workload(cid, args.shape_steps, 8, P, dev, torch, repeats=3)
+            log("full step, workload %d (%s): %.2f us/step (%.0f GB/s)"
+                % (cid, rec["workload"], rec["us_per_step"], rec["step_GBps"]))
+            shapes.append({key: rec[key] for key in ("workload", "batch", "vocab", "verified_rows", "dtype",
+                                                     "us_per_step", "us_per_step_min", "us_per_step_max",
+                                                     "steps_per_s", "step_GBps", "step_frac_of_peak")})
+
     # ---------------- CPU oracle on a bounded sample ----------------
     cpu = None
     if not args.no_cpu_baseline:
-        from oracle import oracle as O
-        from oracle.driver import OracleGraft
-        host_logits = [b.view(torch.int16).cpu().numpy().view(np.uint16) for b in pool_logits]
-        host_drafts = [{"parent": d["parent"].cpu().numpy(), "layer": d["layer"].cpu().numpy(),
-                        "logp": d["score"].cpu().numpy(), "tok": d["tok"].cpu().numpy()} for d in pool_drafts]
-        og = OracleGraft(cfg)
-        og.table = pipe.table.cpu().numpy()
-        og.set_roots(pipe.roots.cpu().numpy(), pipe.base_pos.cpu().numpy())
-        n_cpu = 0
-        c_start = time.perf_counter()
-        while True:
-            p = n_cpu % P
-            og.build(host_drafts[p])
-            og.verify_update(host_logits[p])
-            n_cpu += 1
-            el = time.perf_counter() - c_start
-            if el >= args.cpu_seconds or n_cpu >= 1000:
-                break
-        cpu = {"value": round(n_cpu / el, 3), "unit": "steps/s", "cores": O.num_threads(), "kind": "oracle",
-               "sample": "%d full oracle steps (B=16, V=151936, 61 rows/request) on host copies of the "
-                         "same pool inputs, %.1f s" % (n_cpu, el)}
-        log("cpu oracle: %d steps in %.1f s with %d threads" % (n_cpu, el, O.num_threads()))
+        cpu = cpu_baseline(cfg, pipe, pool_drafts, pool_logits, step_bytes, args.cpu_seconds, torch)
 
     out = {
         "metric": METRIC,
@@ -723,6 +809,11 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms_step, 6),
+        "repeats": {"n": args.repeats, "steps_each": K, "us_per_step_median": round(ms_step * 1e3, 3),
+                    "us_per_step_min": round(min(win_ms) * 1e3 / K, 3),
+                    "us_per_step_max": round(max(win_ms) * 1e3 / K, 3),
+                    "timing": "HIP events on the replay stream around each window of exactly K steps; the "
+                              "first event is recorded behind the queued warm-up steps; value = the median"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -755,6 +846,7 @@ def main():
             "note": "k_topk_rows on the TAIL shape (16 x 17 rows, graft_verify_update) and on one 2048-row "
                     "prompt-ingest chunk and on one request's 61 rows (graft_update_topk with logits), "
                     "event-timed single launches outside the timed step"},
+        "full_step_other_workloads": shapes or None,
         "roofline": {"kernel": "k_topk_rows (graft_verify_update: row-wise top-k + acceptance walk + matrix update)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,

@@ -318,11 +318,15 @@ def row_descriptors(pool: NoisePool, rng, cols):
     return {"idx": idx, "shift": shift, "col": cols, "bits": pool.bump_bits(idx, cols, shift)}
 
 
-def materialize_rows_np(pool: NoisePool, desc) -> np.ndarray:
-    """Host copy: row r = roll(pool[idx_r], -shift_r) with the bump written in."""
+def materialize_rows_np(pool: NoisePool, desc, out=None) -> np.ndarray:
+    """Host copy: row r = roll(pool[idx_r], -shift_r) with the bump written in
+    (into `out`, an array of at least n rows of V, when given)."""
     V = pool.V
     n = len(desc["idx"])
-    out = np.empty((n, V), pool.bits.dtype)
+    if out is None or out.dtype != pool.bits.dtype or out.shape[0] < n or out.shape[1] != V:
+        out = np.empty((n, V), pool.bits.dtype)
+    else:
+        out = out[:n]
     for r in range(n):
         src = pool.bits[desc["idx"][r]]
         s = int(desc["shift"][r])

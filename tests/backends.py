@@ -28,7 +28,12 @@ class OracleBackend:
         return self.o.build(draft)
 
     def materialize(self, pool, desc):
-        rows = G.materialize_rows_np(pool, desc)
+        # one host buffer reused across steps (a fresh one per step would page-fault
+        # hundreds of MB each time at the full shapes)
+        buf = getattr(self, "_rows", None)
+        rows = G.materialize_rows_np(pool, desc, out=buf)
+        if buf is None or rows.base is not buf:
+            self._rows = rows if rows.base is None else rows.base
         return rows if self.cfg.dtype == "bf16" else rows.view(np.float32)
 
     def verify_update(self, rows):
