@@ -18,6 +18,8 @@ GRAFT_OK = 0
 GRAFT_EINVAL = -1
 GRAFT_EUNSUPPORTED = -2
 GRAFT_EDEVICE = -3
+GRAFT_ESCRATCH = -4
+GRAFT_NOALLOC_SCRATCH_BYTES = 8 << 20  # static scratch of graft_verify_update_noalloc per GPU
 GRAFT_MAX_ROWS = 64
 GRAFT_MAX_K = 8
 GRAFT_MAX_VOCAB = 1000000   # logits per row accepted by the top-k calls
@@ -35,7 +37,8 @@ MAX_K = 8
 EXPORTS = (
     "graft_prune_select", "graft_check_draft", "graft_check_tree", "graft_checkpoint_stats", "graft_calibrate_thresholds", "graft_template_master", "graft_template_branching", "graft_retrieve_expand",
     "graft_build_tree_mask", "graft_verify_accept", "graft_update_topk",
-    "graft_build_hybrid_tree", "graft_build_after_retrieval", "graft_verify_update", "graft_coverage_gain",
+    "graft_build_hybrid_tree", "graft_build_after_retrieval", "graft_verify_update",
+    "graft_verify_update_noalloc", "graft_coverage_gain",
     "graft_launch_plan", "graft_workspace_bytes", "graft_status_string",
 )
 
@@ -93,6 +96,7 @@ def load():
     L.graft_build_after_retrieval.argtypes = [I, I, I, I, I, C.POINTER(PruneCfg), P, P, P, P, P, P, P, P, P, P,
                                               P, P, P, I, P, P, P, P, P, P, P]
     L.graft_verify_update.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
+    L.graft_verify_update_noalloc.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P]
     L.graft_coverage_gain.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
     L.graft_launch_plan.argtypes = [I64, I, I, I, C.POINTER(Plan)]
     L.graft_workspace_bytes.argtypes = [I64, I, I, I]
@@ -225,6 +229,13 @@ def graft_verify_update(B, T1, V, k, dtype, logits, tok, parent, depth, table, t
     return _chk("graft_verify_update", load().graft_verify_update(
         B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob, row_stats,
         accept_len, accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, stream))
+
+
+def graft_verify_update_noalloc(B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk,
+                                topk_prob, row_stats, accept_len, accept_idx, dmax, bonus, base_pos_io, stream):
+    return _chk("graft_verify_update_noalloc", load().graft_verify_update_noalloc(
+        B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob, row_stats,
+        accept_len, accept_idx, dmax, bonus, base_pos_io, stream))
 
 
 def graft_coverage_gain(B, T1, V, dtype, logits, tok, parent, row_src, row_stats, gain, stream):

@@ -3,6 +3,7 @@
 // allocates, frees or keeps state; every launch is asynchronous on the
 // caller's stream.
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "graft.h"
@@ -48,6 +49,81 @@ bool dtype_ok(int dtype) { return dtype == GRAFT_DTYPE_F32 || dtype == GRAFT_DTY
 
 }  // namespace
 
+// Scratch of graft_verify_update_noalloc: the top-k launch's completion words,
+// holder words and hand-offs.  One copy per GPU the library runs on, kept until
+// the process ends.  Host code never uses this name as an address (on the host
+// it is only a stand-in for the symbol): the device address comes from
+// scratch_ptr().
+static __device__ __align__(256) unsigned char scratch[GRAFT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current and kept; nullptr if the lookup fails.
+void *scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_dev[dev] = p;
+    }
+    return g_scratch_dev[dev];
+}
+
+// graft_verify_update with a caller workspace, or (static_scratch) with the
+// library's per-GPU scratch, cleared by a fill kernel on `stream` first.
+int verify_update_impl(int B, int T1, int V, int k, int dtype, const void *logits, const int32_t *tok,
+                       const int32_t *parent, const int32_t *depth, int32_t *table, float *table_prob,
+                       int32_t *topk, float *topk_prob, float *row_stats, int32_t *accept_len,
+                       int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws,
+                       size_t ws_bytes, bool static_scratch, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
+    if (B < 0 || B > GRAFT_MAX_BATCH || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB || k < 1 ||
+        k > GRAFT_MAX_K || k > V || dmax < 0)
+        return GRAFT_EINVAL;
+    if (B == 0) return GRAFT_OK;
+    if (!logits || !tok || !parent || !depth || !table || !topk || !accept_len || !bonus ||
+        (dmax > 0 && !accept_idx) || (!static_scratch && !ws) || (table_prob && !topk_prob))
+        return GRAFT_EINVAL;
+    if (!aligned(logits, 16) || !aligned(row_stats, 8)) return GRAFT_EINVAL;
+    const int64_t n_rows = (int64_t)B * T1;
+    const WsLayout L = ws_layout(n_rows, V, k, dtype);
+    if (!L.fits) return GRAFT_EINVAL;
+    if (static_scratch) {
+        if (L.plan.ws_bytes > (size_t)GRAFT_NOALLOC_SCRATCH_BYTES) return GRAFT_ESCRATCH;
+        ws = scratch_ptr();
+        if (!ws) {
+            (void)hipGetLastError();
+            return GRAFT_EDEVICE;
+        }
+        launch_zero(ws, L.plan.ws_bytes, stream);
+    } else if (!aligned(ws, 256) || ws_bytes < L.total) {
+        return GRAFT_EINVAL;
+    }
+    VerifyArgs v;
+    v.T1 = T1;
+    v.tok = tok;
+    v.parent = parent;
+    v.depth = depth;
+    v.accept_len = accept_len;
+    v.accept_idx = accept_idx;
+    v.dmax = dmax;
+    v.bonus = bonus;
+    v.base_pos_io = base_pos_io;
+    v.table = table;
+    v.table_prob = table_prob;
+    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, row_stats, ws, &v, stream);
+    return launch_status();
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *graft_status_string(int status) {
@@ -56,6 +132,7 @@ const char *graft_status_string(int status) {
         case GRAFT_EINVAL: return "invalid argument (null or misaligned pointer, bad size or shape)";
         case GRAFT_EUNSUPPORTED: return "unsupported dtype, mode or layout";
         case GRAFT_EDEVICE: return "HIP launch error";
+        case GRAFT_ESCRATCH: return "sizes need more than the static scratch of graft_verify_update_noalloc";
         default: return "unknown status";
     }
 }
@@ -361,32 +438,19 @@ int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logi
                         int32_t *topk, float *topk_prob, float *row_stats, int32_t *accept_len,
                         int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws,
                         size_t ws_bytes, hipStream_t stream) {
-    if (!dtype_ok(dtype)) return GRAFT_EUNSUPPORTED;
-    if (B < 0 || B > GRAFT_MAX_BATCH || T1 < 1 || T1 > GRAFT_MAX_ROWS || V < 1 || V > GRAFT_MAX_VOCAB || k < 1 || k > GRAFT_MAX_K ||
-        k > V || dmax < 0)
-        return GRAFT_EINVAL;
-    if (B == 0) return GRAFT_OK;
-    if (!logits || !tok || !parent || !depth || !table || !topk || !accept_len || !bonus ||
-        (dmax > 0 && !accept_idx) || !ws || (table_prob && !topk_prob))
-        return GRAFT_EINVAL;
-    if (!aligned(logits, 16) || !aligned(ws, 256) || !aligned(row_stats, 8)) return GRAFT_EINVAL;
-    const int64_t n_rows = (int64_t)B * T1;
-    const WsLayout L = ws_layout(n_rows, V, k, dtype);
-    if (!L.fits || ws_bytes < L.total) return GRAFT_EINVAL;
-    VerifyArgs v;
-    v.T1 = T1;
-    v.tok = tok;
-    v.parent = parent;
-    v.depth = depth;
-    v.accept_len = accept_len;
-    v.accept_idx = accept_idx;
-    v.dmax = dmax;
-    v.bonus = bonus;
-    v.base_pos_io = base_pos_io;
-    v.table = table;
-    v.table_prob = table_prob;
-    launch_topk(L.plan, dtype, logits, k, topk, topk_prob, row_stats, ws, &v, stream);
-    return launch_status();
+    return verify_update_impl(B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob,
+                              row_stats, accept_len, accept_idx, dmax, bonus, base_pos_io, ws, ws_bytes, false,
+                              stream);
+}
+
+int graft_verify_update_noalloc(int B, int T1, int V, int k, int dtype, const void *logits, const int32_t *tok,
+                                const int32_t *parent, const int32_t *depth, int32_t *table, float *table_prob,
+                                int32_t *topk, float *topk_prob, float *row_stats, int32_t *accept_len,
+                                int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io,
+                                hipStream_t stream) {
+    return verify_update_impl(B, T1, V, k, dtype, logits, tok, parent, depth, table, table_prob, topk, topk_prob,
+                              row_stats, accept_len, accept_idx, dmax, bonus, base_pos_io, nullptr, 0, true,
+                              stream);
 }
 
 int graft_verify_accept(int B, int T1, int V, int k, int dtype, const void *logits,

@@ -153,6 +153,9 @@ void launch_topk(const TopkPlan &plan, int dtype, const void *logits, int k, int
 void launch_update(int64_t n_rows, int V, int k, const int32_t *topk, const float *prob,
                    const int32_t *row_tok, int32_t *table, float *table_prob, hipStream_t s);
 
+// ---- zero fill of a device range, bytes a multiple of 16 (verify_kernels.hip) -------
+void launch_zero(void *p, size_t bytes, hipStream_t s);
+
 // ---- coverage gain (verify_kernels.hip) ---------------------------------------------
 struct CoverageArgs {
     int B, T1, V, dtype;

@@ -117,7 +117,26 @@ __global__ __launch_bounds__(kWave *kCovReqPerBlock) void k_coverage(CoverageArg
     if (lane == 0) a.gain[b] = g;
 }
 
+// Zero fill of a scratch range with 16-byte vector stores (a kernel rather
+// than a memset node, so the clear can sit inside a captured graph).
+constexpr int kZeroThreads = 256;
+constexpr int64_t kZeroMaxBlocks = 1024;
+
+__global__ __launch_bounds__(kZeroThreads) void k_zero(uint4 *__restrict__ p, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * kZeroThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kZeroThreads + threadIdx.x; i < n16; i += stride)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 }  // namespace
+
+void launch_zero(void *p, size_t bytes, hipStream_t s) {
+    const int64_t n16 = (int64_t)(bytes / 16);
+    if (n16 <= 0) return;
+    int64_t blocks = (n16 + kZeroThreads - 1) / kZeroThreads;
+    blocks = blocks < kZeroMaxBlocks ? blocks : kZeroMaxBlocks;
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(kZeroThreads), 0, s, (uint4 *)p, n16);
+}
 
 void launch_coverage(const CoverageArgs &a, hipStream_t s) {
     if (a.B <= 0) return;

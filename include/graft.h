@@ -46,6 +46,7 @@ extern "C" {
 #define GRAFT_EINVAL (-1)       /* null/misaligned pointer, bad size or shape */
 #define GRAFT_EUNSUPPORTED (-2) /* unknown dtype, mode or layout */
 #define GRAFT_EDEVICE (-3)      /* the HIP runtime reported a launch error */
+#define GRAFT_ESCRATCH (-4)     /* graft_verify_update_noalloc: sizes beyond its static scratch */
 
 #define GRAFT_DTYPE_F32 0
 #define GRAFT_DTYPE_BF16 1
@@ -343,6 +344,30 @@ int graft_verify_update(int B, int T1, int V, int k, int dtype, const void *logi
                         int32_t *accept_idx,
                         int dmax, int32_t *bonus, int32_t *base_pos_io, void *ws, size_t ws_bytes,
                         hipStream_t stream);
+
+/* graft_verify_update_noalloc -- graft_verify_update without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * call allocates and frees nothing; its scratch is a static device array of
+ * GRAFT_NOALLOC_SCRATCH_BYTES held by each GPU the library runs on until the
+ * process ends (its address looked up once per device, on the device current
+ * at the first call there).  Each call first clears the part it uses with a
+ * fill kernel on `stream`, then runs the same launch as graft_verify_update.
+ * All calls on one GPU share that array: calls that overlap on one GPU (other
+ * streams, other host threads, without ordering between them) race and give
+ * wrong results.  The scratch needed is the top-k launch's completion words,
+ * one holder word per vocabulary entry and one hand-off word per row (plus
+ * per-slice results when rows are split), about 4 * (V + 2 * B * T1) bytes:
+ * sizes that need more than GRAFT_NOALLOC_SCRATCH_BYTES return
+ * GRAFT_ESCRATCH and enqueue nothing (V = 151936 at B * T1 = 976 rows needs
+ * about 0.6 MB).  Arguments, outputs and every other status are as for
+ * graft_verify_update. */
+#define GRAFT_NOALLOC_SCRATCH_BYTES (8u << 20)
+int graft_verify_update_noalloc(int B, int T1, int V, int k, int dtype, const void *logits, const int32_t *tok,
+                                const int32_t *parent, const int32_t *depth, int32_t *table, float *table_prob,
+                                int32_t *topk, float *topk_prob, float *row_stats, int32_t *accept_len,
+                                int32_t *accept_idx, int dmax, int32_t *bonus, int32_t *base_pos_io,
+                                hipStream_t stream);
 
 /* graft_coverage_gain -- section 三: what the grafted candidates add where
  * pruning cut.  For every row v of a request that has retrieved children, the

@@ -73,6 +73,14 @@ def test_launch_size_limits():
         L.GRAFT_EINVAL
     assert lib.graft_verify_update(1_100_200, 61, 100, 8, bf, *([P] * 11), 60, P, None, P, huge, None) == \
         L.GRAFT_EINVAL
+    # the call without a workspace: sizes beyond its static scratch are refused before anything runs
+    assert lib.graft_verify_update_noalloc(20000, 61, 10 ** 6, 8, bf, *([P] * 11), 60, P, None, None) == \
+        L.GRAFT_ESCRATCH
+    assert lib.graft_verify_update_noalloc(20000, 61, 100, 8, bf, *([P] * 11), 60, P, None, None) == \
+        L.GRAFT_ESCRATCH
+    assert lib.graft_verify_update_noalloc(1_100_200, 61, 100, 8, bf, *([P] * 11), 60, P, None, None) == \
+        L.GRAFT_EINVAL
+    assert "static scratch" in L.graft_status_string(L.GRAFT_ESCRATCH)
     # per-request calls: at most 2^24 requests
     cfg = L.prune_cfg((0, 1, 5), (-1.2, -1.6, -2.3), (8, 24, 40), 0.5)
     assert lib.graft_prune_select(L.GRAFT_MAX_BATCH + 1, 60, 0, P, P, P, ctypes.byref(cfg), P, P, P, None, None) == \
