@@ -14,11 +14,11 @@ up); during timing the matrix and roots keep evolving, so accepted lengths
 differ from the pool's own trajectory but every byte is still read.
 
 Timed region: exactly `--warmup` untimed steps, then `--repeats` windows of
-exactly `--steps` steps each, as HIP-graph replays (a whole pass over the pool
-per replay where the rotation allows, single-step graphs otherwise), each window
-bracketed by HIP events on the replay stream; the first event is recorded
-behind the queued warm-up, the host synchronises before the warm-up and after
-the last window.  The value is the median window.
+exactly `--steps` steps each, every window one HIP-graph replay (one graph per
+window, captured beforehand), each bracketed by HIP events
+on the replay stream; the first event is recorded behind the queued warm-up,
+the host synchronises before the warm-up and after the last window.  The value
+is the median window.
 The dominant kernel (graft_verify_update's single launch: row-wise top-k,
 acceptance walk and matrix update) is then timed on its own with HIP events on
 the stream it is launched on: one pair around back-to-back launches (the
@@ -359,14 +359,18 @@ def setup_pool(cfg, P, dev, torch):
 
 class StepReplayer:
     """Enqueues steps i = s .. s+n-1 of a rotating pool (step i uses pool entry
-    i mod P): a whole pass over the pool as one HIP-graph replay when the
-    rotation allows, every other step as its own one-step graph, so any step
-    count is run exactly and the rotation never repeats a buffer back to back."""
+    i mod P).  Untimed runs replay a whole pass over the pool as one HIP graph
+    where the rotation allows and every other step as its own one-step graph;
+    each timed window of exactly K steps is one HIP graph of its own, so a
+    window pays one graph launch whatever K is and the rotation never repeats
+    a buffer back to back."""
 
     def __init__(self, pipe, pool_drafts, pool_logits, torch, use_graph=True):
         self.P = len(pool_logits)
         self.pipe, self.drafts, self.logits = pipe, pool_drafts, pool_logits
         self.use_graph = use_graph
+        self.torch = torch
+        self.g_win = {}
         if use_graph:
             self._pass()            # warm the launch path before capture
             torch.cuda.synchronize()
@@ -389,6 +393,30 @@ class StepReplayer:
         for p in range(self.P):
             self._step(p)
 
+    def prepare_window(self, r, s, n):
+        """Capture the graph of window r: steps s .. s+n-1.  Each window has a
+        graph of its own, so consecutive windows never replay one graph twice
+        in a row (a replay of a graph waits for that graph's previous replay
+        to finish, which would leave the device idle while the host launches)."""
+        if self.use_graph and r not in self.g_win:
+            g = self.torch.cuda.CUDAGraph()
+            with self.torch.cuda.graph(g):
+                for i in range(s, s + n):
+                    self._step(i % self.P)
+            self.torch.cuda.synchronize()
+            g.replay()              # the first launch of a graph also uploads it
+            self.torch.cuda.synchronize()
+            self.g_win[r] = g
+
+    def window(self, r, s, n):
+        """Enqueue window r (steps s .. s+n-1) as one graph replay."""
+        if self.use_graph:
+            self.g_win[r].replay()
+        else:
+            for i in range(s, s + n):
+                self._step(i % self.P)
+        return s + n
+
     def run(self, s, n):
         while n > 0:
             p = s % self.P
@@ -408,11 +436,14 @@ class StepReplayer:
 
 
 def timed_steps(rep, K, W, repeats, torch):
-    """Synchronise, enqueue exactly W untimed warm-up steps, then `repeats`
-    windows of exactly K steps, each bracketed by HIP events on the replay
-    stream; the first event is recorded behind the queued warm-up, so no window
-    starts on an idle device, and the host synchronises once all are done.
-    Returns the per-window milliseconds and the wall-clock seconds."""
+    """Capture the window graphs, synchronise, enqueue exactly W untimed
+    warm-up steps, then `repeats` windows of exactly K steps (one graph replay
+    each), each bracketed by HIP events on the replay stream; the first event
+    is recorded behind the queued warm-up, so no window starts on an idle
+    device, and the host synchronises once all are done.  Returns the
+    per-window milliseconds and the wall-clock seconds."""
+    for r in range(repeats):
+        rep.prepare_window(r, W + r * K, K)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -420,7 +451,7 @@ def timed_steps(rep, K, W, repeats, torch):
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(repeats + 1)]
     evs[0].record(stream)
     for r in range(repeats):
-        s = rep.run(s, K)
+        s = rep.window(r, s, K)
         evs[r + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -812,8 +843,9 @@ def main():
         "repeats": {"n": args.repeats, "steps_each": K, "us_per_step_median": round(ms_step * 1e3, 3),
                     "us_per_step_min": round(min(win_ms) * 1e3 / K, 3),
                     "us_per_step_max": round(max(win_ms) * 1e3 / K, 3),
-                    "timing": "HIP events on the replay stream around each window of exactly K steps; the "
-                              "first event is recorded behind the queued warm-up steps; value = the median"},
+                    "timing": "HIP events on the replay stream around each window of exactly K steps, "
+                              "each window one HIP-graph replay; the first event is recorded behind the "
+                              "queued warm-up steps; value = the median"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
