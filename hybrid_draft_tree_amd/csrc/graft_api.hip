@@ -41,7 +41,7 @@ WsLayout ws_layout(int64_t n_rows, int V, int k, int dtype) {
     // the launch's thread count is 32-bit: (row slices + coordinators, at most
     // GRAFT_MAX_COORD_GROUPS and never more than the rows) x wavefronts per slice x 64 lanes
     const int64_t units = n_rows * L.plan.groups + std::min<int64_t>(n_rows, GRAFT_MAX_COORD_GROUPS);
-    L.fits = units * L.plan.splits * 64 <= (int64_t)UINT32_MAX;
+    L.fits = units * (L.plan.splits + L.plan.merge_wave) * 64 <= (int64_t)UINT32_MAX;
     return L;
 }
 
@@ -144,7 +144,7 @@ int graft_launch_plan(int64_t n_rows, int V, int dtype, int T1, graft_plan *out)
     const WsLayout L = ws_layout(n_rows, V, 1, dtype);
     if (!L.fits) return GRAFT_EINVAL;
     const int B = T1 > 0 ? (int)std::min<int64_t>(n_rows / T1, INT32_MAX) : 0;
-    out->waves_per_group = L.plan.splits;
+    out->waves_per_group = L.plan.splits + L.plan.merge_wave;
     out->groups_per_row = L.plan.groups;
     out->blocks_per_batch = L.plan.loads;
     out->coord_groups = n_rows == 0 ? 0 : (T1 > 0 ? coord_groups(L.plan, B) : 1);

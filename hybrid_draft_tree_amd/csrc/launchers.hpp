@@ -94,6 +94,7 @@ struct TopkPlan {
     size_t off_occ = 0;       // last holder per token [V], one spare word, hand-offs [n_rows]
     int groups = 1;           // workgroups per row (rows split when there are few of them)
     int loads = 2;            // 1 KB blocks per wave per batch (2 or 4)
+    int merge_wave = 0;       // 1: a merge wavefront per row beside the `splits` streaming waves
     size_t off_cnt = 0;       // groups > 1: arrival counters [n_rows], slice results [n_rows, groups]
     size_t off_part = 0;
     size_t off_pstat = 0;
@@ -116,6 +117,7 @@ struct TopkArgs {
     // sum packed in one word), all in the workspace, zero between calls
     int groups;
     int loads;  // 1 KB blocks per wave per batch: selects the kernel instantiation
+    int merge_wave;  // 1: S streaming wavefronts and a merge wavefront per row
     uint32_t *cnt;
     uint64_t *part;
     uint64_t *pstat;

@@ -73,6 +73,9 @@ struct Bf16Traits {
     }
     __device__ static int32_t rank_key(Rank r) { return (int32_t)(r >> 16) - 0x8000; }
     __device__ static uint32_t local_off(Rank r) { return 0xffffu - (r & 0xffffu); }
+    // fp32 key of the value (the row ranks' key) and back to the filter's bf16 key
+    __device__ static int32_t row_key(uint32_t raw) { return bf16_key(raw) * 65536; }
+    __device__ static int32_t filter_key(int32_t rk) { return rk / 65536; }
     // Largest raw bit pattern of the group read as int16 (equals the largest key
     // whenever that is positive).
     __device__ static int raw_max(const uint4 &d) {
@@ -124,6 +127,8 @@ struct F32Traits {
     __device__ static Rank make(uint32_t raw, int off) { return rank64(f32_key(raw), (uint32_t)off); }
     __device__ static int32_t rank_key(Rank r) { return rank64_key(r); }
     __device__ static uint32_t local_off(Rank r) { return rank64_id(r); }
+    __device__ static int32_t row_key(uint32_t raw) { return f32_key(raw); }
+    __device__ static int32_t filter_key(int32_t rk) { return rk; }
     __device__ static int raw_max(const uint4 &d) {
         return max(max((int)d.x, (int)d.y), max((int)d.z, (int)d.w));
     }
@@ -208,6 +213,44 @@ __device__ __forceinline__ Rank merge_top8_compact(Rank (&c)[N], Rank &top, Rank
         if (v == M) v = 0;
     }
     top = newtop;
+    return kth;
+}
+
+// Few candidates: insert them one by one into the top-8 held in lanes 0..7
+// (row ranks, descending, zero = empty).  A candidate's place is the number of
+// entries above it (one ballot); the entries below it move down one lane (a
+// DPP shift within the first row of 16 lanes).  Candidates at or below the
+// 8th best are skipped.  Returns the new 8th best (0 while fewer than 8).
+__device__ __forceinline__ uint64_t dpp_shr1_u64(uint64_t v) {
+    const int l = (int)(uint32_t)v, h = (int)(uint32_t)(v >> 32);
+    constexpr int kRowShr1 = 0x111;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(l, l, kRowShr1, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(h, h, kRowShr1, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int N>
+__device__ __forceinline__ uint64_t insert_top8(const uint64_t (&c)[N], uint64_t &top, uint64_t kth) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        uint64_t bal = ballot(c[e] > kth);
+        while (bal) {
+            const int src = __ffsll((unsigned long long)bal) - 1;
+            bal &= bal - 1ull;
+            const uint32_t xl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c[e], src);
+            const uint32_t xh = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(c[e] >> 32), src);
+            const uint64_t x = ((uint64_t)xh << 32) | xl;
+            if (x <= kth) continue;
+            const int pos = __popcll(ballot(lane < kTop && top > x));
+            const uint64_t left = dpp_shr1_u64(top);
+            if (lane < kTop && lane > pos) top = left;
+            if (lane == pos) top = x;
+            const uint32_t kl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, kTop - 1);
+            const uint32_t kh = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(top >> 32), kTop - 1);
+            kth = ((uint64_t)kh << 32) | kl;
+        }
+    }
     return kth;
 }
 
@@ -318,16 +361,19 @@ __device__ __forceinline__ void accept_walk(const VerifyArgs &v, int b, int g, i
 // workgroup, the registration workgroup} arrives second at the row's hand-off
 // word, so neither waits for the other.
 
-// One row from registers (wave 0 of the row's workgroup): lanes j < k hold the
-// row's j-th id and probability.  t is the row's token (valid, uniform).
-// occ_read: the token's holder word if the row already read it (nonzero, lane
-// 0), else 0 and it is read here.
+// One row from registers (one wavefront): lanes j < k hold the row's j-th id
+// and probability.  t is the row's token (valid, uniform).  occ_read: the
+// token's holder word if the row already read it (nonzero, uniform), else 0
+// and it is read here (only then does this wait for memory).
 __device__ __forceinline__ void update_row_regs(const VerifyArgs &v, int k, int64_t P, int t, int32_t id,
                                                 float pj, bool with_prob, int occ_read) {
     const int lane = lane_id();
     int occ = occ_read;
-    if (occ == 0 && lane == 0) occ = ld_agent(&v.last_occ[t]);
-    occ = readlane_i32(occ, 0);
+    if (occ == 0) {
+        int x = 0;
+        if (lane == 0) x = ld_agent(&v.last_occ[t]);
+        occ = readlane_i32(x, 0);
+    }
     if (occ != (int32_t)(P + 1)) return;
     if (lane < k) {
         v.table[(size_t)t * k + lane] = id;
@@ -427,6 +473,448 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
         accept_walk(v, b, g - 1, t, p, d, A, base);
         if (row) st_agent(&v.done[o], 0);
     }
+}
+
+// A row's result, from one wavefront whose lanes 0..7 hold the row's top-8
+// row ranks (descending; zero where the row has fewer elements): the top-k ids
+// (and softmax probabilities), the completion word the coordinators watch, and
+// the hand-off to the matrix update.  Uniform (scalar) arguments, so that no
+// wait for an earlier load falls after this row's stores (a wait on the vector
+// memory counter also waits for the stores issued before it): row_tok, the
+// row's token (-1 without an update); handoff_seen, the row's hand-off word as
+// read earlier (1 = the registration had arrived, so the fast path applies),
+// else 0; occ, the token's holder word read after handoff_seen showed 1, else 0.
+template <bool PROB, bool ACCEPT>
+__device__ __forceinline__ void finish_row(const TopkArgs &a, const VerifyArgs &v, int64_t row, uint64_t rtop,
+                                           float rowM, float rowS, int row_tok, int handoff_seen, int occ) {
+    const int lane = lane_id();
+    const int32_t my_id = rtop ? (int32_t)rank64_id(rtop) : -1;  // lanes j < k: the row's j-th id
+    float my_p = 0.0f;
+    if (lane < a.k) st_agent(&a.topk[row * a.k + lane], my_id);
+    if (PROB) {
+        if (a.stats && lane == 0) *(float2 *)&a.stats[row * 2] = make_float2(rowM, rowS);
+        if (a.prob && lane < a.k) {
+            const float x = key_to_f32(rank64_key(rtop));
+            my_p = rtop ? __expf(x - rowM) / rowS : 0.0f;
+            st_agent((int32_t *)&a.prob[row * a.k + lane], __float_as_int(my_p));
+        }
+    }
+    if constexpr (ACCEPT) {
+        // Completion word for the coordinator: greedy token + 1 (lane 0 holds it).
+        if (v.B > 0 && lane == 0) st_agent(&v.done[row], my_id + 1);
+        // Fused update: hand the row to the update.  Fast path: the registration
+        // already arrived (it finishes long before the rows do); otherwise the
+        // second arrival at the row's hand-off word updates the row.
+        const int t = v.table ? row_tok : -1;
+        if (t >= 0 && t < a.V) {
+            const bool fast = handoff_seen == 1;
+            bool mine = fast;
+            if (!mine) {
+                publish();
+                uint32_t o = 0;
+                if (lane == 0) o = count_in(&v.handoff[row]);
+                mine = readlane_i32((int)o, 0) == 1;
+            }
+            if (mine) {
+                // the holder word read after the hand-off showed the registration
+                // needs no further ordering (an acquire here would also wait for
+                // this row's stores above); otherwise order the read that follows
+                if (!fast || occ == 0) after_count();
+                update_row_regs(v, a.k, row, t, my_id, my_p, a.prob != nullptr, occ);
+                if (lane == 0) st_agent(&v.handoff[row], 0u);
+            }
+        }
+    }
+}
+
+// ---- rows with long streams: S streaming wavefronts and one merge wavefront ----------
+// The S streaming waves of a row only filter: each 16-byte group with an
+// element at or above the current threshold (the larger of the wave's own seed
+// and the row threshold the merge wave publishes in LDS) goes into the wave's
+// ring in LDS (one producer, one consumer, no atomics: entries are written,
+// then the producer's count).  The merge wave drains the rings into the row's
+// exact top-8 (64-bit row ranks: value key, inverted element id), publishes
+// the new threshold, and when every streaming wave has raised its flag and the
+// rings are empty, finishes the row itself.  A streaming wave never stops
+// issuing loads to merge, and no cross-wave selection is left at the row's end.
+template <int U>
+struct MwSmem {
+    static constexpr int kRing = kWave * U;  // pending groups per streaming wave: one full batch
+    // control block: counts [16] @0 (entries written, kRingDone once the
+    // wave is done), consumed [16] @64, threshold @128; softmax statistics
+    // float2 [16] @256; merge scratch u64 [64] @512
+    static constexpr size_t kCtrl = 1024;
+    static size_t bytes(int S) { return kCtrl + (size_t)S * kRing * (sizeof(uint4) + sizeof(uint32_t)); }
+};
+
+// Control words in LDS: relaxed workgroup-scope atomics, so each access is one
+// LDS instruction (a volatile access through a generic pointer would become a
+// flat access, which also waits for the wave's loads in flight).
+__device__ __forceinline__ uint32_t lds_ld(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// LDS ordering: one wavefront's LDS accesses are performed in program order,
+// so a consumer that sees a count written after the entries sees the entries.
+// The compiler is kept from moving memory accesses across these points.
+__device__ __forceinline__ void lds_order() { __asm__ volatile("" ::: "memory"); }
+__device__ __forceinline__ void lds_drain() {
+    lds_order();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS accesses have completed
+    lds_order();
+}
+
+constexpr uint64_t kHandoffTicks = 500;     // the merge wave reads the row's hand-off word ~5 us in
+constexpr uint32_t kRingDone = 0x80000000u;  // a ring's count word: the streaming wave is done
+constexpr uint32_t kMaxIdlePolls = 1u << 25; // ~2 s of 64-cycle sleeps: a stuck row gives up (never in normal operation)
+constexpr int kInsertMax = 24;  // candidates inserted one by one; more take the wave merge
+
+template <typename TR, bool PROB, bool ACCEPT, int U>
+__global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
+    using SM = MwSmem<U>;
+    constexpr int kRing = SM::kRing;
+    constexpr int EPG = TR::kPerGroup;
+    constexpr int ESZ = 16 / EPG;
+    constexpr int BLK = kWave * EPG;  // elements per 1 KB block
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *s_cnt = (uint32_t *)smem;
+    uint32_t *s_rd = s_cnt + 16;
+    uint32_t *s_thr = s_cnt + 32;  // int32 filter key as its bits
+    float2 *s_stat = (float2 *)(smem + 256);
+    uint64_t *s_scr = (uint64_t *)(smem + 512);
+
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = (int)(blockDim.x >> 6) - 1;  // streaming waves; wave S merges
+    int64_t row = blockIdx.x;
+    if constexpr (ACCEPT) {
+        if (row < v.ncoord) {
+            coordinate(a, v, (int)row);
+            return;
+        }
+        row -= v.ncoord;
+    }
+    if (row >= a.n_rows) return;
+    uint4 *ring_d = (uint4 *)(smem + SM::kCtrl);
+    uint32_t *ring_g = (uint32_t *)(smem + SM::kCtrl + (size_t)S * kRing * sizeof(uint4));
+
+    const int V = a.V;
+    const char *rowp = (const char *)a.logits + (size_t)row * (size_t)V * ESZ;
+    // head (until 16-byte alignment), body of 16-byte groups in 1 KB blocks, tail
+    int head = (int)(((16u - (uint32_t)((uintptr_t)rowp & 15u)) & 15u) / ESZ);
+    head = min(head, V);
+    const int ng = (V - head) / EPG;
+    const int ntail = V - head - ng * EPG;
+    const int nblk = (ng + kWave - 1) / kWave;
+    const uint4 *vp = (const uint4 *)(rowp + (size_t)head * ESZ);
+
+    if (wv < S) {
+        // ---------------- streaming wave ----------------
+        uint4 *rd_ring = ring_d + (size_t)wv * kRing;
+        uint32_t *rg_ring = ring_g + (size_t)wv * kRing;
+        const int kcount = nblk > wv ? (nblk - wv + S - 1) / S : 0;  // blocks of this wave
+        const int nfull = ng / kWave;                                 // complete blocks of the row
+        const int kfull = nfull > wv ? (nfull - wv + S - 1) / S : 0;
+        int seed = INT_MIN;          // the wave's own lower bound of the row's 8th best key
+        uint32_t wr = 0, seen = 0;   // entries written; entries the merge wave had taken when last read
+        SoftStats st;
+        auto push = [&](const uint4 (&d)[U], const bool (&pass)[U], int kq0) __attribute__((always_inline)) {
+            uint64_t bal[U];
+            uint32_t n = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                bal[u] = ballot(pass[u]);
+                n += (uint32_t)__popcll(bal[u]);
+            }
+            if (n == 0) return;
+            if (wr + n - seen > (uint32_t)kRing) {
+                // wait for room (only when candidates pile up, e.g. rising rows)
+                const uint64_t t0 = wall_clock64();
+                while (true) {
+                    seen = __builtin_amdgcn_readfirstlane(lds_ld(&s_rd[wv]));
+                    if (wr + n - seen <= (uint32_t)kRing || wall_clock64() - t0 > kSpinTicks) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            uint32_t base = wr;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (pass[u]) {
+                    const uint32_t slot = (base + (uint32_t)lanes_below(bal[u])) & (uint32_t)(kRing - 1);
+                    rd_ring[slot] = d[u];
+                    rg_ring[slot] = (uint32_t)(head + (wv + (kq0 + u) * S) * BLK + lane * EPG);
+                }
+                base += (uint32_t)__popcll(bal[u]);
+            }
+            wr += n;
+            lds_drain();
+            if (lane == 0) lds_st(&s_cnt[wv], wr);
+            lds_order();
+        };
+        auto cur_thr = [&]() __attribute__((always_inline)) {
+            return max(seed, __builtin_amdgcn_readfirstlane((int)lds_ld(s_thr)));
+        };
+        auto filter_full = [&](const uint4 (&d)[U], int kq) __attribute__((always_inline)) {
+            if constexpr (PROB) add_groups<TR, U>(st, d);
+            const int t = cur_thr();
+            bool pass[U];
+            if (t >= 1) {
+                const uint32_t t2 = TR::splat_below(t);
+#pragma unroll
+                for (int u = 0; u < U; ++u) pass[u] = TR::pass_positive(d[u], t2);
+            } else if (t == INT_MIN) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) pass[u] = true;
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) pass[u] = TR::group_pass(d[u], t);
+            }
+            push(d, pass, kq);
+        };
+        auto issue_full = [&](uint4 (&d)[U], int kk) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) d[u] = load16<true>(vp + (size_t)(wv + (kk + u) * S) * kWave + lane);
+        };
+        auto load_rem = [&](uint4 (&d)[U], int k0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int gi = min((wv + (k0 + u) * S) * kWave + lane, ng - 1);
+                d[u] = load16<true>(vp + gi);
+            }
+        };
+        auto filter_rem = [&](const uint4 (&d)[U], int k0) __attribute__((always_inline)) {
+            const int t = cur_thr();
+            bool pass[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool inb = (k0 + u < kcount) && ((wv + (k0 + u) * S) * kWave + lane < ng);
+                if constexpr (PROB) {
+                    if (inb) {
+                        const uint4 one[1] = {d[u]};
+                        add_groups<TR, 1>(st, one);
+                    }
+                }
+                pass[u] = inb && (t == INT_MIN || TR::group_pass(d[u], t));
+            }
+            push(d, pass, k0);
+        };
+        uint4 cur[U], nxt[U];
+        if (kfull >= U) issue_full(cur, 0);
+        // the merge wave has initialised the control block (a plain barrier: a
+        // workgroup fence would wait for the batch just issued)
+        lds_order();
+        __builtin_amdgcn_s_barrier();
+        lds_order();
+        int kk = 0;
+        if (kfull >= U) {
+            {
+                // Seed: the 8th largest lane maximum of the first batch is a lower
+                // bound of the row's 8th best key when positive (8 distinct
+                // elements reach it).
+                int m = TR::kRawMin;
+#pragma unroll
+                for (int u = 0; u < U; ++u) m = max(m, TR::raw_max(cur[u]));
+                int m8 = TR::kRawMin;
+#pragma unroll
+                for (int j = 0; j < kTop; ++j) {
+                    m8 = wave_max_i32(m);
+                    const uint64_t own = ballot(m == m8);
+                    if (lane == __ffsll((unsigned long long)own) - 1) m = TR::kRawMin;
+                }
+                if (m8 >= 1) seed = __builtin_amdgcn_readfirstlane(m8);
+            }
+            for (; kk + 2 * U <= kfull; kk += U) {
+                issue_full(nxt, kk + U);
+                filter_full(cur, kk);
+#pragma unroll
+                for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+            }
+            const bool rem = kk + U < kcount;
+            if (rem) load_rem(nxt, kk + U);
+            filter_full(cur, kk);
+            kk += U;
+            if (rem) {
+                filter_rem(nxt, kk);
+                kk += U;
+            }
+        }
+        for (; kk < kcount; kk += U) {
+            uint4 d[U];
+            load_rem(d, kk);
+            filter_rem(d, kk);
+        }
+        if constexpr (PROB) {
+            const float M = wave_max_f32(st.m);
+            const float s = (st.m == -INFINITY) ? 0.0f : st.s * __expf(st.m - M);
+            const float Ssum = wave_sum_f32(s);
+            if (lane == 0) s_stat[wv] = make_float2(M, Ssum);
+        }
+        lds_drain();
+        if (lane == 0) lds_st(&s_cnt[wv], wr | kRingDone);
+        return;
+    }
+
+    // ---------------- merge wave ----------------
+    // head and tail elements (at most EPG-1 each), loaded before the barrier
+    bool have = false;
+    int hidx = 0;
+    uint32_t hraw = 0;
+    if (lane < head) {
+        hidx = lane;
+        have = true;
+    } else if (lane >= 16 && lane - 16 < ntail) {
+        hidx = head + ng * EPG + (lane - 16);
+        have = true;
+    }
+    if (have) hraw = TR::load_scalar(rowp, hidx);
+    if (lane < 32) lds_st(&s_cnt[lane], 0u);  // counts, consumed
+    if (lane == 32) lds_st(s_thr, (uint32_t)INT_MIN);
+    int row_tok = -1;
+    if constexpr (ACCEPT) {
+        if (v.table) row_tok = v.tok[row];
+    }
+    lds_drain();
+    __builtin_amdgcn_s_barrier();
+    lds_order();
+
+    uint64_t top = 0;  // lanes 0..7: the row's top-8 so far, descending
+    uint64_t kth = 0;  // the 8th best (uniform); 0 while fewer than 8
+    SoftStats st;
+    {
+        uint64_t c[1] = {have ? rank64(TR::row_key(hraw), (uint32_t)hidx) : 0ull};
+        if constexpr (PROB) {
+            if (have) st.add(TR::value(hraw));
+        }
+        if (ballot(have)) kth = merge_top8<uint64_t, 1>(c, top);
+    }
+    int thr_pub = INT_MIN;
+    if (kth) {
+        thr_pub = TR::filter_key(rank64_key(kth));
+        if (lane == 0) lds_st(s_thr, (uint32_t)thr_pub);
+    }
+    uint32_t taken = 0;  // lane w < S: entries of ring w taken so far
+    int hs = 0, occ = 0;
+    bool hs_read = false, occ_read = false;
+    uint32_t idle = 0, iter = 0;  // idle polls; loop passes
+    const uint64_t t_start = wall_clock64();
+    while (true) {
+        const uint32_t cw = lane < S ? lds_ld(&s_cnt[lane]) : kRingDone;  // count and done bit in one word
+        const bool fl = (cw & kRingDone) != 0u;
+        const uint32_t av = lane < S ? (cw & ~kRingDone) - taken : 0u;
+        if constexpr (ACCEPT) {
+            // the row's hand-off word some microseconds in (the registration is
+            // done within the launch's first microseconds), then the token's
+            // holder word; the clock is read on every 8th pass
+            if (v.table && !occ_read && (++iter & 7u) == 0u) {
+                const uint64_t dt = wall_clock64() - t_start;
+                if (!hs_read && dt > kHandoffTicks) {
+                    hs = ld_agent((const int32_t *)&v.handoff[row]);
+                    hs_read = true;
+                } else if (hs_read && dt > 2 * kHandoffTicks) {
+                    occ_read = true;
+                    if (__builtin_amdgcn_readfirstlane(hs) == 1 && row_tok >= 0 && row_tok < V) {
+                        after_count();
+                        occ = ld_agent(&v.last_occ[row_tok]);
+                    }
+                }
+            }
+        }
+        if (!ballot(av != 0u)) {
+            if (!ballot(!fl)) break;                 // every streaming wave is done and its ring is empty
+            if (++idle > kMaxIdlePolls) break;       // never in normal operation
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+        }
+        // lane i takes the i-th pending entry, rings in order, 64 at most
+        int my_w = -1;
+        uint32_t my_j = 0, tk = 0;
+        int got = 0;
+        for (int w = 0; w < S && got < kWave; ++w) {
+            const int aw = __builtin_amdgcn_readlane((int)av, w);
+            if (aw == 0) continue;
+            const int t = min(aw, kWave - got);
+            const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)taken, w);
+            if (lane >= got && lane < got + t) {
+                my_w = w;
+                my_j = r0 + (uint32_t)(lane - got);
+            }
+            if (lane == w) tk = (uint32_t)t;
+            got += t;
+        }
+        uint4 d = make_uint4(0u, 0u, 0u, 0u);
+        uint32_t g0 = 0;
+        if (my_w >= 0) {
+            const uint32_t slot = (uint32_t)my_w * kRing + (my_j & (uint32_t)(kRing - 1));
+            d = ring_d[slot];
+            g0 = ring_g[slot];
+        }
+        // the slots are handed back at once: this wave's LDS accesses are
+        // performed in order, so the reads above complete before the producer
+        // can see the new count and overwrite them
+        lds_order();
+        taken += tk;
+        if (lane < S && tk) lds_st(&s_rd[lane], taken);
+        lds_order();
+        // an entry that passed an older threshold may hold nothing above the
+        // current one: only the others are ranked
+        const bool live = my_w >= 0 && (thr_pub == INT_MIN || TR::group_pass(d, thr_pub));
+        uint64_t c[EPG];
+        bool any = false;
+#pragma unroll
+        for (int e = 0; e < EPG; ++e) {
+            const uint64_t r = rank64(TR::row_key(TR::elem(d, e)), g0 + (uint32_t)e);
+            c[e] = live && r > kth ? r : 0ull;
+            any |= c[e] != 0ull;
+        }
+        if (ballot(any)) {
+            int ncand = 0;
+#pragma unroll
+            for (int e = 0; e < EPG; ++e) ncand += __popcll(ballot(c[e] != 0ull));
+            kth = ncand <= kInsertMax ? insert_top8<EPG>(c, top, kth) : merge_top8_compact<uint64_t, EPG>(c, top, s_scr);
+            const int nt = kth ? TR::filter_key(rank64_key(kth)) : INT_MIN;
+            if (nt > thr_pub) {
+                thr_pub = nt;
+                if (lane == 0) lds_st(s_thr, (uint32_t)nt);
+            }
+        }
+    }
+    int handoff_seen = 0, occ_val = 0;
+    if constexpr (ACCEPT) {
+        if (v.table) {
+            if (!hs_read) hs = ld_agent((const int32_t *)&v.handoff[row]);
+            handoff_seen = __builtin_amdgcn_readfirstlane(hs);
+            if (handoff_seen == 1 && row_tok >= 0 && row_tok < V) {
+                if (!occ_read) {
+                    after_count();
+                    occ = ld_agent(&v.last_occ[row_tok]);
+                }
+                occ_val = __builtin_amdgcn_readfirstlane(occ);
+            }
+        }
+    }
+    row_tok = __builtin_amdgcn_readfirstlane(row_tok);
+    float rowM = -INFINITY, rowS = 0.0f;
+    if constexpr (PROB) {
+        // the streaming waves' statistics and the merge wave's own (head and tail)
+        const float ownM = wave_max_f32(st.m);
+        const float ownS = wave_sum_f32((st.m == -INFINITY) ? 0.0f : st.s * __expf(st.m - ownM));
+        lds_order();
+        float m = -INFINITY, ss = 0.0f;
+        if (lane < S) {
+            const float2 sv = s_stat[lane];
+            m = sv.x;
+            ss = sv.y;
+        } else if (lane == S) {
+            m = ownM;
+            ss = ownS;
+        }
+        rowM = wave_max_f32(m);
+        rowS = wave_sum_f32((m == -INFINITY) ? 0.0f : ss * __expf(m - rowM));
+    }
+    finish_row<PROB, ACCEPT>(a, v, row, top, rowM, rowS, row_tok, handoff_seen, occ_val);
 }
 
 // Dynamic LDS layout of a row's workgroup (S waves, U blocks per batch).
@@ -852,48 +1340,18 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         }
         if (lane == 0) st_agent(&a.cnt[row], 0u);
     }
-    int32_t my_id = -1;  // lanes j < k: the row's j-th id and probability
-    float my_p = 0.0f;
-    {
-        my_id = rtop ? (int32_t)rank64_id(rtop) : -1;
-        if (lane < a.k) st_agent(&a.topk[row * a.k + lane], my_id);
-        if (PROB) {
-            const float M = rowM;
-            const float Ssum = rowS;
-            if (a.stats && lane == 0) *(float2 *)&a.stats[row * 2] = make_float2(M, Ssum);
-            if (a.prob && lane < a.k) {
-                const float x = key_to_f32(rank64_key(rtop));
-                my_p = rtop ? __expf(x - M) / Ssum : 0.0f;
-                st_agent((int32_t *)&a.prob[row * a.k + lane], __float_as_int(my_p));
-            }
-        }
-    }
-    if constexpr (ACCEPT) {
-        // Completion word for the coordinator: greedy token + 1 (lane 0 holds it).
-        if (v.B > 0 && lane == 0) st_agent(&v.done[row], my_id + 1);
-        // Fused update: hand the row to the update.  Fast path: the registration
-        // already arrived (it finishes long before the rows do); otherwise the
-        // second arrival at the row's hand-off word updates the row.
-        const int t = v.table ? __builtin_amdgcn_readfirstlane(row_tok) : -1;
-        if (t >= 0 && t < a.V) {
-            bool mine = readlane_i32(handoff_seen, 0) == 1;
-            if (!mine) {
-                publish();
-                uint32_t o = 0;
-                if (lane == 0) o = count_in(&v.handoff[row]);
-                mine = readlane_i32((int)o, 0) == 1;
-            }
-            if (mine) {
-                after_count();
-                update_row_regs(v, a.k, row, t, my_id, my_p, a.prob != nullptr, readlane_i32(occ_read, 0));
-                if (lane == 0) st_agent(&v.handoff[row], 0u);
-            }
-        }
-    }
+    const int tok_u = __builtin_amdgcn_readfirstlane(row_tok);
+    const int hs_u = readlane_i32(handoff_seen, 0);
+    const int occ_u = readlane_i32(occ_read, 0);
+    finish_row<PROB, ACCEPT>(a, v, row, rtop, rowM, rowS, tok_u, hs_u, occ_u);
 }
 
 template <typename TR, bool PROB, bool ACCEPT, int U>
 void launch_rows_u(const TopkArgs &a, const VerifyArgs &vv, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.merge_wave) {
+        hipLaunchKernelGGL((k_topk_mw<TR, PROB, ACCEPT, U>), grid, block, MwSmem<U>::bytes(a.S), s, a, vv);
+        return;
+    }
     const size_t lds = RowSmem<typename TR::Rank, U>::bytes(a.S);
     if (a.groups > 1)
         hipLaunchKernelGGL((k_topk_rows<TR, PROB, ACCEPT, true, true, U>), grid, block, lds, s, a, vv);
@@ -904,7 +1362,8 @@ void launch_rows_u(const TopkArgs &a, const VerifyArgs &vv, dim3 grid, dim3 bloc
 template <typename TR, bool PROB, bool ACCEPT>
 void launch_rows_as(const TopkArgs &a, const VerifyArgs &vv, dim3 grid, dim3 block, hipStream_t s) {
     // four blocks per batch where the plan asks for them and the LDS allows
-    if (a.loads == 4 && RowSmem<typename TR::Rank, 4>::bytes(a.S) <= (size_t)kMaxLdsPerGroup)
+    const size_t lds4 = a.merge_wave ? MwSmem<4>::bytes(a.S) : RowSmem<typename TR::Rank, 4>::bytes(a.S);
+    if (a.loads == 4 && lds4 <= (size_t)kMaxLdsPerGroup)
         launch_rows_u<TR, PROB, ACCEPT, 4>(a, vv, grid, block, s);
     else
         launch_rows_u<TR, PROB, ACCEPT, 2>(a, vv, grid, block, s);
@@ -914,7 +1373,7 @@ template <typename TR>
 void launch_rows(const TopkArgs &a, const VerifyArgs *v, hipStream_t s) {
     const int extra = v ? v->ncoord : 0;  // the coordinator workgroups
     const dim3 grid((unsigned)(a.n_rows * a.groups + extra));
-    const dim3 block(kWave * a.S);
+    const dim3 block(kWave * (a.S + a.merge_wave));
     const VerifyArgs vv = v ? *v : VerifyArgs{};
     const bool prob = a.prob != nullptr || a.stats != nullptr;  // softmax statistics wanted
     if (v) {
@@ -997,6 +1456,20 @@ static int groups_per_row(int64_t n_rows, int V, int dtype) {
     return G < 1 ? 1 : (int)G;
 }
 
+// One workgroup per row with long streams gets a merge wavefront beside its
+// streaming waves: at least kMwMinBlocks 1 KB blocks per streaming wave, and
+// at most kMwMaxStreams of them (measured: 244 rows of 12 streaming waves took
+// 35 us with one merge wave against 20 us without; 976 rows of 3, 48.4 against
+// 48.9 us; a 2048-row prompt chunk of 3, 98.6 against 100.3 us).
+constexpr int64_t kMwMinBlocks = 16;
+constexpr int kMwMaxStreams = 4;
+static int merge_wave_for(int V, int dtype, int groups, int S) {
+    if (groups != 1 || S > kMwMaxStreams) return 0;
+    const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
+    const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
+    return nblk / S >= kMwMinBlocks ? 1 : 0;
+}
+
 // Coordinator workgroups of a verify launch: one wavefront per request, at
 // most GRAFT_MAX_COORD_GROUPS workgroups (each wavefront then watches every
 // (groups x S)-th request in turn).  The coordinators are dispatched ahead of
@@ -1004,7 +1477,8 @@ static int groups_per_row(int64_t n_rows, int V, int dtype) {
 // workgroups of at most 16 wavefronts and 64 KB of LDS take at most a quarter
 // of its wavefront slots and half the LDS of 128 CUs, whatever the batch.
 int coord_groups(const TopkPlan &p, int B) {
-    const int64_t want = ((int64_t)B + p.splits - 1) / p.splits;
+    const int w = p.splits + p.merge_wave;  // wavefronts per workgroup
+    const int64_t want = ((int64_t)B + w - 1) / w;
     return (int)(want < GRAFT_MAX_COORD_GROUPS ? want : GRAFT_MAX_COORD_GROUPS);
 }
 
@@ -1016,6 +1490,7 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     p.groups = groups_per_row(n_rows, V, dtype);
     p.splits = waves_per_row(n_rows, V, dtype, p.groups > 1 ? kSplitTargetWaves : kTargetWaves, p.groups);
     p.loads = loads_for(n_rows, V, dtype, p.groups, p.splits);
+    p.merge_wave = merge_wave_for(V, dtype, p.groups, p.splits);
     // workspace: [completion words [n_rows] | last holder per token [V], spare,
     //             hand-offs [n_rows]]
     p.off_counters = 0;
@@ -1041,6 +1516,7 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
     a.S = p.splits;
     a.groups = p.groups;
     a.loads = p.loads;
+    a.merge_wave = p.merge_wave;
     a.cnt = p.groups > 1 ? (uint32_t *)((char *)ws + p.off_cnt) : nullptr;
     a.part = p.groups > 1 ? (uint64_t *)((char *)ws + p.off_part) : nullptr;
     a.pstat = p.groups > 1 ? (uint64_t *)((char *)ws + p.off_pstat) : nullptr;

@@ -172,6 +172,33 @@ def test_topk_launch_plans(n, V, dtype, prob):
         assert (got == want).all(), np.nonzero((got != want).any(1))[0][:5]
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 30011), ("f32", 16411)])
+def test_topk_merge_wave_launch(dtype, V):
+    """1024 rows of long streams take the merge-wavefront plan (3 streaming
+    waves and one merge wave per row): every adversarial row kind of the suite
+    (ties, all-equal rows whose every group passes the filter and fills the
+    rings, negative-only rows, signed zeros, ascending and descending rows, a
+    bump) with unaligned row starts (odd V), each row compared with the oracle;
+    probabilities within 1e-5 relative on the normal rows."""
+    n = 1024
+    dt = L.DTYPE_BF16 if dtype == "bf16" else L.DTYPE_F32
+    plan = L.graft_launch_plan(n, V, dt, 0)
+    assert plan["groups_per_row"] == 1 and plan["waves_per_group"] == 4
+    rng = np.random.default_rng(V)
+    for name, rows in _rows_suite(rng, n, V).items():
+        if dtype == "f32":
+            rows = G.bf16_bits_to_f32(rows).reshape(rows.shape)
+        got = gpu_topk(rows, 8, dtype)
+        want = O.topk(rows, 8, dtype)
+        assert (got == want).all(), (name, np.nonzero((got != want).any(1))[0][:5])
+    z = rng.standard_normal((n, V)).astype(np.float32)
+    rows = _bf16(z) if dtype == "bf16" else z
+    tk, tprob, table = gpu_topk(rows, 8, dtype, want_prob=True)
+    want_tk, want_p = O.topk(rows, 8, dtype, want_prob=True)
+    assert (tk == want_tk).all()
+    np.testing.assert_allclose(tprob[:n], want_p, rtol=1e-5, atol=0)
+
+
 def test_topk_max_vocab_unsplit_sampled():
     """512 rows at the largest vocabulary (one workgroup per row, 16 waves per
     row, where four-block batches would need more LDS than a workgroup may

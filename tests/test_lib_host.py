@@ -261,12 +261,12 @@ def test_coordinators_are_bounded_whatever_the_batch():
     assert seen_cap
     # the case found by reading the old code: 8192 one-wavefront coordinators
     p = L.graft_launch_plan(8192 * 17, 16000, bf, 17)
-    assert p["waves_per_group"] == 1 and p["coord_groups"] == L.GRAFT_MAX_COORD_GROUPS
+    assert p["waves_per_group"] <= 2 and p["coord_groups"] == L.GRAFT_MAX_COORD_GROUPS
     # the prompt ingest has no requests: one registration workgroup
     assert L.graft_launch_plan(2048, 151936, bf, 0)["coord_groups"] == 1
     assert L.graft_launch_plan(0, 151936, bf, 0)["workgroups"] == 0
     # the metric shape keeps one coordinator wavefront per request
     p = L.graft_launch_plan(16 * 61, 151936, bf, 61)
-    assert (p["waves_per_group"], p["groups_per_row"], p["blocks_per_batch"], p["coord_groups"]) == (3, 1, 4, 6)
+    assert (p["waves_per_group"], p["groups_per_row"], p["blocks_per_batch"], p["coord_groups"]) == (4, 1, 4, 4)
     with pytest.raises(L.GraftError):
         L.graft_launch_plan(100, 1000, bf, 61)   # T1 does not divide the rows
