@@ -623,7 +623,7 @@ def main():
         % (args.repeats, K, W, ["%.3f" % x for x in win_ms], ms_step * 1e3, wall))
 
     # ---------------- dominant kernel alone ----------------
-    # graft_verify_update: one launch of k_topk_rows (row-wise top-k + acceptance
+    # graft_verify_update: one launch of k_topk_mw (row-wise top-k + acceptance
     # walk + matrix update), the kernel that carries the step's logits traffic.
     def verify_call(i):
         L.graft_verify_update(B, T1, V, k, pipe.dtype, pool_logits[i % P].data_ptr(), pipe.tok.data_ptr(),
@@ -748,7 +748,7 @@ def main():
     # ---------------- the same kernel on the other shapes (outside the step) ----------------
     # TAIL (16 requests x 17 rows: a 16-token block plus its anchor, 82.65 MB of
     # logits) and one prompt-ingest chunk (2048 rows, 622.3 MB): each a single
-    # k_topk_rows launch, timed like the dominant kernel.
+    # top-k launch, timed like the dominant kernel.
     tcfg = WORKLOADS[5]
     tp = GraftPipeline.from_config(tcfg, device=dev)
     tad = _Adapter(tp, torch)
@@ -875,11 +875,11 @@ def main():
             "ingest_GBps": round(ingest_bytes / (ingest_ms * 1e-3) / 1e9, 1),
             "one_request_61_rows_us": round(b1_ms * 1e3, 3),
             "one_request_61_rows_GBps": round(b1_bytes / (b1_ms * 1e-3) / 1e9, 1),
-            "note": "k_topk_rows on the TAIL shape (16 x 17 rows, graft_verify_update) and on one 2048-row "
+            "note": "the top-k launch on the TAIL shape (16 x 17 rows, graft_verify_update) and on one 2048-row "
                     "prompt-ingest chunk and on one request's 61 rows (graft_update_topk with logits), "
                     "event-timed single launches outside the timed step"},
         "full_step_other_workloads": shapes or None,
-        "roofline": {"kernel": "k_topk_rows (graft_verify_update: row-wise top-k + acceptance walk + matrix update)", "bound": "hbm",
+        "roofline": {"kernel": "k_topk_mw (graft_verify_update: row-wise top-k + acceptance walk + matrix update)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "kernel_us_mean": round(k_ms * 1e3, 3),

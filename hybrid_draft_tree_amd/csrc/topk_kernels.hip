@@ -1361,9 +1361,11 @@ void launch_rows_u(const TopkArgs &a, const VerifyArgs &vv, dim3 grid, dim3 bloc
 
 template <typename TR, bool PROB, bool ACCEPT>
 void launch_rows_as(const TopkArgs &a, const VerifyArgs &vv, dim3 grid, dim3 block, hipStream_t s) {
-    // four blocks per batch where the plan asks for them and the LDS allows
+    // four blocks per batch where the plan asks for them and the LDS allows;
+    // merge-wave rows with softmax statistics always take four (an exponential
+    // per element: 976 x 151936 with statistics 55.8 us with four, 68.6 with two)
     const size_t lds4 = a.merge_wave ? MwSmem<4>::bytes(a.S) : RowSmem<typename TR::Rank, 4>::bytes(a.S);
-    if (a.loads == 4 && lds4 <= (size_t)kMaxLdsPerGroup)
+    if ((a.loads == 4 || (PROB && a.merge_wave)) && lds4 <= (size_t)kMaxLdsPerGroup)
         launch_rows_u<TR, PROB, ACCEPT, 4>(a, vv, grid, block, s);
     else
         launch_rows_u<TR, PROB, ACCEPT, 2>(a, vv, grid, block, s);
@@ -1463,6 +1465,7 @@ static int groups_per_row(int64_t n_rows, int V, int dtype) {
 // 48.9 us; a 2048-row prompt chunk of 3, 98.6 against 100.3 us).
 constexpr int64_t kMwMinBlocks = 16;
 constexpr int kMwMaxStreams = 4;
+constexpr int64_t kMwDeepBatchRows = 1536;
 static int merge_wave_for(int V, int dtype, int groups, int S) {
     if (groups != 1 || S > kMwMaxStreams) return 0;
     const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
@@ -1491,6 +1494,11 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     p.splits = waves_per_row(n_rows, V, dtype, p.groups > 1 ? kSplitTargetWaves : kTargetWaves, p.groups);
     p.loads = loads_for(n_rows, V, dtype, p.groups, p.splits);
     p.merge_wave = merge_wave_for(V, dtype, p.groups, p.splits);
+    // streaming waves that never stop to merge do best with two blocks per batch
+    // while every row's workgroup is resident at once (976 x 151936: 47.98 against
+    // 48.31 us with four; 2 or 4 streaming waves with two blocks, 57.1 and 48.6
+    // us); more rows keep four (2048-row prompt chunk: 98.0 us against 108.7)
+    if (p.merge_wave && n_rows < kMwDeepBatchRows) p.loads = 2;
     // workspace: [completion words [n_rows] | last holder per token [V], spare,
     //             hand-offs [n_rows]]
     p.off_counters = 0;

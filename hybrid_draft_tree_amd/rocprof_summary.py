@@ -6,8 +6,8 @@
 ``trace`` groups a ``--kernel-trace`` CSV by kernel and launch shape
 (workgroups x threads) and reports calls and begin-to-end durations.  ``pmc``
 averages ``FETCH_SIZE`` / ``WRITE_SIZE`` (KiB per dispatch) over the verify
-launches at the B=16, V=151936 shape (976 rows + 6 coordinator workgroups of
-192 threads: 3 wavefronts per row) and scales each counter by what it reads for the run's plain 1 GiB
+launches at the B=16, V=151936 shape (976 rows + 4 coordinator workgroups of
+256 threads: 3 streaming wavefronts and a merge wavefront per row) and scales each counter by what it reads for the run's plain 1 GiB
 device copy (``__amd_rocclr_copyBuffer``, 1 GiB read and 1 GiB written), giving
 HBM bytes per launch.  Reads CSV text only.
 """
@@ -28,19 +28,20 @@ KERNEL_SRCS = ["hybrid_draft_tree_amd/csrc/topk_kernels.hip", "hybrid_draft_tree
                "hybrid_draft_tree_amd/csrc/launchers.hpp"]
 
 B, T1, V, K = 16, 61, 151936, 8
-VERIFY_WG = 192                        # 3 wavefronts per row at the metric shape
-VERIFY_GRID = (B * T1 + 6) * VERIFY_WG  # threads of the metric-shape verify launch (6 coordinator workgroups)
+VERIFY_WG = 256                        # 3 streaming wavefronts and a merge wavefront per row at the metric shape
+VERIFY_GRID = (B * T1 + 4) * VERIFY_WG  # threads of the metric-shape verify launch (4 coordinator workgroups)
 ALG_BYTES = B * T1 * V * 2 + B * T1 * K * 4
 COPY_KIB = 1 << 20                      # 1 GiB
 
-# bench.py's top-k launches: (kernel with its template flags, workgroups, threads) -> label;
-# the flags are <element traits, softmax statistics, acceptance, non-temporal, split rows, blocks per batch>
-VERIFY = "k_topk_rows<Bf16, false, true, true, false, 4>"
+# bench.py's top-k launches: (kernel with its template flags, workgroups, threads) -> label.
+# k_topk_mw<element traits, softmax statistics, acceptance, blocks per batch>: rows with a merge wavefront;
+# k_topk_rows<element traits, softmax statistics, acceptance, non-temporal, split rows, blocks per batch>
+VERIFY = "k_topk_mw<Bf16, false, true, 2>"
 SHAPES = {
-    (VERIFY, 982, 192): "verify, 976 rows (the timed step's launch)",
-    ("k_topk_rows<Bf16, true, true, true, false, 4>", 982, 192): "verify with row statistics (coverage leg)",
+    (VERIFY, 980, 256): "verify, 976 rows (the timed step's launch)",
+    ("k_topk_mw<Bf16, true, true, 4>", 980, 256): "verify with row statistics (coverage leg)",
     ("k_topk_rows<Bf16, false, true, true, true, 4>", 1096, 128): "TAIL verify, 272 rows in 4 slices",
-    ("k_topk_rows<Bf16, false, true, true, false, 4>", 2049, 192): "ingest chunk, 2048 rows, update fused",
+    ("k_topk_mw<Bf16, false, true, 4>", 2049, 256): "ingest chunk, 2048 rows, update fused",
     ("k_topk_rows<Bf16, false, true, true, true, 4>", 245, 512): "one request, 61 rows in 4 slices",
 }
 
@@ -54,30 +55,56 @@ def kernel_source_hash() -> str:
 
 
 def short_name(name: str) -> str:
-    """Kernel name without namespaces; the top-k kernel keeps its template
-    arguments (its instantiations differ in what they compute)."""
-    t = re.search(r"k_topk_rows<(.*)>\(", name)
+    """Kernel name without namespaces; the top-k kernels keep their template
+    arguments (their instantiations differ in what they compute)."""
+    t = re.search(r"(k_topk_rows|k_topk_mw)<(.*)>\(", name)
     if t:
-        args = [a.strip().split("::")[-1].replace("Traits", "") for a in t.group(1).split(",")]
-        return "k_topk_rows<%s>" % ", ".join(args)
+        args = [a.strip().split("::")[-1].replace("Traits", "") for a in t.group(2).split(",")]
+        return "%s<%s>" % (t.group(1), ", ".join(args))
     m = re.search(r"graft::\(anonymous namespace\)::(\w+)", name)
     return m.group(1) if m else name[:60]
 
 
+def _median(xs):
+    ys = sorted(xs)
+    return ys[len(ys) // 2] if ys else float("nan")
+
+
 def trace(path: str) -> str:
     groups = defaultdict(list)
+    seq = []
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
             wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
             grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
-            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
-            groups[(short_name(r["Kernel_Name"]), grid // max(wg, 1), wg)].append(dur)
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            key = (short_name(r["Kernel_Name"]), grid // max(wg, 1), wg)
+            groups[key].append((t1 - t0) / 1000.0)
+            seq.append((t0, t1, key))
     rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
     out = ["| kernel | workgroups x threads | shape | calls | avg us | min us | max us |",
            "|---|---|---|---:|---:|---:|---:|"]
     for (name, nwg, wg), d in rows:
         out.append("| `%s` | %d x %d | %s | %d | %.2f | %.2f | %.2f |"
                    % (name, nwg, wg, SHAPES.get((name, nwg, wg), ""), len(d), sum(d) / len(d), min(d), max(d)))
+    # the timed steps: a build launch followed by the metric-shape verify launch,
+    # followed by the next step's build launch
+    seq.sort()
+    build, verify, g_bv, g_vb, step = [], [], [], [], []
+    for i in range(len(seq) - 2):
+        (b0, b1, kb), (v0, v1, kv), (n0, _, kn) = seq[i], seq[i + 1], seq[i + 2]
+        if kb[0] == "k_build_tree" and kb[1] == B and kv == (VERIFY, 980, VERIFY_WG) and kn[0] == "k_build_tree":
+            build.append((b1 - b0) / 1000.0)
+            verify.append((v1 - v0) / 1000.0)
+            g_bv.append((v0 - b1) / 1000.0)
+            g_vb.append((n0 - v1) / 1000.0)
+            step.append((n0 - b0) / 1000.0)
+    if step:
+        out.append("")
+        out.append("Timed steps (a `k_build_tree` launch, the metric-shape verify launch, the next step's build; "
+                   "%d steps, medians in us): build %.2f, gap build -> verify %.2f, verify %.2f, "
+                   "gap verify -> next build %.2f, step (build start to next build start) %.2f."
+                   % (len(step), _median(build), _median(g_bv), _median(verify), _median(g_vb), _median(step)))
     return "\n".join(out) + "\n"
 
 
@@ -102,7 +129,7 @@ def pmc(fetch_csv: str, write_csv: str, commands) -> dict:
     fs, ws = COPY_KIB / f_copy, COPY_KIB / w_copy
     rd, wr = int(round(f_avg * fs * 1024)), int(round(w_avg * ws * 1024))
     return {
-        "kernel": "k_topk_rows (graft_verify_update / graft_verify_accept), bf16, 976 rows x 151936",
+        "kernel": "k_topk_mw (graft_verify_update / graft_verify_accept), bf16, 976 rows x 151936",
         "kernel_source_sha256_16": kernel_source_hash(),
         "kernel_sources": KERNEL_SRCS,
         "dispatches": n,
@@ -119,7 +146,7 @@ def pmc(fetch_csv: str, write_csv: str, commands) -> dict:
         "traffic_over_alg": round((rd + wr) / ALG_BYTES, 4),
         "commands": list(commands),
         "note": "FETCH_SIZE/WRITE_SIZE averaged over the run's plain verify launches at the metric shape "
-                "(k_topk_rows dispatches of 982 workgroups x 192 threads: 976 rows and 6 coordinators; the "
+                "(k_topk_mw dispatches of 980 workgroups x 256 threads: 976 rows and 4 coordinators; the "
                 "other shapes the run times are left out), scaled by what the same counter reads for the run's "
                 "plain 1 GiB device copy (__amd_rocclr_copyBuffer, 1048576 KiB read and written)",
     }

@@ -67,7 +67,7 @@ def test_summary_tool_scales_counters_by_the_copy(tmp_path):
         p = tmp_path / name
         lines = [hdr]
         for i, v in enumerate(verify_vals):
-            lines.append('%d,%d,%d,"void graft::(anonymous namespace)::k_topk_rows<graft::(anonymous namespace)::Bf16Traits, false, true, true, false, 4>(graft::TopkArgs, graft::VerifyArgs)",%d,%s,%f\n'
+            lines.append('%d,%d,%d,"void graft::(anonymous namespace)::k_topk_mw<graft::(anonymous namespace)::Bf16Traits, false, true, 2>(graft::TopkArgs, graft::VerifyArgs)",%d,%s,%f\n'
                          % (i, i, rs.VERIFY_GRID, rs.VERIFY_WG, counter, v))
         lines.append('9,9,%d,"void graft::(anonymous namespace)::k_topk_rows<graft::(anonymous namespace)::Bf16Traits, false, true, true, false, 4>(graft::TopkArgs, graft::VerifyArgs)",256,%s,1.0\n'
                      % (1092 * 256, counter))
@@ -83,3 +83,26 @@ def test_summary_tool_scales_counters_by_the_copy(tmp_path):
     assert d["hbm_read_bytes_per_launch"] == 200 * 2 * 1024
     assert d["hbm_write_bytes_per_launch"] == 10 * 1024
     assert d["alg_bytes_per_launch"] == 976 * 151936 * 2 + 976 * 8 * 4
+
+
+def test_summary_tool_step_breakdown(tmp_path):
+    """Build / verify / build triples in a kernel trace give the per-step
+    durations and the two inter-launch gaps (medians)."""
+    from hybrid_draft_tree_amd import rocprof_summary as rs
+    hdr = ("Kernel_Name,Workgroup_Size_X,Workgroup_Size_Y,Workgroup_Size_Z,Grid_Size_X,Grid_Size_Y,Grid_Size_Z,"
+           "Start_Timestamp,End_Timestamp\n")
+    build = '"void graft::(anonymous namespace)::k_build_tree(graft::BuildKernelArgs)",128,1,1,2048,1,1'
+    verify = ('"void graft::(anonymous namespace)::k_topk_mw<graft::(anonymous namespace)::Bf16Traits, false, '
+              'true, 2>(graft::TopkArgs, graft::VerifyArgs)",256,1,1,%d,1,1' % rs.VERIFY_GRID)
+    lines, t = [hdr], 1000000
+    for _ in range(5):       # build 5 us, gap 0.5, verify 48 us, gap 0.7
+        lines.append("%s,%d,%d\n" % (build, t, t + 5000))
+        lines.append("%s,%d,%d\n" % (verify, t + 5500, t + 53500))
+        t += 54200
+    lines.append("%s,%d,%d\n" % (build, t, t + 5000))
+    p = tmp_path / "trace.csv"
+    p.write_text("".join(lines))
+    text = rs.trace(str(p))
+    assert "5 steps" in text
+    assert "build 5.00, gap build -> verify 0.50, verify 48.00, gap verify -> next build 0.70, " \
+           "step (build start to next build start) 54.20" in text

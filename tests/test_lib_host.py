@@ -267,6 +267,6 @@ def test_coordinators_are_bounded_whatever_the_batch():
     assert L.graft_launch_plan(0, 151936, bf, 0)["workgroups"] == 0
     # the metric shape keeps one coordinator wavefront per request
     p = L.graft_launch_plan(16 * 61, 151936, bf, 61)
-    assert (p["waves_per_group"], p["groups_per_row"], p["blocks_per_batch"], p["coord_groups"]) == (4, 1, 4, 4)
+    assert (p["waves_per_group"], p["groups_per_row"], p["blocks_per_batch"], p["coord_groups"]) == (4, 1, 2, 4)
     with pytest.raises(L.GraftError):
         L.graft_launch_plan(100, 1000, bf, 61)   # T1 does not divide the rows
