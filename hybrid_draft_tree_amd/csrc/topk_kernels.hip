@@ -570,7 +570,7 @@ __device__ __forceinline__ void lds_drain() {
 constexpr uint64_t kHandoffTicks = 500;     // the merge wave reads the row's hand-off word ~5 us in
 constexpr uint32_t kRingDone = 0x80000000u;  // a ring's count word: the streaming wave is done
 constexpr uint32_t kMaxIdlePolls = 1u << 25; // ~2 s of 64-cycle sleeps: a stuck row gives up (never in normal operation)
-constexpr int kInsertMax = 24;  // candidates inserted one by one; more take the wave merge
+constexpr int kInsertMax = 8;  // candidates inserted one by one; more take the wave merge (4-8 measured best)
 
 template <typename TR, bool PROB, bool ACCEPT, int U>
 __global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
@@ -800,6 +800,7 @@ __global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
     bool hs_read = false, occ_read = false;
     uint32_t idle = 0, iter = 0;  // idle polls; loop passes
     const uint64_t t_start = wall_clock64();
+    uint64_t hs_at = kHandoffTicks;  // when the hand-off word is (next) read
     while (true) {
         const uint32_t cw = lane < S ? lds_ld(&s_cnt[lane]) : kRingDone;  // count and done bit in one word
         const bool fl = (cw & kRingDone) != 0u;
@@ -810,14 +811,20 @@ __global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
             // holder word; the clock is read on every 8th pass
             if (v.table && !occ_read && (++iter & 7u) == 0u) {
                 const uint64_t dt = wall_clock64() - t_start;
-                if (!hs_read && dt > kHandoffTicks) {
+                if (!hs_read && dt > hs_at) {
                     hs = ld_agent((const int32_t *)&v.handoff[row]);
                     hs_read = true;
-                } else if (hs_read && dt > 2 * kHandoffTicks) {
-                    occ_read = true;
-                    if (__builtin_amdgcn_readfirstlane(hs) == 1 && row_tok >= 0 && row_tok < V) {
-                        after_count();
-                        occ = ld_agent(&v.last_occ[row_tok]);
+                } else if (hs_read && dt > hs_at + kHandoffTicks) {
+                    if (__builtin_amdgcn_readfirstlane(hs) == 1) {
+                        occ_read = true;
+                        if (row_tok >= 0 && row_tok < V) {
+                            after_count();
+                            occ = ld_agent(&v.last_occ[row_tok]);
+                        }
+                    } else {
+                        // the registration has not reached this row yet: read again later
+                        hs_read = false;
+                        hs_at = dt + kHandoffTicks;
                     }
                 }
             }
