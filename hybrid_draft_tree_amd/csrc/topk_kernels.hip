@@ -435,9 +435,14 @@ __device__ __forceinline__ void register_rows(const TopkArgs &a, const VerifyArg
 // the fused update.  Row P publishes (greedy token + 1) into done[P], zero
 // meaning "not yet"; wavefront w watches requests w, w + N, w + 2N, ... (N =
 // coordinator wavefronts) in turn, in the order their rows are dispatched (one
-// load per unfinished row per poll, no atomics), runs each acceptance walk as
-// soon as all the request's rows are in, then clears the words.  A watch that
-// exceeds kSpinTicks reports accept_len = -1 for that request and moves on.
+// load per unfinished row per poll, no atomics), clearing each word as soon as
+// it has been read.  The walk does not wait for every row: its outcome is
+// fixed once each row is either cut off by a known failed edge on its path
+// (an ancestor-or-self whose parent's greedy token is in and differs from its
+// token) or accepted with its own greedy token in, which for most requests is
+// long before their last row ends; the wave then only keeps clearing words.
+// A watch that exceeds kSpinTicks reports accept_len = -1 for that request and
+// moves on.
 __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &v, int cw) {
     if (cw == 0 && v.table) register_rows(a, v);
     const int lane = lane_id();
@@ -457,21 +462,31 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
         const uint64_t A = ancestor_mask(row, p);
         const int base = v.base_pos_io ? v.base_pos_io[b] : 0;  // only this wave writes it
         const uint64_t t0 = wall_clock64();
-        bool ok = true;
+        bool walked = false;
         while (true) {
-            if (g == 0) g = ld_agent(&v.done[o]);
-            if (!ballot(g == 0)) break;
+            if (g == 0) {
+                g = ld_agent(&v.done[o]);
+                if (g != 0) st_agent(&v.done[o], 0);  // the row writes it once per launch
+            }
+            if (!walked) {
+                const int gp = __shfl(g, p >= 0 ? p : lane);     // parent's greedy token + 1, 0 = not in
+                const bool known = lane == 0 || gp != 0;          // the edge into this row can be checked
+                const bool holds = lane == 0 || (gp != 0 && t == gp - 1);
+                const uint64_t cut = ballot(row && known && !holds);
+                const uint64_t held = ballot(row && holds);
+                const bool fixed = !row || (A & cut) != 0ull || ((A & ~held) == 0ull && g != 0);
+                if (!ballot(!fixed)) {
+                    // rows not in yet are all cut off: their greedy tokens are not used
+                    accept_walk(v, b, g - 1, t, p, d, A, base);
+                    walked = true;
+                }
+            }
+            if (walked && !ballot(g == 0)) break;
             if (wall_clock64() - t0 > kSpinTicks) {
-                ok = false;
+                if (lane == 0) v.accept_len[b] = -1;
                 break;
             }
         }
-        if (!ok) {
-            if (lane == 0) v.accept_len[b] = -1;
-            continue;
-        }
-        accept_walk(v, b, g - 1, t, p, d, A, base);
-        if (row) st_agent(&v.done[o], 0);
     }
 }
 
