@@ -20,6 +20,7 @@ GRAFT_EUNSUPPORTED = -2
 GRAFT_EDEVICE = -3
 GRAFT_ESCRATCH = -4
 GRAFT_NOALLOC_SCRATCH_BYTES = 8 << 20  # static scratch of graft_verify_update_noalloc per GPU
+GRAFT_WS_COUNTER_BYTES = 196608  # leading workspace bytes kept between calls (per-row launch counters)
 GRAFT_MAX_ROWS = 64
 GRAFT_MAX_K = 8
 GRAFT_MAX_VOCAB = 1000000   # logits per row accepted by the top-k calls
@@ -63,7 +64,8 @@ class Template(C.Structure):
 
 class Plan(C.Structure):
     _fields_ = [("waves_per_group", C.c_int32), ("groups_per_row", C.c_int32),
-                ("blocks_per_batch", C.c_int32), ("coord_groups", C.c_int32), ("workgroups", C.c_int64)]
+                ("blocks_per_batch", C.c_int32), ("coord_groups", C.c_int32), ("workgroups", C.c_int64),
+                ("merge_wave", C.c_int32), ("launch_counters", C.c_int32)]
 
 
 _LIB = None

@@ -85,12 +85,23 @@ void launch_flatten(const FlattenKernelArgs &a, hipStream_t s);
 void launch_build(const BuildKernelArgs &a, hipStream_t s);
 
 // ---- row-wise top-k + fused acceptance walk / matrix update (topk_kernels.hip) ------
+// The first kCounterBytes of every top-k workspace hold, for rows below
+// kTagRows, the rows' tagged completion words (launch counter << 32 | greedy
+// token + 1) and the coordinators' launch counter per row.  Unlike the rest of
+// the workspace these words are not cleared: each launch advances both counters
+// of its rows by one, so a completion word is current iff its counter is the
+// one the coordinator expects, and no coordinator has to wait for a row only to
+// clear its word.  They sit at the same place whatever the launch's size, so
+// calls of any size can share one workspace.
+constexpr int64_t kTagRows = 16384;
+constexpr size_t kCounterBytes = (size_t)kTagRows * (sizeof(uint64_t) + sizeof(uint32_t));
+
 struct TopkPlan {
     int64_t n_rows = 0;
     int V = 0;
     int splits = 1;           // wavefronts per row (one workgroup per row), plain launches
     int dtype = 0;            // GRAFT_DTYPE_*
-    size_t off_counters = 0;  // completion words [n_rows]
+    size_t off_counters = 0;  // untagged completion words [n_rows] (after the kCounterBytes of tagged ones)
     size_t off_occ = 0;       // last holder per token [V], one spare word, hand-offs [n_rows]
     int groups = 1;           // workgroups per row (rows split when there are few of them)
     int loads = 2;            // 1 KB blocks per wave per batch (2 or 4)
@@ -98,10 +109,13 @@ struct TopkPlan {
     size_t off_cnt = 0;       // groups > 1: arrival counters [n_rows], slice results [n_rows, groups]
     size_t off_part = 0;
     size_t off_pstat = 0;
-    size_t ws_bytes = 0;      // workspace bytes the kernel uses (all zero between calls)
+    size_t ws_bytes = 0;      // workspace bytes the kernel uses (zero between calls past kCounterBytes)
 };
 
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype);
+// A verify launch of this plan tags its completion words with the per-row
+// launch counters (merge-wave rows, at most kTagRows of them).
+inline bool uses_launch_counters(const TopkPlan &p) { return p.merge_wave && p.n_rows > 0 && p.n_rows <= kTagRows; }
 int coord_groups(const TopkPlan &plan, int B);  // coordinator workgroups of a verify launch of B requests
 
 struct TopkArgs {
@@ -134,6 +148,11 @@ struct VerifyArgs {
     int32_t *bonus = nullptr;
     int32_t *base_pos_io = nullptr;
     int32_t *done = nullptr;       // [n_rows] completion words (greedy token + 1), zero between calls
+    // tagged completion words [kTagRows] (launch counter << 32 | greedy token + 1)
+    // and the coordinators' launch counters [kTagRows], kept between calls; set
+    // (instead of `done`) for merge-wave launches of at most kTagRows rows
+    uint64_t *tag_done = nullptr;
+    uint32_t *tag_want = nullptr;
     // fused matrix update (table != nullptr)
     int32_t *table = nullptr;
     float *table_prob = nullptr;
@@ -147,7 +166,8 @@ struct VerifyArgs {
 // Row-wise top-k of logits [n_rows, V] into topk [n_rows, k] (+ probabilities);
 // with `verify` the acceptance walk of every request (n_rows = B * verify->T1)
 // runs in the same launch, and with verify->table the matrix update too.  The
-// workspace counters must be zero on entry and are zero again on exit.
+// workspace past its first kCounterBytes must be zero on entry and is zero
+// again on exit; the first kCounterBytes (zero once) carry launch counters.
 void launch_topk(const TopkPlan &plan, int dtype, const void *logits, int k, int32_t *topk,
                  float *prob, float *stats, void *ws, const VerifyArgs *verify, hipStream_t s);
 

@@ -441,8 +441,11 @@ __device__ __forceinline__ void register_rows(const TopkArgs &a, const VerifyArg
 // (an ancestor-or-self whose parent's greedy token is in and differs from its
 // token) or accepted with its own greedy token in, which for most requests is
 // long before their last row ends; the wave then only keeps clearing words.
-// A watch that exceeds kSpinTicks reports accept_len = -1 for that request and
-// moves on.
+// With tagged completion words (v.tag_done) nothing is cleared: a word is the
+// row's for this launch iff its launch counter is the one the coordinator
+// expects for that row (its own counter, advanced once per launch), so the
+// wave is done with the walk.  A watch that exceeds kSpinTicks reports
+// accept_len = -1 for that request and moves on.
 __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &v, int cw) {
     if (cw == 0 && v.table) register_rows(a, v);
     const int lane = lane_id();
@@ -461,12 +464,23 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
         if (!row || lane == 0) p = -1;
         const uint64_t A = ancestor_mask(row, p);
         const int base = v.base_pos_io ? v.base_pos_io[b] : 0;  // only this wave writes it
+        const bool tagged = v.tag_done != nullptr;
+        uint32_t want = 0;  // tagged: the launch counter of this launch's words
+        if (tagged && row) {
+            want = v.tag_want[o] + 1u;  // only this wave touches the row's counter
+            v.tag_want[o] = want;
+        }
         const uint64_t t0 = wall_clock64();
         bool walked = false;
         while (true) {
             if (g == 0) {
-                g = ld_agent(&v.done[o]);
-                if (g != 0) st_agent(&v.done[o], 0);  // the row writes it once per launch
+                if (tagged) {
+                    const uint64_t w = ld_agent(&v.tag_done[o]);
+                    if ((uint32_t)(w >> 32) == want) g = (int)(uint32_t)w;
+                } else {
+                    g = ld_agent(&v.done[o]);
+                    if (g != 0) st_agent(&v.done[o], 0);  // the row writes it once per launch
+                }
             }
             if (!walked) {
                 const int gp = __shfl(g, p >= 0 ? p : lane);     // parent's greedy token + 1, 0 = not in
@@ -479,6 +493,7 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
                     // rows not in yet are all cut off: their greedy tokens are not used
                     accept_walk(v, b, g - 1, t, p, d, A, base);
                     walked = true;
+                    if (tagged) break;
                 }
             }
             if (walked && !ballot(g == 0)) break;
@@ -498,10 +513,13 @@ __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &
 // memory counter also waits for the stores issued before it): row_tok, the
 // row's token (-1 without an update); handoff_seen, the row's hand-off word as
 // read earlier (1 = the registration had arrived, so the fast path applies),
-// else 0; occ, the token's holder word read after handoff_seen showed 1, else 0.
+// else 0; occ, the token's holder word read after handoff_seen showed 1, else 0;
+// tag, this launch's counter for the row's tagged completion word (with
+// v.tag_done).
 template <bool PROB, bool ACCEPT>
 __device__ __forceinline__ void finish_row(const TopkArgs &a, const VerifyArgs &v, int64_t row, uint64_t rtop,
-                                           float rowM, float rowS, int row_tok, int handoff_seen, int occ) {
+                                           float rowM, float rowS, int row_tok, int handoff_seen, int occ,
+                                           uint32_t tag = 0) {
     const int lane = lane_id();
     const int32_t my_id = rtop ? (int32_t)rank64_id(rtop) : -1;  // lanes j < k: the row's j-th id
     float my_p = 0.0f;
@@ -515,8 +533,14 @@ __device__ __forceinline__ void finish_row(const TopkArgs &a, const VerifyArgs &
         }
     }
     if constexpr (ACCEPT) {
-        // Completion word for the coordinator: greedy token + 1 (lane 0 holds it).
-        if (v.B > 0 && lane == 0) st_agent(&v.done[row], my_id + 1);
+        // Completion word for the coordinator: greedy token + 1 (lane 0 holds it),
+        // tagged with the launch counter or plain.
+        if (v.B > 0 && lane == 0) {
+            if (v.tag_done)
+                st_agent(&v.tag_done[row], ((uint64_t)tag << 32) | (uint32_t)(my_id + 1));
+            else
+                st_agent(&v.done[row], my_id + 1);
+        }
         // Fused update: hand the row to the update.  Fast path: the registration
         // already arrived (it finishes long before the rows do); otherwise the
         // second arrival at the row's hand-off word updates the row.
@@ -788,8 +812,10 @@ __global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
     if (lane < 32) lds_st(&s_cnt[lane], 0u);  // counts, consumed
     if (lane == 32) lds_st(s_thr, (uint32_t)INT_MIN);
     int row_tok = -1;
+    uint64_t tag_old = 0;  // the row's tagged completion word from the last launch
     if constexpr (ACCEPT) {
         if (v.table) row_tok = v.tok[row];
+        if (v.tag_done && lane == 0) tag_old = ld_agent(&v.tag_done[row]);
     }
     lds_drain();
     __builtin_amdgcn_s_barrier();
@@ -936,7 +962,9 @@ __global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
         rowM = wave_max_f32(m);
         rowS = wave_sum_f32((m == -INFINITY) ? 0.0f : ss * __expf(m - rowM));
     }
-    finish_row<PROB, ACCEPT>(a, v, row, top, rowM, rowS, row_tok, handoff_seen, occ_val);
+    uint32_t tag = 0;
+    if constexpr (ACCEPT) tag = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(tag_old >> 32)) + 1u;
+    finish_row<PROB, ACCEPT>(a, v, row, top, rowM, rowS, row_tok, handoff_seen, occ_val, tag);
 }
 
 // Dynamic LDS layout of a row's workgroup (S waves, U blocks per batch).
@@ -1507,6 +1535,9 @@ int coord_groups(const TopkPlan &p, int B) {
     return (int)(want < GRAFT_MAX_COORD_GROUPS ? want : GRAFT_MAX_COORD_GROUPS);
 }
 
+static_assert(kCounterBytes == GRAFT_WS_COUNTER_BYTES, "the header states the counter region's size");
+static_assert(kCounterBytes % 256 == 0, "the regions after the counters stay 256-byte aligned");
+
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     TopkPlan p;
     p.n_rows = n_rows;
@@ -1521,10 +1552,11 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     // 48.31 us with four; 2 or 4 streaming waves with two blocks, 57.1 and 48.6
     // us); more rows keep four (2048-row prompt chunk: 98.0 us against 108.7)
     if (p.merge_wave && n_rows < kMwDeepBatchRows) p.loads = 2;
-    // workspace: [completion words [n_rows] | last holder per token [V], spare,
+    // workspace: [tagged completion words [kTagRows], launch counters [kTagRows] |
+    //             completion words [n_rows] | last holder per token [V], spare,
     //             hand-offs [n_rows]]
-    p.off_counters = 0;
-    p.off_occ = ((size_t)n_rows * sizeof(int32_t) + 255) / 256 * 256;
+    p.off_counters = kCounterBytes;
+    p.off_occ = p.off_counters + ((size_t)n_rows * sizeof(int32_t) + 255) / 256 * 256;
     p.ws_bytes = p.off_occ + ((size_t)(V + 1 + n_rows) * sizeof(uint32_t) + 255) / 256 * 256;
     if (p.groups > 1) {  // [arrival counters [n_rows] | slice top-8s [n_rows, G, 8] | slice statistics]
         const size_t nr = (size_t)n_rows, G = (size_t)p.groups;
@@ -1566,6 +1598,10 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
         } else {
             v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
             v.ncoord = coord_groups(p, v.B);
+            if (uses_launch_counters(p)) {
+                v.tag_done = (uint64_t *)ws;
+                v.tag_want = (uint32_t *)((char *)ws + (size_t)kTagRows * sizeof(uint64_t));
+            }
         }
     }
     if (dtype == GRAFT_DTYPE_BF16)

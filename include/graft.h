@@ -15,9 +15,13 @@
  *  - Array arguments are DEVICE pointers owned by the caller unless marked
  *    "host".  The library never allocates, frees or retains them.  Scratch
  *    comes from a caller workspace sized by graft_workspace_bytes(): it must
- *    be zero-filled once after allocation; every call leaves it zero-filled
- *    again (its completion words are cleared by the kernel that used them).
- *    Calls that share one workspace must be ordered (same stream).
+ *    be zero-filled once after allocation.  Its first GRAFT_WS_COUNTER_BYTES
+ *    hold per-row launch counters that carry over from call to call (each
+ *    verify call advances those of its rows); every call leaves the rest
+ *    zero-filled again.  Zero-filling the whole workspace again between calls
+ *    is always allowed (it resets the counters together).  Calls of any size
+ *    may share one workspace; calls that share it must be ordered (same
+ *    stream).
  *  - Work is enqueued asynchronously on `stream`; nothing is synchronised.
  *    Calls on different streams touching disjoint buffers are independent.
  *  - Return value: GRAFT_OK, or a negative status.  Arguments are validated
@@ -68,6 +72,7 @@ extern "C" {
 #define GRAFT_MAX_K 8     /* successors per matrix row */
 #define GRAFT_MAX_VOCAB 1000000 /* logits per row for the top-k calls (at most 16 wavefronts per row) */
 #define GRAFT_MAX_BATCH (1 << 24) /* requests per call (a launch's thread count is 32-bit); larger B: EINVAL */
+#define GRAFT_WS_COUNTER_BYTES 196608u /* leading workspace bytes kept between calls: per-row launch counters */
 
 /* Prune configuration (host POD).  Section 二, gear 1: checkpoints at draft
  * depths 0, 1 and 5 compare the best cumulative path confidence with a
@@ -401,12 +406,16 @@ typedef struct graft_plan {
     int32_t blocks_per_batch; /* 1 KB blocks each wavefront loads per batch */
     int32_t coord_groups;     /* coordinator (or registration) workgroups ahead of the rows */
     int64_t workgroups;       /* all workgroups of the launch */
+    int32_t merge_wave;       /* 1: one wavefront of each row's workgroup merges, the others stream */
+    int32_t launch_counters;  /* 1: the rows' completion words carry the workspace's per-row launch
+                                 counters (merge-wave verify launches of at most 16384 rows) */
 } graft_plan;
 int graft_launch_plan(int64_t n_rows, int V, int dtype, int T1, graft_plan *out);
 
 /* Workspace bytes needed by graft_verify_accept / graft_verify_update /
  * graft_update_topk for n_rows rows of V logits (0 on invalid sizes).  Zero-fill it once after
- * allocating it; calls leave it zero-filled.  Also 0 when n_rows rows do not fit one launch:
+ * allocating it; calls keep its first GRAFT_WS_COUNTER_BYTES as per-row launch counters and
+ * leave the rest zero-filled.  Also 0 when n_rows rows do not fit one launch:
  * n_rows must be below 2^31 - 1, and (n_rows x workgroups per row + coordinator workgroups) x
  * wavefronts per workgroup x 64 threads below 2^32 (one wavefront per row from ~3000 rows on
  * at V <= 127 x 512 bf16, so up to ~67 million rows there; rows of larger V take more

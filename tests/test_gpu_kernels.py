@@ -894,7 +894,115 @@ def test_verify_update_batch_above_resident_coordinators():
         np.testing.assert_array_equal(bp.cpu().numpy(), base + acc["accept_len"] + 1)
         np.testing.assert_array_equal(tb.cpu().numpy(), want_tab)
         assert acc["accept_len"].max() >= T1 - 2
-    assert not ws.any().item()      # left zero-filled
+    assert not ws[L.GRAFT_WS_COUNTER_BYTES:].any().item()      # left zero-filled past the launch counters
+
+
+def test_verify_update_merge_wave_past_the_counters():
+    """A merge-wave verify launch of more rows than the launch counters cover
+    (16385 rows of V = 8192) falls back to completion words that its
+    coordinators clear; the next call on the same workspace (15000 rows) uses the
+    counters.  Both match the oracle and leave the workspace past the counters
+    zero-filled."""
+    rng = np.random.default_rng(16385)
+    V, k = 8192, 8
+    calls = [(3277, 5), (3000, 5)]
+    plans = [L.graft_launch_plan(B * T1, V, L.DTYPE_BF16, T1) for B, T1 in calls]
+    assert [(p["merge_wave"], p["launch_counters"]) for p in plans] == [(1, 0), (1, 1)]
+    i32 = dict(dtype=torch.int32, device=DEV)
+    table0 = rng.integers(0, V, size=(V, k)).astype(np.int32)
+    tb = _t(table0, torch.int32)
+    want_tab = table0.copy()
+    wsb = L.graft_workspace_bytes(3277 * 5, V, k, L.DTYPE_BF16)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    for B, T1 in calls:
+        rows, tok, par, dep = _chain_batch(rng, B, T1, V)
+        base = rng.integers(0, 10000, size=B).astype(np.int32)
+        lg = _t(rows.view(np.int16)).view(torch.bfloat16)
+        tk = torch.zeros(B, T1, k, **i32)
+        al, bo = torch.zeros(B, **i32), torch.zeros(B, **i32)
+        bp = _t(base, torch.int32)
+        ai = torch.zeros(B, T1 - 1, **i32)
+        t_, p_, d_ = (_t(x, torch.int32) for x in (tok, par, dep))
+        print("verify_update B=%d T1=%d V=%d" % (B, T1, V), flush=True)
+        L.graft_verify_update(B, T1, V, k, L.DTYPE_BF16, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
+                              tb.data_ptr(), None, tk.data_ptr(), None, None, al.data_ptr(), ai.data_ptr(), T1 - 1,
+                              bo.data_ptr(), bp.data_ptr(), ws.data_ptr(), wsb, _s())
+        torch.cuda.synchronize()
+        want_tk = O.topk(rows.reshape(-1, V), k, "bf16").reshape(B, T1, k)
+        acc = O.accept(tok, par, want_tk[:, :, 0], T1 - 1)
+        O.update(want_tab, tok.reshape(-1), want_tk.reshape(-1, k))
+        np.testing.assert_array_equal(tk.cpu().numpy(), want_tk)
+        np.testing.assert_array_equal(al.cpu().numpy(), acc["accept_len"])
+        np.testing.assert_array_equal(ai.cpu().numpy(), acc["accept_idx"])
+        np.testing.assert_array_equal(bo.cpu().numpy(), acc["bonus"])
+        np.testing.assert_array_equal(bp.cpu().numpy(), base + acc["accept_len"] + 1)
+        np.testing.assert_array_equal(tb.cpu().numpy(), want_tab)
+        assert not ws[L.GRAFT_WS_COUNTER_BYTES:].any().item()
+
+
+def test_verify_update_launch_counters_across_sizes():
+    """Merge-wave verify launches of at most 16384 rows tag each row's completion
+    word with a per-row launch counter instead of clearing it.  One workspace
+    serves tagged launches of 1024, 976, 1037 and 2048 rows and an untagged one
+    (488 rows cut into slices) in any order, and
+    a zero fill between calls; every call matches the oracle, the workspace past
+    the counters is zero after each, and each row's two counters equal the
+    number of tagged launches that held it since the last zero fill."""
+    rng = np.random.default_rng(16384)
+    V, k = 30011, 8
+    calls = [(16, 64), (8, 61), (16, 61), (17, 61), (32, 64), (16, 64), None, (16, 61), (16, 61)]
+    # tagged: 1024, 976, 1037 and 2048 rows (a merge wavefront each); 488 rows are cut into slices
+    assert [bool(L.graft_launch_plan(B * T1, V, L.DTYPE_BF16, T1)["launch_counters"]) for B, T1 in
+            [c for c in calls if c]] == [True, False, True, True, True, True, True, True]
+    i32 = dict(dtype=torch.int32, device=DEV)
+    table0 = rng.integers(0, V, size=(V, k)).astype(np.int32)
+    tb = _t(table0, torch.int32)
+    want_tab = table0.copy()
+    wsb = max(L.graft_workspace_bytes(B * T1, V, k, L.DTYPE_BF16) for c in calls if c for B, T1 in [c])
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    n_tag = L.GRAFT_WS_COUNTER_BYTES // 12
+    count = np.zeros(n_tag, np.int64)
+    for c in calls:
+        if c is None:
+            ws.zero_()
+            count[:] = 0
+            continue
+        B, T1 = c
+        n = B * T1
+        plan = L.graft_launch_plan(n, V, L.DTYPE_BF16, T1)
+        tagged = bool(plan["launch_counters"])
+        rows, tok, par, dep = _chain_batch(rng, B, T1, V)
+        base = rng.integers(0, 10000, size=B).astype(np.int32)
+        lg = _t(rows.view(np.int16)).view(torch.bfloat16)
+        tk = torch.zeros(B, T1, k, **i32)
+        al, bo = torch.zeros(B, **i32), torch.zeros(B, **i32)
+        bp = _t(base, torch.int32)
+        ai = torch.zeros(B, T1 - 1, **i32)
+        t_, p_, d_ = (_t(x, torch.int32) for x in (tok, par, dep))
+        print("verify_update B=%d T1=%d V=%d tagged=%s plan=%s" % (B, T1, V, tagged, plan), flush=True)
+        L.graft_verify_update(B, T1, V, k, L.DTYPE_BF16, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
+                              tb.data_ptr(), None, tk.data_ptr(), None, None, al.data_ptr(), ai.data_ptr(), T1 - 1,
+                              bo.data_ptr(), bp.data_ptr(), ws.data_ptr(), wsb, _s())
+        torch.cuda.synchronize()
+        want_tk = O.topk(rows.reshape(-1, V), k, "bf16").reshape(B, T1, k)
+        acc = O.accept(tok, par, want_tk[:, :, 0], T1 - 1)
+        O.update(want_tab, tok.reshape(-1), want_tk.reshape(-1, k))
+        np.testing.assert_array_equal(tk.cpu().numpy(), want_tk)
+        np.testing.assert_array_equal(al.cpu().numpy(), acc["accept_len"])
+        np.testing.assert_array_equal(ai.cpu().numpy(), acc["accept_idx"])
+        np.testing.assert_array_equal(bo.cpu().numpy(), acc["bonus"])
+        np.testing.assert_array_equal(bp.cpu().numpy(), base + acc["accept_len"] + 1)
+        np.testing.assert_array_equal(tb.cpu().numpy(), want_tab)
+        assert not ws[L.GRAFT_WS_COUNTER_BYTES:].any().item()
+        if tagged:
+            count[:n] += 1
+        words = ws[:n_tag * 8].view(torch.int64).cpu().numpy().view(np.uint64)
+        want_ctr = ws[n_tag * 8:n_tag * 12].view(torch.int32).cpu().numpy().view(np.uint32)
+        np.testing.assert_array_equal(want_ctr.astype(np.int64), count)
+        np.testing.assert_array_equal((words >> np.uint64(32)).astype(np.int64), count)
+        if tagged:  # this launch's words: its counter and the row's greedy token + 1
+            np.testing.assert_array_equal((words[:n] & np.uint64(0xffffffff)).astype(np.int64),
+                                          want_tk.reshape(-1, k)[:, 0].astype(np.int64) + 1)
 
 
 # ----------------------------------------------------------------------------- coverage gain
