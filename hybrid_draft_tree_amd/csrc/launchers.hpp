@@ -114,8 +114,8 @@ struct TopkPlan {
 
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype);
 // A verify launch of this plan tags its completion words with the per-row
-// launch counters (merge-wave rows, at most kTagRows of them).
-inline bool uses_launch_counters(const TopkPlan &p) { return p.merge_wave && p.n_rows > 0 && p.n_rows <= kTagRows; }
+// launch counters (at most kTagRows rows).
+inline bool uses_launch_counters(const TopkPlan &p) { return p.n_rows > 0 && p.n_rows <= kTagRows; }
 int coord_groups(const TopkPlan &plan, int B);  // coordinator workgroups of a verify launch of B requests
 
 struct TopkArgs {
@@ -150,7 +150,7 @@ struct VerifyArgs {
     int32_t *done = nullptr;       // [n_rows] completion words (greedy token + 1), zero between calls
     // tagged completion words [kTagRows] (launch counter << 32 | greedy token + 1)
     // and the coordinators' launch counters [kTagRows], kept between calls; set
-    // (instead of `done`) for merge-wave launches of at most kTagRows rows
+    // (instead of `done`) for launches of at most kTagRows rows
     uint64_t *tag_done = nullptr;
     uint32_t *tag_want = nullptr;
     // fused matrix update (table != nullptr)

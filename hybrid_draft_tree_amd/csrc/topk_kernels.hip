@@ -1044,10 +1044,14 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         return head + ng_row * EPG + (q - (uint32_t)kcount * BLK);
     };
 
-    // the row's token for the matrix update, loaded now and used at the row's end
+    // the row's token for the matrix update and its tagged completion word from
+    // the last launch, loaded now and used at the row's end (with split rows,
+    // by the slice that finishes the row: its own load came before its store)
     int row_tok = -1;
+    uint64_t tag_old = 0;
     if constexpr (ACCEPT) {
         if (wv == 0 && v.table) row_tok = v.tok[row];
+        if (wv == 0 && lane == 0 && v.tag_done) tag_old = ld_agent(&v.tag_done[row]);
     }
     Rank top = 0;   // lanes 0..7: the wave's top-8, descending
     Rank kth = 0;   // the 8th best (uniform); 0 while fewer than 8 candidates
@@ -1393,7 +1397,8 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     const int tok_u = __builtin_amdgcn_readfirstlane(row_tok);
     const int hs_u = readlane_i32(handoff_seen, 0);
     const int occ_u = readlane_i32(occ_read, 0);
-    finish_row<PROB, ACCEPT>(a, v, row, rtop, rowM, rowS, tok_u, hs_u, occ_u);
+    const uint32_t tag_u = (uint32_t)readlane_i32((int)(uint32_t)(tag_old >> 32), 0) + 1u;
+    finish_row<PROB, ACCEPT>(a, v, row, rtop, rowM, rowS, tok_u, hs_u, occ_u, tag_u);
 }
 
 template <typename TR, bool PROB, bool ACCEPT, int U>

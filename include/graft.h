@@ -408,7 +408,7 @@ typedef struct graft_plan {
     int64_t workgroups;       /* all workgroups of the launch */
     int32_t merge_wave;       /* 1: one wavefront of each row's workgroup merges, the others stream */
     int32_t launch_counters;  /* 1: the rows' completion words carry the workspace's per-row launch
-                                 counters (merge-wave verify launches of at most 16384 rows) */
+                                 counters (verify launches of at most 16384 rows) */
 } graft_plan;
 int graft_launch_plan(int64_t n_rows, int V, int dtype, int T1, graft_plan *out);
 

@@ -270,15 +270,15 @@ def test_coordinators_are_bounded_whatever_the_batch():
     assert (p["waves_per_group"], p["groups_per_row"], p["blocks_per_batch"], p["coord_groups"]) == (4, 1, 2, 4)
     # ... with a merge wavefront per row and the per-row launch counters
     assert (p["merge_wave"], p["launch_counters"]) == (1, 1)
-    # the counters cover 16384 rows of merge-wave verify launches; an update-only
-    # launch has no completion words, rows cut into slices keep cleared ones
+    # the counters cover verify launches of up to 16384 rows (rows cut into slices
+    # too); an update-only launch has no completion words
     n_ctr = L.GRAFT_WS_COUNTER_BYTES // 12
     assert n_ctr == 16384
     assert L.graft_launch_plan(n_ctr, 151936, bf, 1)["launch_counters"] == 1
     assert L.graft_launch_plan(n_ctr + 1, 151936, bf, 1)["launch_counters"] == 0
     assert L.graft_launch_plan(2048, 151936, bf, 0)["launch_counters"] == 0
     q = L.graft_launch_plan(16 * 17, 151936, bf, 17)
-    assert q["groups_per_row"] > 1 and (q["merge_wave"], q["launch_counters"]) == (0, 0)
+    assert q["groups_per_row"] > 1 and (q["merge_wave"], q["launch_counters"]) == (0, 1)
     # every workspace starts with the counters
     assert L.graft_workspace_bytes(1, 100, 8, bf) > L.GRAFT_WS_COUNTER_BYTES
     with pytest.raises(L.GraftError):
