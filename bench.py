@@ -661,6 +661,30 @@ def main():
     log("dominant kernel: %.2f us per launch back to back (%.0f GB/s algorithmic); bracketed one by one: mean "
         "%.2f us, median %.2f us" % (k_ms * 1e3, achieved, kb_ms * 1e3, kb_med * 1e3))
 
+    # ---------------- measured read ceiling of the same rows ----------------
+    # graft_stream_read: the pool's logits read with the verify launch's geometry
+    # (one workgroup of four wavefronts per row, 16-byte non-temporal loads) and
+    # nothing else, back to back like the dominant kernel above
+    sink = torch.zeros(n_rows, dtype=torch.int32, device=dev)
+
+    def stream_call(i):
+        L.graft_stream_read(pool_logits[i % P].data_ptr(), n_rows, V * 2, sink.data_ptr(), stream.cuda_stream)
+
+    for i in range(min(iters, 8)):
+        stream_call(i)
+    torch.cuda.synchronize()
+    f0.record(stream)
+    for i in range(iters):
+        stream_call(i)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    s_ms = f0.elapsed_time(f1) / iters
+    ceiling = bytes_logits / (s_ms * 1e-3) / 1e9
+    log("read ceiling of the same rows (graft_stream_read): %.2f us per launch, %.0f GB/s (%.1f %% of peak); the "
+        "dominant kernel reaches %.1f %% of it, the step %.1f %%" % (s_ms * 1e3, ceiling, 100 * ceiling / PEAK_HBM_GBPS,
+                                                                  100 * achieved / ceiling,
+                                                                  100 * step_bytes / (ms_step * 1e-3) / 1e9 / ceiling))
+
     # ---------------- coverage-gain diagnostic (outside the step) ----------------
     # The verify launch with per-row softmax statistics, then graft_coverage_gain,
     # on pool step 0 rebuilt with row sources.
@@ -856,6 +880,12 @@ def main():
                    "pool_steps": P, "hip_graph": not args.no_graph},
         "step_hbm_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "step_frac_of_ceiling": round(step_bytes / (ms_step * 1e-3) / 1e9 / ceiling, 4),
+        "read_ceiling": {"GBps": round(ceiling, 1), "frac_of_peak": round(ceiling / PEAK_HBM_GBPS, 4),
+                         "us_per_launch": round(s_ms * 1e3, 3), "bytes": bytes_logits,
+                         "what": "graft_stream_read over the same pool rows with the verify launch's geometry "
+                                 "(976 workgroups x 4 wavefronts, 16-byte non-temporal loads, two 1 KB blocks per "
+                                 "batch with the next in flight), %d back-to-back launches" % iters},
         "coverage_diagnostic": {"verify_with_row_stats_us": round(vs_ms * 1e3, 3),
                                 "row_stats_overhead_us": round((vs_ms - kb_ms) * 1e3, 3),
                                 "coverage_kernel_us": round(cov_ms * 1e3, 3),
@@ -882,6 +912,7 @@ def main():
         "roofline": {"kernel": "k_topk_mw (graft_verify_update: row-wise top-k + acceptance walk + matrix update)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "frac_of_ceiling": round(achieved / ceiling, 4),
                      "kernel_us_mean": round(k_ms * 1e3, 3),
                      "kernel_us_bracketed_mean": round(kb_ms * 1e3, 3),
                      "kernel_us_bracketed_median": round(kb_med * 1e3, 3),

@@ -39,7 +39,7 @@ EXPORTS = (
     "graft_prune_select", "graft_check_draft", "graft_check_tree", "graft_checkpoint_stats", "graft_calibrate_thresholds", "graft_template_master", "graft_template_branching", "graft_retrieve_expand",
     "graft_build_tree_mask", "graft_verify_accept", "graft_update_topk",
     "graft_build_hybrid_tree", "graft_build_after_retrieval", "graft_verify_update",
-    "graft_verify_update_noalloc", "graft_coverage_gain",
+    "graft_verify_update_noalloc", "graft_coverage_gain", "graft_stream_read",
     "graft_launch_plan", "graft_workspace_bytes", "graft_status_string",
 )
 
@@ -100,6 +100,7 @@ def load():
     L.graft_verify_update.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
     L.graft_verify_update_noalloc.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P]
     L.graft_coverage_gain.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
+    L.graft_stream_read.argtypes = [P, I64, I64, P, P]
     L.graft_launch_plan.argtypes = [I64, I, I, I, C.POINTER(Plan)]
     L.graft_workspace_bytes.argtypes = [I64, I, I, I]
     L.graft_workspace_bytes.restype = S
@@ -243,6 +244,11 @@ def graft_verify_update_noalloc(B, T1, V, k, dtype, logits, tok, parent, depth, 
 def graft_coverage_gain(B, T1, V, dtype, logits, tok, parent, row_src, row_stats, gain, stream):
     return _chk("graft_coverage_gain", load().graft_coverage_gain(
         B, T1, V, dtype, logits, tok, parent, row_src, row_stats, gain, stream))
+
+
+def graft_stream_read(data, n_rows, row_bytes, sink, stream):
+    """Read ceiling of the verify launch's geometry (measurement aid): one XOR word per row into sink."""
+    return _chk("graft_stream_read", load().graft_stream_read(data, n_rows, row_bytes, sink, stream))
 
 
 def graft_launch_plan(n_rows, V, dtype, T1):

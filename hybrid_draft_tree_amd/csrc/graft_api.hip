@@ -531,4 +531,12 @@ int graft_coverage_gain(int B, int T1, int V, int dtype, const void *logits, con
     return launch_status();
 }
 
+int graft_stream_read(const void *data, int64_t n_rows, int64_t row_bytes, uint32_t *sink, hipStream_t stream) {
+    if (n_rows < 0 || n_rows > INT32_MAX || row_bytes <= 0 || row_bytes % 16 != 0) return GRAFT_EINVAL;
+    if (n_rows == 0) return GRAFT_OK;
+    if (!data || !sink || !aligned(data, 16)) return GRAFT_EINVAL;
+    launch_stream_read(data, n_rows, row_bytes, sink, stream);
+    return launch_status();
+}
+
 }  // extern "C"

@@ -178,6 +178,10 @@ void launch_update(int64_t n_rows, int V, int k, const int32_t *topk, const floa
 // ---- zero fill of a device range, bytes a multiple of 16 (verify_kernels.hip) -------
 void launch_zero(void *p, size_t bytes, hipStream_t s);
 
+// ---- streaming read of n_rows rows of row_bytes (a multiple of 16) bytes, one XOR
+// word per row into sink: the read ceiling of the verify launch's geometry ---------
+void launch_stream_read(const void *data, int64_t n_rows, int64_t row_bytes, uint32_t *sink, hipStream_t s);
+
 // ---- coverage gain (verify_kernels.hip) ---------------------------------------------
 struct CoverageArgs {
     int B, T1, V, dtype;

@@ -128,7 +128,59 @@ __global__ __launch_bounds__(kZeroThreads) void k_zero(uint4 *__restrict__ p, in
         p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Streaming-read ceiling (a measurement aid, no part of the Graft step): one
+// workgroup of kStreamWaves wavefronts per row, the verify launch's geometry.
+// Wavefront w reads the row's 1 KB blocks w, w + kStreamWaves, ... with 16-byte
+// non-temporal loads, two blocks per batch with the next batch in flight, and
+// folds every 32-bit word into an XOR so that no load can be dropped; the row's
+// XOR goes to sink[row].  Loads past the row's last 16-byte group are skipped.
+constexpr int kStreamWaves = 4;
+
+__device__ __forceinline__ uint4 stream_load(const uint4 *p, int64_t g, int64_t groups) {
+    if (g >= groups) return make_uint4(0u, 0u, 0u, 0u);
+    typedef int int4v __attribute__((ext_vector_type(4)));
+    const int4v v = __builtin_nontemporal_load((const int4v *)(p + g));
+    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+__global__ __launch_bounds__(kWave *kStreamWaves) void k_stream_read(const uint4 *__restrict__ data, int64_t groups,
+                                                                      uint32_t *__restrict__ sink) {
+    __shared__ uint32_t s_x[kStreamWaves];
+    const int lane = lane_id();
+    const int wv = (int)(threadIdx.x / kWave);
+    const uint4 *p = data + (int64_t)blockIdx.x * groups;
+    const int64_t nblk = (groups + kWave - 1) / kWave;
+    constexpr int64_t kStep = kStreamWaves;
+    int64_t b = wv;
+    uint4 c0 = stream_load(p, b * kWave + lane, groups);
+    uint4 c1 = stream_load(p, (b + kStep) * kWave + lane, groups);
+    uint32_t x = 0;
+    for (; b < nblk; b += 2 * kStep) {
+        const uint4 n0 = stream_load(p, (b + 2 * kStep) * kWave + lane, groups);
+        const uint4 n1 = stream_load(p, (b + 3 * kStep) * kWave + lane, groups);
+        x ^= c0.x ^ c0.y ^ c0.z ^ c0.w ^ c1.x ^ c1.y ^ c1.z ^ c1.w;
+        c0 = n0;
+        c1 = n1;
+    }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o);
+    if (lane == 0) s_x[wv] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+#pragma unroll
+        for (int w = 0; w < kStreamWaves; ++w) r ^= s_x[w];
+        sink[blockIdx.x] = r;
+    }
+}
+
 }  // namespace
+
+void launch_stream_read(const void *data, int64_t n_rows, int64_t row_bytes, uint32_t *sink, hipStream_t s) {
+    if (n_rows <= 0) return;
+    hipLaunchKernelGGL(k_stream_read, dim3((unsigned)n_rows), dim3(kWave * kStreamWaves), 0, s, (const uint4 *)data,
+                       row_bytes / 16, sink);
+}
 
 void launch_zero(void *p, size_t bytes, hipStream_t s) {
     const int64_t n16 = (int64_t)(bytes / 16);

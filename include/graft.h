@@ -388,6 +388,18 @@ int graft_coverage_gain(int B, int T1, int V, int dtype, const void *logits, con
                         const int32_t *parent, const uint8_t *row_src, const float *row_stats,
                         float *gain, hipStream_t stream);
 
+/* graft_stream_read -- a measurement aid, no part of the Graft step: the read
+ * bandwidth the verify launch's geometry can reach on this device.  Reads
+ * n_rows rows of row_bytes bytes (data, device, 16-byte aligned; row_bytes a
+ * positive multiple of 16; rows contiguous) with one workgroup of four
+ * wavefronts per row, 16-byte non-temporal loads in 1 KB blocks interleaved
+ * over the wavefronts, two blocks per batch with the next batch in flight, and
+ * writes the XOR of each row's 32-bit words to sink uint32 [n_rows] (so no load
+ * is skipped, and the result can be checked).  One launch.  Requires
+ * 0 <= n_rows <= 2^31 - 1; n_rows == 0 returns GRAFT_OK before any pointer is
+ * looked at. */
+int graft_stream_read(const void *data, int64_t n_rows, int64_t row_bytes, uint32_t *sink, hipStream_t stream);
+
 /* Launch plan of the top-k launch of graft_verify_accept / graft_verify_update
  * (T1 = rows per request, n_rows = B * T1) or of graft_update_topk with logits
  * (T1 = 0: no requests, one registration workgroup); host only, nothing is

@@ -1006,6 +1006,21 @@ def test_verify_update_launch_counters_across_sizes():
                                           want_tk.reshape(-1, k)[:, 0].astype(np.int64) + 1)
 
 
+@pytest.mark.parametrize("n_rows,row_bytes", [(3, 16 * 13), (5, 16 * (64 * 9 + 5)), (61, 256512), (976, 303872)])
+def test_stream_read_xor(n_rows, row_bytes):
+    """The streaming-read probe reads every byte: each row's XOR of its 32-bit
+    words equals numpy's, for ragged rows (not whole 1 KB blocks), rows of fewer
+    blocks than wavefronts and the metric shape (976 rows of 151936 bf16)."""
+    rng = np.random.default_rng(n_rows)
+    host = rng.integers(0, 2 ** 32, size=(n_rows, row_bytes // 4), dtype=np.uint32)
+    d = torch.from_numpy(host.view(np.int32)).to(DEV)
+    sink = torch.zeros(n_rows, dtype=torch.int32, device=DEV)
+    print("stream_read rows=%d bytes=%d" % (n_rows, row_bytes), flush=True)
+    L.graft_stream_read(d.data_ptr(), n_rows, row_bytes, sink.data_ptr(), _s())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sink.cpu().numpy().view(np.uint32), np.bitwise_xor.reduce(host, axis=1))
+
+
 # ----------------------------------------------------------------------------- coverage gain
 
 def _coverage_case(rng, B, T1, V, layout, dtype):

@@ -232,6 +232,19 @@ def test_empty_batches_enqueue_nothing():
     assert lib.graft_update_topk(0, 100, 8, 1, *([None] * 7), None, 0, None) == L.GRAFT_OK
     assert lib.graft_coverage_gain(0, 61, 100, 1, *([None] * 6), None) == L.GRAFT_OK
     assert lib.graft_checkpoint_stats(0, 60, None, None, None, cb, None, None) == L.GRAFT_OK
+    assert lib.graft_stream_read(None, 0, 16, None, None) == L.GRAFT_OK
+
+
+def test_stream_read_rejects_bad_arguments_on_the_host():
+    """graft_stream_read checks its sizes and pointers before it enqueues
+    anything: rows of a positive multiple of 16 bytes, 0 <= n_rows < 2^31,
+    non-null 16-byte-aligned data and a non-null sink."""
+    lib = L.load()
+    bad = [(None, 1, 16, None), (None, -1, 16, None), (None, 1, 0, None), (None, 1, 24, None),
+           (None, 1 << 31, 16, None), (ctypes.c_void_p(8), 1, 16, ctypes.c_void_p(64)),
+           (ctypes.c_void_p(64), 1, 16, None)]
+    for data, n, rb, sink in bad:
+        assert lib.graft_stream_read(data, n, rb, sink, None) == L.GRAFT_EINVAL, (data, n, rb, sink)
 
 
 def test_coordinators_are_bounded_whatever_the_batch():
