@@ -43,6 +43,7 @@ SHAPES = {
     ("k_topk_rows<Bf16, false, true, true, true, 4>", 1096, 128): "TAIL verify, 272 rows in 4 slices",
     ("k_topk_mw<Bf16, false, true, 4>", 2049, 256): "ingest chunk, 2048 rows, update fused",
     ("k_topk_rows<Bf16, false, true, true, true, 4>", 245, 512): "one request, 61 rows in 4 slices",
+    ("k_stream_read", 976, 256): "read ceiling of the verify launch's rows (graft_stream_read)",
 }
 
 
