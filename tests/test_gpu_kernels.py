@@ -897,6 +897,53 @@ def test_verify_update_batch_above_resident_coordinators():
     assert not ws[L.GRAFT_WS_COUNTER_BYTES:].any().item()      # left zero-filled past the launch counters
 
 
+def test_verify_update_launch_counters_wrap():
+    """The per-row launch counters are 32-bit and wrap: with both counters of
+    every row preset to 2^32 - 2 (and stale completion words of the counter
+    before), three calls in a row run through 2^32 - 1, 0 and 1 and each still
+    matches the oracle."""
+    rng = np.random.default_rng(4242)
+    V, k, B, T1 = 30011, 8, 16, 61
+    assert L.graft_launch_plan(B * T1, V, L.DTYPE_BF16, T1)["launch_counters"] == 1
+    i32 = dict(dtype=torch.int32, device=DEV)
+    table0 = rng.integers(0, V, size=(V, k)).astype(np.int32)
+    tb = _t(table0, torch.int32)
+    want_tab = table0.copy()
+    wsb = L.graft_workspace_bytes(B * T1, V, k, L.DTYPE_BF16)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    n_tag = L.GRAFT_WS_COUNTER_BYTES // 12
+    start = (1 << 32) - 2
+    words = np.full(n_tag, (start << 32) | 1, dtype=np.uint64)  # a stale word of counter 2^32 - 2, greedy 0
+    ws[:n_tag * 8] = torch.from_numpy(words.view(np.uint8)).to(DEV)
+    ws[n_tag * 8:n_tag * 12] = torch.from_numpy(np.full(n_tag, start, dtype=np.uint32).view(np.uint8)).to(DEV)
+    for call in range(3):
+        rows, tok, par, dep = _chain_batch(rng, B, T1, V)
+        base = rng.integers(0, 10000, size=B).astype(np.int32)
+        lg = _t(rows.view(np.int16)).view(torch.bfloat16)
+        tk = torch.zeros(B, T1, k, **i32)
+        al, bo = torch.zeros(B, **i32), torch.zeros(B, **i32)
+        bp = _t(base, torch.int32)
+        ai = torch.zeros(B, T1 - 1, **i32)
+        t_, p_, d_ = (_t(x, torch.int32) for x in (tok, par, dep))
+        print("verify_update call %d, counters at %d" % (call, (start + call + 1) % (1 << 32)), flush=True)
+        L.graft_verify_update(B, T1, V, k, L.DTYPE_BF16, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(), d_.data_ptr(),
+                              tb.data_ptr(), None, tk.data_ptr(), None, None, al.data_ptr(), ai.data_ptr(), T1 - 1,
+                              bo.data_ptr(), bp.data_ptr(), ws.data_ptr(), wsb, _s())
+        torch.cuda.synchronize()
+        want_tk = O.topk(rows.reshape(-1, V), k, "bf16").reshape(B, T1, k)
+        acc = O.accept(tok, par, want_tk[:, :, 0], T1 - 1)
+        O.update(want_tab, tok.reshape(-1), want_tk.reshape(-1, k))
+        np.testing.assert_array_equal(tk.cpu().numpy(), want_tk)
+        np.testing.assert_array_equal(al.cpu().numpy(), acc["accept_len"])
+        np.testing.assert_array_equal(ai.cpu().numpy(), acc["accept_idx"])
+        np.testing.assert_array_equal(bo.cpu().numpy(), acc["bonus"])
+        np.testing.assert_array_equal(bp.cpu().numpy(), base + acc["accept_len"] + 1)
+        np.testing.assert_array_equal(tb.cpu().numpy(), want_tab)
+        ctr = ws[n_tag * 8:n_tag * 12].view(torch.int32).cpu().numpy().view(np.uint32)
+        assert (ctr[:B * T1] == (start + call + 1) % (1 << 32)).all()
+        assert (ctr[B * T1:] == start).all()
+
+
 def test_verify_update_merge_wave_past_the_counters():
     """A merge-wave verify launch of more rows than the launch counters cover
     (16385 rows of V = 8192) falls back to completion words that its
