@@ -65,7 +65,7 @@ class Template(C.Structure):
 class Plan(C.Structure):
     _fields_ = [("waves_per_group", C.c_int32), ("groups_per_row", C.c_int32),
                 ("blocks_per_batch", C.c_int32), ("coord_groups", C.c_int32), ("workgroups", C.c_int64),
-                ("merge_wave", C.c_int32), ("launch_counters", C.c_int32)]
+                ("merge_wave", C.c_int32), ("launch_counters", C.c_int32), ("holder_scan", C.c_int32)]
 
 
 _LIB = None

@@ -147,10 +147,11 @@ int graft_launch_plan(int64_t n_rows, int V, int dtype, int T1, graft_plan *out)
     out->waves_per_group = L.plan.splits + L.plan.merge_wave;
     out->groups_per_row = L.plan.groups;
     out->blocks_per_batch = L.plan.loads;
-    out->coord_groups = n_rows == 0 ? 0 : (T1 > 0 ? coord_groups(L.plan, B) : 1);
+    out->coord_groups = n_rows == 0 ? 0 : (T1 > 0 ? coord_groups(L.plan, B) : (scans_holders(L.plan) ? 0 : 1));
     out->workgroups = n_rows == 0 ? 0 : n_rows * L.plan.groups + out->coord_groups;
     out->merge_wave = L.plan.merge_wave;
     out->launch_counters = (T1 > 0 && uses_launch_counters(L.plan)) ? 1 : 0;
+    out->holder_scan = scans_holders(L.plan) ? 1 : 0;
     return GRAFT_OK;
 }
 

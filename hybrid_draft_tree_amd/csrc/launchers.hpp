@@ -113,6 +113,15 @@ struct TopkPlan {
 };
 
 TopkPlan plan_topk(int64_t n_rows, int V, int dtype);
+// Launches of merge-wave rows with the matrix update, at most kScanRows rows:
+// each row finds whether it is its token's last holder by comparing its token
+// with the later rows' tokens, which its merge wave loads into registers (at
+// most 16 per lane) near its start and compares at its end, so no registration
+// workgroup, hand-off word or atomic is needed.
+constexpr int kScanRegs = 16;
+constexpr int64_t kScanRows = 64 * kScanRegs + 1;
+inline bool scans_holders(const TopkPlan &p) { return p.merge_wave && p.n_rows > 0 && p.n_rows <= kScanRows; }
+
 // A verify launch of this plan tags its completion words with the per-row
 // launch counters (at most kTagRows rows).
 inline bool uses_launch_counters(const TopkPlan &p) { return p.n_rows > 0 && p.n_rows <= kTagRows; }
@@ -161,6 +170,7 @@ struct VerifyArgs {
     int B = 0;
     int ncoord = 0;                // coordinator workgroups (one wavefront per request)
     int update_only = 0;           // no requests: the matrix update alone (one registration workgroup)
+    int scan_holders = 0;          // rows find their token's last holder by scanning (no registration)
 };
 
 // Row-wise top-k of logits [n_rows, V] into topk [n_rows, k] (+ probabilities);

@@ -447,7 +447,7 @@ __device__ __forceinline__ void register_rows(const TopkArgs &a, const VerifyArg
 // wave is done with the walk.  A watch that exceeds kSpinTicks reports
 // accept_len = -1 for that request and moves on.
 __device__ __forceinline__ void coordinate(const TopkArgs &a, const VerifyArgs &v, int cw) {
-    if (cw == 0 && v.table) register_rows(a, v);
+    if (cw == 0 && v.table && !v.scan_holders) register_rows(a, v);
     const int lane = lane_id();
     const int S = blockDim.x >> 6;
     const int T1 = v.T1;
@@ -545,7 +545,13 @@ __device__ __forceinline__ void finish_row(const TopkArgs &a, const VerifyArgs &
         // already arrived (it finishes long before the rows do); otherwise the
         // second arrival at the row's hand-off word updates the row.
         const int t = v.table ? row_tok : -1;
-        if (t >= 0 && t < a.V) {
+        if (t >= 0 && t < a.V && v.scan_holders) {
+            // occ: 1 iff no later row of the launch holds this row's token
+            if (occ == 1 && lane < a.k) {
+                v.table[(size_t)t * a.k + lane] = my_id;
+                if (v.table_prob && a.prob) v.table_prob[(size_t)t * a.k + lane] = my_p;
+            }
+        } else if (t >= 0 && t < a.V) {
             const bool fast = handoff_seen == 1;
             bool mine = fast;
             if (!mine) {
@@ -813,6 +819,9 @@ __global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
     if (lane == 32) lds_st(s_thr, (uint32_t)INT_MIN);
     int row_tok = -1;
     uint64_t tag_old = 0;  // the row's tagged completion word from the last launch
+    int later_tok[kScanRegs];  // scan mode: tokens of rows row+1+lane+64i, -1 past the launch
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) later_tok[i] = -1;
     if constexpr (ACCEPT) {
         if (v.table) row_tok = v.tok[row];
         if (v.tag_done && lane == 0) tag_old = ld_agent(&v.tag_done[row]);
@@ -836,10 +845,26 @@ __global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
         thr_pub = TR::filter_key(rank64_key(kth));
         if (lane == 0) lds_st(s_thr, (uint32_t)thr_pub);
     }
+    if constexpr (ACCEPT) {
+        // scan mode: the later rows' tokens, loaded now (after the head and tail
+        // elements are used, so nothing waits for them before the row's end)
+        if (v.scan_holders) {
+#pragma unroll
+            for (int i = 0; i < kScanRegs; ++i) {
+                const int64_t q = row + 1 + lane + (int64_t)kWave * i;
+                if (q < a.n_rows) later_tok[i] = v.tok[q];
+            }
+        }
+    }
     uint32_t taken = 0;  // lane w < S: entries of ring w taken so far
     int hs = 0, occ = 0;
     bool hs_read = false, occ_read = false;
     uint32_t idle = 0, iter = 0;  // idle polls; loop passes
+    // scan mode: the row's token (uniform), compared with the later rows' at the end
+    int scan_tok = -1;
+    if constexpr (ACCEPT) {
+        if (v.scan_holders) scan_tok = __builtin_amdgcn_readfirstlane(row_tok);
+    }
     const uint64_t t_start = wall_clock64();
     uint64_t hs_at = kHandoffTicks;  // when the hand-off word is (next) read
     while (true) {
@@ -850,7 +875,7 @@ __global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
             // the row's hand-off word some microseconds in (the registration is
             // done within the launch's first microseconds), then the token's
             // holder word; the clock is read on every 8th pass
-            if (v.table && !occ_read && (++iter & 7u) == 0u) {
+            if (v.table && !v.scan_holders && !occ_read && (++iter & 7u) == 0u) {
                 const uint64_t dt = wall_clock64() - t_start;
                 if (!hs_read && dt > hs_at) {
                     hs = ld_agent((const int32_t *)&v.handoff[row]);
@@ -931,7 +956,13 @@ __global__ __launch_bounds__(1024) void k_topk_mw(TopkArgs a, VerifyArgs v) {
     }
     int handoff_seen = 0, occ_val = 0;
     if constexpr (ACCEPT) {
-        if (v.table) {
+        if (v.scan_holders) {
+            // the last holder: no later row of the launch holds the row's token
+            bool hit = false;
+#pragma unroll
+            for (int i = 0; i < kScanRegs; ++i) hit |= later_tok[i] == scan_tok;
+            occ_val = (scan_tok >= 0 && scan_tok < V && !ballot(hit)) ? 1 : 0;
+        } else if (v.table) {
             if (!hs_read) hs = ld_agent((const int32_t *)&v.handoff[row]);
             handoff_seen = __builtin_amdgcn_readfirstlane(hs);
             if (handoff_seen == 1 && row_tok >= 0 && row_tok < V) {
@@ -1597,9 +1628,10 @@ void launch_topk(const TopkPlan &p, int dtype, const void *logits, int k, int32_
         v.done = (int32_t *)((char *)ws + p.off_counters);
         v.last_occ = (int32_t *)((char *)ws + p.off_occ);
         v.handoff = (uint32_t *)(v.last_occ + p.V + 1);
+        v.scan_holders = (v.table && scans_holders(p)) ? 1 : 0;
         if (v.update_only) {
             v.B = 0;
-            v.ncoord = 1;  // the registration
+            v.ncoord = v.scan_holders ? 0 : 1;  // the registration, unless the rows scan
         } else {
             v.B = (int)(p.n_rows / (v.T1 > 0 ? v.T1 : 1));
             v.ncoord = coord_groups(p, v.B);

@@ -402,7 +402,7 @@ int graft_stream_read(const void *data, int64_t n_rows, int64_t row_bytes, uint3
 
 /* Launch plan of the top-k launch of graft_verify_accept / graft_verify_update
  * (T1 = rows per request, n_rows = B * T1) or of graft_update_topk with logits
- * (T1 = 0: no requests, one registration workgroup); host only, nothing is
+ * (T1 = 0: no requests; one registration workgroup unless holder_scan); host only, nothing is
  * enqueued.  A verify launch puts its coordinator workgroups (one wavefront
  * per request, at most GRAFT_MAX_COORD_GROUPS workgroups; each wavefront then
  * watches several requests in turn) ahead of the rows.  They wait for rows
@@ -421,6 +421,9 @@ typedef struct graft_plan {
     int32_t merge_wave;       /* 1: one wavefront of each row's workgroup merges, the others stream */
     int32_t launch_counters;  /* 1: the rows' completion words carry the workspace's per-row launch
                                  counters (verify launches of at most 16384 rows) */
+    int32_t holder_scan;      /* 1: with the fused matrix update, each row finds whether it is its
+                                 token's last holder by reading the later rows' tokens, with no
+                                 registration workgroup (merge-wave launches of at most 1025 rows) */
 } graft_plan;
 int graft_launch_plan(int64_t n_rows, int V, int dtype, int T1, graft_plan *out);
 

@@ -838,6 +838,62 @@ def test_verify_update_matches_oracle_with_collisions():
         lg = _t(rows.view(np.int16)).view(torch.bfloat16)
 
 
+@pytest.mark.parametrize("kind,B,T1", [("verify", 16, 61), ("verify", 25, 41), ("ingest", 1, 0)],
+                         ids=["verify_976", "verify_1025", "ingest_1024"])
+def test_holder_scan_collisions(kind, B, T1):
+    """Merge-wave launches of at most 1025 rows find each token's last holder by
+    comparing its token with the later rows' tokens (no registration workgroup;
+    at 1025 rows the first row reads all 1024 later ones): with the rows' tokens
+    drawn from 37 values (many holders per token), some rows empty (-1) and two
+    calls in a row, the matrix and every output match the oracle's sequential
+    overwrite."""
+    rng = np.random.default_rng(37 + B)
+    V, k = 30011, 8
+    n = B * T1 if kind == "verify" else 1024
+    plan = L.graft_launch_plan(n, V, L.DTYPE_BF16, T1)
+    assert plan["merge_wave"] == 1 and plan["holder_scan"] == 1
+    vals = rng.choice(V, size=37, replace=False).astype(np.int32)
+    table0 = rng.integers(0, V, size=(V, k)).astype(np.int32)
+    tb = _t(table0, torch.int32)
+    want_tab = table0.copy()
+    wsb = L.graft_workspace_bytes(n, V, k, L.DTYPE_BF16)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    for call in range(2):
+        tok = vals[rng.integers(0, len(vals), size=n)]
+        tok[rng.random(n) < 0.05] = -1
+        if kind == "verify":
+            tok = tok.reshape(B, T1)
+            tok[:, 0] = vals[0]                  # every root holds one token
+            _, par, dep = _random_flat_trees(rng, B, T1, V)
+        rows = _bf16(rng.standard_normal((n, V)).astype(np.float32))
+        lg = _t(rows.view(np.int16)).view(torch.bfloat16)
+        t_ = _t(tok.reshape(-1), torch.int32)
+        tk = torch.zeros(n, k, **i32)
+        print("%s holder scan: %d rows, call %d" % (kind, n, call), flush=True)
+        want_tk = O.topk(rows, k, "bf16")
+        if kind == "verify":
+            al, bo = torch.zeros(B, **i32), torch.zeros(B, **i32)
+            ai = torch.zeros(B, T1 - 1, **i32)
+            p_, d_ = _t(par, torch.int32), _t(dep, torch.int32)
+            L.graft_verify_update(B, T1, V, k, L.DTYPE_BF16, lg.data_ptr(), t_.data_ptr(), p_.data_ptr(),
+                                  d_.data_ptr(), tb.data_ptr(), None, tk.data_ptr(), None, None, al.data_ptr(),
+                                  ai.data_ptr(), T1 - 1, bo.data_ptr(), None, ws.data_ptr(), wsb, _s())
+            torch.cuda.synchronize()
+            acc = O.accept(tok, par, want_tk.reshape(B, T1, k)[:, :, 0], T1 - 1)
+            np.testing.assert_array_equal(al.cpu().numpy(), acc["accept_len"])
+            np.testing.assert_array_equal(ai.cpu().numpy(), acc["accept_idx"])
+            np.testing.assert_array_equal(bo.cpu().numpy(), acc["bonus"])
+        else:
+            L.graft_update_topk(n, V, k, L.DTYPE_BF16, lg.data_ptr(), None, None, t_.data_ptr(), tb.data_ptr(),
+                                None, tk.data_ptr(), ws.data_ptr(), wsb, _s())
+            torch.cuda.synchronize()
+        O.update(want_tab, tok.reshape(-1), want_tk)
+        np.testing.assert_array_equal(tk.cpu().numpy(), want_tk)
+        np.testing.assert_array_equal(tb.cpu().numpy(), want_tab)
+        assert not ws[L.GRAFT_WS_COUNTER_BYTES:].any().item()
+
+
 def _chain_batch(rng, B, T1, V):
     """Chain trees whose first p_b candidates carry the target's bumped greedy
     token: logits N(0, 1) with +6 at a random column per row."""

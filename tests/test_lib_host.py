@@ -275,8 +275,16 @@ def test_coordinators_are_bounded_whatever_the_batch():
     # the case found by reading the old code: 8192 one-wavefront coordinators
     p = L.graft_launch_plan(8192 * 17, 16000, bf, 17)
     assert p["waves_per_group"] <= 2 and p["coord_groups"] == L.GRAFT_MAX_COORD_GROUPS
-    # the prompt ingest has no requests: one registration workgroup
-    assert L.graft_launch_plan(2048, 151936, bf, 0)["coord_groups"] == 1
+    # the prompt ingest has no requests: an update-only launch needs a registration
+    # workgroup unless its rows find their token's last holder themselves (merge-wave
+    # rows, at most 1025 of them: 16 x 64 later rows held in registers)
+    q = L.graft_launch_plan(2048, 151936, bf, 0)
+    assert q["merge_wave"] == 1 and q["holder_scan"] == 0 and q["coord_groups"] == 1
+    q = L.graft_launch_plan(1024, 151936, bf, 0)
+    assert q["merge_wave"] == 1 and q["holder_scan"] == 1 and q["coord_groups"] == 0
+    assert L.graft_launch_plan(1025, 151936, bf, 1)["holder_scan"] == 1
+    assert L.graft_launch_plan(1026, 151936, bf, 1)["holder_scan"] == 0
+    assert L.graft_launch_plan(16 * 17, 151936, bf, 17)["holder_scan"] == 0      # rows cut into slices
     assert L.graft_launch_plan(0, 151936, bf, 0)["workgroups"] == 0
     # the metric shape keeps one coordinator wavefront per request
     p = L.graft_launch_plan(16 * 61, 151936, bf, 61)
