@@ -14,8 +14,11 @@
 //   filtered.  A wave-uniform threshold -- the key of the wave's current
 //   8th-best value -- filters each 16-byte group with a few packed integer
 //   ops; the rare groups that pass are compacted into LDS with a ballot and
-//   merged into the wave's exact top-8 (DPP wave maxima) when 64 are pending.
+//   merged into the wave's exact top-8 when 64 are pending (their elements
+//   below the threshold dropped; a few inserted one by one, more by DPP wave
+//   maxima).
 // Epilogue: the S waves meet at one barrier; wave 0 ranks their candidates
+//   by counting over LDS broadcasts
 //   (and combines their softmax statistics) into the row's top-k; with G > 1
 //   the row's last slice to arrive merges the slices' results.  The row then
 //   publishes its greedy token in a completion word, which coordinator
@@ -252,6 +255,47 @@ __device__ __forceinline__ uint64_t insert_top8(const uint64_t (&c)[N], uint64_t
         }
     }
     return kth;
+}
+
+// insert_top8 for the 32-bit wave-local ranks of bf16 rows.
+template <int N>
+__device__ __forceinline__ uint32_t insert_top8_u32(const uint32_t (&c)[N], uint32_t &top, uint32_t kth) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        uint64_t bal = ballot(c[e] > kth);
+        while (bal) {
+            const int src = __ffsll((unsigned long long)bal) - 1;
+            bal &= bal - 1ull;
+            const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)c[e], src);
+            if (x <= kth) continue;
+            const int pos = __popcll(ballot(lane < kTop && top > x));
+            const uint32_t left = (uint32_t)__builtin_amdgcn_update_dpp((int)top, (int)top, 0x111, 0xf, 0xf, false);
+            if (lane < kTop && lane > pos) top = left;
+            if (lane == pos) top = x;
+            kth = (uint32_t)__builtin_amdgcn_readlane((int)top, kTop - 1);
+        }
+    }
+    return kth;
+}
+
+// A row wave's pending candidates c (0 = none, else above kth) into its top-8:
+// up to kPendingInsert live ones are inserted one by one, up to a wavefront's
+// worth are compacted, more take the full merge.  Returns the new 8th best.
+constexpr int kPendingInsert = 8;
+template <typename Rank, int N>
+__device__ __forceinline__ Rank merge_pending(Rank (&c)[N], Rank &top, Rank kth, Rank *scratch) {
+    int total = 0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) total += __popcll(ballot(c[e] != 0));
+    if (total == 0) return kth;
+    if (total <= kPendingInsert) {
+        if constexpr (sizeof(Rank) == 4)
+            return insert_top8_u32<N>(c, top, kth);
+        else
+            return insert_top8<N>(c, top, kth);
+    }
+    return merge_top8_compact<Rank, N>(c, top, scratch);
 }
 
 // Per-lane online softmax statistics: running maximum m and sum of exp(x - m).
@@ -1007,11 +1051,11 @@ struct RowSmem {
     static constexpr size_t kGidx = sizeof(uint16_t) * kCap;   // pending group indices
     static constexpr size_t kPerWave = kData + kMerge + kGidx;
     // row tail: the waves' top-8 (S*kTop u64, at least one wavefront's worth), the
-    // row's top-8 (u64), per-wave 8th best keys (int), softmax statistics (float2)
+    // row's top-8 (u64), softmax statistics (float2)
     __host__ __device__ static size_t cand_entries(int S) { return (size_t)(S * kTop > kWave ? S * kTop : kWave); }
     static size_t bytes(int S) {
         return (size_t)S * kPerWave + (cand_entries(S) + kTop) * sizeof(uint64_t) +
-               (size_t)S * (sizeof(int) + sizeof(float2)) + 16;
+               (size_t)S * sizeof(float2) + 16;
     }
 };
 
@@ -1048,7 +1092,6 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     uint64_t *s_cand = (uint64_t *)(smem + (size_t)S * SM::kPerWave);
     uint64_t *s_top = s_cand + SM::cand_entries(S);
     float2 *s_stat = (float2 *)(s_top + kTop);
-    int *s_kth = (int *)(s_stat + S);
 
     const int V = a.V;
     const char *rowp = (const char *)a.logits + (size_t)row * (size_t)V * ESZ;
@@ -1116,24 +1159,25 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
     int count = 0;
     auto set_thr = [&](int t) __attribute__((always_inline)) { thr = __builtin_amdgcn_readfirstlane(t); };
     auto process = [&]() __attribute__((always_inline)) {
+        // candidates: above the 8th best so far and at or above the threshold,
+        // a lower bound of the wave's 8th best key (its seed or an earlier merge)
+        const int tq = thr;
         for (int base = 0; base < count; base += kWave) {
             const int gi = base + lane;
             Rank c[EPG];
-            bool any = false;
             if (gi < count) {
                 const uint4 d = sd[gi];
                 const int goff = kHeadPad + (int)sg[gi] * EPG;
 #pragma unroll
                 for (int e = 0; e < EPG; ++e) {
                     const Rank r = TR::make(TR::elem(d, e), goff + e);
-                    c[e] = r > kth ? r : (Rank)0;
-                    any |= c[e] != 0;
+                    c[e] = (r > kth && TR::rank_key(r) >= tq) ? r : (Rank)0;
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < EPG; ++e) c[e] = 0;
             }
-            if (ballot(any)) kth = merge_top8_compact<Rank, EPG>(c, top, scratch);
+            kth = merge_pending<Rank, EPG>(c, top, kth, scratch);
         }
         count = 0;
         set_thr(kth ? TR::rank_key(kth) : INT_MIN);
@@ -1263,19 +1307,14 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         process();
     }
 
-    // The row's S waves meet: each publishes its exact top-8 (row ranks) and its
-    // 8th best key.  Every wave holds 8 elements at or above its 8th best key, so
-    // the row's 8th best key is at least T = the largest of these; wave 0 keeps
-    // the entries with key >= T (typically a dozen) and picks the 8 best by
-    // counting, for each, the entries that rank above it.  Massive ties at T
-    // (more than one wavefront of entries) take the full merge instead.
+    // The row's S waves meet: each publishes its exact top-8 (row ranks); wave 0
+    // ranks the S x 8 entries by counting, for each, the entries above it.
     constexpr int kScale = sizeof(Rank) == 4 ? 65536 : 1;  // wave key -> fp32 key
     if (lane < kTop) {
         uint64_t r = 0;
         if (top) r = rank64(TR::rank_key(top) * kScale, global_id(TR::local_off(top)));
         s_cand[wv * kTop + lane] = r;
     }
-    if (lane == 0) s_kth[wv] = kth ? TR::rank_key(kth) * kScale : INT_MIN;
     if constexpr (PROB) {
         const float M = wave_max_f32(st.m);
         const float s = (st.m == -INFINITY) ? 0.0f : st.s * __expf(st.m - M);
@@ -1295,59 +1334,31 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         }
     }
     uint64_t rtop = 0;  // lanes 0..7: the row's top-8 (row ranks), descending
-    if (S * kTop <= kWave) {
-        // one entry per lane: its rank is the number of entries above it (row
-        // ranks are distinct, zeros mark empty slots), read as LDS broadcasts
+    {
+        // each entry's rank is the number of entries above it (row ranks are
+        // distinct, zeros mark empty slots), counted over LDS broadcasts; up to
+        // two entries per lane
         const int nent = S * kTop;
-        const uint64_t x = lane < nent ? s_cand[lane] : 0ull;
-        int above = 0;
-        for (int j = 0; j < nent; ++j) above += s_cand[j] > x ? 1 : 0;
-        if (lane < kTop) s_top[lane] = 0ull;
-        if (x != 0ull && above < kTop) s_top[above] = x;
+        const uint64_t x0 = lane < nent ? s_cand[lane] : 0ull;
+        int a0 = 0, a1 = 0;
+        if (nent <= kWave) {
+            for (int j = 0; j < nent; ++j) a0 += s_cand[j] > x0 ? 1 : 0;
+        } else {
+            const uint64_t x1 = lane + kWave < nent ? s_cand[lane + kWave] : 0ull;
+            for (int j = 0; j < nent; ++j) {
+                const uint64_t y = s_cand[j];
+                a0 += y > x0 ? 1 : 0;
+                a1 += y > x1 ? 1 : 0;
+            }
+            if (lane < kTop) s_top[lane] = 0ull;
+            if (x1 != 0ull && a1 < kTop) s_top[a1] = x1;
+        }
+        if (nent <= kWave && lane < kTop) s_top[lane] = 0ull;
+        if (x0 != 0ull && a0 < kTop) s_top[a0] = x0;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         rtop = lane < kTop ? s_top[lane] : 0ull;
-    } else {
-        int T = INT_MIN;
-        for (int w = 0; w < S; ++w) T = max(T, s_kth[w]);
-        uint64_t c[2];
-        bool keep[2];
-        uint64_t bal[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int j = i * kWave + lane;
-            c[i] = j < S * kTop ? s_cand[j] : 0ull;
-            keep[i] = c[i] != 0ull && rank64_key(c[i]) >= T;
-            bal[i] = ballot(keep[i]);
-        }
-        const int n0 = __popcll(bal[0]);
-        const int ncand = n0 + __popcll(bal[1]);
-        if (ncand <= kWave) {
-            // compact the kept entries to lanes 0..ncand-1 (s_cand is wave 0's now)
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            if (keep[0]) s_cand[lanes_below(bal[0])] = c[0];
-            if (keep[1]) s_cand[n0 + lanes_below(bal[1])] = c[1];
-            if (lane < kTop) s_top[lane] = 0ull;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const uint64_t x = lane < ncand ? s_cand[lane] : 0ull;
-            int above = 0;
-            for (int j = 0; j < ncand; ++j) {
-                const uint32_t lo = (uint32_t)readlane_i32((int)(uint32_t)x, j);
-                const uint32_t hi = (uint32_t)readlane_i32((int)(uint32_t)(x >> 32), j);
-                above += (((uint64_t)hi << 32) | lo) > x ? 1 : 0;
-            }
-            if (lane < ncand && above < kTop) s_top[above] = x;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            rtop = lane < kTop ? s_top[lane] : 0ull;
-        } else {
-            merge_top8<uint64_t, 2>(c, rtop);
-        }
     }
     // the workgroup's softmax statistics (largest value, sum of exp(x - largest))
     float rowM = -INFINITY, rowS = 0.0f;
@@ -1374,6 +1385,12 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
         if (lane == 0) old = __hip_atomic_fetch_add(&a.cnt[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((int)readlane_i32((int)old, 0) != G - 1) return;
         after_count();
+        // the finisher reads the token's holder word now, beside the slices'
+        // results, once its hand-off word has shown the registration (as above)
+        if constexpr (ACCEPT) {
+            if (v.table && lane == 0 && handoff_seen == 1 && row_tok >= 0 && row_tok < a.V)
+                occ_read = ld_agent(&v.last_occ[row_tok]);
+        }
         const int n = G * kTop;  // <= 64: one entry per lane
         const bool own = lane >= g * kTop && lane < (g + 1) * kTop;
         const bool other = lane < n && !own;
@@ -1393,12 +1410,13 @@ __global__ __launch_bounds__(kWave *kMaxWavesPerRow) void k_topk_rows(TopkArgs a
             }
         }
         if (x == kEmptyRank) x = 0ull;
+        // rank over LDS broadcasts (the row's candidate area is this wave's now)
+        if (lane < n) s_cand[lane] = x;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         int above = 0;
-        for (int j = 0; j < n; ++j) {
-            const uint32_t lo = (uint32_t)readlane_i32((int)(uint32_t)x, j);
-            const uint32_t hi = (uint32_t)readlane_i32((int)(uint32_t)(x >> 32), j);
-            above += (((uint64_t)hi << 32) | lo) > x ? 1 : 0;
-        }
+        for (int j = 0; j < n; ++j) above += s_cand[j] > x ? 1 : 0;
         if (lane < kTop) s_top[lane] = 0ull;
         if (x != 0ull && above < kTop) s_top[above] = x;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1516,10 +1534,11 @@ constexpr int64_t kSplitTargetWaves = 1920;
 
 // Blocks per batch (measured): four for one workgroup per row (a 2048-row
 // ingest chunk: 109 -> 101 us; 976 rows at 3 waves per row: see kTargetWaves)
-// and for split rows whose waves stream at least 8 blocks each (TAIL 272 rows:
-// 26.1 -> 23.9 us; 244 rows: 1.8 us off the step); two for split rows with only
-// a few blocks per wave (61 rows: 3.4 us slower with four at V=32000 fp32).
-constexpr int64_t kDeepBatchMinBlocks = 8;
+// and for split rows whose waves stream at least 6 blocks each (TAIL 272 rows:
+// 26.1 -> 23.9 us; 244 rows: 1.8 us off the step; 61 rows of 128256 bf16, ~7.8
+// blocks per wave: 11.27 -> 10.98 us); two for split rows with only a few
+// blocks per wave (61 rows: 3.4 us slower with four at V=32000 fp32).
+constexpr int64_t kDeepBatchMinBlocks = 6;
 static int loads_for(int64_t n_rows, int V, int dtype, int groups, int S) {
     if (n_rows >= kSplitBelowRows) return 4;
     const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
@@ -1588,6 +1607,14 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     // 48.31 us with four; 2 or 4 streaming waves with two blocks, 57.1 and 48.6
     // us); more rows keep four (2048-row prompt chunk: 98.0 us against 108.7)
     if (p.merge_wave && n_rows < kMwDeepBatchRows) p.loads = 2;
+    // four blocks per batch only where that workgroup's LDS stays within the cap
+    // (the 244-row launch's 12 waves take two: 71 KB with four; with a 160 KB
+    // cap four measured no faster there)
+    if (p.loads == 4 && !p.merge_wave) {
+        const size_t lds4 = dtype == GRAFT_DTYPE_BF16 ? RowSmem<uint32_t, 4>::bytes(p.splits)
+                                                      : RowSmem<uint64_t, 4>::bytes(p.splits);
+        if (lds4 > (size_t)kMaxLdsPerGroup) p.loads = 2;
+    }
     // workspace: [tagged completion words [kTagRows], launch counters [kTagRows] |
     //             completion words [n_rows] | last holder per token [V], spare,
     //             hand-offs [n_rows]]

@@ -291,6 +291,14 @@ def test_coordinators_are_bounded_whatever_the_batch():
     assert (p["waves_per_group"], p["groups_per_row"], p["blocks_per_batch"], p["coord_groups"]) == (4, 1, 2, 4)
     # ... with a merge wavefront per row and the per-row launch counters
     assert (p["merge_wave"], p["launch_counters"]) == (1, 1)
+    # few-row launches: 61 rows cut into 4 slices of 8 waves, four blocks per
+    # batch from 6 blocks per wave (128256 bf16: ~7.8), two below (32000 fp32:
+    # ~3.9); 244 rows whole, 12 waves each; TAIL rows in 4 slices of 2 waves
+    shape = lambda q: (q["waves_per_group"], q["groups_per_row"], q["blocks_per_batch"], q["merge_wave"])
+    assert shape(L.graft_launch_plan(61, 128256, bf, 61)) == (8, 4, 4, 0)
+    assert shape(L.graft_launch_plan(61, 32000, L.DTYPE_F32, 61)) == (8, 4, 2, 0)
+    assert shape(L.graft_launch_plan(4 * 61, 151936, bf, 61)) == (12, 1, 2, 0)   # four would need 71 KB of LDS
+    assert shape(L.graft_launch_plan(16 * 17, 151936, bf, 17)) == (2, 4, 4, 0)
     # the counters cover verify launches of up to 16384 rows (rows cut into slices
     # too); an update-only launch has no completion words
     n_ctr = L.GRAFT_WS_COUNTER_BYTES // 12
