@@ -219,6 +219,52 @@ __device__ __forceinline__ Rank merge_top8_compact(Rank (&c)[N], Rank &top, Rank
     return kth;
 }
 
+// Same result as merge_top8, by counting: the live candidates and the current
+// top-8 are compacted into the wave's LDS scratch (64 entries), each counts the
+// entries above it over LDS broadcasts (ranks are distinct), and the 8 best are
+// written to scratch[0..7] at their rank and read back.  A wave's LDS accesses
+// complete in order, so the scratch is rewritten only after every read.
+template <typename Rank, int N>
+__device__ __forceinline__ Rank merge_top8_count(Rank (&c)[N], Rank &top, Rank *scratch) {
+    const int lane = lane_id();
+    uint64_t bal[N];
+    int total = 0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        bal[e] = ballot(c[e] != 0);
+        total += __popcll(bal[e]);
+    }
+    if (total + kTop > kWave) return merge_top8<Rank, N>(c, top);
+    int base = 0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        if (c[e] != 0) scratch[base + lanes_below(bal[e])] = c[e];
+        base += __popcll(bal[e]);
+    }
+    if (lane < kTop) scratch[total + lane] = top;
+    const int n = total + kTop;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const Rank x = lane < n ? scratch[lane] : (Rank)0;
+    int above = 0;
+    for (int j = 0; j < n; ++j) above += scratch[j] > x ? 1 : 0;
+    if (lane < kTop) scratch[lane] = 0;
+    if (x != 0 && above < kTop) scratch[above] = x;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    top = lane < kTop ? scratch[lane] : (Rank)0;
+    __builtin_amdgcn_wave_barrier();
+    if constexpr (sizeof(Rank) == 4) {
+        return (Rank)__builtin_amdgcn_readlane((int)top, kTop - 1);
+    } else {
+        const uint32_t kl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, kTop - 1);
+        const uint32_t kh = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(top >> 32), kTop - 1);
+        return ((uint64_t)kh << 32) | kl;
+    }
+}
+
 // Few candidates: insert them one by one into the top-8 held in lanes 0..7
 // (row ranks, descending, zero = empty).  A candidate's place is the number of
 // entries above it (one ballot); the entries below it move down one lane (a
@@ -281,7 +327,8 @@ __device__ __forceinline__ uint32_t insert_top8_u32(const uint32_t (&c)[N], uint
 
 // A row wave's pending candidates c (0 = none, else above kth) into its top-8:
 // up to kPendingInsert live ones are inserted one by one, up to a wavefront's
-// worth are compacted, more take the full merge.  Returns the new 8th best.
+// worth are compacted and ranked, more take the full merge.  Returns the new
+// 8th best.
 constexpr int kPendingInsert = 8;
 template <typename Rank, int N>
 __device__ __forceinline__ Rank merge_pending(Rank (&c)[N], Rank &top, Rank kth, Rank *scratch) {
@@ -295,7 +342,13 @@ __device__ __forceinline__ Rank merge_pending(Rank (&c)[N], Rank &top, Rank kth,
         else
             return insert_top8<N>(c, top, kth);
     }
-    return merge_top8_compact<Rank, N>(c, top, scratch);
+    // 64-bit ranks (fp32 rows) rank faster by counting than by eight 64-bit DPP
+    // wave maxima (61 rows of 32000 fp32: 10.22 -> 9.37 us); for 32-bit ranks
+    // the two measured alike
+    if constexpr (sizeof(Rank) == 8)
+        return merge_top8_count<Rank, N>(c, top, scratch);
+    else
+        return merge_top8_compact<Rank, N>(c, top, scratch);
 }
 
 // Per-lane online softmax statistics: running maximum m and sum of exp(x - m).
