@@ -42,7 +42,13 @@ SHAPES = {
     ("k_topk_mw<Bf16, true, true, 4>", 980, 256): "verify with row statistics (coverage leg)",
     ("k_topk_rows<Bf16, false, true, true, true, 4>", 1096, 128): "TAIL verify, 272 rows in 4 slices",
     ("k_topk_mw<Bf16, false, true, 4>", 2049, 256): "ingest chunk, 2048 rows, update fused",
-    ("k_topk_rows<Bf16, false, true, true, true, 4>", 245, 512): "one request, 61 rows in 4 slices",
+    ("k_topk_rows<Bf16, false, true, true, true, 4>", 245, 512):
+        "61 rows in 4 slices: B=1, V=128256 verify; one request's rows at V=151936",
+    ("k_topk_rows<Bf16, false, true, true, false, 2>", 245, 768): "B=4 decode verify, 244 rows x 151936, 12 waves each",
+    ("k_topk_rows<F32, false, true, true, true, 2>", 245, 512): "B=1, V=32000 fp32 verify, 61 rows in 4 slices",
+    ("k_build_tree", 16, 128): "build, B=16 (the timed step's launch)",
+    ("k_build_tree", 4, 128): "build, B=4",
+    ("k_build_tree", 1, 128): "build, B=1",
     ("k_stream_read", 976, 256): "read ceiling of the verify launch's rows (graft_stream_read)",
 }
 
