@@ -104,6 +104,24 @@ def test_topk_f32_parity(V, k):
     assert (got == want).all(), np.nonzero((got != want).any(1))[0]
 
 
+@pytest.mark.parametrize("n,V", [(61, 32000), (61, 128256), (244, 4097), (1100, 1003)])
+def test_topk_f32_adversarial(n, V):
+    """fp32 rows whose groups all pass the filter (ascending, all equal), heavy
+    ties and negative-only rows, on split launches (61 rows: the one-by-one
+    inserts, the count over LDS and the full merge of a wave's pending groups)
+    and unsplit ones."""
+    rng = np.random.default_rng(n + V)
+    z = rng.standard_normal((n, V)).astype(np.float32)
+    asc = np.tile(np.linspace(-3, 3, V, dtype=np.float32), (n, 1))
+    suite = {"normal": z, "quantised_ties": np.round(z * 2) / 2, "all_equal": np.ones((n, V), np.float32),
+             "negative_only": -np.abs(z) - 0.25, "ascending": asc, "descending": asc[:, ::-1].copy(),
+             "few_values": rng.integers(-3, 4, size=(n, V)).astype(np.float32)}
+    for name, rows in suite.items():
+        got = gpu_topk(rows, 8, "f32")
+        want = O.topk(rows, 8, "f32")
+        assert (got == want).all(), (name, n, V, np.nonzero((got != want).any(1))[0][:5])
+
+
 def test_topk_prob_parity():
     rng = np.random.default_rng(3)
     V = 151936
