@@ -1605,6 +1605,7 @@ static int loads_for(int64_t n_rows, int V, int dtype, int groups, int S) {
 // us off the step; 272 rows whole (16 CUs with two rows, finishing last) cost
 // 2.8 us, so they stay split.
 constexpr int64_t kCUs = 256;
+constexpr int kFewRowWaves = 8;
 static int groups_per_row(int64_t n_rows, int V, int dtype) {
     if (n_rows <= 0 || n_rows >= kSplitBelowRows) return 1;
     if (n_rows <= kCUs && (kTargetWaves + n_rows - 1) / n_rows <= kMaxWavesPerRow) return 1;
@@ -1653,6 +1654,16 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     p.dtype = dtype;
     p.groups = groups_per_row(n_rows, V, dtype);
     p.splits = waves_per_row(n_rows, V, dtype, p.groups > 1 ? kSplitTargetWaves : kTargetWaves, p.groups);
+    // whole rows at one workgroup per CU (183-256 rows) stream best with 8 waves
+    // of four blocks per batch (244 rows x 151936 bf16: 17.7 us against 18.8 with
+    // 12 waves of two, 18.1 with 6 and 18.9 with 10 of four; 183 rows: 16.2
+    // against 18.3 us), where 8 waves keep within the per-wave block cap
+    if (p.groups == 1 && n_rows <= kCUs && p.splits > kFewRowWaves) {
+        const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
+        const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
+        const int64_t per_wave = dtype == GRAFT_DTYPE_BF16 ? 127 : 1023;
+        if ((nblk + kFewRowWaves - 1) / kFewRowWaves <= per_wave) p.splits = kFewRowWaves;
+    }
     p.loads = loads_for(n_rows, V, dtype, p.groups, p.splits);
     p.merge_wave = merge_wave_for(V, dtype, p.groups, p.splits);
     // streaming waves that never stop to merge do best with two blocks per batch

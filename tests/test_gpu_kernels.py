@@ -154,14 +154,14 @@ def test_topk_prompt_sized_launch(dtype):
 
 
 # launch plans on both sides of their thresholds: split below 512 rows (at most
-# 4 slices) unless 183-256 rows fill the CUs one workgroup each, four blocks per
-# batch for unsplit launches and for split rows whose waves stream 8 or more
-# blocks, two otherwise or when four exceed the LDS
+# 4 slices) unless 183-256 rows fill the CUs one workgroup each (8 waves), four
+# blocks per batch for unsplit launches and for split rows whose waves stream 6
+# or more blocks, two otherwise or when four exceed the LDS
 @pytest.mark.parametrize("n,V,dtype,prob", [
     (511, 40000, "bf16", False),    # split into 3 slices, 13 blocks per wave: four
     (512, 40000, "bf16", True),     # one workgroup per row, 6 waves: four, with probabilities
     (300, 20000, "bf16", False),    # split, 5 blocks per wave: two
-    (200, 30000, "bf16", True),     # whole rows, one workgroup per CU, 15 waves of 4 blocks: two
+    (200, 30000, "bf16", True),     # whole rows, one workgroup per CU, 8 waves of ~7 blocks: four
     (100, 151936, "f32", True),     # split fp32, 30 blocks per wave: four, with probabilities
     (2000, 3000, "f32", False),     # unsplit, short rows
     (700, 9, "bf16", False),        # a row shorter than one block

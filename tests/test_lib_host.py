@@ -293,11 +293,13 @@ def test_coordinators_are_bounded_whatever_the_batch():
     assert (p["merge_wave"], p["launch_counters"]) == (1, 1)
     # few-row launches: 61 rows cut into 4 slices of 8 waves, four blocks per
     # batch from 6 blocks per wave (128256 bf16: ~7.8), two below (32000 fp32:
-    # ~3.9); 244 rows whole, 12 waves each; TAIL rows in 4 slices of 2 waves
+    # ~3.9); 183-256 rows whole, 8 waves each; TAIL rows in 4 slices of 2 waves
     shape = lambda q: (q["waves_per_group"], q["groups_per_row"], q["blocks_per_batch"], q["merge_wave"])
     assert shape(L.graft_launch_plan(61, 128256, bf, 61)) == (8, 4, 4, 0)
     assert shape(L.graft_launch_plan(61, 32000, L.DTYPE_F32, 61)) == (8, 4, 2, 0)
-    assert shape(L.graft_launch_plan(4 * 61, 151936, bf, 61)) == (12, 1, 2, 0)   # four would need 71 KB of LDS
+    assert shape(L.graft_launch_plan(4 * 61, 151936, bf, 61)) == (8, 1, 4, 0)
+    assert shape(L.graft_launch_plan(183, 151936, bf, 61)) == (8, 1, 4, 0)
+    assert shape(L.graft_launch_plan(256, 10 ** 6, bf, 0)) == (16, 1, 2, 0)   # 8 waves would exceed 127 blocks each
     assert shape(L.graft_launch_plan(16 * 17, 151936, bf, 17)) == (2, 4, 4, 0)
     # the counters cover verify launches of up to 16384 rows (rows cut into slices
     # too); an update-only launch has no completion words
