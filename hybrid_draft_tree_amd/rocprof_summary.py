@@ -44,7 +44,7 @@ SHAPES = {
     ("k_topk_mw<Bf16, false, true, 4>", 2049, 256): "ingest chunk, 2048 rows, update fused",
     ("k_topk_rows<Bf16, false, true, true, true, 4>", 245, 512):
         "61 rows in 4 slices: B=1, V=128256 verify; one request's rows at V=151936",
-    ("k_topk_rows<Bf16, false, true, true, false, 2>", 245, 768): "B=4 decode verify, 244 rows x 151936, 12 waves each",
+    ("k_topk_rows<Bf16, false, true, true, false, 4>", 245, 512): "B=4 decode verify, 244 rows x 151936, 8 waves each",
     ("k_topk_rows<F32, false, true, true, true, 2>", 245, 512): "B=1, V=32000 fp32 verify, 61 rows in 4 slices",
     ("k_build_tree", 16, 128): "build, B=16 (the timed step's launch)",
     ("k_build_tree", 4, 128): "build, B=4",
