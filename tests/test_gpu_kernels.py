@@ -163,6 +163,7 @@ def test_topk_prompt_sized_launch(dtype):
     (300, 20000, "bf16", False),    # split, 5 blocks per wave: two
     (200, 30000, "bf16", True),     # whole rows, one workgroup per CU, 8 waves of ~7 blocks: four
     (100, 151936, "f32", True),     # split fp32, 30 blocks per wave: four, with probabilities
+    (244, 40000, "f32", True),      # whole fp32 rows, one workgroup per CU, 8 waves of ~20 blocks: four
     (2000, 3000, "f32", False),     # unsplit, short rows
     (700, 9, "bf16", False),        # a row shorter than one block
     (5, 151936, "bf16", False),     # split, 16 waves per slice: two
