@@ -315,3 +315,29 @@ def test_coordinators_are_bounded_whatever_the_batch():
     assert L.graft_workspace_bytes(1, 100, 8, bf) > L.GRAFT_WS_COUNTER_BYTES
     with pytest.raises(L.GraftError):
         L.graft_launch_plan(100, 1000, bf, 61)   # T1 does not divide the rows
+
+
+def test_launch_plans_keep_the_per_wave_block_cap():
+    """Over many shapes, every plan keeps each wavefront of a row (or slice) within
+    the blocks its local offsets can address (bf16: 127 blocks of 512 elements;
+    fp32: 1023 blocks of 256 — past that, wave-local ranks would collide), uses
+    the merge wavefront only for whole rows of at most 4 streaming waves, and
+    never more than 16 wavefronts per workgroup."""
+    rng = np.random.default_rng(11)
+    shapes = [(n, V) for n in (1, 5, 61, 100, 182, 183, 244, 256, 272, 300, 488, 511, 512, 976, 1024, 1600, 2048,
+                               4096, 16384) for V in (9, 1001, 4097, 16000, 32000, 128256, 151936, 999_999)]
+    shapes += [(int(rng.integers(1, 20000)), int(rng.integers(8, 1_000_001))) for _ in range(300)]
+    for n, V in shapes:
+        for dt, epg, cap in ((L.DTYPE_BF16, 8, 127), (L.DTYPE_F32, 4, 1023)):
+            if L.graft_workspace_bytes(n, V, min(8, V), dt) == 0:
+                continue
+            p = L.graft_launch_plan(n, V, dt, 0)
+            S = p["waves_per_group"] - p["merge_wave"]
+            G = p["groups_per_row"]
+            assert 1 <= S and p["waves_per_group"] <= 16, (n, V, dt, p)
+            assert p["blocks_per_batch"] in (2, 4)
+            if p["merge_wave"]:
+                assert G == 1 and S <= 4, (n, V, dt, p)
+            nblk = -(-(-(-V // epg)) // 64)          # 1 KB blocks of a row, at most
+            per_wave = -(-(-(-nblk // G)) // S)      # blocks of one wavefront, at most
+            assert per_wave <= cap, (n, V, dt, p, per_wave)
