@@ -24,10 +24,14 @@ pytestmark = pytest.mark.gpu
 STATE = ("table", "roots", "base_pos", "stage", "n_keep", "tok", "parent", "depth", "pos_id", "anc", "topk",
          "accept_len", "accept_idx")
 
-# (workload, vocabulary): the B=16 tree step takes the merge-wave plan with
-# launch counters and the holder scan; the TAIL step (272 rows) takes split
-# rows with launch counters and the registration hand-off.
-CASES = [(3, 30011, (1, 1, 1)), (5, 30011, (0, 1, 0))]
+# (workload, vocabulary, extra settings, expected plan): the B=16 tree step
+# takes the merge-wave plan with launch counters and the holder scan; the TAIL
+# step (272 rows) and the B=1 step (61 rows cut into 4 slices of 8 waves) split
+# rows with launch counters and the registration hand-off; the B=4 decode step
+# (244 whole rows of 8 waves, after a shortened prompt ingest) whole rows with
+# the registration hand-off.
+CASES = [(3, 30011, {}, (1, 1, 1)), (5, 30011, {}, (0, 1, 0)), (2, 128256, {}, (0, 1, 0)),
+         (4, 151936, {"prompt_len": 4096}, (0, 1, 0))]
 
 
 def _state(pipe):
@@ -45,9 +49,9 @@ def _steps(pipe, drafts, logits, order):
         pipe.verify_update_device(logits[i])
 
 
-@pytest.mark.parametrize("cfg_id,V,plan", CASES, ids=["tree_b16", "tail_b16"])
-def test_graph_replay_matches_eager(cfg_id, V, plan):
-    cfg = WORKLOADS[cfg_id].scaled(V=V, noise_pool_rows=16)
+@pytest.mark.parametrize("cfg_id,V,extra,plan", CASES, ids=["tree_b16", "tail_b16", "tree_b1", "decode_b4"])
+def test_graph_replay_matches_eager(cfg_id, V, extra, plan):
+    cfg = WORKLOADS[cfg_id].scaled(V=V, noise_pool_rows=16, **extra)
     dev = torch.device("cuda", 0)
     P = 3
     pipe_g, drafts_g, logits_g, acc_g = bench.setup_pool(cfg, P, dev, torch)
