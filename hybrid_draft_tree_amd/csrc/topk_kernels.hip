@@ -1606,6 +1606,7 @@ static int loads_for(int64_t n_rows, int V, int dtype, int groups, int S) {
 // 2.8 us, so they stay split.
 constexpr int64_t kCUs = 256;
 constexpr int kFewRowWaves = 8;
+constexpr int64_t kTwoRowsMin = 436;  // about 0.85 x two rows on every CU
 static int groups_per_row(int64_t n_rows, int V, int dtype) {
     if (n_rows <= 0 || n_rows >= kSplitBelowRows) return 1;
     if (n_rows <= kCUs && (kTargetWaves + n_rows - 1) / n_rows <= kMaxWavesPerRow) return 1;
@@ -1657,12 +1658,21 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
     // whole rows at one workgroup per CU (183-256 rows) stream best with 8 waves
     // of four blocks per batch (244 rows x 151936 bf16: 17.7 us against 18.8 with
     // 12 waves of two, 18.1 with 6 and 18.9 with 10 of four; 183 rows: 16.2
-    // against 18.3 us), where 8 waves keep within the per-wave block cap
-    if (p.groups == 1 && n_rows <= kCUs && p.splits > kFewRowWaves) {
+    // against 18.3 us), and so do whole rows at two workgroups on nearly every CU
+    // (436-511 rows; 448 rows: 27.7 against 29.3 us in slices, 476: 28.9 against
+    // 30.1, 488: 29.4 against 30.4; at 427 rows the two tie and below that the
+    // CUs holding a second row finish last: 305 rows 24.5 against 22.6 us),
+    // where 8 waves keep within the per-wave block cap
+    {
         const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
         const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
         const int64_t per_wave = dtype == GRAFT_DTYPE_BF16 ? 127 : 1023;
-        if ((nblk + kFewRowWaves - 1) / kFewRowWaves <= per_wave) p.splits = kFewRowWaves;
+        const bool fits = (nblk + kFewRowWaves - 1) / kFewRowWaves <= per_wave;
+        if (fits && p.groups == 1 && n_rows <= kCUs && p.splits > kFewRowWaves) p.splits = kFewRowWaves;
+        if (fits && p.groups > 1 && n_rows >= kTwoRowsMin && n_rows < kSplitBelowRows) {
+            p.groups = 1;
+            p.splits = kFewRowWaves;
+        }
     }
     p.loads = loads_for(n_rows, V, dtype, p.groups, p.splits);
     p.merge_wave = merge_wave_for(V, dtype, p.groups, p.splits);

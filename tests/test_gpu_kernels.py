@@ -154,11 +154,13 @@ def test_topk_prompt_sized_launch(dtype):
 
 
 # launch plans on both sides of their thresholds: split below 512 rows (at most
-# 4 slices) unless 183-256 rows fill the CUs one workgroup each (8 waves), four
+# 4 slices) unless 183-256 rows fill the CUs one workgroup each or 436-511 rows
+# two workgroups each (8 waves), four
 # blocks per batch for unsplit launches and for split rows whose waves stream 6
 # or more blocks, two otherwise or when four exceed the LDS
 @pytest.mark.parametrize("n,V,dtype,prob", [
-    (511, 40000, "bf16", False),    # split into 3 slices, 13 blocks per wave: four
+    (430, 40000, "bf16", False),    # split into 3 slices, 13 blocks per wave: four
+    (511, 40000, "bf16", False),    # whole rows, two on nearly every CU, 8 waves of ~10 blocks: four
     (512, 40000, "bf16", True),     # one workgroup per row, 6 waves: four, with probabilities
     (300, 20000, "bf16", False),    # split, 5 blocks per wave: two
     (200, 30000, "bf16", True),     # whole rows, one workgroup per CU, 8 waves of ~7 blocks: four

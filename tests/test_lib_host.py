@@ -300,6 +300,11 @@ def test_coordinators_are_bounded_whatever_the_batch():
     assert shape(L.graft_launch_plan(4 * 61, 151936, bf, 61)) == (8, 1, 4, 0)
     assert shape(L.graft_launch_plan(183, 151936, bf, 61)) == (8, 1, 4, 0)
     assert shape(L.graft_launch_plan(244, 40000, L.DTYPE_F32, 0)) == (8, 1, 4, 0)
+    # 436-511 rows: two whole rows on nearly every CU, 8 waves; 427 rows stay in slices
+    assert shape(L.graft_launch_plan(8 * 61, 151936, bf, 61)) == (8, 1, 4, 0)
+    assert shape(L.graft_launch_plan(436, 151936, bf, 0)) == (8, 1, 4, 0)
+    assert shape(L.graft_launch_plan(7 * 61, 151936, bf, 61))[1] > 1
+    assert shape(L.graft_launch_plan(488, 10 ** 6, bf, 0))[1] > 1           # 8 waves would exceed the cap
     assert shape(L.graft_launch_plan(256, 10 ** 6, bf, 0)) == (16, 1, 2, 0)   # 8 waves would exceed 127 blocks each
     assert shape(L.graft_launch_plan(16 * 17, 151936, bf, 17)) == (2, 4, 4, 0)
     # the counters cover verify launches of up to 16384 rows (rows cut into slices
