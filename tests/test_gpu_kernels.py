@@ -1067,15 +1067,15 @@ def test_verify_update_merge_wave_past_the_counters():
 def test_verify_update_launch_counters_across_sizes():
     """Verify launches of at most 16384 rows tag each row's completion word with a
     per-row launch counter instead of clearing it.  One workspace serves launches
-    of 1024, 976, 1037 and 2048 rows with a merge wavefront and of 488 rows cut
+    of 1024, 976, 1037 and 2048 rows with a merge wavefront and of 427 rows cut
     into slices, in any order, and a zero fill between calls; every call matches
     the oracle, the workspace past the counters is zero after each, and each
     row's two counters equal the number of launches that held it since the last
     zero fill."""
     rng = np.random.default_rng(16384)
     V, k = 30011, 8
-    calls = [(16, 64), (8, 61), (16, 61), (17, 61), (32, 64), (16, 64), None, (16, 61), (16, 61)]
-    # every one tagged: 1024, 976, 1037 and 2048 rows with a merge wavefront, 488 rows cut into slices
+    calls = [(16, 64), (7, 61), (16, 61), (17, 61), (32, 64), (16, 64), None, (16, 61), (16, 61)]
+    # every one tagged: 1024, 976, 1037 and 2048 rows with a merge wavefront, 427 rows cut into slices
     plans = [L.graft_launch_plan(B * T1, V, L.DTYPE_BF16, T1) for B, T1 in [c for c in calls if c]]
     assert [(p["merge_wave"], p["groups_per_row"] > 1, p["launch_counters"]) for p in plans] == \
         [(1, False, 1), (0, True, 1)] + [(1, False, 1)] * 6
