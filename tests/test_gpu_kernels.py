@@ -161,6 +161,7 @@ def test_topk_prompt_sized_launch(dtype):
 @pytest.mark.parametrize("n,V,dtype,prob", [
     (430, 40000, "bf16", False),    # split into 3 slices, 13 blocks per wave: four
     (511, 40000, "bf16", False),    # whole rows, two on nearly every CU, 8 waves of ~10 blocks: four
+    (450, 20000, "f32", True),      # whole fp32 rows, two on nearly every CU, 8 waves of ~10 blocks: four
     (512, 40000, "bf16", True),     # one workgroup per row, 6 waves: four, with probabilities
     (300, 20000, "bf16", False),    # split, 5 blocks per wave: two
     (200, 30000, "bf16", True),     # whole rows, one workgroup per CU, 8 waves of ~7 blocks: four
