@@ -1607,6 +1607,7 @@ static int loads_for(int64_t n_rows, int V, int dtype, int groups, int S) {
 constexpr int64_t kCUs = 256;
 constexpr int kFewRowWaves = 8;
 constexpr int64_t kTwoRowsMin = 436;  // about 0.85 x two rows on every CU
+constexpr int64_t kSliceBlocksFor8 = 68, kSliceWavesMax = 4096;
 static int groups_per_row(int64_t n_rows, int V, int dtype) {
     if (n_rows <= 0 || n_rows >= kSplitBelowRows) return 1;
     if (n_rows <= kCUs && (kTargetWaves + n_rows - 1) / n_rows <= kMaxWavesPerRow) return 1;
@@ -1673,6 +1674,18 @@ TopkPlan plan_topk(int64_t n_rows, int V, int dtype) {
             p.groups = 1;
             p.splits = kFewRowWaves;
         }
+    }
+    // split bf16 rows: 8 waves per slice while every slice still holds at least
+    // 68 blocks and the launch stays within 4096 waves (122 rows: 13.76 against
+    // 14.14 us at V=151936, 13.26 against 13.65 at 140000, 14.43 against 15.52 at
+    // 180000; with fewer blocks the wave target's 4 waves do better: 12.38 against
+    // 12.68 us at 128256, 10.38 against 11.65 at 64000).  fp32 rows keep the wave
+    // target (122 rows of 151936: 19.53 against 19.30 us with 8 waves)
+    if (dtype == GRAFT_DTYPE_BF16 && p.groups > 1 && p.splits < kFewRowWaves) {
+        const int epg = dtype == GRAFT_DTYPE_BF16 ? 8 : 4;
+        const int64_t nblk = ((int64_t)V / epg + kWave - 1) / kWave;
+        const int64_t per_slice = (nblk + p.groups - 1) / p.groups;
+        if (per_slice >= kSliceBlocksFor8 && n_rows * p.groups * kFewRowWaves <= kSliceWavesMax) p.splits = kFewRowWaves;
     }
     p.loads = loads_for(n_rows, V, dtype, p.groups, p.splits);
     p.merge_wave = merge_wave_for(V, dtype, p.groups, p.splits);

@@ -305,6 +305,10 @@ def test_coordinators_are_bounded_whatever_the_batch():
     assert shape(L.graft_launch_plan(436, 151936, bf, 0)) == (8, 1, 4, 0)
     assert shape(L.graft_launch_plan(7 * 61, 151936, bf, 61))[1] > 1
     assert shape(L.graft_launch_plan(488, 10 ** 6, bf, 0))[1] > 1           # 8 waves would exceed the cap
+    # split bf16 rows: 8 waves per slice from 68 blocks per slice (122 rows at 151936), 4 below (128256); fp32 unchanged
+    assert shape(L.graft_launch_plan(2 * 61, 151936, bf, 61)) == (8, 4, 4, 0)
+    assert shape(L.graft_launch_plan(2 * 61, 128256, bf, 61)) == (4, 4, 4, 0)
+    assert shape(L.graft_launch_plan(2 * 61, 151936, L.DTYPE_F32, 61))[0] == 4
     assert shape(L.graft_launch_plan(256, 10 ** 6, bf, 0)) == (16, 1, 2, 0)   # 8 waves would exceed 127 blocks each
     assert shape(L.graft_launch_plan(16 * 17, 151936, bf, 17)) == (2, 4, 4, 0)
     # the counters cover verify launches of up to 16384 rows (rows cut into slices
